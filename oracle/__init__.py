@@ -1,0 +1,14 @@
+"""CPU oracle of the DSA forward path (float64 NumPy).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, the smoke check and the
+benchmark's CPU-baseline leg, never by the library.
+"""
+from .dsa_oracle import (OracleInputs, decode_bf16, decode_e4m3fn, decode, E4M3FN_TABLE,
+                         sequence_of, candidate_count, gather_rows, index_scores,
+                         query_index_operands, query_index_scores, topk, topk_padded,
+                         sparse_mla, query_attention, forward)
+
+__all__ = ["OracleInputs", "decode_bf16", "decode_e4m3fn", "decode", "E4M3FN_TABLE",
+           "sequence_of", "candidate_count", "gather_rows", "index_scores",
+           "query_index_operands", "query_index_scores", "topk", "topk_padded", "sparse_mla",
+           "query_attention", "forward"]

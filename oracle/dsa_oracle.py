@@ -1,0 +1,292 @@
+"""CPU oracle of the DeepSeek Sparse Attention (DSA) forward path, in float64 NumPy.
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  It shares no code with
+the HIP library (its own bf16 and e4m3fn decoders, its own cache addressing)
+and the library never calls it.
+
+Sources (the pages this follows; cited below by tag):
+
+* [ZS]  "DeepSeek V3.2: How Far Can Open Models Go If You Actually Try?"
+        (zeroshot.it.com) -- section 3.1: the indexer score equation (eq. I),
+        the selection-then-attention equation (eq. U) and the MQA-mode note;
+        section 3.4: short prompts behave like dense masked attention.
+* [LD]  "DeepSeek-V3.2: Pushing the Frontier of Open Large Language Models"
+        (papers.lunadong.com summary) -- System Modules (indexer scores the
+        preceding tokens; a top-k operation selects; MLA in MQA mode attends),
+        Key Hyperparameters (k = 2048).
+* [BT]  baseten.co "DeepSeek-V3.2" -- section (1) DSA + MLA: the indexer and
+        selector amount to an attention mask over past tokens.
+
+Every step is the plain definition:
+
+1. decode the input bytes to float64 exactly (bf16: bits << 16; e4m3fn: the
+   OCP format, 1 sign, 4 exponent bits biased by 7, 3 mantissa bits,
+   subnormals m * 2^-9, S.1111.111 NaN);
+2. query t of sequence b at position p sees the candidates s = 0..p
+   (the query's own position included);
+3. eq. I:  I(t,s) = sum_j w(t,j) * ReLU(q(t,j) . k(s));  with an e4m3fn
+   indexer the operands are dequantised first, q = q8 * q_scale(t,j),
+   k = k8 * k_scale(s);
+4. top-k: the first min(k, n) candidates in the order (score descending,
+   position ascending);
+5. eq. U in MQA mode: every head h attends over the selected latent rows c(s)
+   with logits sm_scale * q(t,h) . c(s) over all D dims and values c(s)[:Dv];
+   softmax; lse = max + ln(sum exp(z - max)).
+
+Readings where the pages are silent are stated at each function.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# 1. exact decoding of the element types
+# --------------------------------------------------------------------------
+
+def decode_bf16(bits) -> np.ndarray:
+    """bfloat16 bit patterns -> float64.  A bf16 value is the top half of an fp32."""
+    b = np.asarray(bits).astype(np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):                 # signalling-NaN patterns stay NaN
+        return b.view(np.float32).astype(np.float64)
+
+
+def _build_e4m3fn_table() -> np.ndarray:
+    """All 256 OCP FP8 E4M3 ("fn": no infinities, one NaN mantissa) values."""
+    table = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        sign = -1.0 if (code >> 7) & 1 else 1.0
+        exp = (code >> 3) & 0xF
+        man = code & 0x7
+        if exp == 0xF and man == 0x7:
+            table[code] = math.nan
+        elif exp == 0:
+            table[code] = sign * man * 2.0 ** -9          # subnormal: (m/8) * 2^(1-7)
+        else:
+            table[code] = sign * (1.0 + man / 8.0) * 2.0 ** (exp - 7)
+    return table
+
+
+E4M3FN_TABLE = _build_e4m3fn_table()
+
+
+def decode_e4m3fn(codes) -> np.ndarray:
+    return E4M3FN_TABLE[np.asarray(codes).astype(np.uint8)]
+
+
+def decode(raw, dtype: str) -> np.ndarray:
+    """Raw element bytes of type ``dtype`` ("f32" | "bf16" | "fp8") -> float64."""
+    if dtype == "bf16":
+        return decode_bf16(raw)
+    if dtype == "fp8":
+        return decode_e4m3fn(raw)
+    if dtype == "f32":
+        return np.asarray(raw, dtype=np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def _finite(x: np.ndarray, what: str) -> np.ndarray:
+    if not np.all(np.isfinite(x)):
+        raise ValueError(f"oracle read a non-finite {what}: inputs must be finite")
+    return x
+
+
+# --------------------------------------------------------------------------
+# 2. inputs and cache addressing
+# --------------------------------------------------------------------------
+
+@dataclass
+class OracleInputs:
+    """Host copies of the bytes the library receives (see workloads.raw_numpy)."""
+    mode: str                       # "prefill": every query reads sequence 0; "decode": query t reads sequence t
+    q_pos: np.ndarray               # int [T]
+    block_table: Optional[np.ndarray]   # int [B, max_blocks] or None (contiguous)
+    block_size: int
+    index_dtype: str
+    q_idx: np.ndarray               # raw [T, H_I, d_I]
+    q_scale: Optional[np.ndarray]   # f32 [T, H_I] (fp8 only)
+    w: np.ndarray                   # f32 [T, H_I]
+    k_cache: np.ndarray             # raw [B, Lmax, d_I] or [N_blk, bs, d_I]
+    k_scale: Optional[np.ndarray]   # f32 [B, Lmax] or [N_blk, bs] (fp8 only)
+    mla_dtype: str
+    q: np.ndarray                   # raw [T, H, D]
+    kv_cache: np.ndarray            # raw [B, Lmax, D] or [N_blk, bs, D]
+    topk: int
+    sm_scale: float
+    v_dim: int
+
+    @property
+    def num_q(self) -> int:
+        return int(self.q_pos.shape[0])
+
+
+def sequence_of(inp: OracleInputs, t: int) -> int:
+    return t if inp.mode == "decode" else 0
+
+
+def candidate_count(inp: OracleInputs, t: int) -> int:
+    """Reading: a query sees every earlier token and itself, s = 0..pos (n = pos + 1)."""
+    return max(int(inp.q_pos[t]) + 1, 0)
+
+
+def gather_rows(cache: np.ndarray, inp: OracleInputs, b: int, positions: np.ndarray) -> np.ndarray:
+    """Raw cache rows of sequence ``b`` at logical ``positions``.
+
+    Contiguous cache: ``cache[b, s]``.  Paged cache: logical position s lives in
+    physical block ``block_table[b, s // bs]`` at offset ``s % bs``.
+    """
+    positions = np.asarray(positions, dtype=np.int64)
+    if inp.block_table is None:
+        return cache[b][positions]
+    bs = inp.block_size
+    blocks = np.asarray(inp.block_table[b], dtype=np.int64)[positions // bs]
+    if np.any(blocks < 0) or np.any(blocks >= cache.shape[0]):
+        raise ValueError("block table entry out of range for a candidate position")
+    return cache[blocks, positions % bs]
+
+
+def gather_scales(scale: np.ndarray, inp: OracleInputs, b: int, positions: np.ndarray) -> np.ndarray:
+    positions = np.asarray(positions, dtype=np.int64)
+    if inp.block_table is None:
+        return scale[b][positions]
+    bs = inp.block_size
+    blocks = np.asarray(inp.block_table[b], dtype=np.int64)[positions // bs]
+    return scale[blocks, positions % bs]
+
+
+# --------------------------------------------------------------------------
+# 3. the lightning indexer, eq. I  [ZS 3.1; LD System Modules]
+# --------------------------------------------------------------------------
+
+def index_scores(q_t: np.ndarray, w_t: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """eq. I for one query: I(s) = sum_j w_j * ReLU(q_j . k_s).
+
+    q_t [H_I, d_I], w_t [H_I], keys [n, d_I], all float64 -> I [n].
+    Reading: no extra scale or normalisation inside the sum; w may have any sign.
+    """
+    dots = q_t @ keys.T                      # [H_I, n]: q(t,j) . k(s)
+    return w_t @ np.maximum(dots, 0.0)       # sum over heads of w * ReLU
+
+
+def query_index_operands(inp: OracleInputs, t: int):
+    """Dequantised float64 (q_t [H_I,d_I], w_t [H_I], keys [n,d_I]) for query t."""
+    b = sequence_of(inp, t)
+    n = candidate_count(inp, t)
+    pos = np.arange(n)
+    q_t = decode(inp.q_idx[t], inp.index_dtype)
+    keys = decode(gather_rows(inp.k_cache, inp, b, pos), inp.index_dtype)
+    w_t = np.asarray(inp.w[t], dtype=np.float64)
+    if inp.index_dtype == "fp8":
+        # "runs in FP8" [ZS 3.1]: e4m3fn operands with per-row fp32 scales; dequantise, then eq. I.
+        q_t = q_t * np.asarray(inp.q_scale[t], dtype=np.float64)[:, None]
+        keys = keys * gather_scales(inp.k_scale, inp, b, pos).astype(np.float64)[:, None]
+    _finite(q_t, "indexer query")
+    _finite(keys, "indexer key")
+    _finite(w_t, "head weight")
+    return q_t, w_t, keys
+
+
+def query_index_scores(inp: OracleInputs, t: int) -> np.ndarray:
+    """I(t, s) for s = 0..pos_t (float64 [n_t])."""
+    q_t, w_t, keys = query_index_operands(inp, t)
+    return index_scores(q_t, w_t, keys)
+
+
+# --------------------------------------------------------------------------
+# 4. fine-grained top-k selection  [ZS 3.1 eq. U; LD "Top-k operation"]
+# --------------------------------------------------------------------------
+
+def topk(scores: np.ndarray, k: int) -> np.ndarray:
+    """Positions of the min(k, n) largest scores, in order (score desc, position asc).
+
+    Readings: exactly min(k, n) positions even when scores tie (ties go to the
+    lower position); -0.0 counts as equal to +0.0; when n <= k every candidate
+    is selected (dense behaviour for short prompts, [ZS 3.4]).
+    """
+    s = np.asarray(scores, dtype=np.float64) + 0.0          # -0.0 + 0.0 == +0.0
+    _finite(s, "score")
+    m = min(int(k), s.shape[0])
+    order = np.argsort(-s, kind="stable")                    # stable: equal keys keep position order
+    return order[:m].astype(np.int64)
+
+
+def topk_padded(scores: np.ndarray, k: int) -> np.ndarray:
+    """``topk`` written into a length-k int row padded with -1."""
+    out = np.full(int(k), -1, dtype=np.int64)
+    sel = topk(scores, k)
+    out[: sel.shape[0]] = sel
+    return out
+
+
+# --------------------------------------------------------------------------
+# 5. sparse MLA in MQA mode, eq. U  [ZS 3.1; LD Novel Architectural Elements]
+# --------------------------------------------------------------------------
+
+def sparse_mla(q_t: np.ndarray, rows: np.ndarray, v_dim: int, sm_scale: float):
+    """Attention of every head of one query over the selected latent rows.
+
+    q_t [H, D], rows [m, D] float64.  Every head shares the same rows (MQA
+    mode): the key is the whole D-wide row, the value its first ``v_dim``
+    entries.  Returns (out [H, v_dim], lse [H]).  An empty selection gives a
+    zero output and lse = -inf.
+    """
+    H = q_t.shape[0]
+    m = rows.shape[0]
+    if m == 0:
+        return np.zeros((H, v_dim)), np.full(H, -np.inf)
+    z = sm_scale * (q_t @ rows.T)                  # [H, m] logits
+    zmax = z.max(axis=1, keepdims=True)
+    e = np.exp(z - zmax)
+    denom = e.sum(axis=1, keepdims=True)
+    p = e / denom                                  # softmax over the selected rows
+    out = p @ rows[:, :v_dim]
+    lse = zmax[:, 0] + np.log(denom[:, 0])
+    return out, lse
+
+
+def query_attention(inp: OracleInputs, t: int, selected) -> tuple:
+    """eq. U for query t over the given selected positions (entries < 0 ignored)."""
+    sel = np.asarray(selected, dtype=np.int64)
+    sel = sel[sel >= 0]
+    n = candidate_count(inp, t)
+    if np.any(sel >= n):
+        raise ValueError("selected position outside the causal candidates")
+    b = sequence_of(inp, t)
+    q_t = _finite(decode(inp.q[t], inp.mla_dtype), "MLA query")
+    rows = _finite(decode(gather_rows(inp.kv_cache, inp, b, sel), inp.mla_dtype), "latent row")
+    return sparse_mla(q_t, rows, inp.v_dim, inp.sm_scale)
+
+
+# --------------------------------------------------------------------------
+# the whole path
+# --------------------------------------------------------------------------
+
+def forward(inp: OracleInputs, rows=None, keep_scores: bool = False) -> dict:
+    """Indexer -> top-k -> sparse MLA for the query rows ``rows`` (default: all).
+
+    Returns a dict with ``rows``, ``idx`` [R, k] (selection order, -1 padded),
+    ``out`` [R, H, Dv], ``lse`` [R, H] and, when asked, ``scores`` (list of [n_t]).
+    """
+    rows = list(range(inp.num_q)) if rows is None else [int(r) for r in rows]
+    k = inp.topk
+    H = inp.q.shape[1]
+    idx = np.full((len(rows), k), -1, dtype=np.int64)
+    out = np.zeros((len(rows), H, inp.v_dim))
+    lse = np.zeros((len(rows), H))
+    scores = []
+    for i, t in enumerate(rows):
+        s = query_index_scores(inp, t)
+        sel = topk(s, k)
+        idx[i, : sel.shape[0]] = sel
+        out[i], lse[i] = query_attention(inp, t, sel)
+        if keep_scores:
+            scores.append(s)
+    res = {"rows": rows, "idx": idx, "out": out, "lse": lse}
+    if keep_scores:
+        res["scores"] = scores
+    return res

@@ -1,0 +1,385 @@
+"""Pins of the CPU oracle to facts fixed outside it.
+
+Each ``pin_*`` takes the oracle module and raises ``AssertionError`` when the
+oracle disagrees with: hand-derived worked examples (tests/golden), closed
+forms, brute force on tiny inputs, an independent library routine (torch's
+dtype casts, torch's scaled_dot_product_attention in float64), or an
+invariant of the definition.  ``test_oracle.py`` runs every pin on the real
+oracle; ``test_oracle_mutations.py`` runs them on deliberately broken copies
+and requires each break to be caught.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+from workloads import generate
+from tests.helpers import small_workload, to_oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _close(a, b, tol=1e-12, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} != {b.shape}"
+    err = np.max(np.abs(a - b) / (1.0 + np.abs(b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max rel err {err:.3e} > {tol}"
+
+
+# ---------------------------------------------------------------- decoding
+
+def pin_bf16_decode(o):
+    """All 65536 bf16 patterns against torch's bfloat16 -> float64 cast."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = o.decode_bf16(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan), "bf16 NaN patterns"
+    assert np.array_equal(got[~nan], ref[~nan]), "bf16 values"
+    assert np.signbit(got[0x8000]) and got[0x8000] == 0.0
+
+
+def pin_e4m3_table(o):
+    """All 256 e4m3fn codes against torch.float8_e4m3fn -> float64 (an independent implementation)."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = o.decode_e4m3fn(codes)
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert np.array_equal(np.isnan(got), nan), "e4m3fn NaN codes"
+    assert np.array_equal(got[~nan], ref[~nan]), "e4m3fn values"
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x38] == 1.0
+
+
+# ---------------------------------------------------------------- indexer (eq. I)
+
+def pin_indexer_golden(o):
+    d = _golden("indexer_hand.json")
+    for c in d["cases"]:
+        got = o.index_scores(np.array(c["q"], float), np.array(c["w"], float),
+                             np.array(c["keys"], float))
+        assert np.array_equal(got, np.array(c["expected"], float)), c["name"]
+    for c in d["fp8_cases"]:
+        n = len(c["k_codes"])
+        inp = o.OracleInputs(
+            mode="decode", q_pos=np.array([n - 1]), block_table=None, block_size=64,
+            index_dtype="fp8", q_idx=np.array([c["q_codes"]], np.uint8),
+            q_scale=np.array([c["q_scale"]], np.float32), w=np.array([c["w"]], np.float32),
+            k_cache=np.array([c["k_codes"]], np.uint8), k_scale=np.array([c["k_scale"]], np.float32),
+            mla_dtype="f32", q=np.zeros((1, 1, 2), np.float32), kv_cache=np.zeros((1, n, 2), np.float32),
+            topk=1, sm_scale=1.0, v_dim=1)
+        got = o.query_index_scores(inp, 0)
+        assert np.array_equal(got, np.array(c["expected"], float)), c["name"]
+
+
+def pin_indexer_bruteforce(o):
+    """Explicit loops over heads, dims and keys on tiny random inputs."""
+    rng = np.random.default_rng(7)
+    for _ in range(25):
+        H_I, d_I, n = rng.integers(1, 5), rng.integers(1, 6), rng.integers(1, 8)
+        q = rng.normal(size=(H_I, d_I))
+        w = rng.normal(size=H_I)
+        keys = rng.normal(size=(n, d_I))
+        want = []
+        for s in range(n):
+            tot = 0.0
+            for j in range(H_I):
+                dot = 0.0
+                for dd in range(d_I):
+                    dot += q[j, dd] * keys[s, dd]
+                tot += w[j] * (dot if dot > 0.0 else 0.0)
+            want.append(tot)
+        _close(o.index_scores(q, w, keys), want, 1e-12, "indexer brute force")
+
+
+def pin_indexer_homogeneity(o):
+    """ReLU is positively homogeneous: scaling a key by c > 0 scales its score by c;
+    moving a positive factor from a head's query to its weight changes nothing;
+    scaling all weights by c > 0 keeps the top-k; the folded fp8 form
+    k_scale(s) * sum_j (w_j q_scale_j) ReLU(q8_j . k8_s) equals dequantise-first."""
+    rng = np.random.default_rng(8)
+    q = rng.normal(size=(4, 6))
+    w = rng.uniform(-1, 1, size=4)
+    keys = rng.normal(size=(9, 6))
+    base = o.index_scores(q, w, keys)
+    c = rng.uniform(0.1, 5.0, size=9)
+    _close(o.index_scores(q, w, keys * c[:, None]), base * c, 1e-12, "key scaling")
+    f = rng.uniform(0.1, 5.0, size=4)
+    _close(o.index_scores(q * f[:, None], w / f, keys), base, 1e-12, "query/weight factor")
+    wp = np.abs(w)
+    sel = o.topk(o.index_scores(q, wp, keys), 4)
+    sel2 = o.topk(o.index_scores(q, 3.7 * wp, keys), 4)
+    assert np.array_equal(sel, sel2)
+
+    wl = small_workload(mode="decode", num_seqs=2, length=33, H_I=4, d_I=16, index_dtype="fp8")
+    oi = to_oracle(generate(wl, "cpu"))
+    for t in range(2):
+        got = o.query_index_scores(oi, t)
+        n = int(oi.q_pos[t]) + 1
+        q8 = o.decode_e4m3fn(oi.q_idx[t])
+        k8 = o.decode_e4m3fn(oi.k_cache[t, :n])
+        ws = oi.w[t].astype(float) * oi.q_scale[t].astype(float)
+        folded = oi.k_scale[t, :n].astype(float) * (ws @ np.maximum(q8 @ k8.T, 0.0))
+        _close(got, folded, 1e-12, "fp8 folded form")
+
+
+def pin_indexer_single_head_textbook(o):
+    """H_I = 1, w = 1: I = ReLU(q . k); its top-k is a plain stable sort by (-score, position)."""
+    rng = np.random.default_rng(9)
+    q = rng.normal(size=(1, 5))
+    keys = rng.normal(size=(40, 5))
+    keys[::7] = -keys[::7]
+    I = o.index_scores(q, np.ones(1), keys)
+    dots = [float(np.dot(q[0], keys[s])) for s in range(40)]
+    _close(I, [max(d, 0.0) for d in dots], 1e-12, "single head")
+    want = sorted(range(40), key=lambda s: (-max(dots[s], 0.0), s))[:12]
+    assert list(o.topk(I, 12)) == want
+
+
+# ---------------------------------------------------------------- top-k
+
+def pin_topk_golden(o):
+    for c in _golden("topk_hand.json")["cases"]:
+        got = list(o.topk(np.array(c["scores"], float), c["k"]))
+        assert got == c["expected"], (c, got)
+        pad = o.topk_padded(np.array(c["scores"], float), c["k"])
+        assert list(pad[: len(c["expected"])]) == c["expected"] and all(pad[len(c["expected"]):] == -1)
+
+
+def pin_topk_bruteforce(o):
+    """Every subset of size min(k, n) for n <= 9: the selection has the largest score
+    multiset, and among those the lexicographically smallest position tuple."""
+    rng = np.random.default_rng(10)
+    for n in range(0, 10):
+        for _ in range(4):
+            s = rng.integers(-2, 3, size=n).astype(float)
+            for k in range(1, n + 2):
+                m = min(k, n)
+                best = None
+                for sub in itertools.combinations(range(n), m):
+                    key = (sorted((s[i] for i in sub), reverse=True), [-i for i in sub])
+                    if best is None or key > best[0]:
+                        best = (key, sub)
+                got = o.topk(s, k)
+                assert sorted(got.tolist()) == list(best[1]), (s, k, got, best)
+                order = [(-s[i], i) for i in got]
+                assert order == sorted(order), "selection order"
+
+
+def certificate(scores, sel, k):
+    """The O(n) top-k certificate (no sort): size, uniqueness, range, separation, ties."""
+    s = np.asarray(scores, float) + 0.0
+    n = s.shape[0]
+    sel = np.asarray(sel, dtype=np.int64)
+    m = min(k, n)
+    assert sel.shape[0] == m, f"selected {sel.shape[0]} != {m}"
+    assert np.unique(sel).shape[0] == m, "duplicate selection"
+    assert np.all((sel >= 0) & (sel < n)), "selection out of range"
+    if m == n:
+        return
+    mask = np.zeros(n, bool)
+    mask[sel] = True
+    lo = s[mask].min()
+    hi = s[~mask].max()
+    assert lo >= hi, f"separation {lo} < {hi}"
+    if lo == hi:
+        assert np.max(np.nonzero(mask & (s == lo))[0]) < np.min(np.nonzero(~mask & (s == lo))[0]), "tie order"
+
+
+def pin_topk_certificate(o):
+    rng = np.random.default_rng(11)
+    for _ in range(40):
+        n = int(rng.integers(1, 300))
+        s = rng.normal(size=n)
+        if rng.random() < 0.5:
+            s = np.round(s * 2) / 2                       # many ties
+        k = int(rng.integers(1, 320))
+        certificate(s, o.topk(s, k), k)
+
+
+# ---------------------------------------------------------------- sparse MLA (eq. U)
+
+def pin_mla_golden(o):
+    for c in _golden("mla_hand.json")["cases"]:
+        out, lse = o.sparse_mla(np.array(c["q"], float), np.array(c["rows"], float),
+                                c["v_dim"], c["sm_scale"])
+        _close(out, c["expected_out"], 1e-14, c["name"])
+        _close(lse, c["expected_lse"], 1e-14, c["name"])
+
+
+def pin_mla_closed_forms(o):
+    rng = np.random.default_rng(12)
+    H, D, Dv, m = 3, 10, 6, 7
+    rows = rng.normal(size=(m, D))
+    out, lse = o.sparse_mla(np.zeros((H, D)), rows, Dv, 0.3)            # q = 0: plain mean
+    _close(out, np.tile(rows[:, :Dv].mean(axis=0), (H, 1)), 1e-13, "q=0 mean")
+    _close(lse, np.full(H, math.log(m)), 1e-13, "q=0 lse")
+    same = np.tile(rows[:1], (m, 1))                                    # identical rows
+    out, _ = o.sparse_mla(rng.normal(size=(H, D)), same, Dv, 0.3)
+    _close(out, np.tile(rows[0, :Dv], (H, 1)), 1e-13, "identical rows")
+    qh = rng.normal(size=(H, D))                                        # one row
+    out, lse = o.sparse_mla(qh, rows[2:3], Dv, 0.3)
+    assert np.array_equal(out, np.tile(rows[2, :Dv], (H, 1)))
+    _close(lse, 0.3 * qh @ rows[2], 1e-13, "one-row lse")
+    out, lse = o.sparse_mla(qh, rows[:0], Dv, 0.3)                     # empty
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+    out, _ = o.sparse_mla(rng.normal(size=(H, D)) * 4, rows, Dv, 1.0)   # convex hull
+    lo, hi = rows[:, :Dv].min(axis=0), rows[:, :Dv].max(axis=0)
+    assert np.all(out >= lo - 1e-12) and np.all(out <= hi + 1e-12)
+
+
+def _sdpa(q, rows, Dv, scale, mask):
+    """torch float64 SDPA, MQA: every head reads the same rows; mask [n] True = attend."""
+    H, D = q.shape
+    n = rows.shape[0]
+    qt = torch.from_numpy(q).reshape(1, H, 1, D)
+    kt = torch.from_numpy(rows).reshape(1, 1, n, D).expand(1, H, n, D)
+    vt = torch.from_numpy(np.ascontiguousarray(rows[:, :Dv])).reshape(1, 1, n, Dv).expand(1, H, n, Dv)
+    mt = torch.from_numpy(np.asarray(mask, bool)).reshape(1, 1, 1, n)
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mt, scale=scale)
+    logits = (qt @ kt.transpose(-1, -2)) * scale
+    lse = torch.logsumexp(logits.masked_fill(~mt, -math.inf), dim=-1)
+    return out.reshape(H, Dv).numpy(), lse.reshape(H).numpy()
+
+
+def pin_mla_dense_masked(o):
+    """Sparse attention over the chosen rows == dense attention over every candidate
+    with a mask equal to the chosen set (baseten (1): the selector acts as a mask)."""
+    rng = np.random.default_rng(13)
+    for _ in range(10):
+        H, D, Dv, n = 4, 12, 8, int(rng.integers(2, 40))
+        q = rng.normal(size=(H, D))
+        rows = rng.normal(size=(n, D))
+        sel = np.sort(rng.choice(n, size=int(rng.integers(1, n + 1)), replace=False))
+        mask = np.zeros(n, bool)
+        mask[sel] = True
+        want_out, want_lse = _sdpa(q, rows, Dv, 0.37, mask)
+        out, lse = o.sparse_mla(q, rows[sel], Dv, 0.37)
+        _close(out, want_out, 1e-12, "masked dense out")
+        _close(lse, want_lse, 1e-12, "masked dense lse")
+
+
+# ---------------------------------------------------------------- whole path
+
+def pin_forward_dense_causal(o):
+    """k >= n: every causal candidate is selected and the path is dense causal MLA
+    (short prompts behave like dense attention, zeroshot section 3.4)."""
+    wl = small_workload(mode="prefill", length=24, k=32, H=3, D=10, Dv=6)
+    oi = to_oracle(generate(wl, "cpu"))
+    res = o.forward(oi)
+    kv = oi.kv_cache[0].astype(float)
+    for t in range(24):
+        sel = res["idx"][t]
+        assert sorted(sel[sel >= 0].tolist()) == list(range(t + 1)), f"row {t} selection"
+        mask = np.arange(24) <= t
+        want_out, want_lse = _sdpa(oi.q[t].astype(float), kv, 6, oi.sm_scale, mask)
+        _close(res["out"][t], want_out, 1e-12, f"row {t} dense causal")
+        _close(res["lse"][t], want_lse, 1e-12, f"row {t} lse")
+    # the first query sees only itself
+    assert res["idx"][0, 0] == 0 and np.all(res["idx"][0, 1:] == -1)
+    assert np.array_equal(res["out"][0], np.tile(kv[0, :6], (3, 1)))
+
+
+def pin_forward_mask_consistency(o):
+    """k < n: the output equals dense attention masked to the oracle's own selection,
+    and the selection passes the top-k certificate against the oracle's scores."""
+    wl = small_workload(mode="prefill", length=50, k=9, H=2, D=12, Dv=8)
+    oi = to_oracle(generate(wl, "cpu"))
+    res = o.forward(oi, keep_scores=True)
+    kv = oi.kv_cache[0].astype(float)
+    for t in range(50):
+        sel = res["idx"][t]
+        sel = sel[sel >= 0]
+        certificate(res["scores"][t], sel, 9)
+        mask = np.zeros(50, bool)
+        mask[sel] = True
+        want_out, _ = _sdpa(oi.q[t].astype(float), kv, 8, oi.sm_scale, mask)
+        _close(res["out"][t], want_out, 1e-12, f"row {t}")
+
+
+def pin_causality_poison(o):
+    """Cache slots past each sequence's length hold NaN (generator poison): the oracle
+    must never read them, and replacing them by huge values changes nothing."""
+    wl = small_workload(mode="decode", num_seqs=3, length=30, k=5)
+    inp = generate(wl, "cpu", lengths=[7, 30, 18])
+    oi = to_oracle(inp)
+    assert np.isnan(oi.kv_cache[0, 7:]).all() and np.isnan(oi.k_cache[2, 18:]).all()
+    a = o.forward(oi)
+    oi.kv_cache = np.where(np.isnan(oi.kv_cache), np.float32(1e30), oi.kv_cache)
+    oi.k_cache = np.where(np.isnan(oi.k_cache), np.float32(1e30), oi.k_cache)
+    b = o.forward(oi)
+    for key in ("idx", "out", "lse"):
+        assert np.array_equal(a[key], b[key]), key
+    assert np.all(a["idx"][0][a["idx"][0] >= 0] < 7)
+
+
+def pin_paged_equals_contiguous(o):
+    """The same logical data laid out in permuted 4-token blocks gives identical results."""
+    rng = np.random.default_rng(14)
+    wl = small_workload(mode="decode", num_seqs=3, length=29, k=6)
+    oi = to_oracle(generate(wl, "cpu", lengths=[29, 13, 21]))
+    a = o.forward(oi)
+    bs = 4
+    B, L = oi.kv_cache.shape[:2]
+    nb = (L + bs - 1) // bs
+    perm = rng.permutation(B * nb)
+    table = perm.reshape(B, nb)
+    kc = np.full((B * nb, bs) + oi.k_cache.shape[2:], np.nan, oi.k_cache.dtype)
+    vc = np.full((B * nb, bs) + oi.kv_cache.shape[2:], np.nan, oi.kv_cache.dtype)
+    for b in range(B):
+        for s in range(L):
+            kc[table[b, s // bs], s % bs] = oi.k_cache[b, s]
+            vc[table[b, s // bs], s % bs] = oi.kv_cache[b, s]
+    oi.block_table, oi.block_size, oi.k_cache, oi.kv_cache = table, bs, kc, vc
+    b_ = o.forward(oi)
+    for key in ("idx", "out", "lse"):
+        assert np.array_equal(a[key], b_[key]), key
+
+
+def pin_prefill_row_equals_decode(o):
+    """Prefill row t equals a decode step whose context is the first t+1 tokens."""
+    wl = small_workload(mode="prefill", length=30, k=7)
+    oi = to_oracle(generate(wl, "cpu"))
+    a = o.forward(oi)
+    for t in (0, 6, 7, 8, 29):
+        d = o.OracleInputs(
+            mode="decode", q_pos=np.array([t]), block_table=None, block_size=oi.block_size,
+            index_dtype=oi.index_dtype, q_idx=oi.q_idx[t:t + 1], q_scale=None, w=oi.w[t:t + 1],
+            k_cache=oi.k_cache[:, : t + 1], k_scale=None, mla_dtype=oi.mla_dtype, q=oi.q[t:t + 1],
+            kv_cache=oi.kv_cache[:, : t + 1], topk=oi.topk, sm_scale=oi.sm_scale, v_dim=oi.v_dim)
+        b = o.forward(d)
+        for key in ("idx", "out", "lse"):
+            assert np.array_equal(a[key][t], b[key][0]), (t, key)
+
+
+def pin_permutation_invariance(o):
+    """Permuting a decode context (keys and latents together) permutes the selected
+    positions and leaves the attention output unchanged."""
+    rng = np.random.default_rng(15)
+    wl = small_workload(mode="decode", num_seqs=1, length=31, k=8)
+    oi = to_oracle(generate(wl, "cpu"))
+    a = o.forward(oi)
+    perm = rng.permutation(31)
+    kc = np.empty_like(oi.k_cache)
+    vc = np.empty_like(oi.kv_cache)
+    kc[0, perm] = oi.k_cache[0]
+    vc[0, perm] = oi.kv_cache[0]
+    oi.k_cache, oi.kv_cache = kc, vc
+    b = o.forward(oi)
+    assert sorted(perm[a["idx"][0]].tolist()) == sorted(b["idx"][0].tolist())
+    _close(a["out"], b["out"], 1e-12, "permuted out")
+    _close(a["lse"], b["lse"], 1e-12, "permuted lse")
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

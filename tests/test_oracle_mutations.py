@@ -1,0 +1,134 @@
+"""Plants plausible mistakes in the oracle (on the CPU) and requires the pins to catch each.
+
+A mutation replaces one function or table of the oracle module; the pins run
+against the mutated module and at least one must fail."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle.dsa_oracle as od
+from tests import pins
+
+
+def _no_relu(q, w, keys):
+    return w @ (q @ keys.T)
+
+
+def _relu_after_weight(q, w, keys):
+    return np.maximum(w[:, None] * (q @ keys.T), 0.0).sum(axis=0)
+
+
+def _no_weight(q, w, keys):
+    return np.maximum(q @ keys.T, 0.0).sum(axis=0)
+
+
+def _key_index_swapped(q, w, keys):
+    return w @ np.maximum(q @ keys[::-1].T, 0.0)
+
+
+def _ties_high(scores, k):
+    s = np.asarray(scores, float) + 0.0
+    n = s.shape[0]
+    order = n - 1 - np.argsort(-s[::-1], kind="stable")
+    return order[: min(k, n)].astype(np.int64)
+
+
+def _k_minus_one(scores, k):
+    s = np.asarray(scores, float) + 0.0
+    return np.argsort(-s, kind="stable")[: max(min(k, s.shape[0]) - 1, 0)].astype(np.int64)
+
+
+def _smallest(scores, k):
+    s = np.asarray(scores, float) + 0.0
+    return np.argsort(s, kind="stable")[: min(k, s.shape[0])].astype(np.int64)
+
+
+def _mla_value_tail(q, rows, v_dim, sm):
+    r = rows.copy()
+    r[:, :v_dim] = rows[:, rows.shape[1] - v_dim:]
+    return od.__dict__["_orig_sparse_mla"](q, r, v_dim, sm)
+
+
+def _mla_no_rope(q, rows, v_dim, sm):
+    q2 = q.copy()
+    q2[:, v_dim:] = 0.0
+    return od.__dict__["_orig_sparse_mla"](q2, rows, v_dim, sm)
+
+
+def _mla_no_scale(q, rows, v_dim, sm):
+    return od.__dict__["_orig_sparse_mla"](q, rows, v_dim, 1.0)
+
+
+def _mla_lse_log2(q, rows, v_dim, sm):
+    out, lse = od.__dict__["_orig_sparse_mla"](q, rows, v_dim, sm)
+    return out, lse / math.log(2.0)
+
+
+def _exclude_self(inp, t):
+    return max(int(inp.q_pos[t]), 0)
+
+
+def _bias8_table():
+    t = od.E4M3FN_TABLE.copy()
+    finite = np.isfinite(t)
+    t[finite] = t[finite] / 2.0
+    return t
+
+
+def _fp8_no_kscale(inp, t):
+    q_t, w_t, keys = od.__dict__["_orig_query_index_operands"](inp, t)
+    if inp.index_dtype == "fp8":
+        b = od.sequence_of(inp, t)
+        n = od.candidate_count(inp, t)
+        keys = od.decode(od.gather_rows(inp.k_cache, inp, b, np.arange(n)), "fp8")
+    return q_t, w_t, keys
+
+
+def _paged_ignores_table(cache, inp, b, positions):
+    positions = np.asarray(positions, dtype=np.int64)
+    if inp.block_table is None:
+        return cache[b][positions]
+    bs = inp.block_size
+    nb = inp.block_table.shape[1]
+    return cache[b * nb + positions // bs, positions % bs]
+
+
+def _bf16_truncated_low(bits):
+    b = np.asarray(bits).astype(np.uint16).astype(np.uint32) << np.uint32(15)
+    return b.view(np.float32).astype(np.float64)
+
+
+MUTATIONS = {
+    "indexer_no_relu": ("index_scores", _no_relu),
+    "indexer_relu_after_weight": ("index_scores", _relu_after_weight),
+    "indexer_no_weight": ("index_scores", _no_weight),
+    "indexer_key_index_swapped": ("index_scores", _key_index_swapped),
+    "topk_ties_to_higher_position": ("topk", _ties_high),
+    "topk_one_short": ("topk", _k_minus_one),
+    "topk_smallest": ("topk", _smallest),
+    "mla_value_from_tail": ("sparse_mla", _mla_value_tail),
+    "mla_key_without_rope": ("sparse_mla", _mla_no_rope),
+    "mla_missing_scale": ("sparse_mla", _mla_no_scale),
+    "mla_lse_base2": ("sparse_mla", _mla_lse_log2),
+    "candidates_exclude_self": ("candidate_count", _exclude_self),
+    "e4m3_exponent_bias_8": ("E4M3FN_TABLE", _bias8_table()),
+    "fp8_key_scale_dropped": ("query_index_operands", _fp8_no_kscale),
+    "paged_ignores_block_table": ("gather_rows", _paged_ignores_table),
+    "bf16_wrong_shift": ("decode_bf16", _bf16_truncated_low),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, repl = MUTATIONS[name]
+    monkeypatch.setattr(od, "_orig_sparse_mla", od.sparse_mla, raising=False)
+    monkeypatch.setattr(od, "_orig_query_index_operands", od.query_index_operands, raising=False)
+    monkeypatch.setattr(od, attr, repl)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(od)
+        except Exception as e:           # AssertionError or a crash both count as caught
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"mutation {name} passed every pin"
