@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Throughput of the DSA forward path (indexer -> top-k -> sparse MLA) on one MI355X.
+
+A step is one dsa_forward call over one batch of seeded synthetic inputs that
+are resident in HBM before timing starts.  The default workload is the
+long-context decode batch: 32 sequences, context ~ U[32768, 131072], paged
+64-token blocks, k = 2048, H_I = 64, d_I = 128, H = 128, D = 576, Dv = 512,
+bf16.  Prints one JSON line (stdout); progress goes to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DSA decode tokens/s + prefill tokens/s at L=128K, k=2048; % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0                                  # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(inp):
+    """Bytes the method must move per step, and per indexer launch (score and index
+    round trips through HBM are overhead and not counted)."""
+    wl = inp.wl
+    n = inp.q_pos.to("cpu").long() + 1
+    T = inp.num_q
+    e_i = ELEM[wl.index_dtype]
+    e_m = ELEM[wl.mla_dtype]
+    keys = int(n.sum()) * wl.index_dim * e_i
+    if wl.index_dtype == "fp8":
+        keys += int(n.sum()) * 4 + T * wl.index_heads * 4
+    idx_bytes = keys + T * wl.index_heads * (wl.index_dim * e_i + 4)
+    rows = int(n.clamp(max=wl.topk).sum())
+    mla_bytes = rows * wl.qk_dim * e_m + T * wl.heads * (wl.qk_dim + wl.v_dim) * e_m
+    return idx_bytes, idx_bytes + mla_bytes
+
+
+def algorithmic_flops(inp):
+    wl = inp.wl
+    n = inp.q_pos.to("cpu").long() + 1
+    idx = int(n.sum()) * wl.index_heads * 2 * wl.index_dim
+    mla = int(n.clamp(max=wl.topk).sum()) * wl.heads * 2 * (wl.qk_dim + wl.v_dim)
+    return idx, mla
+
+
+def make_events(torch, count):
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(count)]
+    for e in evs:            # torch creates the HIP event on first record
+        e.record()
+    torch.cuda.synchronize()
+    return evs
+
+
+def time_forward(B, torch, inp, steps, warmup):
+    pb = B.problem_from_inputs(inp)
+    ws = torch.empty(B.workspace_size(B.OP_FORWARD, pb), dtype=torch.uint8, device="cuda")
+    T, H, Dv, k = inp.num_q, inp.wl.heads, inp.wl.v_dim, inp.topk
+    out = torch.empty((T, H, Dv), dtype=inp.q.dtype, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    call = lambda ev=None: B.forward(pb, inp.q_idx, inp.q_scale, inp.w, inp.k_cache, inp.k_scale, inp.q,
+                                     inp.kv_cache, inp.sm_scale, out=out, lse=lse, topk_idx=idx, ws=ws,
+                                     stage_events=ev)
+    for _ in range(warmup):
+        call()
+    stage = [make_events(torch, 4) for _ in range(steps)]
+    start, end = make_events(torch, 2)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        call(stage[i])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    st = [[stage[i][j].elapsed_time(stage[i][j + 1]) for j in range(3)] for i in range(steps)]
+    mean = [sum(s[j] for s in st) / steps for j in range(3)]
+    return total_ms / steps, mean
+
+
+def cpu_baseline(inp, seconds):
+    """The float64 oracle, as it stands, on the first queries of the same batch."""
+    import numpy as np
+    import oracle
+    from workloads import raw_numpy, dtype_tag
+    oi = oracle.OracleInputs(
+        mode=inp.mode, q_pos=raw_numpy(inp.q_pos).astype(np.int64),
+        block_table=None if inp.block_table is None else raw_numpy(inp.block_table).astype(np.int64),
+        block_size=inp.block_size, index_dtype=dtype_tag(inp.q_idx), q_idx=raw_numpy(inp.q_idx),
+        q_scale=raw_numpy(inp.q_scale), w=raw_numpy(inp.w), k_cache=raw_numpy(inp.k_cache),
+        k_scale=raw_numpy(inp.k_scale), mla_dtype=dtype_tag(inp.q), q=raw_numpy(inp.q),
+        kv_cache=raw_numpy(inp.kv_cache), topk=inp.topk, sm_scale=inp.sm_scale, v_dim=inp.wl.v_dim)
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        pass
+    done = 0
+    t0 = time.perf_counter()
+    for t in range(inp.num_q):
+        oracle.forward(oi, rows=[t])
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": threads or os.cpu_count(), "kind": "oracle",
+            "sample": f"the first {done} of {inp.num_q} decode queries of the timed batch (full indexer over "
+                      f"each context, top-k, attention), float64 NumPy, {el:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurement")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path is data-parallel across sequences; sharding is described, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_long_context_relu_amd import binding as B
+    from workloads import WORKLOADS, BENCH_DEFAULT, generate
+
+    name = args.workload or BENCH_DEFAULT
+    wl = WORKLOADS[name]
+    log(f"generating {name} on cuda:0")
+    inp = generate(wl, "cuda")
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
+    ms, stages = time_forward(B, torch, inp, args.steps, args.warmup)
+    tokens = inp.num_q
+    value = tokens / (ms * 1e-3)
+    idx_bytes, step_bytes = algorithmic_bytes(inp)
+    idx_flops, mla_flops = algorithmic_flops(inp)
+    log(f"{ms:.3f} ms/step; stages (indexer, top-k, attention) ms = {[round(s, 4) for s in stages]}")
+
+    if wl.mode == "decode":
+        achieved = idx_bytes / (stages[0] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "indexer_decode_kernel", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None, "bytes_per_launch": idx_bytes, "launch_ms": round(stages[0], 5)}
+    else:
+        achieved = idx_flops / (stages[0] * 1e-3) / 1e12
+        peak = MFMA_PEAK_TFLOPS[wl.index_dtype]
+        roof = {"bound": "mfma", "kernel": "indexer_prefill_kernel", "achieved": round(achieved, 2),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "note": "first query chunk only"}
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.mla_dtype if wl.index_dtype != "fp8" else "bf16+fp8",
+        "data": "synthetic (seeded; no dataset or weights)",
+        "config": {"workload": name, "mode": wl.mode, "batch": wl.num_seqs,
+                   "context": list(wl.length_range) if wl.length_range else wl.length,
+                   "context_total": int((inp.q_pos.long() + 1).sum()), "paged": wl.paged, "topk": wl.topk,
+                   "index_heads": wl.index_heads, "index_dim": wl.index_dim, "heads": wl.heads,
+                   "qk_dim": wl.qk_dim, "v_dim": wl.v_dim, "index_dtype": wl.index_dtype,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "stages_ms": {"indexer": round(stages[0], 4), "topk": round(stages[1], 4), "attention": round(stages[2], 4)},
+        "step_algorithmic_bytes": step_bytes,
+        "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+    if not args.no_prefill:
+        pname = "prefill_16k_bf16"
+        log(f"secondary: {pname}")
+        del inp
+        torch.cuda.empty_cache()
+        pin = generate(WORKLOADS[pname], "cuda")
+        pms, pst = time_forward(B, torch, pin, 2, 1)
+        pf_idx, pf_mla = algorithmic_flops(pin)
+        # the indexer alone over every query row, one launch
+        pb = B.problem_from_inputs(pin)
+        sc = torch.empty((pin.num_q, pin.max_ctx), dtype=torch.float32, device="cuda")
+        B.index_scores(pb, pin.q_idx, pin.q_scale, pin.w, pin.k_cache, pin.k_scale, scores=sc)
+        e0, e1 = make_events(torch, 2)
+        e0.record()
+        B.index_scores(pb, pin.q_idx, pin.q_scale, pin.w, pin.k_cache, pin.k_scale, scores=sc)
+        e1.record()
+        torch.cuda.synchronize()
+        ims = e0.elapsed_time(e1)
+        result["prefill"] = {
+            "workload": pname, "tokens_per_s": round(pin.num_q / (pms * 1e-3), 1), "ms_per_step": round(pms, 3),
+            "indexer_ms_all_rows": round(ims, 3),
+            "indexer_mfma_frac": round(pf_idx / (ims * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
+            "step_mfma_frac": round((pf_idx + pf_mla) / (pms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4)}
+        log(f"prefill {pms:.2f} ms/step, indexer {ims:.2f} ms")
+        del pin, sc
+        torch.cuda.empty_cache()
+        inp = generate(wl, "cuda") if not args.no_cpu_baseline else None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

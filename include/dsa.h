@@ -1,0 +1,210 @@
+/*
+ * dsa.h -- C ABI of the DeepSeek Sparse Attention (DSA) forward path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The path has three steps.  Sources, cited below by tag:
+ *   [ZS] "DeepSeek V3.2: How Far Can Open Models Go If You Actually Try?"
+ *        (zeroshot.it.com), section 3.1 (indexer equation, selection-then-
+ *        attention equation, MQA mode) and section 3.4 (short prompts).
+ *   [LD] "DeepSeek-V3.2: Pushing the Frontier of Open Large Language Models"
+ *        (papers.lunadong.com summary), Pipeline Flow, System Modules, Key
+ *        Hyperparameters (selected_tokens_k = 2048, 128K context).
+ *   [BT] baseten.co "DeepSeek-V3.2", section (1) DSA + MLA.
+ *   [NH] news.han.ihouse.idv.tw article 1495, section "Introducing DSA
+ *        Efficient Sparse Attention Mechanism" (ReLU, FP8, k = 2048).
+ *
+ *   1. lightning indexer  I(t,s) = sum_j w(t,j) * ReLU(q(t,j) . k(s))  over
+ *      every candidate s of query t                     [ZS 3.1; LD; NH]
+ *   2. fine-grained top-k: the k best candidates of each query
+ *                                                       [ZS 3.1; LD; BT]
+ *   3. MLA in MQA mode over the selected rows of the shared latent cache:
+ *      every head attends over the same fetched rows    [ZS 3.1; LD]
+ *
+ * Conventions (every entry point):
+ *   - Pointers are DEVICE pointers unless marked "host".  Structs passed by
+ *     pointer are host memory, read during the call only.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *     null stream).  The library never synchronises, never allocates device
+ *     memory and keeps no state between calls; callers own every buffer,
+ *     including the workspace sized by dsa_workspace_size().
+ *   - Arguments are checked on the host before any launch; a failed check
+ *     returns a negative dsa_status and launches nothing.  A launch failure
+ *     returns DSA_ERR_HIP.  No C++ exception crosses the ABI.
+ *   - Device-side metadata is bounds-checked in the kernels and never makes
+ *     them read outside the caches: a query position is clamped to
+ *     [-1, max_ctx-1] (a negative position means no candidates); a block
+ *     table entry outside [0, num_blocks) makes the tokens of that block
+ *     absent (score -inf, never attended); a selected index that is negative
+ *     or above the query's position is skipped.
+ *   - Candidates: query t at position p = q_pos[t] sees the positions
+ *     s = 0..p of its sequence, p included (n_t = p + 1).  Reading of the
+ *     pages' "preceding tokens"; with k >= n_t the path is dense causal MLA.
+ *   - Results are deterministic: the same inputs give the same bytes.
+ *
+ * Layouts (row-major, last index fastest; all arrays dense):
+ *   indexer queries  q_idx    [T, H_I, d_I]   index_dtype
+ *   indexer q scales q_scale  [T, H_I] fp32   (e4m3fn only, > 0)
+ *   head weights     w        [T, H_I] fp32   (any sign)
+ *   indexer keys     k_cache  contiguous [B, max_seq_len, d_I] or paged
+ *                             [num_blocks, block_size, d_I]     index_dtype
+ *   key scales       k_scale  [B, max_seq_len] / [num_blocks, block_size]
+ *                             fp32 (e4m3fn only, > 0)
+ *   MLA queries      q        [T, H, D]   mla_dtype (already absorbed into
+ *                             the latent space; D = latent Dv + rope)
+ *   latent cache     kv_cache contiguous [B, max_seq_len, D] or paged
+ *                             [num_blocks, block_size, D]       mla_dtype
+ *   scores           [T, ld_scores] fp32
+ *   selected         topk_idx [T, k] int32
+ *   output           out      [T, H, Dv]  mla_dtype;  lse [T, H] fp32
+ *
+ * Supported shapes (others return DSA_ERR_UNSUPPORTED):
+ *   indexer  bf16 / e4m3fn: H_I = 64, d_I = 128;
+ *            fp32: H_I <= 64, d_I <= 128, H_I * d_I <= 4096
+ *   MLA      bf16: H = 128, D = 576, Dv = 512;
+ *            fp32: H <= 16, D <= 128, Dv <= D, k <= 1024
+ *   1 <= k <= 2048; max_ctx <= 262144; paged block_size = 64.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dsa_dtype {
+  DSA_F32 = 0,
+  DSA_BF16 = 1,
+  DSA_FP8_E4M3FN = 2 /* OCP FP8 E4M3 (max 448, no infinities); indexer only */
+} dsa_dtype;
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent shape */
+  DSA_ERR_UNSUPPORTED = -2, /* valid but outside the supported shapes/types */
+  DSA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  DSA_ERR_HIP = -4          /* a kernel launch failed */
+} dsa_status;
+
+typedef enum dsa_mode {
+  DSA_PREFILL = 0, /* all T queries belong to sequence 0 of the caches */
+  DSA_DECODE = 1   /* query t belongs to sequence t (T <= B) */
+} dsa_mode;
+
+typedef enum dsa_op {
+  DSA_OP_INDEX_SCORES = 0,
+  DSA_OP_TOPK = 1,
+  DSA_OP_SPARSE_MLA = 2,
+  DSA_OP_FORWARD = 3
+} dsa_op;
+
+/* Where each query sits and which cache rows it may read (host struct). */
+typedef struct dsa_seqs {
+  int32_t mode;              /* dsa_mode */
+  int32_t num_seqs;          /* B: sequences in the caches (prefill: >= 1, only sequence 0 is read) */
+  int32_t num_q;             /* T >= 0 */
+  int32_t max_ctx;           /* host bound: max over t of q_pos[t] + 1 (1..262144); sizes grids */
+  const int32_t *q_pos;      /* [T] device: position of query t in its sequence */
+  const int32_t *block_table;/* [B, max_blocks] device, or NULL for contiguous caches */
+  int32_t max_blocks;        /* columns of block_table (>= ceil(max_ctx / block_size)) */
+  int32_t num_blocks;        /* blocks in each paged pool */
+  int32_t block_size;        /* tokens per block: 64 (paged only) */
+  int32_t reserved;          /* must be 0 */
+  int64_t max_seq_len;       /* contiguous caches: token slots per sequence (>= max_ctx) */
+} dsa_seqs;
+
+/* Problem dimensions and element types (host struct). */
+typedef struct dsa_dims {
+  int32_t index_heads; /* H_I */
+  int32_t index_dim;   /* d_I */
+  int32_t topk;        /* k */
+  int32_t heads;       /* H */
+  int32_t qk_dim;      /* D (score dim: latent + rope) */
+  int32_t v_dim;       /* Dv (value dim: latent) */
+  int32_t index_dtype; /* dsa_dtype of q_idx / k_cache */
+  int32_t mla_dtype;   /* dsa_dtype of q / kv_cache / out (F32 or BF16) */
+} dsa_dims;
+
+/* Inputs and outputs of dsa_forward (host struct of device pointers). */
+typedef struct dsa_forward_args {
+  const void *q_idx;     /* [T, H_I, d_I] */
+  const float *q_scale;  /* [T, H_I] (e4m3fn only, else NULL) */
+  const float *w;        /* [T, H_I] */
+  const void *k_cache;   /* indexer key cache */
+  const float *k_scale;  /* key scales (e4m3fn only, else NULL) */
+  const void *q;         /* [T, H, D] */
+  const void *kv_cache;  /* latent cache */
+  float sm_scale;        /* softmax scale applied to q . c (e.g. 1/sqrt(D)) */
+  int32_t reserved;      /* must be 0 */
+  int32_t *topk_idx;     /* optional [T, k] output of the selection, or NULL */
+  void *out;             /* [T, H, Dv] */
+  float *lse;            /* optional [T, H], or NULL */
+  /* optional host array of 4 hipEvent_t recorded on `stream` at the start and
+   * after the indexer, top-k and attention stages of the first query chunk
+   * (decode always runs as one chunk); NULL records nothing */
+  void *const *stage_events;
+} dsa_forward_args;
+
+/* Bytes of workspace the given entry point needs for these shapes (0 when
+ * none).  op is a dsa_op.  Returns 0 as well for invalid arguments; the
+ * entry point itself then reports the error. */
+size_t dsa_workspace_size(int op, const dsa_seqs *seqs, const dsa_dims *dims);
+
+/* Step 1, the lightning indexer [ZS 3.1 indexer equation; LD System Modules;
+ * NH: ReLU chosen for throughput, FP8].
+ * scores[t, s] = sum_j w[t,j] * ReLU(q_idx[t,j,:] . k(s)) for s = 0..q_pos[t];
+ * with e4m3fn operands q = q8 * q_scale[t,j] and k = k8 * k_scale(s), which
+ * the kernel folds out of the ReLU (scales must be positive).  Entries
+ * q_pos[t] < s < ld_scores are set to -inf.  Products are accumulated in
+ * fp32 (bf16 / e4m3fn / fp32 operands); the head sum is fp32.
+ * ld_scores >= max_ctx.  No workspace. */
+int dsa_index_scores(const dsa_seqs *seqs, const dsa_dims *dims, const void *q_idx,
+                     const float *q_scale, const float *w, const void *k_cache,
+                     const float *k_scale, float *scores, int64_t ld_scores,
+                     hipStream_t stream);
+
+/* Step 2, fine-grained top-k [ZS 3.1 selection equation; LD "Top-k
+ * operation"; LD Key Hyperparameters k = 2048].
+ * For each query the first m = min(k, q_pos[t]+1) positions in the order
+ * (score descending, position ascending) -- ties go to the lower position,
+ * -0.0 equals +0.0 -- written in ASCENDING position order to topk_idx[t, 0..m)
+ * and -1 to topk_idx[t, m..k).  Reads scores[t, 0..q_pos[t]] only; scores
+ * must not be NaN.  Exact: integer radix select on order-preserving keys.
+ * Workspace: dsa_workspace_size(DSA_OP_TOPK, ...). */
+int dsa_topk(const dsa_seqs *seqs, int32_t k, const float *scores, int64_t ld_scores,
+             int32_t *topk_idx, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Step 3, sparse MLA in MQA mode [ZS 3.1 selection equation and MQA-mode
+ * paragraph: one shared latent row per token, every head reads the same
+ * fetched rows; LD Novel Architectural Elements].
+ * For query t and head h over the valid entries s of topk_idx[t, :]:
+ *   z_s = sm_scale * (q[t,h,:] . c(s)[0:D]),  p = softmax(z),
+ *   out[t,h,:] = sum_s p_s * c(s)[0:Dv],  lse[t,h] = max z + ln sum exp(z - max z).
+ * bf16 operands, fp32 logits / softmax / accumulation, bf16 round-to-nearest-
+ * even output (fp32 throughout for DSA_F32).  An empty selection gives
+ * out = 0 and lse = -inf.  lse may be NULL.
+ * Workspace: dsa_workspace_size(DSA_OP_SPARSE_MLA, ...). */
+int dsa_sparse_mla(const dsa_seqs *seqs, const dsa_dims *dims, float sm_scale, const void *q,
+                   const void *kv_cache, const int32_t *topk_idx, void *out, float *lse,
+                   void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Steps 1-3 fused into one call for prefill or decode [LD Pipeline Flow:
+ * indexer, then token selection, then sparse attention].  Results equal
+ * dsa_index_scores -> dsa_topk -> dsa_sparse_mla on the same inputs.
+ * Prefill runs in query chunks so the score rows of a chunk stay on chip.
+ * Workspace: dsa_workspace_size(DSA_OP_FORWARD, ...). */
+int dsa_forward(const dsa_seqs *seqs, const dsa_dims *dims, const dsa_forward_args *args,
+                void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Static string naming a dsa_status value. */
+const char *dsa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

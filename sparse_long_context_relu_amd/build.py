@@ -1,0 +1,79 @@
+"""Builds libdsa.so (the HIP kernels and the C ABI) for gfx950 with hipcc, in-tree.
+
+Run ``python -m sparse_long_context_relu_amd.build`` (or call ``build()``).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(ROOT, "_build")
+LIB_PATH = os.path.join(PKG, "libdsa.so")
+SOURCES = ["dsa_api.hip", "indexer.hip", "topk.hip", "sparse_mla.hip"]
+HEADERS = ["common.h", "kernels.h"]
+
+ARCH = "gfx950"
+CXXFLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
+    # keep the compiler from emitting packed fp32 vector instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+    "-I", INCLUDE, "-I", CSRC,
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the DSA library needs ROCm's hipcc to build")
+
+
+def build(verbose: bool = False, jobs: int = 4) -> str:
+    """Compile every source for gfx950 and link libdsa.so next to this file."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    cc = hipcc()
+    procs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmd = [cc, *CXXFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        if len(procs) >= jobs:
+            _wait(procs.pop(0), verbose)
+    for p in procs:
+        _wait(p, verbose)
+    tmp = LIB_PATH + ".tmp"
+    link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(link), flush=True)
+    res = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stdout}")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def _wait(item, verbose):
+    src, p = item
+    out, _ = p.communicate()
+    text = out.decode(errors="replace")
+    # hipcc's host pass does not know the packed-fp32 feature flag; that notice is harmless
+    lines = [l for l in text.splitlines() if "packed-fp32-ops" not in l]
+    if p.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n" + "\n".join(lines))
+    if verbose and lines:
+        print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

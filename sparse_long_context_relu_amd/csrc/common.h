@@ -1,0 +1,153 @@
+// Device-side building blocks shared by the DSA kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dsa.h"
+
+namespace dsa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- scalars
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// OCP e4m3fn byte -> fp32 via the gfx950 converter.
+__device__ __forceinline__ float fp8_to_f32(uint32_t byte) {
+  return __builtin_amdgcn_cvt_f32_fp8(int(byte), 0);
+}
+
+// Order-preserving unsigned key of an fp32 score: a > b  <=>  key(a) > key(b);
+// -0.0 and +0.0 map to the same key.
+__device__ __forceinline__ uint32_t score_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float neg_inf() { return __uint_as_float(0xff800000u); }
+
+// ---------------------------------------------------------------- wave helpers
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, kWave); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor(v, m);
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int o = __shfl_up(v, d, kWave);
+    if (l >= d) v += o;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- MFMA
+//
+// 32x32x16 bf16:  A lane l holds row l%32, 8 k-values of k-group l/32;
+//                 B lane l holds column l%32, the same 8 k-values;
+//                 C element v (0..15) of lane l: row 8*(v/4) + 4*(l/32) + v%4, column l%32.
+// 16x16x32 bf16:  A lane l: row l%16, 8 k-values of k-group l/16; B likewise by column;
+//                 C element v (0..3) of lane l: row 4*(l/16) + v, column l%16.
+// 32x32x64 fp8:   A lane l: row l%32, 32 k-values of k-group l/32 (e4m3, byte-packed); B likewise.
+// Because A and B map (lane, slot) to k identically, any fixed permutation of
+// the reduction index applied to both operands leaves the product unchanged;
+// the kernels use that to make each lane read contiguous bytes.
+
+__device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// e4m3 x e4m3 with unit block scales (E8M0 127 == 2^0).
+__device__ __forceinline__ f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+template <typename V>
+__device__ __forceinline__ V zero_vec() {
+  V v;
+#pragma unroll
+  for (int i = 0; i < int(sizeof(V) / sizeof(v[0])); ++i) v[i] = 0;
+  return v;
+}
+
+// 16-byte global load / store helpers.
+__device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ---------------------------------------------------------------- geometry
+
+struct SeqView {
+  int mode;
+  int num_seqs;
+  int num_q;
+  int max_ctx;
+  const int32_t *q_pos;
+  const int32_t *block_table;
+  int max_blocks;
+  int num_blocks;
+  int block_size;
+  long long max_seq_len;
+
+  // Candidates of query t: positions 0..n-1, n = q_pos + 1 clamped to [0, max_ctx].
+  __device__ __forceinline__ int candidates(int t) const {
+    int p = q_pos[t];
+    p = p < -1 ? -1 : p;
+    p = p > max_ctx - 1 ? max_ctx - 1 : p;
+    return p + 1;
+  }
+  __device__ __forceinline__ int seq_of(int t) const { return mode == DSA_DECODE ? t : 0; }
+
+  // Slot (row index into a [slots, width] cache) of logical position s of
+  // sequence b, or -1 when the position is absent (block outside the pool).
+  __device__ __forceinline__ long long slot(int b, int s) const {
+    if (block_table == nullptr) return (long long)b * max_seq_len + s;
+    const int blk = block_table[(long long)b * max_blocks + (s >> 6)];
+    if (blk < 0 || blk >= num_blocks) return -1;
+    return (long long)blk * 64 + (s & 63);
+  }
+};
+
+}  // namespace dsa

@@ -1,0 +1,309 @@
+// C ABI of the DSA forward path: host-side argument checks, workspace carving
+// and kernel orchestration on the caller's stream.  See include/dsa.h for the
+// contract of every entry point.
+#include "kernels.h"
+
+#define DSA_EXPORT extern "C" __attribute__((visibility("default")))
+
+using namespace dsa;
+
+namespace {
+
+constexpr int kMaxCtx = 262144;
+constexpr long long kScoreBudget = 256ll << 20;  // bytes of score rows per prefill chunk
+
+long long align256(long long x) { return (x + 255) & ~255ll; }
+
+int check_seqs(const dsa_seqs *s) {
+  if (s == nullptr) return DSA_ERR_INVALID_ARG;
+  if (s->mode != DSA_PREFILL && s->mode != DSA_DECODE) return DSA_ERR_INVALID_ARG;
+  if (s->num_seqs < 1 || s->num_q < 0 || s->reserved != 0) return DSA_ERR_INVALID_ARG;
+  if (s->max_ctx < 1) return DSA_ERR_INVALID_ARG;
+  if (s->max_ctx > kMaxCtx) return DSA_ERR_UNSUPPORTED;
+  if (s->num_q > 0 && s->q_pos == nullptr) return DSA_ERR_INVALID_ARG;
+  if (s->mode == DSA_DECODE && s->num_q > s->num_seqs) return DSA_ERR_INVALID_ARG;
+  if (s->block_table != nullptr) {
+    if (s->block_size != 64) return DSA_ERR_UNSUPPORTED;
+    if (s->num_blocks < 1 || s->max_blocks < (s->max_ctx + 63) / 64) return DSA_ERR_INVALID_ARG;
+  } else {
+    if (s->max_seq_len < s->max_ctx) return DSA_ERR_INVALID_ARG;
+  }
+  return DSA_OK;
+}
+
+int check_index_dims(const dsa_dims *d) {
+  if (d == nullptr || d->index_heads < 1 || d->index_dim < 1) return DSA_ERR_INVALID_ARG;
+  switch (d->index_dtype) {
+    case DSA_F32:
+      if (d->index_heads > 64 || d->index_dim > 128 || d->index_heads * d->index_dim > 4096)
+        return DSA_ERR_UNSUPPORTED;
+      return DSA_OK;
+    case DSA_BF16:
+    case DSA_FP8_E4M3FN:
+      return (d->index_heads == 64 && d->index_dim == 128) ? DSA_OK : DSA_ERR_UNSUPPORTED;
+    default:
+      return DSA_ERR_INVALID_ARG;
+  }
+}
+
+int check_k(int k) {
+  if (k < 1) return DSA_ERR_INVALID_ARG;
+  return k <= kTopkMaxK ? DSA_OK : DSA_ERR_UNSUPPORTED;
+}
+
+int check_mla_dims(const dsa_dims *d) {
+  if (d == nullptr || d->heads < 1 || d->qk_dim < 1 || d->v_dim < 1 || d->v_dim > d->qk_dim)
+    return DSA_ERR_INVALID_ARG;
+  if (int e = check_k(d->topk)) return e;
+  switch (d->mla_dtype) {
+    case DSA_BF16:
+      return (d->heads == 128 && d->qk_dim == 576 && d->v_dim == 512) ? DSA_OK : DSA_ERR_UNSUPPORTED;
+    case DSA_F32:
+      if (d->heads > 16 || d->qk_dim > 128 || d->topk > 1024)
+        return DSA_ERR_UNSUPPORTED;
+      return DSA_OK;
+    case DSA_FP8_E4M3FN:
+      return DSA_ERR_UNSUPPORTED;
+    default:
+      return DSA_ERR_INVALID_ARG;
+  }
+}
+
+SeqView view(const dsa_seqs *s) {
+  SeqView v;
+  v.mode = s->mode;
+  v.num_seqs = s->num_seqs;
+  v.num_q = s->num_q;
+  v.max_ctx = s->max_ctx;
+  v.q_pos = s->q_pos;
+  v.block_table = s->block_table;
+  v.max_blocks = s->max_blocks;
+  v.num_blocks = s->num_blocks;
+  v.block_size = s->block_size;
+  v.max_seq_len = s->max_seq_len;
+  return v;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+long long score_ld(const dsa_seqs *s) { return ((long long)s->max_ctx + 63) & ~63ll; }
+
+int mla_split_count(const dsa_dims *d, int rows) {
+  return d->mla_dtype == DSA_BF16 ? mla_splits(rows, d->topk) : 1;
+}
+
+long long mla_ws_bytes(const dsa_dims *d, int rows) {
+  const int ns = mla_split_count(d, rows);
+  if (ns <= 1) return 0;
+  return (long long)rows * ns * d->heads * (d->v_dim + 4) * (long long)sizeof(float);
+}
+
+long long topk_ws_bytes(int rows) { return (long long)rows * kTopkRowWords * (long long)sizeof(uint32_t); }
+
+int forward_chunk_rows(const dsa_seqs *s) {
+  if (s->mode == DSA_DECODE || s->num_q == 0) return s->num_q;
+  long long rows = kScoreBudget / (score_ld(s) * 4);
+  rows = rows / 8 * 8;
+  if (rows < 8) rows = 8;
+  return rows < s->num_q ? (int)rows : s->num_q;
+}
+
+struct ForwardLayout {
+  int chunk;
+  long long ld, off_scores, off_idx, off_topk, off_mla, total;
+};
+
+ForwardLayout forward_layout(const dsa_seqs *s, const dsa_dims *d) {
+  ForwardLayout L;
+  L.chunk = forward_chunk_rows(s);
+  L.ld = score_ld(s);
+  L.off_scores = 0;
+  L.off_idx = align256(L.ld * L.chunk * 4);
+  L.off_topk = L.off_idx + align256((long long)L.chunk * d->topk * 4);
+  L.off_mla = L.off_topk + align256(topk_ws_bytes(L.chunk));
+  L.total = L.off_mla + align256(mla_ws_bytes(d, L.chunk));
+  return L;
+}
+
+int check_ws(size_t need, const void *ws, size_t ws_bytes) {
+  if (need == 0) return DSA_OK;
+  if (ws == nullptr || ws_bytes < need) return DSA_ERR_WORKSPACE;
+  return DSA_OK;
+}
+
+IndexerArgs indexer_args(const dsa_seqs *s, const dsa_dims *d, const void *q_idx, const float *q_scale,
+                         const float *w, const void *k_cache, const float *k_scale, float *scores,
+                         long long ld, int q_begin, int rows, int fill) {
+  IndexerArgs a;
+  a.sv = view(s);
+  a.H_I = d->index_heads;
+  a.d_I = d->index_dim;
+  a.dtype = d->index_dtype;
+  a.q_idx = q_idx;
+  a.q_scale = q_scale;
+  a.w = w;
+  a.k_cache = k_cache;
+  a.k_scale = k_scale;
+  a.scores = scores;
+  a.ld = ld;
+  a.q_begin = q_begin;
+  a.rows = rows;
+  a.fill_masked = fill;
+  return a;
+}
+
+TopkArgs topk_args(const dsa_seqs *s, int k, const float *scores, long long ld, int32_t *idx, void *ws,
+                   int q_begin, int rows) {
+  TopkArgs a;
+  a.sv = view(s);
+  a.k = k;
+  a.scores = scores;
+  a.ld = ld;
+  a.q_begin = q_begin;
+  a.rows = rows;
+  a.idx = idx;
+  a.ws = reinterpret_cast<uint32_t *>(ws);
+  a.slices = topk_slices(rows, s->max_ctx);
+  return a;
+}
+
+MlaArgs mla_args(const dsa_seqs *s, const dsa_dims *d, float sm_scale, const void *q, const void *kv,
+                 const int32_t *idx, void *out, float *lse, void *ws, int q_begin, int rows) {
+  MlaArgs a;
+  a.sv = view(s);
+  a.H = d->heads;
+  a.D = d->qk_dim;
+  a.Dv = d->v_dim;
+  a.k = d->topk;
+  a.dtype = d->mla_dtype;
+  a.sm_scale = sm_scale;
+  a.q = q;
+  a.kv = kv;
+  a.idx = idx;
+  a.out = out;
+  a.lse = lse;
+  a.q_begin = q_begin;
+  a.rows = rows;
+  a.n_split = mla_split_count(d, rows);
+  a.part = reinterpret_cast<float *>(ws);
+  return a;
+}
+
+int check_index_ptrs(const dsa_dims *d, const void *q_idx, const float *q_scale, const float *w,
+                     const void *k_cache, const float *k_scale) {
+  if (q_idx == nullptr || w == nullptr || k_cache == nullptr) return DSA_ERR_INVALID_ARG;
+  if (d->index_dtype == DSA_FP8_E4M3FN && (q_scale == nullptr || k_scale == nullptr)) return DSA_ERR_INVALID_ARG;
+  return DSA_OK;
+}
+
+}  // namespace
+
+DSA_EXPORT size_t dsa_workspace_size(int op, const dsa_seqs *seqs, const dsa_dims *dims) {
+  if (check_seqs(seqs) != DSA_OK || dims == nullptr || seqs->num_q == 0) return 0;
+  switch (op) {
+    case DSA_OP_INDEX_SCORES:
+      return 0;
+    case DSA_OP_TOPK:
+      if (check_k(dims->topk) != DSA_OK) return 0;
+      return (size_t)topk_ws_bytes(seqs->num_q);
+    case DSA_OP_SPARSE_MLA:
+      if (check_mla_dims(dims) != DSA_OK) return 0;
+      return (size_t)mla_ws_bytes(dims, seqs->num_q);
+    case DSA_OP_FORWARD:
+      if (check_index_dims(dims) != DSA_OK || check_mla_dims(dims) != DSA_OK) return 0;
+      return (size_t)forward_layout(seqs, dims).total;
+    default:
+      return 0;
+  }
+}
+
+DSA_EXPORT int dsa_index_scores(const dsa_seqs *seqs, const dsa_dims *dims, const void *q_idx,
+                                const float *q_scale, const float *w, const void *k_cache,
+                                const float *k_scale, float *scores, int64_t ld_scores,
+                                hipStream_t stream) {
+  if (int e = check_seqs(seqs)) return e;
+  if (int e = check_index_dims(dims)) return e;
+  if (seqs->num_q == 0) return DSA_OK;
+  if (int e = check_index_ptrs(dims, q_idx, q_scale, w, k_cache, k_scale)) return e;
+  if (scores == nullptr || ld_scores < seqs->max_ctx) return DSA_ERR_INVALID_ARG;
+  IndexerArgs a = indexer_args(seqs, dims, q_idx, q_scale, w, k_cache, k_scale, scores, ld_scores, 0,
+                               seqs->num_q, 1);
+  return hip_status(launch_index_scores(a, stream));
+}
+
+DSA_EXPORT int dsa_topk(const dsa_seqs *seqs, int32_t k, const float *scores, int64_t ld_scores,
+                        int32_t *topk_idx, void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (int e = check_seqs(seqs)) return e;
+  if (int e = check_k(k)) return e;
+  if (seqs->num_q == 0) return DSA_OK;
+  if (scores == nullptr || topk_idx == nullptr || ld_scores < seqs->max_ctx) return DSA_ERR_INVALID_ARG;
+  if (int e = check_ws((size_t)topk_ws_bytes(seqs->num_q), ws, ws_bytes)) return e;
+  TopkArgs a = topk_args(seqs, k, scores, ld_scores, topk_idx, ws, 0, seqs->num_q);
+  return hip_status(launch_topk(a, stream));
+}
+
+DSA_EXPORT int dsa_sparse_mla(const dsa_seqs *seqs, const dsa_dims *dims, float sm_scale, const void *q,
+                              const void *kv_cache, const int32_t *topk_idx, void *out, float *lse,
+                              void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (int e = check_seqs(seqs)) return e;
+  if (int e = check_mla_dims(dims)) return e;
+  if (seqs->num_q == 0) return DSA_OK;
+  if (q == nullptr || kv_cache == nullptr || topk_idx == nullptr || out == nullptr) return DSA_ERR_INVALID_ARG;
+  if (!(sm_scale == sm_scale)) return DSA_ERR_INVALID_ARG;
+  if (int e = check_ws((size_t)mla_ws_bytes(dims, seqs->num_q), ws, ws_bytes)) return e;
+  MlaArgs a = mla_args(seqs, dims, sm_scale, q, kv_cache, topk_idx, out, lse, ws, 0, seqs->num_q);
+  return hip_status(launch_sparse_mla(a, stream));
+}
+
+DSA_EXPORT int dsa_forward(const dsa_seqs *seqs, const dsa_dims *dims, const dsa_forward_args *args,
+                           void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (int e = check_seqs(seqs)) return e;
+  if (int e = check_index_dims(dims)) return e;
+  if (int e = check_mla_dims(dims)) return e;
+  if (args == nullptr || args->reserved != 0) return DSA_ERR_INVALID_ARG;
+  if (seqs->num_q == 0) return DSA_OK;
+  if (int e = check_index_ptrs(dims, args->q_idx, args->q_scale, args->w, args->k_cache, args->k_scale))
+    return e;
+  if (args->q == nullptr || args->kv_cache == nullptr || args->out == nullptr) return DSA_ERR_INVALID_ARG;
+  if (!(args->sm_scale == args->sm_scale)) return DSA_ERR_INVALID_ARG;
+  const ForwardLayout L = forward_layout(seqs, dims);
+  if (int e = check_ws((size_t)L.total, ws, ws_bytes)) return e;
+
+  uint8_t *base = reinterpret_cast<uint8_t *>(ws);
+  float *scores = reinterpret_cast<float *>(base + L.off_scores);
+  int32_t *idx_ws = reinterpret_cast<int32_t *>(base + L.off_idx);
+  void *topk_ws = base + L.off_topk;
+  void *mla_ws = base + L.off_mla;
+  hipEvent_t const *ev = reinterpret_cast<hipEvent_t const *>(args->stage_events);
+
+  const int T = seqs->num_q;
+  for (int c0 = 0; c0 < T; c0 += L.chunk) {
+    const int rows = c0 + L.chunk < T ? L.chunk : T - c0;
+    const bool timed = ev != nullptr && c0 == 0;
+    if (timed && hipEventRecord(ev[0], stream) != hipSuccess) return DSA_ERR_HIP;
+    IndexerArgs ia = indexer_args(seqs, dims, args->q_idx, args->q_scale, args->w, args->k_cache,
+                                  args->k_scale, scores, L.ld, c0, rows, 0);
+    if (launch_index_scores(ia, stream) != hipSuccess) return DSA_ERR_HIP;
+    if (timed && hipEventRecord(ev[1], stream) != hipSuccess) return DSA_ERR_HIP;
+    int32_t *idx = args->topk_idx != nullptr ? args->topk_idx + (long long)c0 * dims->topk : idx_ws;
+    TopkArgs ta = topk_args(seqs, dims->topk, scores, L.ld, idx, topk_ws, c0, rows);
+    if (launch_topk(ta, stream) != hipSuccess) return DSA_ERR_HIP;
+    if (timed && hipEventRecord(ev[2], stream) != hipSuccess) return DSA_ERR_HIP;
+    MlaArgs ma = mla_args(seqs, dims, args->sm_scale, args->q, args->kv_cache, idx, args->out, args->lse,
+                          mla_ws, c0, rows);
+    if (launch_sparse_mla(ma, stream) != hipSuccess) return DSA_ERR_HIP;
+    if (timed && hipEventRecord(ev[3], stream) != hipSuccess) return DSA_ERR_HIP;
+  }
+  return DSA_OK;
+}
+
+DSA_EXPORT const char *dsa_status_string(int status) {
+  switch (status) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG: invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: shape or type not supported";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP: kernel launch failed";
+    default: return "unknown dsa_status";
+  }
+}

@@ -1,0 +1,344 @@
+// Lightning indexer: I(t,s) = sum_j w(t,j) * ReLU(q(t,j) . k(s)) for every
+// candidate s of query t ("DeepSeek V3.2: How Far Can Open Models Go If You
+// Actually Try?", section 3.1, indexer equation; news.han.ihouse.idv.tw
+// article 1495, DSA section: ReLU for throughput, FP8 execution).
+//
+// bf16 / e4m3fn (H_I = 64, d_I = 128): the q.k contraction runs on MFMA with
+// the 64 heads of one query as the M dimension and 32 keys as N; the ReLU,
+// the head weights and the head sum are applied to the accumulators in
+// registers, so only one fp32 score per (query, key) leaves the kernel.
+//   * decode tiling: one query per workgroup row of the grid, the candidate
+//     keys split into chunks across workgroups; each wave streams 32-key
+//     tiles straight from HBM into MFMA operand registers.
+//   * prefill tiling: 8 consecutive queries per workgroup (one per wave)
+//     share 64-key tiles staged through LDS.
+// e4m3fn: scores = k_scale(s) * sum_j (w_j q_scale_j) ReLU(q8_j . k8_s),
+// exact because ReLU(a x) = a ReLU(x) for a > 0.
+#include "kernels.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kHeads = 64;
+constexpr int kDim = 128;
+constexpr int kDecodeChunk = 2048;  // keys per decode workgroup
+
+// ------------------------------------------------------------------ helpers
+
+template <int DT>
+struct IdxTraits;
+
+// bf16: 8 k-steps of 16; lane group g holds d = 64 g + 8 ks + [0, 8).
+template <>
+struct IdxTraits<DSA_BF16> {
+  static constexpr int kSteps = 8;
+  static constexpr int kRowBytes = kDim * 2;
+  typedef bf16x8 Op;
+  __device__ static Op load(const uint8_t *row, int g, int ks) {
+    return as_bf16x8(ld16(row + g * 128 + ks * 16));
+  }
+  __device__ static f32x16 mma(Op a, Op b, f32x16 c) { return mfma32_bf16(a, b, c); }
+};
+
+// e4m3fn: 2 k-steps of 64; lane group g holds d = 64 g + 32 ks + [0, 32).
+template <>
+struct IdxTraits<DSA_FP8_E4M3FN> {
+  static constexpr int kSteps = 2;
+  static constexpr int kRowBytes = kDim;
+  typedef i32x8 Op;
+  __device__ static Op load(const uint8_t *row, int g, int ks) {
+    const uint8_t *p = row + g * 64 + ks * 32;
+    uint4 lo = ld16(p), hi = ld16(p + 16);
+    Op o;
+    o[0] = lo.x; o[1] = lo.y; o[2] = lo.z; o[3] = lo.w;
+    o[4] = hi.x; o[5] = hi.y; o[6] = hi.z; o[7] = hi.w;
+    return o;
+  }
+  __device__ static f32x16 mma(Op a, Op b, f32x16 c) { return mfma32_fp8(a, b, c); }
+};
+
+// Weight of accumulator element v of head block hb for lane group g.
+__device__ __forceinline__ int acc_head(int hb, int v, int g) { return hb * 32 + 8 * (v >> 2) + 4 * g + (v & 3); }
+
+template <int DT>
+__device__ __forceinline__ void load_query(const IndexerArgs &a, int t, int col, int g,
+                                           typename IdxTraits<DT>::Op (&qa)[2][IdxTraits<DT>::kSteps],
+                                           float (&wt)[2][16]) {
+  typedef IdxTraits<DT> Tr;
+  const uint8_t *qrow = reinterpret_cast<const uint8_t *>(a.q_idx) + (long long)t * kHeads * Tr::kRowBytes;
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int ks = 0; ks < Tr::kSteps; ++ks) qa[hb][ks] = Tr::load(qrow + (hb * 32 + col) * Tr::kRowBytes, g, ks);
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int h = acc_head(hb, v, g);
+      float wv = a.w[(long long)t * kHeads + h];
+      if (DT == DSA_FP8_E4M3FN) wv *= a.q_scale[(long long)t * kHeads + h];
+      wt[hb][v] = wv;
+    }
+}
+
+// ReLU-weighted head sum of the two 32-head accumulator blocks for the key in
+// column l%32; the result is valid in every lane.
+__device__ __forceinline__ float head_reduce(const f32x16 &c0, const f32x16 &c1, const float (&wt)[2][16]) {
+  float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    p0 = fmaf(wt[0][v], fmaxf(c0[v], 0.f), p0);
+    p1 = fmaf(wt[1][v], fmaxf(c1[v], 0.f), p1);
+  }
+  float p = p0 + p1;
+  return p + shfl_xor(p, 32);
+}
+
+template <int DT>
+__device__ __forceinline__ float key_scale(const IndexerArgs &a, long long slot) {
+  if (DT == DSA_FP8_E4M3FN) return a.k_scale[slot];
+  return 1.f;
+}
+
+// ------------------------------------------------------------------ decode tiling
+
+template <int DT>
+__global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs a) {
+  typedef IdxTraits<DT> Tr;
+  const int r = blockIdx.y;
+  const int t = a.q_begin + r;
+  const int n = a.sv.candidates(t);
+  const int b = a.sv.seq_of(t);
+  const int c0 = blockIdx.x * kDecodeChunk;
+  float *srow = a.scores + (long long)r * a.ld;
+  const long long cend = c0 + kDecodeChunk < a.ld ? c0 + kDecodeChunk : a.ld;
+  if (a.fill_masked) {
+    for (long long s = (c0 > n ? c0 : n) + threadIdx.x; s < cend; s += blockDim.x) srow[s] = neg_inf();
+  }
+  if (c0 >= n) return;
+  const int c1 = c0 + kDecodeChunk < n ? c0 + kDecodeChunk : n;
+
+  const int lane = lane_id();
+  const int wv = threadIdx.x >> 6;
+  const int g = lane >> 5, col = lane & 31;
+  typename Tr::Op qa[2][Tr::kSteps];
+  float wt[2][16];
+  load_query<DT>(a, t, col, g, qa, wt);
+
+  const uint8_t *kbase = reinterpret_cast<const uint8_t *>(a.k_cache);
+  for (int base = c0 + wv * 32; base < c1; base += 4 * 32) {
+    const int s = base + col;
+    const long long sl = s < c1 ? a.sv.slot(b, s) : -1;
+    typename Tr::Op kb[Tr::kSteps];
+    if (sl >= 0) {
+      const uint8_t *row = kbase + sl * Tr::kRowBytes;
+#pragma unroll
+      for (int ks = 0; ks < Tr::kSteps; ++ks) kb[ks] = Tr::load(row, g, ks);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < Tr::kSteps; ++ks) kb[ks] = zero_vec<typename Tr::Op>();
+    }
+    f32x16 c0a = zero_vec<f32x16>(), c1a = zero_vec<f32x16>();
+#pragma unroll
+    for (int ks = 0; ks < Tr::kSteps; ++ks) {
+      c0a = Tr::mma(qa[0][ks], kb[ks], c0a);
+      c1a = Tr::mma(qa[1][ks], kb[ks], c1a);
+    }
+    float sc = head_reduce(c0a, c1a, wt);
+    if (g == 0 && s < c1) srow[s] = sl >= 0 ? sc * key_scale<DT>(a, sl) : neg_inf();
+  }
+}
+
+// ------------------------------------------------------------------ prefill tiling
+
+constexpr int kPrefillQ = 8;     // queries (waves) per workgroup
+constexpr int kPrefillKeys = 64; // keys per LDS tile
+
+template <int DT>
+__global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
+  typedef IdxTraits<DT> Tr;
+  constexpr int kChunks = Tr::kRowBytes / 16;           // 16-byte chunks per key row (16 or 8)
+  constexpr int kTileChunks = kPrefillKeys * kChunks;   // chunks per tile
+  constexpr int kPerThread = kTileChunks / 512;         // 2 (bf16) or 1 (fp8)
+  __shared__ uint4 tile[2][kTileChunks];
+
+  const int grp = gridDim.x - 1 - blockIdx.x;           // longest rows first
+  const int lane = lane_id();
+  const int wv = threadIdx.x >> 6;
+  const int g = lane >> 5, col = lane & 31;
+  const int r = grp * kPrefillQ + wv;
+  const bool row_ok = r < a.rows;
+  const int t = a.q_begin + (row_ok ? r : a.rows - 1);
+  const int n = row_ok ? a.sv.candidates(t) : 0;
+  int nmax = 0;
+  for (int i = 0; i < kPrefillQ; ++i) {
+    const int ri = grp * kPrefillQ + i;
+    if (ri < a.rows) {
+      const int ni = a.sv.candidates(a.q_begin + ri);
+      nmax = ni > nmax ? ni : nmax;
+    }
+  }
+  float *srow = a.scores + (long long)(row_ok ? r : 0) * a.ld;
+
+  typename Tr::Op qa[2][Tr::kSteps];
+  float wt[2][16];
+  load_query<DT>(a, t, col, g, qa, wt);
+
+  const uint8_t *kbase = reinterpret_cast<const uint8_t *>(a.k_cache);
+  // Stage the tile starting at key `base` into registers.
+  uint4 stage[kPerThread];
+  long long stage_slot[kPerThread];
+  auto fetch = [&](int base) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int c = threadIdx.x + i * 512;
+      const int key = c / kChunks, ch = c % kChunks;
+      const int s = base + key;
+      const long long sl = s < nmax ? a.sv.slot(0, s) : -1;
+      stage_slot[i] = sl;
+      stage[i] = sl >= 0 ? ld16(kbase + sl * Tr::kRowBytes + ch * 16) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  // Swizzled store: chunk ch of key `key` goes to slot ch ^ (key & 15) of its row (bf16),
+  // so the 16 lanes of one MFMA operand read touch 16 distinct bank groups.
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int c = threadIdx.x + i * 512;
+      const int key = c / kChunks, ch = c % kChunks;
+      tile[buf][key * kChunks + (ch ^ (key & (kChunks - 1)))] = stage[i];
+    }
+  };
+  __shared__ int absent[2][kPrefillKeys];
+
+  int buf = 0;
+  if (nmax > 0) {
+    fetch(0);
+    put(0);
+    for (int i = 0; i < kPerThread; ++i) {
+      const int c = threadIdx.x + i * 512;
+      if (c % kChunks == 0) absent[0][c / kChunks] = stage_slot[i] < 0;
+    }
+  }
+  __syncthreads();
+  for (int base = 0; base < nmax; base += kPrefillKeys) {
+    const bool more = base + kPrefillKeys < nmax;
+    if (more) fetch(base + kPrefillKeys);
+    if (base < n) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int key = nb * 32 + col;
+        typename Tr::Op kb[Tr::kSteps];
+        const uint4 *trow = &tile[buf][key * kChunks];
+#pragma unroll
+        for (int ks = 0; ks < Tr::kSteps; ++ks) {
+          if constexpr (DT == DSA_BF16) {
+            const int ch = g * 8 + ks;
+            kb[ks] = __builtin_bit_cast(typename Tr::Op, trow[ch ^ (key & 15)]);
+          } else {
+            const int ch = g * 4 + ks * 2;
+            const uint4 lo = trow[ch ^ (key & 7)], hi = trow[(ch + 1) ^ (key & 7)];
+            typename Tr::Op o;
+            o[0] = lo.x; o[1] = lo.y; o[2] = lo.z; o[3] = lo.w;
+            o[4] = hi.x; o[5] = hi.y; o[6] = hi.z; o[7] = hi.w;
+            kb[ks] = o;
+          }
+        }
+        f32x16 c0a = zero_vec<f32x16>(), c1a = zero_vec<f32x16>();
+#pragma unroll
+        for (int ks = 0; ks < Tr::kSteps; ++ks) {
+          c0a = Tr::mma(qa[0][ks], kb[ks], c0a);
+          c1a = Tr::mma(qa[1][ks], kb[ks], c1a);
+        }
+        const float sc = head_reduce(c0a, c1a, wt);
+        const int s = base + key;
+        if (g == 0 && s < n && row_ok) {
+          if (absent[buf][key]) {
+            srow[s] = neg_inf();
+          } else {
+            float v = sc;
+            if (DT == DSA_FP8_E4M3FN) v *= a.k_scale[a.sv.slot(0, s)];
+            srow[s] = v;
+          }
+        }
+      }
+    }
+    if (more) {
+      put(buf ^ 1);
+      for (int i = 0; i < kPerThread; ++i) {
+        const int c = threadIdx.x + i * 512;
+        if (c % kChunks == 0) absent[buf ^ 1][c / kChunks] = stage_slot[i] < 0;
+      }
+    }
+    __syncthreads();
+    buf ^= 1;
+  }
+  if (a.fill_masked && row_ok) {
+    for (long long s = n + lane; s < a.ld; s += 64) srow[s] = neg_inf();
+  }
+}
+
+// ------------------------------------------------------------------ fp32, small shapes
+
+__global__ __launch_bounds__(256) void indexer_f32_kernel(IndexerArgs a) {
+  __shared__ float qs[4096];
+  __shared__ float ws[64];
+  const int r = blockIdx.y;
+  const int t = a.q_begin + r;
+  const int n = a.sv.candidates(t);
+  const int b = a.sv.seq_of(t);
+  const int HD = a.H_I * a.d_I;
+  const float *qrow = reinterpret_cast<const float *>(a.q_idx) + (long long)t * HD;
+  for (int i = threadIdx.x; i < HD; i += blockDim.x) qs[i] = qrow[i];
+  for (int i = threadIdx.x; i < a.H_I; i += blockDim.x) ws[i] = a.w[(long long)t * a.H_I + i];
+  __syncthreads();
+  const long long s = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  float *srow = a.scores + (long long)r * a.ld;
+  if (s >= a.ld) return;
+  if (s >= n) {
+    if (a.fill_masked) srow[s] = neg_inf();
+    return;
+  }
+  const long long sl = a.sv.slot(b, (int)s);
+  if (sl < 0) {
+    srow[s] = neg_inf();
+    return;
+  }
+  const float *key = reinterpret_cast<const float *>(a.k_cache) + sl * a.d_I;
+  float acc = 0.f;
+  for (int j = 0; j < a.H_I; ++j) {
+    float dot = 0.f;
+    for (int d = 0; d < a.d_I; ++d) dot = fmaf(qs[j * a.d_I + d], key[d], dot);
+    acc = fmaf(ws[j], fmaxf(dot, 0.f), acc);
+  }
+  srow[s] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_index_scores(const IndexerArgs &a, hipStream_t st) {
+  if (a.rows <= 0) return hipSuccess;
+  if (a.dtype == DSA_F32) {
+    dim3 grid((unsigned)((a.ld + 255) / 256), (unsigned)a.rows);
+    hipLaunchKernelGGL(indexer_f32_kernel, grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  const bool decode = a.sv.mode == DSA_DECODE;
+  if (decode) {
+    const long long span = a.fill_masked ? a.ld : a.sv.max_ctx;
+    dim3 grid((unsigned)((span + kDecodeChunk - 1) / kDecodeChunk), (unsigned)a.rows);
+    if (a.dtype == DSA_BF16)
+      hipLaunchKernelGGL(indexer_decode_kernel<DSA_BF16>, grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(indexer_decode_kernel<DSA_FP8_E4M3FN>, grid, dim3(256), 0, st, a);
+  } else {
+    dim3 grid((unsigned)((a.rows + kPrefillQ - 1) / kPrefillQ));
+    if (a.dtype == DSA_BF16)
+      hipLaunchKernelGGL(indexer_prefill_kernel<DSA_BF16>, grid, dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL(indexer_prefill_kernel<DSA_FP8_E4M3FN>, grid, dim3(512), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa

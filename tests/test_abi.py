@@ -1,0 +1,171 @@
+"""The C ABI on the CPU: the library loads, exports what include/dsa.h declares,
+its structs match the C layout, and invalid arguments are rejected on the host
+before any launch (no GPU is touched by these calls)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from sparse_long_context_relu_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(B.HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTS), names
+    for n in names:
+        assert hasattr(B.LIB, n), n
+
+
+def test_only_api_symbols_exported():
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    dsa = sorted(l.split()[-1] for l in out.splitlines() if l.split()[-1].startswith("dsa_"))
+    assert dsa == sorted(B.EXPORTS)
+
+
+def test_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text("""
+#include <stdio.h>
+#include <stddef.h>
+#include "dsa.h"
+#define P(T, f) printf(#T "." #f " %zu\\n", offsetof(T, f));
+int main(void) {
+  printf("dsa_seqs %zu\\n", sizeof(dsa_seqs));
+  printf("dsa_dims %zu\\n", sizeof(dsa_dims));
+  printf("dsa_forward_args %zu\\n", sizeof(dsa_forward_args));
+  P(dsa_seqs, q_pos) P(dsa_seqs, block_table) P(dsa_seqs, max_blocks) P(dsa_seqs, max_seq_len)
+  P(dsa_dims, mla_dtype)
+  P(dsa_forward_args, sm_scale) P(dsa_forward_args, topk_idx) P(dsa_forward_args, stage_events)
+  return 0;
+}
+""")
+    exe = tmp_path / "layout"
+    r = subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                        "-I", "/opt/rocm/include", str(src), "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True).stdout.splitlines())
+    assert int(got["dsa_seqs"]) == ctypes.sizeof(B.DsaSeqs)
+    assert int(got["dsa_dims"]) == ctypes.sizeof(B.DsaDims)
+    assert int(got["dsa_forward_args"]) == ctypes.sizeof(B.DsaForwardArgs)
+    for key, v in got.items():
+        if "." in key:
+            struct, field = key.split(".")
+            cls = {"dsa_seqs": B.DsaSeqs, "dsa_dims": B.DsaDims, "dsa_forward_args": B.DsaForwardArgs}[struct]
+            assert getattr(cls, field).offset == int(v), key
+
+
+def _problem(**kw):
+    base = dict(mode="decode", q_pos=torch.tensor([8191, 8191], dtype=torch.int32), max_ctx=8192, num_seqs=2,
+                max_seq_len=8192)
+    base.update(kw)
+    return B.make_problem(**base)
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _index(pb, scores_ld=8192, **ptrs):
+    p = dict(q_idx=FAKE, q_scale=None, w=FAKE, k_cache=FAKE, k_scale=None, scores=FAKE)
+    p.update(ptrs)
+    return B.LIB.dsa_index_scores(ctypes.byref(pb.seqs), ctypes.byref(pb.dims), p["q_idx"], p["q_scale"], p["w"],
+                                  p["k_cache"], p["k_scale"], p["scores"], scores_ld, None)
+
+
+def test_index_scores_validation():
+    pb = _problem()
+    assert _index(pb, q_idx=None) == B.ERR_INVALID_ARG
+    assert _index(pb, scores=None) == B.ERR_INVALID_ARG
+    assert _index(pb, scores_ld=100) == B.ERR_INVALID_ARG
+    pb.dims.index_heads = 32
+    assert _index(pb) == B.ERR_UNSUPPORTED
+    pb = _problem(index_dtype=B.FP8_E4M3FN)
+    assert _index(pb) == B.ERR_INVALID_ARG            # fp8 needs both scale arrays
+    pb = _problem()
+    pb.seqs.mode = 7
+    assert _index(pb) == B.ERR_INVALID_ARG
+    pb = _problem(max_seq_len=100)
+    assert _index(pb) == B.ERR_INVALID_ARG            # cache shorter than the context bound
+    pb = _problem(max_ctx=300000, max_seq_len=300000)
+    assert _index(pb) == B.ERR_UNSUPPORTED
+    pb = _problem()
+    pb.seqs.num_q = 3                                  # decode: more queries than sequences
+    assert _index(pb) == B.ERR_INVALID_ARG
+    pb = _problem()
+    pb.seqs.reserved = 1
+    assert _index(pb) == B.ERR_INVALID_ARG
+    bt = torch.zeros((2, 10), dtype=torch.int32)
+    pb = _problem(block_table=bt, num_blocks=20)
+    assert _index(pb) == B.ERR_INVALID_ARG            # too few block-table columns for max_ctx
+    pb = _problem(q_pos=torch.zeros(0, dtype=torch.int32))
+    assert _index(pb) == B.OK                          # nothing to do, nothing launched
+
+
+def test_topk_validation():
+    pb = _problem()
+    need = B.workspace_size(B.OP_TOPK, pb)
+    assert need > 0
+    call = lambda k, ws, nb, ld=8192, sc=FAKE, idx=FAKE: B.LIB.dsa_topk(
+        ctypes.byref(pb.seqs), k, sc, ld, idx, ws, nb, None)
+    assert call(0, FAKE, need) == B.ERR_INVALID_ARG
+    assert call(4096, FAKE, need) == B.ERR_UNSUPPORTED
+    assert call(2048, None, 0) == B.ERR_WORKSPACE
+    assert call(2048, FAKE, need - 1) == B.ERR_WORKSPACE
+    assert call(2048, FAKE, need, sc=None) == B.ERR_INVALID_ARG
+    assert call(2048, FAKE, need, idx=None) == B.ERR_INVALID_ARG
+
+
+def test_sparse_mla_validation():
+    pb = _problem()
+    need = B.workspace_size(B.OP_SPARSE_MLA, pb)
+    assert need == 2 * 32 * 128 * (512 + 4) * 4         # 2 queries x 32 splits of fp32 partials
+    call = lambda pbx, ws=FAKE, nb=1 << 40, q=FAKE, sm=0.04: B.LIB.dsa_sparse_mla(
+        ctypes.byref(pbx.seqs), ctypes.byref(pbx.dims), sm, q, FAKE, FAKE, FAKE, None, ws, nb, None)
+    assert call(pb, q=None) == B.ERR_INVALID_ARG
+    assert call(pb, sm=float("nan")) == B.ERR_INVALID_ARG
+    if need:
+        assert call(pb, ws=None, nb=0) == B.ERR_WORKSPACE
+    pb2 = _problem(heads=64)
+    assert call(pb2) == B.ERR_UNSUPPORTED
+    pb3 = _problem(mla_dtype=B.FP8_E4M3FN)
+    assert call(pb3) == B.ERR_UNSUPPORTED
+    pb4 = _problem(v_dim=600)
+    assert call(pb4) == B.ERR_INVALID_ARG
+
+
+def test_forward_validation_and_workspace():
+    pb = _problem()
+    need = B.workspace_size(B.OP_FORWARD, pb)
+    # scores (2 x 8192 fp32) + idx + top-k rows + split partials, each 256-byte aligned
+    assert need >= 2 * 8192 * 4 + 2 * 2048 * 4
+    args = B.DsaForwardArgs(q_idx=FAKE, w=FAKE, k_cache=FAKE, q=FAKE, kv_cache=FAKE, sm_scale=0.04, out=FAKE)
+    call = lambda ws, nb: B.LIB.dsa_forward(ctypes.byref(pb.seqs), ctypes.byref(pb.dims), ctypes.byref(args),
+                                            ws, nb, None)
+    assert call(None, 0) == B.ERR_WORKSPACE
+    assert call(FAKE, need - 1) == B.ERR_WORKSPACE
+    args.out = None
+    assert call(FAKE, need) == B.ERR_INVALID_ARG
+    args.out = FAKE
+    args.reserved = 3
+    assert call(FAKE, need) == B.ERR_INVALID_ARG
+    # prefill workspaces are bounded by query chunking, not by T x L scores
+    qp = torch.arange(65536, dtype=torch.int32)
+    pf = B.make_problem(mode="prefill", q_pos=qp, max_ctx=65536, num_seqs=1, max_seq_len=65536,
+                        index_dtype=B.FP8_E4M3FN)
+    assert B.workspace_size(B.OP_FORWARD, pf) < (1 << 30)
+
+
+def test_status_strings():
+    for s in (B.OK, B.ERR_INVALID_ARG, B.ERR_UNSUPPORTED, B.ERR_WORKSPACE, B.ERR_HIP):
+        assert B.status_string(s).startswith("DSA_")
+    assert "unknown" in B.status_string(12345)

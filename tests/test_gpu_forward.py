@@ -1,0 +1,145 @@
+"""The fused path (indexer -> top-k -> sparse MLA) against the oracle, plus the
+invariants that need no oracle: paged == contiguous bit for bit, run-to-run
+determinism, k >= n reducing to dense causal attention, empty contexts."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.helpers import (OUT_TOL, check_attention, check_topk_row_e2e, small_workload, to_oracle)
+from tests.test_gpu_ops import B, DEV, _say, big_dims
+from workloads import generate
+
+pytestmark = pytest.mark.gpu
+
+
+def run_forward(inp):
+    out, lse, idx = B().forward_inputs(inp)
+    torch.cuda.synchronize()
+    return out, lse, idx
+
+
+def check_all_rows(inp, out, lse, idx, name):
+    oi = to_oracle(inp)
+    og, lg, ig = out.float().cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy()
+    swaps = 0
+    for t in range(inp.num_q):
+        scores = oracle.query_index_scores(oi, t)
+        swaps += check_topk_row_e2e(ig[t], scores, inp.topk, f"{name} row {t}")
+        m = min(inp.topk, scores.shape[0])
+        o_ref, l_ref = oracle.query_attention(oi, t, ig[t, :m])
+        check_attention(og[t], lg[t], o_ref, l_ref, OUT_TOL[inp.wl.mla_dtype], f"{name} row {t}")
+    return swaps
+
+
+FORWARD_CASES = [
+    ("decode_contig", dict(mode="decode", num_seqs=4, length=6000, k=2048), [6000, 2048, 2049, 1]),
+    ("decode_paged", dict(mode="decode", num_seqs=3, length=9000, k=2048, paged=True), [9000, 4097, 2000]),
+    ("decode_paged_fp8", dict(mode="decode", num_seqs=3, length=5000, k=2048, paged=True, index_dtype="fp8"),
+     [5000, 2100, 64]),
+    ("prefill", dict(mode="prefill", length=2600, k=2048, prefill_q_start=2000), None),
+    ("prefill_fp8", dict(mode="prefill", length=2300, k=2048, prefill_q_start=2030, index_dtype="fp8"), None),
+    ("prefill_short_k", dict(mode="prefill", length=700, k=100), None),
+]
+
+
+@pytest.mark.parametrize("name,kw,lengths", FORWARD_CASES, ids=[c[0] for c in FORWARD_CASES])
+def test_forward_parity(name, kw, lengths):
+    _say("forward", name)
+    inp = generate(big_dims(**kw), DEV, lengths=lengths)
+    out, lse, idx = run_forward(inp)
+    check_all_rows(inp, out, lse, idx, name)
+
+
+def test_forward_f32_tiny_config():
+    """The tiny fp32 prefill workload, every row."""
+    from workloads import WORKLOADS
+    _say("forward tiny_prefill_f32")
+    inp = generate(WORKLOADS["tiny_prefill_f32"], DEV)
+    out, lse, idx = run_forward(inp)
+    check_all_rows(inp, out, lse, idx, "tiny_prefill_f32")
+
+
+def test_forward_matches_staged_ops():
+    """dsa_forward equals index_scores -> topk -> sparse_mla on the same inputs, bit for bit."""
+    _say("forward vs staged")
+    inp = generate(big_dims(mode="decode", num_seqs=3, length=5000, k=2048, paged=True), DEV,
+                   lengths=[5000, 3000, 4100])
+    out, lse, idx = run_forward(inp)
+    pb = B().problem_from_inputs(inp)
+    sc = B().index_scores(pb, inp.q_idx, inp.q_scale, inp.w, inp.k_cache, inp.k_scale)
+    idx2 = B().topk(pb, sc)
+    out2, lse2 = B().sparse_mla(pb, inp.sm_scale, inp.q, inp.kv_cache, idx2)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+def _paged_copy(inp, rng):
+    """The same logical caches re-laid into permuted 64-token blocks."""
+    B_, L = inp.k_cache.shape[:2]
+    nb = (L + 63) // 64
+    perm = torch.from_numpy(rng.permutation(B_ * nb)).to(DEV)
+    table = perm.reshape(B_, nb).to(torch.int32)
+    kc = torch.zeros((B_ * nb, 64) + tuple(inp.k_cache.shape[2:]), dtype=inp.k_cache.dtype, device=DEV)
+    vc = torch.zeros((B_ * nb, 64) + tuple(inp.kv_cache.shape[2:]), dtype=inp.kv_cache.dtype, device=DEV)
+    pos = torch.arange(L, device=DEV)
+    for b in range(B_):
+        phys = table[b, pos // 64].long() * 64 + pos % 64
+        kc.view(-1, *kc.shape[2:])[phys] = inp.k_cache[b]
+        vc.view(-1, *vc.shape[2:])[phys] = inp.kv_cache[b]
+    import dataclasses
+    return dataclasses.replace(inp, block_table=table.contiguous(), num_blocks=B_ * nb, max_seq_len=0,
+                               k_cache=kc, kv_cache=vc)
+
+
+def test_paged_equals_contiguous_bitwise():
+    _say("paged == contiguous")
+    inp = generate(big_dims(mode="decode", num_seqs=3, length=4500, k=2048), DEV, lengths=[4500, 4000, 2222])
+    a = run_forward(inp)
+    pg = _paged_copy(inp, np.random.default_rng(3))
+    b = run_forward(pg)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_determinism():
+    _say("determinism")
+    inp = generate(big_dims(mode="prefill", length=2400, k=2048, prefill_q_start=2200), DEV)
+    a = run_forward(inp)
+    b = run_forward(inp)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_k_at_least_n_is_dense_causal():
+    """With k >= n every candidate is selected and the output is dense causal attention
+    (computed here in float64 by torch's SDPA on the CPU)."""
+    _say("k >= n dense")
+    inp = generate(big_dims(mode="prefill", length=150, k=256), DEV)
+    out, lse, idx = run_forward(inp)
+    ig = idx.cpu().numpy()
+    for t in range(150):
+        assert list(ig[t, : t + 1]) == list(range(t + 1)) and np.all(ig[t, t + 1:] == -1)
+    q = oracle.decode_bf16(inp.q.view(torch.int16).cpu().numpy().view(np.uint16))
+    kv = oracle.decode_bf16(inp.kv_cache[0].view(torch.int16).cpu().numpy().view(np.uint16))
+    qt = torch.from_numpy(q).permute(1, 0, 2).unsqueeze(0)                   # [1, H, T, D]
+    kt = torch.from_numpy(kv).expand(128, 150, 576).unsqueeze(0)
+    vt = torch.from_numpy(np.ascontiguousarray(kv[:, :512])).expand(128, 150, 512).unsqueeze(0)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=inp.sm_scale)
+    ref = ref[0].permute(1, 0, 2).numpy()
+    err = np.abs(out.float().cpu().numpy() - ref).max()
+    assert err <= 2e-2, err
+
+
+def test_empty_and_single_candidate():
+    """q_pos = -1 (no candidates): idx all -1, out 0, lse -inf; q_pos = 0: the query's own row."""
+    _say("empty / single")
+    inp = generate(big_dims(mode="decode", num_seqs=3, length=300, k=2048), DEV, lengths=[300, 1, 300])
+    inp.q_pos[2] = -1
+    out, lse, idx = run_forward(inp)
+    assert torch.all(idx[2] == -1) and torch.all(out[2] == 0) and torch.all(torch.isneginf(lse[2]))
+    assert int(idx[1, 0]) == 0 and torch.all(idx[1, 1:] == -1)
+    assert torch.equal(out[1], inp.kv_cache[1, 0, :512].expand(128, 512))
