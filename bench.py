@@ -130,6 +130,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurement")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
@@ -140,6 +142,15 @@ def main():
     from sparse_long_context_relu_amd import binding as B
     from workloads import WORKLOADS, BENCH_DEFAULT, generate
 
+    if args.copy_mib:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE calibrate the traffic counters
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.copy_mib} MiB read + {args.copy_mib} MiB written")
+        del src, dst
     name = args.workload or BENCH_DEFAULT
     wl = WORKLOADS[name]
     log(f"generating {name} on cuda:0")

@@ -98,7 +98,7 @@ long long mla_ws_bytes(const dsa_dims *d, int rows) {
   return (long long)rows * ns * d->heads * (d->v_dim + 4) * (long long)sizeof(float);
 }
 
-long long topk_ws_bytes(int rows) { return (long long)rows * kTopkRowWords * (long long)sizeof(uint32_t); }
+long long topk_ws_bytes(int rows) { return (long long)rows * topk_row_words(rows) * (long long)sizeof(uint32_t); }
 
 int forward_chunk_rows(const dsa_seqs *s) {
   if (s->mode == DSA_DECODE || s->num_q == 0) return s->num_q;
@@ -149,6 +149,9 @@ IndexerArgs indexer_args(const dsa_seqs *s, const dsa_dims *d, const void *q_idx
   a.q_begin = q_begin;
   a.rows = rows;
   a.fill_masked = fill;
+  a.hist = nullptr;
+  a.hist_stride = 0;
+  a.hist_mode = 0;
   return a;
 }
 
@@ -163,6 +166,7 @@ TopkArgs topk_args(const dsa_seqs *s, int k, const float *scores, long long ld, 
   a.rows = rows;
   a.idx = idx;
   a.ws = reinterpret_cast<uint32_t *>(ws);
+  a.row_words = topk_row_words(rows);
   a.slices = topk_slices(rows, s->max_ctx);
   return a;
 }
@@ -280,14 +284,25 @@ DSA_EXPORT int dsa_forward(const dsa_seqs *seqs, const dsa_dims *dims, const dsa
   for (int c0 = 0; c0 < T; c0 += L.chunk) {
     const int rows = c0 + L.chunk < T ? L.chunk : T - c0;
     const bool timed = ev != nullptr && c0 == 0;
-    if (timed && hipEventRecord(ev[0], stream) != hipSuccess) return DSA_ERR_HIP;
-    IndexerArgs ia = indexer_args(seqs, dims, args->q_idx, args->q_scale, args->w, args->k_cache,
-                                  args->k_scale, scores, L.ld, c0, rows, 0);
-    if (launch_index_scores(ia, stream) != hipSuccess) return DSA_ERR_HIP;
-    if (timed && hipEventRecord(ev[1], stream) != hipSuccess) return DSA_ERR_HIP;
     int32_t *idx = args->topk_idx != nullptr ? args->topk_idx + (long long)c0 * dims->topk : idx_ws;
     TopkArgs ta = topk_args(seqs, dims->topk, scores, L.ld, idx, topk_ws, c0, rows);
-    if (launch_topk(ta, stream) != hipSuccess) return DSA_ERR_HIP;
+    IndexerArgs ia = indexer_args(seqs, dims, args->q_idx, args->q_scale, args->w, args->k_cache,
+                                  args->k_scale, scores, L.ld, c0, rows, 0);
+    // The MFMA indexers count the top-k's first radix digit as they write the
+    // scores: decode adds per-workgroup counts into rows zeroed first; prefill
+    // stores whole rows (the sliced select still needs its counters zeroed).
+    const bool fused = dims->index_dtype != DSA_F32;
+    if (fused) {
+      ia.hist = ta.ws;
+      ia.hist_stride = ta.row_words;
+      ia.hist_mode = seqs->mode == DSA_DECODE ? 1 : 2;
+      if ((ia.hist_mode == 1 || topk_sliced(rows)) && launch_topk_zero(ta, stream) != hipSuccess)
+        return DSA_ERR_HIP;
+    }
+    if (timed && hipEventRecord(ev[0], stream) != hipSuccess) return DSA_ERR_HIP;
+    if (launch_index_scores(ia, stream) != hipSuccess) return DSA_ERR_HIP;
+    if (timed && hipEventRecord(ev[1], stream) != hipSuccess) return DSA_ERR_HIP;
+    if ((fused ? launch_topk_select(ta, stream) : launch_topk(ta, stream)) != hipSuccess) return DSA_ERR_HIP;
     if (timed && hipEventRecord(ev[2], stream) != hipSuccess) return DSA_ERR_HIP;
     MlaArgs ma = mla_args(seqs, dims, args->sm_scale, args->q, args->kv_cache, idx, args->out, args->lse,
                           mla_ws, c0, rows);

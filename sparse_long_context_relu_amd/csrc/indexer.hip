@@ -84,11 +84,13 @@ __device__ __forceinline__ void load_query(const IndexerArgs &a, int t, int col,
 // ReLU-weighted head sum of the two 32-head accumulator blocks for the key in
 // column l%32; the result is valid in every lane.
 __device__ __forceinline__ float head_reduce(const f32x16 &c0, const f32x16 &c1, const float (&wt)[2][16]) {
+  // ReLU as an integer max on the float's bits: non-negative floats are
+  // non-negative integers, negative floats (and -0.0) negative ones.
   float p0 = 0.f, p1 = 0.f;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    p0 = fmaf(wt[0][v], fmaxf(c0[v], 0.f), p0);
-    p1 = fmaf(wt[1][v], fmaxf(c1[v], 0.f), p1);
+    p0 = fmaf(wt[0][v], __int_as_float(max(__float_as_int(c0[v]), 0)), p0);
+    p1 = fmaf(wt[1][v], __int_as_float(max(__float_as_int(c1[v]), 0)), p1);
   }
   float p = p0 + p1;
   return p + shfl_xor(p, 32);
@@ -101,10 +103,25 @@ __device__ __forceinline__ float key_scale(const IndexerArgs &a, long long slot)
 }
 
 // ------------------------------------------------------------------ decode tiling
+//
+// Each wave owns 32-key tiles (kRowBytes * 32 contiguous bytes: a tile never
+// straddles a 64-token block).  It loads a tile with fully coalesced 16-byte
+// loads -- one instruction covers whole rows -- into registers one tile ahead,
+// stores it into a wave-private LDS buffer with the 16-byte chunks of row r
+// XOR-swizzled by r, and reads the MFMA operands (lane: key l%32, chunks of
+// k-group l/32) back from there without bank conflicts.
+
+constexpr int kDecodeWaves = 4;
 
 template <int DT>
-__global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void indexer_decode_kernel(
+    IndexerArgs a) {
   typedef IdxTraits<DT> Tr;
+  constexpr int kChunks = Tr::kRowBytes / 16;       // 16-byte chunks per key row (16 bf16, 8 fp8)
+  constexpr int kPer = 32 * kChunks / 64;           // chunks each lane loads per tile (8 or 4)
+  __shared__ uint4 wtile[kDecodeWaves][32 * kChunks];
+  __shared__ uint32_t lh[kTopkBins];
+
   const int r = blockIdx.y;
   const int t = a.q_begin + r;
   const int n = a.sv.candidates(t);
@@ -118,6 +135,20 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs a) {
   if (c0 >= n) return;
   const int c1 = c0 + kDecodeChunk < n ? c0 + kDecodeChunk : n;
 
+  // first radix digit of the top-k, counted per workgroup and added to the row's bins
+  const bool hist = a.hist_mode == 1;
+  if (hist)
+    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
+  // Slot of the first key of each 64-token block of this chunk (-1: absent),
+  // read once, so a tile's lookup is an LDS read that never waits on the
+  // vector-memory counter (which also counts the score stores in flight).
+  __shared__ long long blk0[kDecodeChunk / 64];
+  if (threadIdx.x < kDecodeChunk / 64) {
+    const int s = c0 + threadIdx.x * 64;
+    blk0[threadIdx.x] = s < c1 ? a.sv.slot(b, s) : -1;
+  }
+  __syncthreads();
+
   const int lane = lane_id();
   const int wv = threadIdx.x >> 6;
   const int g = lane >> 5, col = lane & 31;
@@ -126,17 +157,66 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs a) {
   load_query<DT>(a, t, col, g, qa, wt);
 
   const uint8_t *kbase = reinterpret_cast<const uint8_t *>(a.k_cache);
-  for (int base = c0 + wv * 32; base < c1; base += 4 * 32) {
-    const int s = base + col;
-    const long long sl = s < c1 ? a.sv.slot(b, s) : -1;
+  uint4 *tile = wtile[wv];
+  // Coalesced fetch of the tile at key `base`: lane l takes chunk (i*64 + l) of
+  // the tile for i < kPer, i.e. row (i*64 + l) / kChunks.  A tile lies inside
+  // one 64-token block, so one wave-uniform lookup gives the slot of its first
+  // row and the others follow.  Rows past c1 or in an absent block load zeros.
+  auto tile_slot = [&](int base) -> long long {
+    const long long b0 = blk0[(base - c0) >> 6];
+    return b0 >= 0 ? b0 + (base & 63) : -1;
+  };
+  // Every lane always loads (absent rows read the chunk's first row instead) and
+  // `put` zeroes what is absent: no branches, and no register initialised
+  // before a load that might be skipped.
+  auto fetch = [&](int base, long long sl0, uint4 (&st)[kPer]) {
+    const long long first = sl0 >= 0 ? sl0 : 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int p = i * 64 + lane;
+      const int row = p / kChunks, ch = p % kChunks;
+      const int rr = base + row < c1 ? row : 0;
+      st[i] = ld16(kbase + (first + rr) * Tr::kRowBytes + ch * 16);
+    }
+  };
+  auto put = [&](const uint4 (&st)[kPer], int base, long long sl0) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int p = i * 64 + lane;
+      const int row = p / kChunks, ch = p % kChunks;
+      const bool ok = sl0 >= 0 && base + row < c1;
+      tile[row * kChunks + (ch ^ (row & (kChunks - 1)))] = ok ? st[i] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  uint4 stage[kPer];
+  int base = c0 + wv * 32;
+  long long sl0 = -1;
+  if (base < c1) {
+    sl0 = tile_slot(base);
+    fetch(base, sl0, stage);
+    put(stage, base, sl0);
+  }
+  // Drain the query, weight and first-tile loads here, so that no wait for them
+  // lands inside the loop (where it would also wait for the prefetch).
+  __builtin_amdgcn_s_waitcnt(0);
+  for (; base < c1; base += kDecodeWaves * 32) {
+    const int nb = base + kDecodeWaves * 32;
+    const long long sln = nb < c1 ? tile_slot(nb) : -1;
+    if (nb < c1) fetch(nb, sln, stage);            // next tile in flight during this one
     typename Tr::Op kb[Tr::kSteps];
-    if (sl >= 0) {
-      const uint8_t *row = kbase + sl * Tr::kRowBytes;
+    const uint4 *trow = tile + col * kChunks;
 #pragma unroll
-      for (int ks = 0; ks < Tr::kSteps; ++ks) kb[ks] = Tr::load(row, g, ks);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < Tr::kSteps; ++ks) kb[ks] = zero_vec<typename Tr::Op>();
+    for (int ks = 0; ks < Tr::kSteps; ++ks) {
+      if constexpr (DT == DSA_BF16) {
+        kb[ks] = __builtin_bit_cast(typename Tr::Op, trow[(g * 8 + ks) ^ (col & 15)]);
+      } else {
+        const int ch = g * 4 + ks * 2;
+        const uint4 lo = trow[ch ^ (col & 7)], hi = trow[(ch + 1) ^ (col & 7)];
+        typename Tr::Op o;
+        o[0] = lo.x; o[1] = lo.y; o[2] = lo.z; o[3] = lo.w;
+        o[4] = hi.x; o[5] = hi.y; o[6] = hi.z; o[7] = hi.w;
+        kb[ks] = o;
+      }
     }
     f32x16 c0a = zero_vec<f32x16>(), c1a = zero_vec<f32x16>();
 #pragma unroll
@@ -144,8 +224,23 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs a) {
       c0a = Tr::mma(qa[0][ks], kb[ks], c0a);
       c1a = Tr::mma(qa[1][ks], kb[ks], c1a);
     }
-    float sc = head_reduce(c0a, c1a, wt);
-    if (g == 0 && s < c1) srow[s] = sl >= 0 ? sc * key_scale<DT>(a, sl) : neg_inf();
+    const float sc = head_reduce(c0a, c1a, wt);
+    // Stage the next tile before storing this one's scores: the wait for the
+    // prefetched rows then does not also wait for the store to be acknowledged.
+    if (nb < c1) put(stage, nb, sln);              // the LDS reads above completed before the MFMAs
+    const int s = base + col;
+    if (g == 0 && s < c1) {
+      const float v = sl0 >= 0 ? sc * key_scale<DT>(a, sl0 + col) : neg_inf();
+      srow[s] = v;
+      if (hist) atomicAdd(&lh[score_key(v) >> 21], 1u);
+    }
+    sl0 = sln;
+  }
+  if (hist) {
+    __syncthreads();
+    uint32_t *hrow = a.hist + (long long)r * a.hist_stride;
+    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x)
+      if (lh[i]) atomicAdd(&hrow[i], lh[i]);
   }
 }
 
@@ -188,13 +283,14 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
   // Stage the tile starting at key `base` into registers.
   uint4 stage[kPerThread];
   long long stage_slot[kPerThread];
+  // A 64-key tile is one 64-token block: one uniform lookup gives its first slot.
   auto fetch = [&](int base) {
+    const long long sl0 = a.sv.slot(0, base);
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
       const int c = threadIdx.x + i * 512;
       const int key = c / kChunks, ch = c % kChunks;
-      const int s = base + key;
-      const long long sl = s < nmax ? a.sv.slot(0, s) : -1;
+      const long long sl = (sl0 >= 0 && base + key < nmax) ? sl0 + key : -1;
       stage_slot[i] = sl;
       stage[i] = sl >= 0 ? ld16(kbase + sl * Tr::kRowBytes + ch * 16) : make_uint4(0, 0, 0, 0);
     }
@@ -210,6 +306,11 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
     }
   };
   __shared__ int absent[2][kPrefillKeys];
+  // first radix digit of the top-k: each wave owns its query row's bins
+  __shared__ uint32_t wh[kPrefillQ][kTopkBins];
+  const bool hist = a.hist_mode == 2;
+  if (hist)
+    for (int i = lane; i < kTopkBins; i += 64) wh[wv][i] = 0u;
 
   int buf = 0;
   if (nmax > 0) {
@@ -253,13 +354,13 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
         const float sc = head_reduce(c0a, c1a, wt);
         const int s = base + key;
         if (g == 0 && s < n && row_ok) {
-          if (absent[buf][key]) {
-            srow[s] = neg_inf();
-          } else {
-            float v = sc;
-            if (DT == DSA_FP8_E4M3FN) v *= a.k_scale[a.sv.slot(0, s)];
-            srow[s] = v;
+          float v = neg_inf();
+          if (!absent[buf][key]) {
+            v = sc;
+            if (DT == DSA_FP8_E4M3FN) v *= a.k_scale[a.sv.slot(0, base) + key];
           }
+          srow[s] = v;
+          if (hist) atomicAdd(&wh[wv][score_key(v) >> 21], 1u);
         }
       }
     }
@@ -275,6 +376,10 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
   }
   if (a.fill_masked && row_ok) {
     for (long long s = n + lane; s < a.ld; s += 64) srow[s] = neg_inf();
+  }
+  if (hist && row_ok) {
+    uint32_t *hrow = a.hist + (long long)r * a.hist_stride;
+    for (int i = lane; i < kTopkBins; i += 64) hrow[i] = wh[wv][i];
   }
 }
 

@@ -23,6 +23,13 @@ struct IndexerArgs {
   long long ld;
   int q_begin, rows;
   int fill_masked;  // write -inf to scores[r, s] for n_t <= s < ld
+  // Optional 2048-bin histogram of score_key >> 21 per row (the top-k's first
+  // radix digit): hist_mode 1 adds into zeroed rows with atomics (decode:
+  // rows split over workgroups), 2 stores each row whole (prefill: one wave
+  // per row).  Row r's bins start at hist + r * hist_stride.
+  uint32_t *hist;
+  long long hist_stride;
+  int hist_mode;
 };
 
 struct TopkArgs {
@@ -32,7 +39,8 @@ struct TopkArgs {
   long long ld;
   int q_begin, rows;
   int32_t *idx;  // [rows, k]
-  uint32_t *ws;  // [rows, kTopkRowWords]
+  uint32_t *ws;  // [rows, row_words]
+  long long row_words;
   int slices;
 };
 
@@ -50,19 +58,25 @@ struct MlaArgs {
   float *part;  // [rows, n_split, H, Dv + 4] when n_split > 1 (acc[Dv], max, sum, pad)
 };
 
-// top-k workspace, per row, in 32-bit words
+// top-k workspace, per row, in 32-bit words: the first-digit histogram and two
+// counters (zeroed per call), then -- for the sliced path only -- the list of
+// selected positions and the candidate list (low 21 key bits, position).
 constexpr int kTopkBins = 2048;        // 11-bit radix digits
-constexpr int kTopkCap = 4096;         // candidates kept after the 22-bit prefix
-constexpr int kTopkHdrWords = 2 * kTopkBins + 64;  // two histograms + counters (zeroed per call)
+constexpr int kTopkCap = 16384;        // candidates listed per row by the sliced path
+constexpr int kTopkHdrWords = kTopkBins + 64;
 constexpr int kTopkMaxK = 2048;
-constexpr long long kTopkRowWords = kTopkHdrWords + kTopkMaxK + 2 * kTopkCap;
+constexpr long long kTopkSlicedRowWords = kTopkHdrWords + kTopkMaxK + 2 * kTopkCap;
 
 int topk_slices(int rows, int max_ctx);
+bool topk_sliced(int rows);
+inline long long topk_row_words(int rows) { return topk_sliced(rows) ? kTopkSlicedRowWords : kTopkHdrWords; }
 int mla_splits(int rows, int k);
 size_t mla_f32_lds(int H, int D, int k);
 
 hipError_t launch_index_scores(const IndexerArgs &a, hipStream_t s);
-hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+hipError_t launch_topk(const TopkArgs &a, hipStream_t s);         // zero + hist1 + select
+hipError_t launch_topk_zero(const TopkArgs &a, hipStream_t s);    // zero the per-row headers
+hipError_t launch_topk_select(const TopkArgs &a, hipStream_t s);  // collect + select (hist1 ready)
 hipError_t launch_sparse_mla(const MlaArgs &a, hipStream_t s);
 
 }  // namespace dsa

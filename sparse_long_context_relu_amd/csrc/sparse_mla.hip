@@ -6,40 +6,189 @@
 //
 // bf16 path (H = 128, D = 576, Dv = 512): a workgroup of 8 waves owns one
 // query (and one split of its selected rows).  Each 32-row tile is gathered
-// from HBM once into LDS, in two layouts: row-major for the logits and
-// transposed (value dim major) for the value product, so every head of the
-// query is served from the single fetch.  Wave w owns heads 16w..16w+15:
+// from HBM once, straight into LDS by the direct-to-LDS loads of gfx950 (no
+// staging registers), double-buffered so the next tile streams in while the
+// current one is multiplied; every head of the query is served from that one
+// fetch.  Wave w owns heads 16w..16w+15 (two waves per SIMD, so the MFMA
+// accumulators of one stay in architectural registers):
 //   S^T[rows, heads] = C_tile[rows, 576] . Q^T          (16x16x32 bf16 MFMA)
 //   online softmax in fp32 (base-2 exponent, running max and sum per head)
 //   O^T[dims, heads] += V^T[dims, rows] . P^T[rows, heads]
-// With several splits per query the unnormalised partials (acc, max, sum)
-// are merged by a second kernel in a fixed order.
+// V^T operands come from the row-major tile through the LDS transpose read
+// (ds_read_b64_tr_b16), so the tile is stored once.  With several splits per
+// query the unnormalised partials (acc, max, sum) are merged by a second
+// kernel in a fixed order.
 #include "kernels.h"
 
 namespace dsa {
 namespace {
 
 constexpr int kH = 128, kD = 576, kDv = 512;
-constexpr int kR = 32;              // latent rows per tile
-constexpr int kRowStride = 1168;    // bytes per row in the row-major tile (1152 + 16 pad)
-constexpr int kVtStride = 80;       // bytes per value dim in the transposed tile (64 + 16 pad)
-constexpr int kChunks = kD * 2 / 16;   // 72 16-byte chunks per row
-constexpr int kVChunks = kDv * 2 / 16; // 64 of them hold value dims
+constexpr int kHB = 1;                        // 16-head blocks per wave
+constexpr int kWaves = kH / (16 * kHB);       // 8 waves, one head block each
+constexpr int kThreads = kWaves * 64;
+constexpr int kR = 32;                        // latent rows per tile
+constexpr int kRowChunks = kD * 2 / 16 + 1;   // 72 data chunks + 1 pad: row stride 1168 B
+constexpr int kRowStride = kRowChunks * 16;
+constexpr int kTileChunks = kR * kRowChunks;  // 2336
+constexpr int kWaveLoads = (kTileChunks + kThreads - 1) / kThreads;  // 10 direct loads per wave
+constexpr int kKs = kD / 32;                  // 18 k-steps of the logits
+constexpr int kDb = kDv / 16;                 // 32 value-dim blocks
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kMaxSplitRows = 2048;
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int split_len(int k, int n_split) {
   int len = (k + n_split - 1) / n_split;
   return (len + kR - 1) / kR * kR;
 }
 
-__global__ __launch_bounds__(512) void mla_bf16_kernel(MlaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t rm[kR * kRowStride];
-  __shared__ __attribute__((aligned(16))) uint8_t vt[kDv * kVtStride];
-  __shared__ int rowok[kR];
+// Block order: the splits of one query are placed on the same XCD (workgroups
+// are dealt to the 8 XCDs round-robin by linear id), so its query rows are
+// fetched from HBM once and then served by that XCD's L2.
+__device__ __forceinline__ void mla_block(const MlaArgs &a, int &sp, int &r) {
+  const int total = a.n_split * a.rows;
+  int v = blockIdx.x;
+  if ((total & 7) == 0) v = (v & 7) * (total >> 3) + (v >> 3);
+  r = v / a.n_split;
+  sp = v - r * a.n_split;
+}
 
-  const int sp = blockIdx.x;
-  const int r = blockIdx.y;
+// One 16-byte direct-to-LDS load: lane l's 16 bytes land at lds_dst + 16 l.
+// It returns nothing in registers.  It is written out here because the
+// compiler's wait insertion cannot tell the two tile buffers apart and would
+// otherwise stall the consumer of one buffer on the loads still streaming into
+// the other; the kernel waits for these loads itself (s_waitcnt vmcnt(0) and a
+// barrier) before any wave reads the buffer they fill.
+__device__ __forceinline__ void lds_dma16(const void *gsrc, const uint4 *lds_dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_dst);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0), "v"(gsrc)
+               : "memory", "m0");
+}
+
+// Issue the direct-to-LDS gather of tile rows [j0, j0+32) of the split into
+// `tile`: lane l of a load writes LDS bytes base + 16 l.  Chunk position p
+// holds (row p/73, chunk p%73); the pad chunk and absent rows load a valid row
+// (`fallback`) so every LDS byte the MFMAs read is finite; absent rows are
+// masked in the softmax.
+__device__ __forceinline__ void issue_tile(uint4 *tile, const uint8_t *kv, const int *slots, int j0, int jend,
+                                           int fallback, int wv, int lane) {
+  // Keep the per-lane chunk coordinates from being hoisted out of the tile loop
+  // (they are cheap to recompute; holding them would cost registers).
+  asm volatile("" : "+v"(lane));
+#pragma unroll
+  for (int j = 0; j < kWaveLoads; ++j) {
+    const int base = (j * kWaves + wv) * 64;
+    const int p = base + lane;
+    if (base < kTileChunks) {
+      const int row = p / kRowChunks;
+      const int ch = p - row * kRowChunks;
+      int sl = (j0 + row < jend) ? slots[j0 + row] : -1;
+      if (sl < 0) sl = fallback;
+      const uint8_t *src = kv + (long long)sl * (kD * 2) + (ch < kRowChunks - 1 ? ch : 0) * 16;
+      if (p < kTileChunks) lds_dma16(src, tile + base);
+    }
+  }
+}
+
+// Logits, online softmax and value product for one resident tile.
+__device__ __forceinline__ void consume_tile(const uint8_t *tile, const int *slots, int j0, int jend,
+                                             const bf16x8 (&qb)[kHB][kKs], f32x4 (&acc)[kHB][kDb],
+                                             float (&m_run)[kHB], float (&l_run)[kHB], float scale2, int col,
+                                             int g) {
+  // ---- S^T for 32 rows x this wave's heads
+  f32x4 st[2][kHB];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int hb = 0; hb < kHB; ++hb) st[rb][hb] = zero_vec<f32x4>();
+#pragma unroll
+  for (int ks = 0; ks < kKs; ++ks)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4 *>(tile + (rb * 16 + col) * kRowStride + g * 16 + ks * 64));
+#pragma unroll
+      for (int hb = 0; hb < kHB; ++hb) st[rb][hb] = mfma16_bf16(a, qb[hb][ks], st[rb][hb]);
+    }
+  // ---- online softmax (base 2), one head per lane column and head block.
+  // Row validity of the tile as a wave-uniform 32-bit mask (bit j: row j present).
+  const int lane = lane_id();
+  const uint32_t rowmask = (uint32_t)__ballot(lane < kR && j0 + lane < jend && slots[j0 + (lane & (kR - 1))] >= 0);
+  bool ok[2][4];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) ok[rb][v] = (rowmask >> (rb * 16 + 4 * g + v)) & 1u;
+  bf16x8 pb[kHB];
+  bool rescale = false;
+  float alpha[kHB];
+#pragma unroll
+  for (int hb = 0; hb < kHB; ++hb) {
+    float mx = neg_inf();
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        st[rb][hb][v] = ok[rb][v] ? st[rb][hb][v] * scale2 : neg_inf();
+        mx = fmaxf(mx, st[rb][hb][v]);
+      }
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run[hb], mx);
+    alpha[hb] = m_run[hb] == neg_inf() ? 0.f : exp2f(m_run[hb] - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float pv = st[rb][hb][v] == neg_inf() ? 0.f : exp2f(st[rb][hb][v] - m_new);
+        psum += pv;
+        pb[hb][rb * 4 + v] = (__bf16)pv;
+      }
+    l_run[hb] = l_run[hb] * alpha[hb] + psum;
+    m_run[hb] = m_new;
+    rescale |= alpha[hb] != 1.f;
+  }
+  if (__any(rescale)) {
+#pragma unroll
+    for (int hb = 0; hb < kHB; ++hb)
+#pragma unroll
+      for (int db = 0; db < kDb; ++db)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[hb][db][v] *= alpha[hb];
+  }
+  // ---- O^T += V^T . P^T.  k-slots 0..3 = tile rows 4g+e, 4..7 = rows 16+4g+e (e = 0..3),
+  // matching the rows this lane holds in P^T.  Lane 4e+c of group g points the
+  // transpose read at row 4g+e (resp. 16+4g+e), dims d0+4c..d0+4c+3, and receives
+  // V[row_e][d0 + (lane%16)] for e = 0..3.
+  const int e = col >> 2, c = col & 3;
+  const uint8_t *v0 = tile + (4 * g + e) * kRowStride + c * 8;
+  const uint8_t *v1 = v0 + 16 * kRowStride;
+#pragma unroll
+  for (int db = 0; db < kDb; ++db) {
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(v0 + db * 32));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(v1 + db * 32));
+    const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+    for (int hb = 0; hb < kHB; ++hb) acc[hb][db] = mfma16_bf16(av, pb[hb], acc[hb][db]);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
+  __shared__ uint4 tile0[kTileChunks];
+  __shared__ uint4 tile1[kTileChunks];
+  __shared__ int slots[kMaxSplitRows];
+  __shared__ int fallback;
+
+  int sp, r;
+  mla_block(a, sp, r);
   const int t = a.q_begin + r;
   const int n = a.sv.candidates(t);
   const int b = a.sv.seq_of(t);
@@ -47,136 +196,92 @@ __global__ __launch_bounds__(512) void mla_bf16_kernel(MlaArgs a) {
   const int len = split_len(a.k, a.n_split);
   const int i0 = sp * len;
   const int i1 = i0 + len < a.k ? i0 + len : a.k;
+  const int rows = i1 > i0 ? i1 - i0 : 0;
 
   const int lane = lane_id();
   const int wv = threadIdx.x >> 6;
   const int col = lane & 15, g = lane >> 4;
-  const int h = wv * 16 + col;
 
-  // Q^T operand for this wave's 16 heads: lane holds head h, dims 32 ks + 8 g + [0, 8).
-  const uint8_t *qrow = reinterpret_cast<const uint8_t *>(a.q) + ((long long)t * kH + h) * (kD * 2);
-  bf16x8 qb[kD / 32];
-#pragma unroll
-  for (int ks = 0; ks < kD / 32; ++ks) qb[ks] = as_bf16x8(ld16(qrow + ks * 64 + g * 16));
-
-  f32x4 acc[kDv / 16];
-#pragma unroll
-  for (int db = 0; db < kDv / 16; ++db) acc[db] = zero_vec<f32x4>();
-  float m_run = neg_inf();
-  float l_run = 0.f;
-  const float scale2 = a.sm_scale * kLog2e;
-  const uint8_t *kv = reinterpret_cast<const uint8_t *>(a.kv);
-
-  for (int i = i0; i < i1; i += kR) {
-    // ---- gather the tile: 32 rows x 72 chunks over 512 threads
-    for (int c = threadIdx.x; c < kR * kChunks; c += 512) {
-      const int row = c / kChunks, ch = c - row * kChunks;
-      const int ii = i + row;
-      const int s = ii < i1 ? irow[ii] : -1;
-      const long long sl = (s >= 0 && s < n) ? a.sv.slot(b, s) : -1;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (sl >= 0) v = ld16(kv + sl * (kD * 2) + ch * 16);
-      *reinterpret_cast<uint4 *>(rm + row * kRowStride + ch * 16) = v;
-      if (ch < kVChunks) {
-        const uint16_t e[8] = {(uint16_t)(v.x & 0xffff), (uint16_t)(v.x >> 16), (uint16_t)(v.y & 0xffff),
-                               (uint16_t)(v.y >> 16),    (uint16_t)(v.z & 0xffff), (uint16_t)(v.z >> 16),
-                               (uint16_t)(v.w & 0xffff), (uint16_t)(v.w >> 16)};
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          *reinterpret_cast<uint16_t *>(vt + (ch * 8 + j) * kVtStride + row * 2) = e[j];
-      }
-      if (ch == 0) rowok[row] = sl >= 0;
-    }
-    __syncthreads();
-    bool any = false;
-#pragma unroll
-    for (int j = 0; j < kR; ++j) any |= rowok[j] != 0;
-    if (any) {
-      // ---- logits S^T for 32 rows x this wave's 16 heads
-      f32x4 st[2] = {zero_vec<f32x4>(), zero_vec<f32x4>()};
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const uint8_t *arow = rm + (rb * 16 + col) * kRowStride + g * 16;
-#pragma unroll
-        for (int ks = 0; ks < kD / 32; ++ks)
-          st[rb] = mfma16_bf16(as_bf16x8(*reinterpret_cast<const uint4 *>(arow + ks * 64)), qb[ks], st[rb]);
-      }
-      // ---- online softmax (base 2), per head = per lane column
-      float z[2][4];
-      float mx = neg_inf();
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = rb * 16 + 4 * g + v;
-          z[rb][v] = rowok[row] ? st[rb][v] * scale2 : neg_inf();
-          mx = fmaxf(mx, z[rb][v]);
-        }
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_run == neg_inf() ? 0.f : exp2f(m_run - m_new);
-      float p[2][4];
-      float psum = 0.f;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          p[rb][v] = z[rb][v] == neg_inf() ? 0.f : exp2f(z[rb][v] - m_new);
-          psum += p[rb][v];
-        }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < kDv / 16; ++db)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[db][v] *= alpha;
-      }
-      bf16x8 pb;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        pb[v] = (__bf16)p[0][v];
-        pb[4 + v] = (__bf16)p[1][v];
-      }
-      // ---- O^T += V^T . P^T: k-slots 0..3 = tile rows 4g.., 4..7 = rows 16 + 4g..
-#pragma unroll
-      for (int db = 0; db < kDv / 16; ++db) {
-        const uint8_t *vrow = vt + (db * 16 + col) * kVtStride;
-        const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + g * 8);
-        const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 32 + g * 8);
-        const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        acc[db] = mfma16_bf16(as_bf16x8(av), pb, acc[db]);
-      }
-    }
-    __syncthreads();
+  if (threadIdx.x == 0) fallback = -1;
+  __syncthreads();
+  // Slots of this split's rows (-1: absent), so the gather depends on LDS only.
+  for (int j = threadIdx.x; j < rows; j += kThreads) {
+    const int s = irow[i0 + j];
+    const int sl = (s >= 0 && s < n) ? (int)a.sv.slot(b, s) : -1;
+    slots[j] = sl;
+    if (sl >= 0) atomicMax(&fallback, sl);
   }
 
-  float l_tot = l_run + shfl_xor(l_run, 16);
-  l_tot += shfl_xor(l_tot, 32);
-  if (a.n_split == 1) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t *orow = reinterpret_cast<uint16_t *>(a.out) + ((long long)t * kH + h) * kDv;
+  // Q^T operands for this wave's heads: lane holds head 16 (kHB wv + hb) + col,
+  // dims 32 ks + 8 g + [0, 8).
+  bf16x8 qb[kHB][kKs];
 #pragma unroll
-    for (int db = 0; db < kDv / 16; ++db) {
-      const int d = db * 16 + 4 * g;
-      uint2 pk;
-      pk.x = (uint32_t)f32_to_bf16(acc[db][0] * inv) | ((uint32_t)f32_to_bf16(acc[db][1] * inv) << 16);
-      pk.y = (uint32_t)f32_to_bf16(acc[db][2] * inv) | ((uint32_t)f32_to_bf16(acc[db][3] * inv) << 16);
-      *reinterpret_cast<uint2 *>(orow + d) = pk;
-    }
-    if (a.lse != nullptr && g == 0)
-      a.lse[(long long)t * kH + h] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : neg_inf();
-  } else {
-    float *prow = a.part + (((long long)r * a.n_split + sp) * kH + h) * (kDv + 4);
+  for (int hb = 0; hb < kHB; ++hb) {
+    const uint8_t *qrow =
+        reinterpret_cast<const uint8_t *>(a.q) + ((long long)t * kH + (wv * kHB + hb) * 16 + col) * (kD * 2);
 #pragma unroll
-    for (int db = 0; db < kDv / 16; ++db) {
-      const int d = db * 16 + 4 * g;
-      *reinterpret_cast<float4 *>(prow + d) = make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+    for (int ks = 0; ks < kKs; ++ks) qb[hb][ks] = as_bf16x8(ld16(qrow + ks * 64 + g * 16));
+  }
+
+  f32x4 acc[kHB][kDb];
+  float m_run[kHB], l_run[kHB];
+#pragma unroll
+  for (int hb = 0; hb < kHB; ++hb) {
+#pragma unroll
+    for (int db = 0; db < kDb; ++db) acc[hb][db] = zero_vec<f32x4>();
+    m_run[hb] = neg_inf();
+    l_run[hb] = 0.f;
+  }
+  const float scale2 = a.sm_scale * kLog2e;
+  const uint8_t *kv = reinterpret_cast<const uint8_t *>(a.kv);
+  __syncthreads();
+  const int fb = fallback;
+
+  if (fb >= 0) {
+    const int ntiles = (rows + kR - 1) / kR;
+    issue_tile(tile0, kv, slots, 0, rows, fb, wv, lane);
+    for (int tt = 0; tt < ntiles; ++tt) {
+      // tile tt (in flight) lands; every wave is done with the other buffer
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      uint4 *cur = (tt & 1) ? tile1 : tile0;
+      uint4 *nxt = (tt & 1) ? tile0 : tile1;
+      if (tt + 1 < ntiles) issue_tile(nxt, kv, slots, (tt + 1) * kR, rows, fb, wv, lane);
+      consume_tile(reinterpret_cast<const uint8_t *>(cur), slots, tt * kR, rows, qb, acc, m_run, l_run, scale2,
+                   col, g);
     }
-    if (g == 0) {
-      prow[kDv] = m_run;
-      prow[kDv + 1] = l_tot;
+  }
+
+#pragma unroll
+  for (int hb = 0; hb < kHB; ++hb) {
+    const int h = (wv * kHB + hb) * 16 + col;
+    float l_tot = l_run[hb] + shfl_xor(l_run[hb], 16);
+    l_tot += shfl_xor(l_tot, 32);
+    if (a.n_split == 1) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      uint16_t *orow = reinterpret_cast<uint16_t *>(a.out) + ((long long)t * kH + h) * kDv;
+#pragma unroll
+      for (int db = 0; db < kDb; ++db) {
+        const int d = db * 16 + 4 * g;
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(acc[hb][db][0] * inv) | ((uint32_t)f32_to_bf16(acc[hb][db][1] * inv) << 16);
+        pk.y = (uint32_t)f32_to_bf16(acc[hb][db][2] * inv) | ((uint32_t)f32_to_bf16(acc[hb][db][3] * inv) << 16);
+        *reinterpret_cast<uint2 *>(orow + d) = pk;
+      }
+      if (a.lse != nullptr && g == 0)
+        a.lse[(long long)t * kH + h] = l_tot > 0.f ? (m_run[hb] + __log2f(l_tot)) * kLn2 : neg_inf();
+    } else {
+      float *prow = a.part + (((long long)r * a.n_split + sp) * kH + h) * (kDv + 4);
+#pragma unroll
+      for (int db = 0; db < kDb; ++db) {
+        const int d = db * 16 + 4 * g;
+        *reinterpret_cast<float4 *>(prow + d) =
+            make_float4(acc[hb][db][0], acc[hb][db][1], acc[hb][db][2], acc[hb][db][3]);
+      }
+      if (g == 0) {
+        prow[kDv] = m_run[hb];
+        prow[kDv + 1] = l_tot;
+      }
     }
   }
 }
@@ -315,7 +420,7 @@ hipError_t launch_sparse_mla(const MlaArgs &a, hipStream_t st) {
     hipLaunchKernelGGL(mla_f32_kernel, dim3(a.rows), dim3(256), lds, st, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(mla_bf16_kernel, dim3(a.n_split, a.rows), dim3(512), 0, st, a);
+  hipLaunchKernelGGL(mla_bf16_kernel, dim3(a.n_split * a.rows), dim3(kThreads), 0, st, a);
   if (a.n_split > 1) hipLaunchKernelGGL(mla_combine_kernel<true>, dim3(a.H, a.rows), dim3(128), 0, st, a);
   return hipGetLastError();
 }
