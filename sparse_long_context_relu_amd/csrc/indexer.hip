@@ -188,21 +188,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       tile[row * kChunks + (ch ^ (row & (kChunks - 1)))] = ok ? st[i] : make_uint4(0, 0, 0, 0);
     }
   };
-  uint4 stage[kPer];
+  // Two tiles in flight per wave: stage A holds tile i+1 (loaded one tile ago),
+  // stage B receives tile i+2 while tile i is multiplied from LDS.  The loop is
+  // unrolled by two so the stages keep fixed registers.
+  constexpr int kStep = kDecodeWaves * 32;
+  uint4 sa[kPer], sb[kPer];
   int base = c0 + wv * 32;
-  long long sl0 = -1;
+  long long sl0 = -1, sla = -1, slb = -1;
   if (base < c1) {
     sl0 = tile_slot(base);
-    fetch(base, sl0, stage);
-    put(stage, base, sl0);
+    fetch(base, sl0, sa);
+    put(sa, base, sl0);
   }
+  sla = base + kStep < c1 ? tile_slot(base + kStep) : -1;
+  fetch(base + kStep, sla, sa);
   // Drain the query, weight and first-tile loads here, so that no wait for them
   // lands inside the loop (where it would also wait for the prefetch).
   __builtin_amdgcn_s_waitcnt(0);
-  for (; base < c1; base += kDecodeWaves * 32) {
-    const int nb = base + kDecodeWaves * 32;
-    const long long sln = nb < c1 ? tile_slot(nb) : -1;
-    if (nb < c1) fetch(nb, sln, stage);            // next tile in flight during this one
+  // Scores of the tile resident in LDS (valid in every lane for key col).
+  auto consume = [&]() {
     typename Tr::Op kb[Tr::kSteps];
     const uint4 *trow = tile + col * kChunks;
 #pragma unroll
@@ -224,17 +228,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       c0a = Tr::mma(qa[0][ks], kb[ks], c0a);
       c1a = Tr::mma(qa[1][ks], kb[ks], c1a);
     }
-    const float sc = head_reduce(c0a, c1a, wt);
-    // Stage the next tile before storing this one's scores: the wait for the
-    // prefetched rows then does not also wait for the store to be acknowledged.
-    if (nb < c1) put(stage, nb, sln);              // the LDS reads above completed before the MFMAs
-    const int s = base + col;
+    return head_reduce(c0a, c1a, wt);
+  };
+  auto emit = [&](int tb, long long tsl, float sc) {
+    const int s = tb + col;
     if (g == 0 && s < c1) {
-      const float v = sl0 >= 0 ? sc * key_scale<DT>(a, sl0 + col) : neg_inf();
+      const float v = tsl >= 0 ? sc * key_scale<DT>(a, tsl + col) : neg_inf();
       srow[s] = v;
       if (hist) atomicAdd(&lh[score_key(v) >> 21], 1u);
     }
-    sl0 = sln;
+  };
+  for (; base < c1; base += 2 * kStep) {
+    const int b1 = base + kStep, b2 = base + 2 * kStep, b3 = base + 3 * kStep;
+    // LDS: tile `base` (slot sl0); stage A: tile b1 (sla); tile b2 -> stage B.
+    // The fetch is unconditional (past c1 it reads slot 0 and is discarded), so
+    // the compiler's wait counts stay exact on every path.
+    slb = b2 < c1 ? tile_slot(b2) : -1;
+    fetch(b2, slb, sb);
+    float sc = consume();
+    put(sa, b1, sla);                              // the LDS reads above completed before the MFMAs
+    emit(base, sl0, sc);
+    if (b1 >= c1) break;
+    // LDS: tile b1; stage B: tile b2 (slb); tile b3 -> stage A
+    const long long s1 = sla;
+    sla = b3 < c1 ? tile_slot(b3) : -1;
+    fetch(b3, sla, sa);
+    sc = consume();
+    put(sb, b2, slb);                              // past c1 this stores zeros that are never read
+    emit(b1, s1, sc);
+    sl0 = slb;
   }
   if (hist) {
     __syncthreads();
