@@ -24,14 +24,20 @@ namespace dsa {
 namespace {
 
 constexpr int kH = 128, kD = 576, kDv = 512;
-constexpr int kHB = 1;                        // 16-head blocks per wave
-constexpr int kWaves = kH / (16 * kHB);       // 8 waves, one head block each
+constexpr int kWaves = kH / 16;               // 8 waves, 16 heads each
 constexpr int kThreads = kWaves * 64;
 constexpr int kR = 32;                        // latent rows per tile
-constexpr int kRowChunks = kD * 2 / 16 + 1;   // 72 data chunks + 1 pad: row stride 1168 B
+// LDS tile layout: row r of the tile occupies kRowChunks 16-byte positions (72
+// data chunks + 2 pad); data chunk c of row r sits at position c ^ swz(r).  With
+// the 1184-byte row stride and this swizzle, the 16-byte logit-operand reads
+// (16 rows, same chunk) and the transpose reads of the value product (4 rows x
+// 32 bytes per 16 lanes) hit distinct LDS banks.
+constexpr int kDataChunks = kD * 2 / 16;      // 72
+constexpr int kRowChunks = kDataChunks + 2;   // row stride 1184 B
 constexpr int kRowStride = kRowChunks * 16;
-constexpr int kTileChunks = kR * kRowChunks;  // 2336
-constexpr int kWaveLoads = (kTileChunks + kThreads - 1) / kThreads;  // 10 direct loads per wave
+constexpr int kTileChunks = kR * kRowChunks;  // 2368
+constexpr int kWaveLoads = (kTileChunks + kThreads - 1) / kThreads;  // 5 direct loads per wave
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 constexpr int kKs = kD / 32;                  // 18 k-steps of the logits
 constexpr int kDb = kDv / 16;                 // 32 value-dim blocks
 constexpr float kLog2e = 1.4426950408889634f;
@@ -40,7 +46,14 @@ constexpr int kMaxSplitRows = 2048;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
-typedef __attribute__((address_space(3))) void lds_void;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+
+// Running maxima are raised only when a tile's maximum exceeds them by more than
+// this many binary orders of magnitude; in between, the softmax weights of a
+// tile stay below 2^kLazy, exact in fp32 and in bf16 (the final result divides
+// by the same running sum, so it does not depend on the base).
+constexpr float kLazy = 8.f;
 
 __device__ __forceinline__ int split_len(int k, int n_split) {
   int len = (k + n_split - 1) / n_split;
@@ -58,133 +71,176 @@ __device__ __forceinline__ void mla_block(const MlaArgs &a, int &sp, int &r) {
   sp = v - r * a.n_split;
 }
 
-// One 16-byte direct-to-LDS load: lane l's 16 bytes land at lds_dst + 16 l.
-// It returns nothing in registers.  It is written out here because the
-// compiler's wait insertion cannot tell the two tile buffers apart and would
-// otherwise stall the consumer of one buffer on the loads still streaming into
-// the other; the kernel waits for these loads itself (s_waitcnt vmcnt(0) and a
-// barrier) before any wave reads the buffer they fill.
-__device__ __forceinline__ void lds_dma16(const void *gsrc, const uint4 *lds_dst) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_dst);
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// One 16-byte direct-to-LDS load: lane l's 16 bytes land at LDS address
+// m0 + 16 l (m0 wave-uniform).  It returns nothing in registers.  It is written
+// out here because the compiler's wait insertion cannot tell the two tile
+// buffers apart and would otherwise stall the consumer of one buffer on the
+// loads still streaming into the other; the kernel waits for these loads itself
+// (s_waitcnt vmcnt(0) and a barrier) before any wave reads the buffer they fill.
+__device__ __forceinline__ void lds_dma16(const void *gsrc, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :
                : "s"(m0), "v"(gsrc)
                : "memory", "m0");
 }
 
-// Issue the direct-to-LDS gather of tile rows [j0, j0+32) of the split into
-// `tile`: lane l of a load writes LDS bytes base + 16 l.  Chunk position p
-// holds (row p/73, chunk p%73); the pad chunk and absent rows load a valid row
-// (`fallback`) so every LDS byte the MFMAs read is finite; absent rows are
-// masked in the softmax.
-__device__ __forceinline__ void issue_tile(uint4 *tile, const uint8_t *kv, const int *slots, int j0, int jend,
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8):
+// wait for vector-memory counts <= 0 / <= 4, leave the others free.
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitVm4 = 0x0F74;
+constexpr int kBufs = 3;
+
+// Workgroup barrier without a memory fence: the fence of __syncthreads would
+// also wait for the tile loads still streaming into the other buffers.  LDS
+// reads are complete once their values are used, and the direct-to-LDS writes
+// are covered by each wave's own s_waitcnt before it arrives here.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Issue the direct-to-LDS gather of split rows [j0, j0+32) into the tile at LDS
+// address `tile`.  Position p of the tile is (row p/74, slot p%74) and holds data
+// chunk slot ^ swz(row) of that row; a wave's j-th load covers positions
+// (8 j + wv) 64 + [0, 64).  The pad chunks and
+// absent rows (slot -1) load a valid row (`fallback`), so every LDS byte the
+// MFMAs read is finite; absent rows are masked in the softmax.  `slots` holds
+// -1 past the split's last row, far enough for every lane's row.
+__device__ __forceinline__ void issue_tile(uint32_t tile, const uint8_t *kv, const int *slots, int j0,
                                            int fallback, int wv, int lane) {
-  // Keep the per-lane chunk coordinates from being hoisted out of the tile loop
-  // (they are cheap to recompute; holding them would cost registers).
+  // Recompute the per-lane coordinates on every call rather than keep them live
+  // across the tile loop (the registers are needed by the MFMA operands).
   asm volatile("" : "+v"(lane));
+  int p = wv * 64 + lane;
+  int row = p / kRowChunks;
+  int ch = p - row * kRowChunks;
 #pragma unroll
   for (int j = 0; j < kWaveLoads; ++j) {
-    const int base = (j * kWaves + wv) * 64;
-    const int p = base + lane;
+    const int base = (j * kWaves + wv) * 64;      // wave-uniform
     if (base < kTileChunks) {
-      const int row = p / kRowChunks;
-      const int ch = p - row * kRowChunks;
-      int sl = (j0 + row < jend) ? slots[j0 + row] : -1;
-      if (sl < 0) sl = fallback;
-      const uint8_t *src = kv + (long long)sl * (kD * 2) + (ch < kRowChunks - 1 ? ch : 0) * 16;
-      if (p < kTileChunks) lds_dma16(src, tile + base);
+      int sl = slots[j0 + row];
+      sl = sl < 0 ? fallback : sl;
+      const int dc = ch < kDataChunks ? ch ^ swz(row) : 0;
+      const uint8_t *src = kv + (long long)sl * (kD * 2) + dc * 16;
+      if (base + 64 <= kTileChunks || p < kTileChunks) lds_dma16(src, tile + base * 16);
+    }
+    // next load: p += 512 = 6 * 74 + 68
+    p += kWaves * 64;
+    row += (kWaves * 64) / kRowChunks;
+    ch += (kWaves * 64) % kRowChunks;
+    if (ch >= kRowChunks) {
+      ch -= kRowChunks;
+      row += 1;
     }
   }
 }
 
-// Logits, online softmax and value product for one resident tile.
-__device__ __forceinline__ void consume_tile(const uint8_t *tile, const int *slots, int j0, int jend,
-                                             const bf16x8 (&qb)[kHB][kKs], f32x4 (&acc)[kHB][kDb],
-                                             float (&m_run)[kHB], float (&l_run)[kHB], float scale2, int col,
-                                             int g) {
-  // ---- S^T for 32 rows x this wave's heads
-  f32x4 st[2][kHB];
+// Logits, online softmax and value product for the tile at LDS address `tile`.
+//
+// The operand reads are issued ahead of the MFMAs that consume them (fixed
+// instruction groups below), so several LDS reads are in flight while the
+// matrix core works.
+__device__ __forceinline__ void consume_tile(uint32_t tile, const int *slots, int j0, const bf16x8 (&qb)[kKs],
+                                             f32x4 (&acc)[kDb], float &m_run, float &l_run, float scale2,
+                                             uint32_t qk_off, uint32_t pv_even, uint32_t pv_odd, int g) {
+  // ---- S^T for 32 rows x this wave's 16 heads.  The 36 operand reads go in
+  // batches of kBatch, each batch issued before the MFMAs of the previous one
+  // (scheduling barriers keep the compiler from sinking the reads to their uses).
+  constexpr int kBatch = 3;
+  constexpr int kSteps = 2 * kKs / kBatch;
+  f32x4 st[2] = {zero_vec<f32x4>(), zero_vec<f32x4>()};
+  u32x4 fr[2][kBatch];
+  auto read = [&](int i, int buf) {
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int hb = 0; hb < kHB; ++hb) st[rb][hb] = zero_vec<f32x4>();
-#pragma unroll
-  for (int ks = 0; ks < kKs; ++ks)
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4 *>(tile + (rb * 16 + col) * kRowStride + g * 16 + ks * 64));
-#pragma unroll
-      for (int hb = 0; hb < kHB; ++hb) st[rb][hb] = mfma16_bf16(a, qb[hb][ks], st[rb][hb]);
+    for (int u = 0; u < kBatch; ++u) {
+      const int q = i * kBatch + u, ks = q >> 1, rb = q & 1;
+      fr[buf][u] = *(lds_u32x4 *)(uintptr_t)(tile + qk_off + rb * 16 * kRowStride + ks * 64);
     }
-  // ---- online softmax (base 2), one head per lane column and head block.
-  // Row validity of the tile as a wave-uniform 32-bit mask (bit j: row j present).
+  };
+  read(0, 0);
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    if (i + 1 < kSteps) read(i + 1, (i + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int q = i * kBatch + u, ks = q >> 1, rb = q & 1;
+      st[rb] = mfma16_bf16(__builtin_bit_cast(bf16x8, fr[i & 1][u]), qb[ks], st[rb]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- online softmax (base 2), one head per lane column.
+  // Row validity of the tile as a wave-uniform mask (bit j: row j present).
   const int lane = lane_id();
-  const uint32_t rowmask = (uint32_t)__ballot(lane < kR && j0 + lane < jend && slots[j0 + (lane & (kR - 1))] >= 0);
-  bool ok[2][4];
+  const uint32_t rowmask = (uint32_t)__ballot(lane < kR && slots[j0 + (lane & (kR - 1))] >= 0);
+  const uint32_t mine = rowmask >> (4 * g);     // bit v: row 4g+v; bit 16+v: row 16+4g+v
+  float mx = neg_inf();
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) ok[rb][v] = (rowmask >> (rb * 16 + 4 * g + v)) & 1u;
-  bf16x8 pb[kHB];
-  bool rescale = false;
-  float alpha[kHB];
+    for (int v = 0; v < 4; ++v) {
+      st[rb][v] = ((mine >> (16 * rb + v)) & 1u) ? st[rb][v] * scale2 : neg_inf();
+      mx = fmaxf(mx, st[rb][v]);
+    }
+  mx = fmaxf(mx, shfl_xor(mx, 16));
+  mx = fmaxf(mx, shfl_xor(mx, 32));
+  if (__any(mx > m_run + kLazy)) {
+    // raise the base of every head whose maximum moved (a head with no row yet
+    // present keeps -inf and a zero accumulator)
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = m_run == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
 #pragma unroll
-  for (int hb = 0; hb < kHB; ++hb) {
-    float mx = neg_inf();
+    for (int db = 0; db < kDb; ++db)
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        st[rb][hb][v] = ok[rb][v] ? st[rb][hb][v] * scale2 : neg_inf();
-        mx = fmaxf(mx, st[rb][hb][v]);
-      }
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run[hb], mx);
-    alpha[hb] = m_run[hb] == neg_inf() ? 0.f : exp2f(m_run[hb] - m_new);
-    float psum = 0.f;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float pv = st[rb][hb][v] == neg_inf() ? 0.f : exp2f(st[rb][hb][v] - m_new);
-        psum += pv;
-        pb[hb][rb * 4 + v] = (__bf16)pv;
-      }
-    l_run[hb] = l_run[hb] * alpha[hb] + psum;
-    m_run[hb] = m_new;
-    rescale |= alpha[hb] != 1.f;
+      for (int v = 0; v < 4; ++v) acc[db][v] *= alpha;
+    m_run = m_new;
   }
-  if (__any(rescale)) {
+  // exponent base 0 while the head has seen nothing: -inf - 0 stays -inf (weight 0)
+  const float base = m_run == neg_inf() ? 0.f : m_run;
+  bf16x8 pb;
+  float psum = 0.f;
 #pragma unroll
-    for (int hb = 0; hb < kHB; ++hb)
+  for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int db = 0; db < kDb; ++db)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[hb][db][v] *= alpha[hb];
-  }
+    for (int v = 0; v < 4; ++v) {
+      const float pv = __builtin_amdgcn_exp2f(st[rb][v] - base);
+      psum += pv;
+      pb[rb * 4 + v] = (__bf16)pv;
+    }
+  l_run += psum;
   // ---- O^T += V^T . P^T.  k-slots 0..3 = tile rows 4g+e, 4..7 = rows 16+4g+e (e = 0..3),
   // matching the rows this lane holds in P^T.  Lane 4e+c of group g points the
   // transpose read at row 4g+e (resp. 16+4g+e), dims d0+4c..d0+4c+3, and receives
-  // V[row_e][d0 + (lane%16)] for e = 0..3.
-  const int e = col >> 2, c = col & 3;
-  const uint8_t *v0 = tile + (4 * g + e) * kRowStride + c * 8;
-  const uint8_t *v1 = v0 + 16 * kRowStride;
+  // V[row_e][d0 + (lane%16)] for e = 0..3.  The swizzle permutes chunks within
+  // aligned groups of four, so even and odd value blocks have their own lane offsets.
 #pragma unroll
   for (int db = 0; db < kDb; ++db) {
-    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(v0 + db * 32));
-    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(v1 + db * 32));
+    const uint32_t v0 = tile + ((db & 1) ? pv_odd : pv_even) + (db >> 1) * 64;
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)v0);
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)(v0 + 16 * kRowStride));
     const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-    for (int hb = 0; hb < kHB; ++hb) acc[hb][db] = mfma16_bf16(av, pb[hb], acc[hb][db]);
+    acc[db] = mfma16_bf16(av, pb, acc[db]);
   }
+  constexpr int kAheadV = 3;     // 64 transpose reads, 32 MFMAs
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAheadV, 1);
+#pragma unroll
+  for (int i = 0; i < kDb - kAheadV; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, kAheadV, 1);
 }
 
 __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
-  __shared__ uint4 tile0[kTileChunks];
-  __shared__ uint4 tile1[kTileChunks];
-  __shared__ int slots[kMaxSplitRows];
+  __shared__ uint4 tiles[kBufs][kTileChunks];
+  __shared__ int slots[kMaxSplitRows + 2 * kR];
   __shared__ int fallback;
 
   int sp, r;
@@ -197,137 +253,163 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
   const int i0 = sp * len;
   const int i1 = i0 + len < a.k ? i0 + len : a.k;
   const int rows = i1 > i0 ? i1 - i0 : 0;
+  const int ntiles = (rows + kR - 1) / kR;
 
   const int lane = lane_id();
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, g = lane >> 4;
 
   if (threadIdx.x == 0) fallback = -1;
   __syncthreads();
-  // Slots of this split's rows (-1: absent), so the gather depends on LDS only.
-  for (int j = threadIdx.x; j < rows; j += kThreads) {
-    const int s = irow[i0 + j];
-    const int sl = (s >= 0 && s < n) ? (int)a.sv.slot(b, s) : -1;
+  // Slots of this split's rows (-1: absent, and past the last row), so the
+  // gather depends on LDS only.
+  for (int j = threadIdx.x; j < ntiles * kR + kR; j += kThreads) {
+    int sl = -1;
+    if (j < rows) {
+      const int s = irow[i0 + j];
+      sl = (s >= 0 && s < n) ? (int)a.sv.slot(b, s) : -1;
+      if (sl >= 0) atomicMax(&fallback, sl);
+    }
     slots[j] = sl;
-    if (sl >= 0) atomicMax(&fallback, sl);
   }
 
-  // Q^T operands for this wave's heads: lane holds head 16 (kHB wv + hb) + col,
+  // Q^T operands for this wave's heads: lane holds head 16 wv + col,
   // dims 32 ks + 8 g + [0, 8).
-  bf16x8 qb[kHB][kKs];
+  bf16x8 qb[kKs];
+  {
+    const uint8_t *qrow = reinterpret_cast<const uint8_t *>(a.q) + ((long long)t * kH + wv * 16 + col) * (kD * 2);
 #pragma unroll
-  for (int hb = 0; hb < kHB; ++hb) {
-    const uint8_t *qrow =
-        reinterpret_cast<const uint8_t *>(a.q) + ((long long)t * kH + (wv * kHB + hb) * 16 + col) * (kD * 2);
-#pragma unroll
-    for (int ks = 0; ks < kKs; ++ks) qb[hb][ks] = as_bf16x8(ld16(qrow + ks * 64 + g * 16));
+    for (int ks = 0; ks < kKs; ++ks) qb[ks] = as_bf16x8(ld16(qrow + ks * 64 + g * 16));
   }
 
-  f32x4 acc[kHB][kDb];
-  float m_run[kHB], l_run[kHB];
+  f32x4 acc[kDb];
 #pragma unroll
-  for (int hb = 0; hb < kHB; ++hb) {
-#pragma unroll
-    for (int db = 0; db < kDb; ++db) acc[hb][db] = zero_vec<f32x4>();
-    m_run[hb] = neg_inf();
-    l_run[hb] = 0.f;
-  }
+  for (int db = 0; db < kDb; ++db) acc[db] = zero_vec<f32x4>();
+  float m_run = neg_inf(), l_run = 0.f;
   const float scale2 = a.sm_scale * kLog2e;
   const uint8_t *kv = reinterpret_cast<const uint8_t *>(a.kv);
+  // per-lane LDS byte offsets: the logit operand (row col, data chunk 4 ks + g)
+  // and the transpose reads (row 4 g + col/4, dims 4 (col%4).. of each 16-dim block)
+  const uint32_t qk_off = col * kRowStride + (g ^ swz(col)) * 16;
+  const int vc = col & 3;
+  const uint32_t pv_row = (4 * g + (col >> 2)) * kRowStride + (vc & 1) * 8;
+  const uint32_t pv_even = pv_row + (((vc >> 1)) ^ g) * 16;
+  const uint32_t pv_odd = pv_row + ((2 + (vc >> 1)) ^ g) * 16;
+  const uint32_t tile_lds = lds_addr(&tiles[0][0]);
+  constexpr uint32_t kTileBytes = kTileChunks * 16;
   __syncthreads();
   const int fb = fallback;
 
   if (fb >= 0) {
-    const int ntiles = (rows + kR - 1) / kR;
-    issue_tile(tile0, kv, slots, 0, rows, fb, wv, lane);
+    // Three tile buffers: tiles tt+1 and tt+2 stream in while tile tt is used.
+    issue_tile(tile_lds, kv, slots, 0, fb, wv, lane);
+    // Drain the query operand loads (with tile 0) here, so that no wait for them
+    // is placed inside the loop, where it would also wait for the prefetches.
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    if (ntiles > 1) issue_tile(tile_lds + kTileBytes, kv, slots, kR, fb, wv, lane);
+    int cur = 0;
     for (int tt = 0; tt < ntiles; ++tt) {
-      // tile tt (in flight) lands; every wave is done with the other buffer
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      uint4 *cur = (tt & 1) ? tile1 : tile0;
-      uint4 *nxt = (tt & 1) ? tile0 : tile1;
-      if (tt + 1 < ntiles) issue_tile(nxt, kv, slots, (tt + 1) * kR, rows, fb, wv, lane);
-      consume_tile(reinterpret_cast<const uint8_t *>(cur), slots, tt * kR, rows, qb, acc, m_run, l_run, scale2,
-                   col, g);
+      // This wave's loads of tile tt have landed once at most the (four or five)
+      // loads of tile tt+1 are outstanding; the barrier then covers every wave's,
+      // and also orders every wave's reads of tile tt-1 before its buffer is refilled.
+      if (tt + 1 < ntiles)
+        __builtin_amdgcn_s_waitcnt(kWaitVm4);
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      lds_barrier();
+      if (tt + 2 < ntiles) {
+        const int nb = cur == 0 ? 2 : cur - 1;     // (tt + 2) % 3
+        issue_tile(tile_lds + nb * kTileBytes, kv, slots, (tt + 2) * kR, fb, wv, lane);
+      }
+      consume_tile(tile_lds + cur * kTileBytes, slots, tt * kR, qb, acc, m_run, l_run, scale2, qk_off, pv_even,
+                   pv_odd, g);
+      cur = cur == 2 ? 0 : cur + 1;
     }
   }
 
+  const int h = wv * 16 + col;
+  float l_tot = l_run + shfl_xor(l_run, 16);
+  l_tot += shfl_xor(l_tot, 32);
+  if (a.n_split == 1) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t *orow = reinterpret_cast<uint16_t *>(a.out) + ((long long)t * kH + h) * kDv;
 #pragma unroll
-  for (int hb = 0; hb < kHB; ++hb) {
-    const int h = (wv * kHB + hb) * 16 + col;
-    float l_tot = l_run[hb] + shfl_xor(l_run[hb], 16);
-    l_tot += shfl_xor(l_tot, 32);
-    if (a.n_split == 1) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      uint16_t *orow = reinterpret_cast<uint16_t *>(a.out) + ((long long)t * kH + h) * kDv;
+    for (int db = 0; db < kDb; ++db) {
+      const int d = db * 16 + 4 * g;
+      uint2 pk;
+      pk.x = (uint32_t)f32_to_bf16(acc[db][0] * inv) | ((uint32_t)f32_to_bf16(acc[db][1] * inv) << 16);
+      pk.y = (uint32_t)f32_to_bf16(acc[db][2] * inv) | ((uint32_t)f32_to_bf16(acc[db][3] * inv) << 16);
+      *reinterpret_cast<uint2 *>(orow + d) = pk;
+    }
+    if (a.lse != nullptr && g == 0)
+      a.lse[(long long)t * kH + h] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : neg_inf();
+  } else {
+    float *prow = a.part + (((long long)r * a.n_split + sp) * kH + h) * (kDv + 4);
 #pragma unroll
-      for (int db = 0; db < kDb; ++db) {
-        const int d = db * 16 + 4 * g;
-        uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16(acc[hb][db][0] * inv) | ((uint32_t)f32_to_bf16(acc[hb][db][1] * inv) << 16);
-        pk.y = (uint32_t)f32_to_bf16(acc[hb][db][2] * inv) | ((uint32_t)f32_to_bf16(acc[hb][db][3] * inv) << 16);
-        *reinterpret_cast<uint2 *>(orow + d) = pk;
-      }
-      if (a.lse != nullptr && g == 0)
-        a.lse[(long long)t * kH + h] = l_tot > 0.f ? (m_run[hb] + __log2f(l_tot)) * kLn2 : neg_inf();
-    } else {
-      float *prow = a.part + (((long long)r * a.n_split + sp) * kH + h) * (kDv + 4);
-#pragma unroll
-      for (int db = 0; db < kDb; ++db) {
-        const int d = db * 16 + 4 * g;
-        *reinterpret_cast<float4 *>(prow + d) =
-            make_float4(acc[hb][db][0], acc[hb][db][1], acc[hb][db][2], acc[hb][db][3]);
-      }
-      if (g == 0) {
-        prow[kDv] = m_run[hb];
-        prow[kDv + 1] = l_tot;
-      }
+    for (int db = 0; db < kDb; ++db) {
+      const int d = db * 16 + 4 * g;
+      *reinterpret_cast<float4 *>(prow + d) = make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+    }
+    if (g == 0) {
+      prow[kDv] = m_run;
+      prow[kDv + 1] = l_tot;
     }
   }
 }
 
-// Merge the split partials of one (query, head) in split order.
-template <bool BF16>
-__global__ __launch_bounds__(128) void mla_combine_kernel(MlaArgs a) {
-  const int h = blockIdx.x, r = blockIdx.y;
+// Merge the split partials of one (query, head): one wave per head, each lane
+// owning 8 of the 512 value dims.  Lane s < n_split reads split s's running
+// maximum and sum; the loads of up to eight splits' accumulators are issued
+// together, and the weighted sum runs in split order.
+__global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
+  const int lane = lane_id();
+  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int r = blockIdx.y;
   const int t = a.q_begin + r;
-  const int H = a.H, Dv = a.Dv;
-  const long long stride = (long long)H * (Dv + 4);
-  const float *base = a.part + ((long long)r * a.n_split * H + h) * (Dv + 4);
-  float M = neg_inf();
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, base[s * stride + Dv]);
-  float L = 0.f;
-  for (int s = 0; s < a.n_split; ++s) {
-    const float ms = base[s * stride + Dv];
-    if (ms != neg_inf()) L += exp2f(ms - M) * base[s * stride + Dv + 1];
+  const int ns = a.n_split;
+  const long long stride = (long long)kH * (kDv + 4);
+  const float *base = a.part + ((long long)r * ns * kH + h) * (kDv + 4);
+  float ms = neg_inf(), ls = 0.f;
+  if (lane < ns) {
+    ms = base[lane * stride + kDv];
+    ls = base[lane * stride + kDv + 1];
   }
+  const float M = wave_max(ms);
+  const float w = ms == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+  const float L = wave_sum(w * ls);
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  for (int d = threadIdx.x * 4; d < Dv; d += 128 * 4) {
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < a.n_split; ++s) {
-      const float ms = base[s * stride + Dv];
-      if (ms == neg_inf()) continue;
-      const float wgt = exp2f(ms - M);
-      const float4 v = *reinterpret_cast<const float4 *>(base + s * stride + d);
-      o.x = fmaf(wgt, v.x, o.x);
-      o.y = fmaf(wgt, v.y, o.y);
-      o.z = fmaf(wgt, v.z, o.z);
-      o.w = fmaf(wgt, v.w, o.w);
-    }
-    const long long ob = ((long long)t * H + h) * Dv + d;
-    if (BF16) {
-      uint16_t *out = reinterpret_cast<uint16_t *>(a.out);
-      uint2 pk;
-      pk.x = (uint32_t)f32_to_bf16(o.x * inv) | ((uint32_t)f32_to_bf16(o.y * inv) << 16);
-      pk.y = (uint32_t)f32_to_bf16(o.z * inv) | ((uint32_t)f32_to_bf16(o.w * inv) << 16);
-      *reinterpret_cast<uint2 *>(out + ob) = pk;
-    } else {
-      float *out = reinterpret_cast<float *>(a.out);
-      *reinterpret_cast<float4 *>(out + ob) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
-    }
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < ns; s0 += 8) {
+    float4 v[8][2];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < ns) {
+        const float *p = base + (s0 + u) * stride + lane * 4;
+        v[u][0] = *reinterpret_cast<const float4 *>(p);
+        v[u][1] = *reinterpret_cast<const float4 *>(p + kDv / 2);
+      }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < ns) {
+        const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), s0 + u));
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          o[4 * hf + 0] = fmaf(wu, v[u][hf].x, o[4 * hf + 0]);
+          o[4 * hf + 1] = fmaf(wu, v[u][hf].y, o[4 * hf + 1]);
+          o[4 * hf + 2] = fmaf(wu, v[u][hf].z, o[4 * hf + 2]);
+          o[4 * hf + 3] = fmaf(wu, v[u][hf].w, o[4 * hf + 3]);
+        }
+      }
   }
-  if (threadIdx.x == 0 && a.lse != nullptr)
-    a.lse[(long long)t * H + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : neg_inf();
+  uint16_t *orow = reinterpret_cast<uint16_t *>(a.out) + ((long long)t * kH + h) * kDv;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    uint2 pk;
+    pk.x = (uint32_t)f32_to_bf16(o[4 * hf + 0] * inv) | ((uint32_t)f32_to_bf16(o[4 * hf + 1] * inv) << 16);
+    pk.y = (uint32_t)f32_to_bf16(o[4 * hf + 2] * inv) | ((uint32_t)f32_to_bf16(o[4 * hf + 3] * inv) << 16);
+    *reinterpret_cast<uint2 *>(orow + hf * (kDv / 2) + lane * 4) = pk;
+  }
+  if (lane == 0 && a.lse != nullptr) a.lse[(long long)t * kH + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : neg_inf();
 }
 
 // fp32, small shapes (H <= 16, D <= 128, k <= 1024): one workgroup per query,
@@ -416,12 +498,16 @@ hipError_t launch_sparse_mla(const MlaArgs &a, hipStream_t st) {
   if (a.rows <= 0) return hipSuccess;
   if (a.dtype == DSA_F32) {
     const size_t lds = mla_f32_lds(a.H, a.D, a.k);
-    if (lds > 65536) hipFuncSetAttribute((const void *)mla_f32_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (lds > 65536) {
+      const hipError_t e =
+          hipFuncSetAttribute((const void *)mla_f32_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(mla_f32_kernel, dim3(a.rows), dim3(256), lds, st, a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(mla_bf16_kernel, dim3(a.n_split * a.rows), dim3(kThreads), 0, st, a);
-  if (a.n_split > 1) hipLaunchKernelGGL(mla_combine_kernel<true>, dim3(a.H, a.rows), dim3(128), 0, st, a);
+  if (a.n_split > 1) hipLaunchKernelGGL(mla_combine_kernel, dim3(kH / 4, a.rows), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

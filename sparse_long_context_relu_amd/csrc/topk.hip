@@ -433,15 +433,19 @@ hipError_t launch_topk_select(const TopkArgs &a, hipStream_t st) {
   if (topk_sliced(a.rows)) {
     hipLaunchKernelGGL(topk_collect_kernel, dim3(a.slices, a.rows), dim3(kNT), 0, st, a);
     const size_t lds = (size_t)(2 * Wmax + kTopkBins + 2 * kLdsCap) * sizeof(uint32_t);
-    if (lds > 65536)
-      hipFuncSetAttribute((const void *)topk_select_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds);
+    if (lds > 65536) {
+      const hipError_t e = hipFuncSetAttribute((const void *)topk_select_kernel<true>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(topk_select_kernel<true>, dim3(a.rows), dim3(kRowNT), lds, st, a);
   } else {
     const size_t lds = (size_t)(2 * Wmax + kTopkBins + 2 * kLdsCap) * sizeof(uint32_t);
-    if (lds > 65536)
-      hipFuncSetAttribute((const void *)topk_select_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds);
+    if (lds > 65536) {
+      const hipError_t e = hipFuncSetAttribute((const void *)topk_select_kernel<false>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(topk_select_kernel<false>, dim3(a.rows), dim3(kRowNT), lds, st, a);
   }
   return hipGetLastError();
