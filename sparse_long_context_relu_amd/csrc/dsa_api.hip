@@ -98,7 +98,9 @@ long long mla_ws_bytes(const dsa_dims *d, int rows) {
   return (long long)rows * ns * d->heads * (d->v_dim + 4) * (long long)sizeof(float);
 }
 
-long long topk_ws_bytes(int rows) { return (long long)rows * topk_row_words(rows) * (long long)sizeof(uint32_t); }
+long long topk_ws_bytes(int rows, int max_ctx) {
+  return (long long)rows * topk_layout(rows, max_ctx).row_words * (long long)sizeof(uint32_t);
+}
 
 int forward_chunk_rows(const dsa_seqs *s) {
   if (s->mode == DSA_DECODE || s->num_q == 0) return s->num_q;
@@ -120,7 +122,7 @@ ForwardLayout forward_layout(const dsa_seqs *s, const dsa_dims *d) {
   L.off_scores = 0;
   L.off_idx = align256(L.ld * L.chunk * 4);
   L.off_topk = L.off_idx + align256((long long)L.chunk * d->topk * 4);
-  L.off_mla = L.off_topk + align256(topk_ws_bytes(L.chunk));
+  L.off_mla = L.off_topk + align256(topk_ws_bytes(L.chunk, s->max_ctx));
   L.total = L.off_mla + align256(mla_ws_bytes(d, L.chunk));
   return L;
 }
@@ -166,8 +168,11 @@ TopkArgs topk_args(const dsa_seqs *s, int k, const float *scores, long long ld, 
   a.rows = rows;
   a.idx = idx;
   a.ws = reinterpret_cast<uint32_t *>(ws);
-  a.row_words = topk_row_words(rows);
-  a.slices = topk_slices(rows, s->max_ctx);
+  const TopkLayout L = topk_layout(rows, s->max_ctx);
+  a.row_words = L.row_words;
+  a.slices = L.slices;
+  a.slice_len = L.slice_len;
+  a.sel_seg = L.sel_seg;
   return a;
 }
 
@@ -209,7 +214,7 @@ DSA_EXPORT size_t dsa_workspace_size(int op, const dsa_seqs *seqs, const dsa_dim
       return 0;
     case DSA_OP_TOPK:
       if (check_k(dims->topk) != DSA_OK) return 0;
-      return (size_t)topk_ws_bytes(seqs->num_q);
+      return (size_t)topk_ws_bytes(seqs->num_q, seqs->max_ctx);
     case DSA_OP_SPARSE_MLA:
       if (check_mla_dims(dims) != DSA_OK) return 0;
       return (size_t)mla_ws_bytes(dims, seqs->num_q);
@@ -241,7 +246,7 @@ DSA_EXPORT int dsa_topk(const dsa_seqs *seqs, int32_t k, const float *scores, in
   if (int e = check_k(k)) return e;
   if (seqs->num_q == 0) return DSA_OK;
   if (scores == nullptr || topk_idx == nullptr || ld_scores < seqs->max_ctx) return DSA_ERR_INVALID_ARG;
-  if (int e = check_ws((size_t)topk_ws_bytes(seqs->num_q), ws, ws_bytes)) return e;
+  if (int e = check_ws((size_t)topk_ws_bytes(seqs->num_q, seqs->max_ctx), ws, ws_bytes)) return e;
   TopkArgs a = topk_args(seqs, k, scores, ld_scores, topk_idx, ws, 0, seqs->num_q);
   return hip_status(launch_topk(a, stream));
 }

@@ -41,7 +41,9 @@ struct TopkArgs {
   int32_t *idx;  // [rows, k]
   uint32_t *ws;  // [rows, row_words]
   long long row_words;
-  int slices;
+  int slices;     // workgroups per row in the sliced path
+  int slice_len;  // the longest slice (a multiple of 64): size of a slice's candidate region
+  int sel_seg;    // size of a slice's selected-position region
 };
 
 struct MlaArgs {
@@ -58,18 +60,27 @@ struct MlaArgs {
   float *part;  // [rows, n_split, H, Dv + 4] when n_split > 1 (acc[Dv], max, sum, pad)
 };
 
-// top-k workspace, per row, in 32-bit words: the first-digit histogram and two
-// counters (zeroed per call), then -- for the sliced path only -- the list of
-// selected positions and the candidate list (low 21 key bits, position).
+// top-k workspace, per row, in 32-bit words.  Header (zeroed before every
+// call): the histogram of the first radix digit (key[31:21]), the histogram of
+// the second digit (key[20:10]) of the candidates, and a few words of row
+// results.  The sliced path (few long rows) adds the per-slice counts of
+// selected positions and candidates, then per slice a region of selected
+// positions and a region of candidates (low 21 key bits, position).
 constexpr int kTopkBins = 2048;        // 11-bit radix digits
-constexpr int kTopkCap = 16384;        // candidates listed per row by the sliced path
-constexpr int kTopkHdrWords = kTopkBins + 64;
 constexpr int kTopkMaxK = 2048;
-constexpr long long kTopkSlicedRowWords = kTopkHdrWords + kTopkMaxK + 2 * kTopkCap;
+constexpr int kTopkMaxSlices = 64;
+constexpr int kTopkHist2 = kTopkBins;                 // word offset of the second histogram
+constexpr int kTopkInfo = 2 * kTopkBins;              // d1, count above d1
+constexpr int kTopkHdrWords = 2 * kTopkBins + 64;
+constexpr int kTopkCounts = kTopkHdrWords;            // [2][kTopkMaxSlices]: selected, candidates
+constexpr int kTopkRegions = kTopkCounts + 2 * kTopkMaxSlices;
 
-int topk_slices(int rows, int max_ctx);
+struct TopkLayout {
+  int slices, slice_len, sel_seg;
+  long long row_words;
+};
+TopkLayout topk_layout(int rows, int max_ctx);
 bool topk_sliced(int rows);
-inline long long topk_row_words(int rows) { return topk_sliced(rows) ? kTopkSlicedRowWords : kTopkHdrWords; }
 int mla_splits(int rows, int k);
 size_t mla_f32_lds(int H, int D, int k);
 

@@ -12,14 +12,16 @@
 //   collect one pass over the row: keys with key[31:21] > d1 are selected
 //           outright (fewer than m of them); keys with key[31:21] == d1 are
 //           the candidates.
-//   select  two radix passes over the candidates (key[20:10], then key[9:0])
+//   select  radix passes over the candidates (key[20:10], then key[9:0])
 //           give the exact threshold T; keys above T are selected and keys
 //           equal to T are taken lowest position first.  The selection is
 //           written in ascending position order through LDS bitmaps: the
 //           output is deterministic and needs no sort.
-// Few long rows (decode): collect splits every row over workgroups that
-// append to global lists; one workgroup per row then selects.  Many rows
-// (prefill): one workgroup per row does collect and select, candidates in LDS.
+// Few long rows (decode): collect splits every row over workgroups; each
+// writes its selected positions and candidates to its own region (no global
+// atomics) and adds the candidates' second-digit histogram to the row's; one
+// workgroup per row then selects.  Many rows (prefill): one workgroup per row
+// does collect and select, candidates in LDS.
 #include "kernels.h"
 
 namespace dsa {
@@ -27,44 +29,43 @@ namespace {
 
 constexpr int kNT = 256;
 constexpr int kRowNT = 512;
-constexpr int kLdsCap = 8192;   // candidates held in LDS by the one-workgroup-per-row path
+constexpr int kLdsCap = 8192;    // candidates held in LDS by the one-workgroup-per-row path
+constexpr int kTieCap = 4096;    // second-digit ties held in LDS by the sliced select
 
 struct RowWs {
-  uint32_t *hist1, *counters, *sel, *cand;
+  uint32_t *hist1, *hist2, *info, *counts, *sel, *cand;
 };
 
-__device__ __forceinline__ RowWs row_ws(uint32_t *ws, long long row_words, int r) {
-  uint32_t *base = ws + (long long)r * row_words;
+__device__ __forceinline__ RowWs row_ws(const TopkArgs &a, int r) {
+  uint32_t *base = a.ws + (long long)r * a.row_words;
   RowWs w;
   w.hist1 = base;
-  w.counters = base + kTopkBins;  // [0] selected, [1] candidates
-  w.sel = base + kTopkHdrWords;
-  w.cand = base + kTopkHdrWords + kTopkMaxK;
+  w.hist2 = base + kTopkHist2;
+  w.info = base + kTopkInfo;
+  w.counts = base + kTopkCounts;
+  w.sel = base + kTopkRegions;
+  w.cand = w.sel + (long long)a.slices * a.sel_seg;
   return w;
 }
 
 // Exclusive prefix over the threads of a block (NT a multiple of 64); `tmp`
-// holds NT/64 + 1 ints of LDS.  Returns the exclusive prefix, sets `total`.
+// holds NT/64 ints of LDS.  Returns the exclusive prefix, sets `total`.
 template <int NT>
 __device__ int block_exclusive_scan(int v, int *tmp, int &total) {
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   const int inc = wave_inclusive_scan(v);
   if (lane == 63) tmp[wv] = inc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int i = 0; i < NT / 64; ++i) {
-      const int x = tmp[i];
-      tmp[i] = acc;
-      acc += x;
-    }
-    tmp[NT / 64] = acc;
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    const int x = tmp[i];
+    before += i < wv ? x : 0;
+    total += x;
   }
   __syncthreads();
-  const int res = tmp[wv] + inc - v;
-  total = tmp[NT / 64];
-  __syncthreads();
-  return res;
+  return before + inc - v;
 }
 
 // Given a histogram (nbins, in LDS) and 1 <= need <= total, find the digit d
@@ -94,26 +95,72 @@ __device__ void find_digit(const uint32_t *hist, int nbins, int need, int *out, 
   __syncthreads();
 }
 
+// Ascending-position compaction of the selection: the bits of selmap, plus the
+// first `quota` bits of eqmap (ties at the threshold, lowest position first),
+// written to out[0, m); out[m, k) = -1.  Thread i owns words [i*wpt, (i+1)*wpt).
+template <int NT>
+__device__ void compact_selection(uint32_t *selmap, const uint32_t *eqmap, int W, int quota, int m, int k,
+                                  int32_t *out, int *tmp) {
+  const int wpt = (W + NT - 1) / NT;
+  const int w0 = threadIdx.x * wpt;
+  const int w1 = w0 + wpt < W ? w0 + wpt : W;
+  int eq_local = 0;
+  for (int i = w0; i < w1; ++i) eq_local += __popc(eqmap[i]);
+  int tot;
+  int eq_before = block_exclusive_scan<NT>(eq_local, tmp, tot);
+  int cnt = 0;
+  for (int i = w0; i < w1; ++i) {
+    uint32_t e = eqmap[i];
+    uint32_t take = 0u;
+    while (e && eq_before < quota) {
+      const uint32_t low = e & (0u - e);
+      take |= low;
+      e ^= low;
+      ++eq_before;
+    }
+    const uint32_t bits = selmap[i] | take;
+    selmap[i] = bits;
+    cnt += __popc(bits);
+  }
+  int pos = block_exclusive_scan<NT>(cnt, tmp, tot);
+  for (int i = w0; i < w1; ++i) {
+    uint32_t bits = selmap[i];
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      bits &= bits - 1;
+      if (pos < m) out[pos] = i * 32 + b;
+      ++pos;
+    }
+  }
+  for (int i = m + threadIdx.x; i < k; i += NT) out[i] = -1;
+}
+
+// Load one round of row[s], s in [base, base + NT*16) clipped to [.., s1),
+// into x: thread t holds elements base + (i*NT + t)*4 + c.  Sixteen scores per
+// thread are in flight together (16-byte loads when the row is aligned).
+template <int NT>
+__device__ __forceinline__ void load_round(const float *row, int base, int s1, bool vec, float (&x)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = base + (i * NT + (int)threadIdx.x) * 4;
+    if (vec && e + 3 < s1) {
+      const float4 v = *reinterpret_cast<const float4 *>(row + e);
+      x[i][0] = v.x; x[i][1] = v.y; x[i][2] = v.z; x[i][3] = v.w;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) x[i][c] = e + c < s1 ? row[e + c] : 0.f;
+    }
+  }
+}
+
 // Visit row[s], s in [s0, s1) (s0 a multiple of 4), in rounds that every lane
-// of the block takes part in: f(s, key, valid).  Each thread loads 16 scores
-// (four 16-byte loads when the row is 16-byte aligned) before using any, so a
-// round has NT*16 scores in flight.
+// of the block takes part in: f(s, key, valid).
 template <int NT, typename F>
 __device__ __forceinline__ void scan_row(const float *row, int s0, int s1, F &&f) {
   const bool vec = ((uintptr_t)(row + s0) & 15) == 0;
   for (int base = s0; base < s1; base += NT * 16) {
     float x[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = base + (i * NT + (int)threadIdx.x) * 4;
-      if (vec && e + 3 < s1) {
-        const float4 v = *reinterpret_cast<const float4 *>(row + e);
-        x[i][0] = v.x; x[i][1] = v.y; x[i][2] = v.z; x[i][3] = v.w;
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) x[i][c] = e + c < s1 ? row[e + c] : 0.f;
-      }
-    }
+    load_round<NT>(row, base, s1, vec, x);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -124,10 +171,12 @@ __device__ __forceinline__ void scan_row(const float *row, int s0, int s1, F &&f
   }
 }
 
-__device__ __forceinline__ void slice_range(const TopkArgs &a, int n, int &s0, int &s1) {
+// Slice b of a row of n candidates: [b per, min(n, (b+1) per)), per a multiple of 64.
+__device__ __forceinline__ void slice_range(const TopkArgs &a, int n, int b, int &s0, int &s1) {
   const int per = ((n + a.slices - 1) / a.slices + 63) & ~63;
-  s0 = blockIdx.x * per;
+  s0 = b * per;
   s1 = s0 + per < n ? s0 + per : n;
+  if (s1 < s0) s1 = s0;
 }
 
 __global__ __launch_bounds__(kNT) void topk_zero_kernel(TopkArgs a) {
@@ -144,82 +193,86 @@ __global__ __launch_bounds__(kNT) void topk_hist1_kernel(TopkArgs a) {
   for (int i = threadIdx.x; i < kTopkBins; i += kNT) h[i] = 0u;
   __syncthreads();
   int s0, s1;
-  slice_range(a, n, s0, s1);
+  slice_range(a, n, blockIdx.x, s0, s1);
   const float *row = a.scores + (long long)r * a.ld;
   scan_row<kNT>(row, s0, s1, [&](int, uint32_t key, bool valid) {
     if (valid) atomicAdd(&h[key >> 21], 1u);
   });
   __syncthreads();
-  RowWs w = row_ws(a.ws, a.row_words, r);
+  RowWs w = row_ws(a, r);
   for (int i = threadIdx.x; i < kTopkBins; i += kNT)
     if (h[i]) atomicAdd(&w.hist1[i], h[i]);
 }
 
-// Sliced collect: keys above the top digit go to the row's selected list,
-// keys in it to the row's candidate list (count kept past the capacity).  Per
-// round of kNT*16 scores the workgroup counts both kinds with wave ballots,
-// reserves its space with one atomic per list, then writes.
+// Sliced collect: keys above the top digit go to this slice's selected
+// region, keys in it to its candidate region, and the candidates' second
+// digits to the row's second histogram.  The first round of scores is in
+// flight while the top digit is searched.
 __global__ __launch_bounds__(kNT) void topk_collect_kernel(TopkArgs a) {
-  const int r = blockIdx.y;
+  const int r = blockIdx.y, b = blockIdx.x;
   const int n = a.sv.candidates(a.q_begin + r);
   if (n <= a.k) return;
-  __shared__ uint32_t h[kTopkBins];
+  __shared__ uint32_t h[kTopkBins];   // hist1 for the digit search, then this slice's hist2
   __shared__ int res[2];
-  __shared__ int tmp[kNT / 64 + 1];
+  __shared__ int tmp[kNT / 64];
   __shared__ uint32_t wcnt[2][kNT / 64];
-  __shared__ uint32_t gbase[2];
-  RowWs w = row_ws(a.ws, a.row_words, r);
+  RowWs w = row_ws(a, r);
+  int s0, s1;
+  slice_range(a, n, b, s0, s1);
+  const float *row = a.scores + (long long)r * a.ld;
+  const bool vec = ((uintptr_t)(row + s0) & 15) == 0;
+  float x[4][4];
+  load_round<kNT>(row, s0, s1, vec, x);
   for (int i = threadIdx.x; i < kTopkBins; i += kNT) h[i] = w.hist1[i];
   __syncthreads();
   find_digit<kNT>(h, kTopkBins, a.k, res, tmp);
   const uint32_t d1 = (uint32_t)res[0];
-  int s0, s1;
-  slice_range(a, n, s0, s1);
-  const float *row = a.scores + (long long)r * a.ld;
+  if (b == 0 && threadIdx.x == 0) {
+    w.info[0] = d1;
+    w.info[1] = (uint32_t)res[1];
+  }
+  for (int i = threadIdx.x; i < kTopkBins; i += kNT) h[i] = 0u;
+  __syncthreads();
+
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const bool vec = ((uintptr_t)(row + s0) & 15) == 0;
+  uint32_t *sel = w.sel + (long long)b * a.sel_seg;
+  uint32_t *cand = w.cand + 2ll * b * a.slice_len;
+  uint32_t ns_run = 0u, nc_run = 0u;   // block-uniform running counts
   for (int base = s0; base < s1; base += kNT * 16) {
+    if (base != s0) load_round<kNT>(row, base, s1, vec, x);
     uint32_t key[4][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = base + (i * kNT + (int)threadIdx.x) * 4;
-      float x[4];
-      if (vec && e + 3 < s1) {
-        const float4 v = *reinterpret_cast<const float4 *>(row + e);
-        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-      } else {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) x[c] = e + c < s1 ? row[e + c] : 0.f;
+      for (int c = 0; c < 4; ++c) {
+        const int e = base + (i * kNT + (int)threadIdx.x) * 4 + c;
+        key[i][c] = e < s1 ? score_key(x[i][c]) : 0u;   // key 0: digit 0, below every valid key
       }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) key[i][c] = e + c < s1 ? score_key(x[c]) : 0u;   // key 0: never d1 > 0
-    }
-    // counts of this round, per wave
     uint32_t ns = 0u, nc = 0u;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const uint32_t dig = key[i][c] >> 21;
-        ns += (uint32_t)__popcll(__ballot(dig > d1 && key[i][c] != 0u));
-        nc += (uint32_t)__popcll(__ballot(dig == d1 && key[i][c] != 0u));
+        ns += (uint32_t)__popcll(__ballot(dig > d1));
+        nc += (uint32_t)__popcll(__ballot(dig == d1));
       }
     if (lane == 0) {
       wcnt[0][wv] = ns;
       wcnt[1][wv] = nc;
     }
     __syncthreads();
-    if (threadIdx.x < 2) {
-      uint32_t tot = 0u;
-      for (int j = 0; j < kNT / 64; ++j) tot += wcnt[threadIdx.x][j];
-      gbase[threadIdx.x] = tot ? atomicAdd(&w.counters[threadIdx.x], tot) : 0u;
-    }
-    __syncthreads();
-    uint32_t os = gbase[0], oc = gbase[1];
-    for (int j = 0; j < wv; ++j) {
-      os += wcnt[0][j];
-      oc += wcnt[1][j];
+    uint32_t os = ns_run, oc = nc_run;
+#pragma unroll
+    for (int j = 0; j < kNT / 64; ++j) {
+      const uint32_t a0 = wcnt[0][j], a1 = wcnt[1][j];
+      if (j < wv) {
+        os += a0;
+        oc += a1;
+      }
+      ns_run += a0;
+      nc_run += a1;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -227,35 +280,156 @@ __global__ __launch_bounds__(kNT) void topk_collect_kernel(TopkArgs a) {
       for (int c = 0; c < 4; ++c) {
         const uint32_t kk = key[i][c];
         const uint32_t dig = kk >> 21;
-        const bool is_sel = dig > d1 && kk != 0u;
-        const bool is_cand = dig == d1 && kk != 0u;
+        const bool is_sel = dig > d1;
+        const bool is_cand = dig == d1;
         const unsigned long long ms = __ballot(is_sel);
         const unsigned long long mc = __ballot(is_cand);
         const int sidx = base + (i * kNT + (int)threadIdx.x) * 4 + c;
         if (is_sel) {
           const uint32_t pos = os + __popcll(ms & below);
-          if (pos < (uint32_t)kTopkMaxK) w.sel[pos] = (uint32_t)sidx;
+          if (pos < (uint32_t)a.sel_seg) sel[pos] = (uint32_t)sidx;
         }
         if (is_cand) {
           const uint32_t pos = oc + __popcll(mc & below);
-          if (pos < (uint32_t)kTopkCap) {
-            w.cand[2 * pos] = kk & 0x1fffffu;
-            w.cand[2 * pos + 1] = (uint32_t)sidx;
-          }
+          cand[2 * pos] = kk & 0x1fffffu;
+          cand[2 * pos + 1] = (uint32_t)sidx;
+          atomicAdd(&h[(kk & 0x1fffffu) >> 10], 1u);
         }
         os += (uint32_t)__popcll(ms);
         oc += (uint32_t)__popcll(mc);
       }
-    __syncthreads();
+    __syncthreads();   // wcnt is rewritten by the next round; h is complete after the last
   }
+  if (threadIdx.x == 0) {
+    w.counts[b] = ns_run;
+    w.counts[kTopkMaxSlices + b] = nc_run;
+  }
+  for (int i = threadIdx.x; i < kTopkBins; i += kNT)
+    if (h[i]) atomicAdd(&w.hist2[i], h[i]);
 }
 
-// One workgroup per row: exact threshold among the candidates, then the
-// ascending bitmap compaction.  GLOBAL_LISTS: the selected and candidate lists
-// come from topk_collect_kernel; otherwise this workgroup collects them itself
-// (selected keys straight into the bitmap, candidates into LDS).
-template <bool GLOBAL_LISTS>
-__global__ __launch_bounds__(kRowNT) void topk_select_kernel(TopkArgs a) {
+// Sliced select, one workgroup per row: the second digit from the collected
+// histogram, one pass over the slices' lists (selected positions and
+// candidates above the second digit go to the bitmap, ties of the second digit
+// to an LDS list), the third digit over those ties, then the compaction.
+// Thread t serves slice t % slices, entries t / slices, t / slices + tps, ...
+__global__ __launch_bounds__(kRowNT) void topk_select_sliced_kernel(TopkArgs a) {
+  extern __shared__ uint32_t smem[];
+  const int r = blockIdx.x;
+  const int n = a.sv.candidates(a.q_begin + r);
+  int32_t *out = a.idx + (long long)r * a.k;
+  if (n <= a.k) {
+    for (int i = threadIdx.x; i < a.k; i += kRowNT) out[i] = i < n ? i : -1;
+    return;
+  }
+  const int m = a.k;
+  const int Wmax = (a.sv.max_ctx + 31) >> 5;
+  const int W = (n + 31) >> 5;
+  uint32_t *selmap = smem;
+  uint32_t *eqmap = smem + Wmax;
+  uint32_t *h = smem + 2 * Wmax;                 // kTopkBins words
+  uint32_t *ties = h + kTopkBins;                // 2 * kTieCap words: (low key bits, position)
+  __shared__ int res[6];
+  __shared__ int tmp[kRowNT / 64];
+  __shared__ uint32_t cnt_s[kTopkMaxSlices], cnt_c[kTopkMaxSlices];
+  __shared__ uint32_t nties;
+
+  RowWs w = row_ws(a, r);
+  for (int i = threadIdx.x; i < kTopkBins; i += kRowNT) h[i] = w.hist2[i];
+  for (int i = threadIdx.x; i < W; i += kRowNT) {
+    selmap[i] = 0u;
+    eqmap[i] = 0u;
+  }
+  if (threadIdx.x < a.slices) {
+    cnt_s[threadIdx.x] = w.counts[threadIdx.x];
+    cnt_c[threadIdx.x] = w.counts[kTopkMaxSlices + threadIdx.x];
+  }
+  if (threadIdx.x == 0) {
+    res[0] = (int)w.info[0];
+    res[1] = (int)w.info[1];
+    nties = 0u;
+  }
+  __syncthreads();
+  const int need = m - res[1];                   // still to take among the candidates (>= 1)
+  find_digit<kRowNT>(h, kTopkBins, need, res + 2, tmp);
+  const uint32_t d2 = (uint32_t)res[2];
+  const int need3 = need - res[3];
+
+  const int sb = threadIdx.x % a.slices;         // this thread's slice
+  const int tps = kRowNT / a.slices;             // threads per slice
+  const int t0 = threadIdx.x / a.slices;
+  const bool active = t0 < tps;
+  const uint32_t *ssel = w.sel + (long long)sb * a.sel_seg;
+  const uint32_t *scand = w.cand + 2ll * sb * a.slice_len;
+  const int nsel = active ? (int)min(cnt_s[sb], (uint32_t)a.sel_seg) : 0;
+  const int ncand = active ? (int)cnt_c[sb] : 0;
+  // selected outright
+  for (int i0 = t0; i0 < nsel; i0 += 4 * tps) {
+    uint32_t s[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s[u] = i0 + u * tps < nsel ? ssel[i0 + u * tps] : 0xffffffffu;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (s[u] < (uint32_t)n) atomicOr(&selmap[s[u] >> 5], 1u << (s[u] & 31));
+  }
+  // candidates: above the second digit -> selected; equal -> the tie list
+  for (int i0 = t0; i0 < ncand; i0 += 4 * tps) {
+    uint2 e[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      e[u] = i0 + u * tps < ncand ? *reinterpret_cast<const uint2 *>(scand + 2 * (i0 + u * tps))
+                                  : make_uint2(0u, 0xffffffffu);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t lo = e[u].x & 0x1fffffu, s = e[u].y;
+      if (s >= (uint32_t)n) continue;
+      const uint32_t dig = lo >> 10;
+      if (dig > d2) {
+        atomicOr(&selmap[s >> 5], 1u << (s & 31));
+      } else if (dig == d2) {
+        const uint32_t p = atomicAdd(&nties, 1u);
+        if (p < (uint32_t)kTieCap) {
+          ties[2 * p] = lo;
+          ties[2 * p + 1] = s;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int nt = (int)nties;
+  // Visit every tie of the second digit: from the LDS list, or from the slices'
+  // candidate lists again when it overflowed.
+  auto for_each_tie = [&](auto &&f) {
+    if (nt <= kTieCap) {
+      for (int i = threadIdx.x; i < nt; i += kRowNT) f(ties[2 * i], ties[2 * i + 1]);
+    } else {
+      for (int i = t0; i < ncand; i += tps) {
+        const uint2 e = *reinterpret_cast<const uint2 *>(scand + 2 * i);
+        const uint32_t lo = e.x & 0x1fffffu;
+        if (e.y < (uint32_t)n && (lo >> 10) == d2) f(lo, e.y);
+      }
+    }
+  };
+  // ---- third digit key[9:0]
+  for (int i = threadIdx.x; i < 1024; i += kRowNT) h[i] = 0u;
+  __syncthreads();
+  for_each_tie([&](uint32_t lo, uint32_t) { atomicAdd(&h[lo & 1023u], 1u); });
+  __syncthreads();
+  find_digit<kRowNT>(h, 1024, need3, res + 4, tmp);
+  const uint32_t T = (d2 << 10) | (uint32_t)res[4];
+  const int quota = need3 - res[5];
+  for_each_tie([&](uint32_t lo, uint32_t s) {
+    if (lo > T) atomicOr(&selmap[s >> 5], 1u << (s & 31));
+    else if (lo == T) atomicOr(&eqmap[s >> 5], 1u << (s & 31));
+  });
+  __syncthreads();
+  compact_selection<kRowNT>(selmap, eqmap, W, quota, m, a.k, out, tmp);
+}
+
+// One workgroup per row (many rows): collect the row itself (selected keys
+// straight into the bitmap, candidates into LDS), then the exact threshold
+// among the candidates and the compaction.
+__global__ __launch_bounds__(kRowNT) void topk_select_rows_kernel(TopkArgs a) {
   extern __shared__ uint32_t smem[];
   const int r = blockIdx.x;
   const int n = a.sv.candidates(a.q_begin + r);
@@ -272,10 +446,10 @@ __global__ __launch_bounds__(kRowNT) void topk_select_kernel(TopkArgs a) {
   uint32_t *h = smem + 2 * Wmax;                 // kTopkBins words
   uint32_t *lcand = h + kTopkBins;               // 2 * kLdsCap words: the candidates
   __shared__ int res[6];
-  __shared__ int tmp[kRowNT / 64 + 1];
+  __shared__ int tmp[kRowNT / 64];
   __shared__ uint32_t lcount;
 
-  RowWs w = row_ws(a.ws, a.row_words, r);
+  RowWs w = row_ws(a, r);
   for (int i = threadIdx.x; i < kTopkBins; i += kRowNT) h[i] = w.hist1[i];
   for (int i = threadIdx.x; i < W; i += kRowNT) {
     selmap[i] = 0u;
@@ -284,64 +458,36 @@ __global__ __launch_bounds__(kRowNT) void topk_select_kernel(TopkArgs a) {
   if (threadIdx.x == 0) lcount = 0u;
   const float *row = a.scores + (long long)r * a.ld;
   const int lane = lane_id();
-  const uint32_t *cand = lcand;
-  int ncand = 0;
-  if (GLOBAL_LISTS) {
-    // the lists do not depend on the digits: fetch them before the digit search
-    ncand = (int)w.counters[1];
-    if (ncand <= kLdsCap) {                      // stage the list in LDS for the three passes
-      const uint4 *src = reinterpret_cast<const uint4 *>(w.cand);
-      uint4 *dst = reinterpret_cast<uint4 *>(lcand);
-      for (int i = threadIdx.x; i < (ncand + 1) / 2; i += kRowNT) dst[i] = src[i];
-    } else {
-      cand = w.cand;
-      ncand = ncand <= kTopkCap ? ncand : -1;    // -1: list overflowed, rescan the row
-    }
-  }
   __syncthreads();
-  if (GLOBAL_LISTS) {
-    const int nsel = (int)min(w.counters[0], (uint32_t)m);
-    for (int i = threadIdx.x; i < nsel; i += kRowNT) {
-      const uint32_t s = w.sel[i];
-      if (s < (uint32_t)n) atomicOr(&selmap[s >> 5], 1u << (s & 31));
-    }
-  }
   find_digit<kRowNT>(h, kTopkBins, m, res, tmp);
   const uint32_t d1 = (uint32_t)res[0];
   const int need = m - res[1];                   // still to take among the candidates (>= 1)
 
-  // ---- per-row path: selected keys straight into the bitmap, candidates into LDS
-  if (!GLOBAL_LISTS) {
-    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    scan_row<kRowNT>(row, 0, n, [&](int s, uint32_t key, bool valid) {
-      const uint32_t dig = key >> 21;
-      if (valid && dig > d1) atomicOr(&selmap[s >> 5], 1u << (s & 31));
-      const bool is_cand = valid && dig == d1;
-      const unsigned long long mc = __ballot(is_cand);
-      if (mc == 0ull) return;
-      uint32_t bc = 0u;
-      if (lane == 0) bc = atomicAdd(&lcount, (uint32_t)__popcll(mc));
-      bc = __shfl(bc, 0, kWave);
-      if (is_cand) {
-        const uint32_t pos = bc + __popcll(mc & below);
-        if (pos < (uint32_t)kLdsCap) {
-          lcand[2 * pos] = key & 0x1fffffu;
-          lcand[2 * pos + 1] = (uint32_t)s;
-        }
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  scan_row<kRowNT>(row, 0, n, [&](int s, uint32_t key, bool valid) {
+    const uint32_t dig = key >> 21;
+    if (valid && dig > d1) atomicOr(&selmap[s >> 5], 1u << (s & 31));
+    const bool is_cand = valid && dig == d1;
+    const unsigned long long mc = __ballot(is_cand);
+    if (mc == 0ull) return;
+    uint32_t bc = 0u;
+    if (lane == 0) bc = atomicAdd(&lcount, (uint32_t)__popcll(mc));
+    bc = __shfl(bc, 0, kWave);
+    if (is_cand) {
+      const uint32_t pos = bc + __popcll(mc & below);
+      if (pos < (uint32_t)kLdsCap) {
+        lcand[2 * pos] = key & 0x1fffffu;
+        lcand[2 * pos + 1] = (uint32_t)s;
       }
-    });
-    __syncthreads();
-    ncand = (int)lcount;
-    ncand = ncand <= kLdsCap ? ncand : -1;
-  }
-  // Visit every candidate (low 21 key bits, position): from the list, or by
+    }
+  });
+  __syncthreads();
+  const int ncand = (int)lcount <= kLdsCap ? (int)lcount : -1;
+  // Visit every candidate (low 21 key bits, position): from the LDS list, or by
   // rescanning the row when the list overflowed.
   auto for_each_cand = [&](auto &&f) {
     if (ncand >= 0) {
-      for (int i = threadIdx.x; i < ncand; i += kRowNT) {
-        const uint32_t s = cand[2 * i + 1];
-        if (s < (uint32_t)n) f(cand[2 * i] & 0x1fffffu, s);
-      }
+      for (int i = threadIdx.x; i < ncand; i += kRowNT) f(lcand[2 * i], lcand[2 * i + 1]);
     } else {
       for (int s = threadIdx.x; s < n; s += kRowNT) {
         const uint32_t key = score_key(row[s]);
@@ -351,7 +497,6 @@ __global__ __launch_bounds__(kRowNT) void topk_select_kernel(TopkArgs a) {
   };
 
   // ---- second digit key[20:10]
-  __syncthreads();
   for (int i = threadIdx.x; i < kTopkBins; i += kRowNT) h[i] = 0u;
   __syncthreads();
   for_each_cand([&](uint32_t lo, uint32_t) { atomicAdd(&h[lo >> 10], 1u); });
@@ -374,52 +519,37 @@ __global__ __launch_bounds__(kRowNT) void topk_select_kernel(TopkArgs a) {
     else if (lo == T) atomicOr(&eqmap[s >> 5], 1u << (s & 31));
   });
   __syncthreads();
+  compact_selection<kRowNT>(selmap, eqmap, W, quota, m, a.k, out, tmp);
+}
 
-  // ---- ascending-position compaction: thread i owns words [i*wpt, (i+1)*wpt)
-  const int wpt = (W + kRowNT - 1) / kRowNT;
-  const int w0 = threadIdx.x * wpt;
-  const int w1 = w0 + wpt < W ? w0 + wpt : W;
-  int eq_local = 0;
-  for (int i = w0; i < w1; ++i) eq_local += __popc(eqmap[i]);
-  int tot;
-  int eq_before = block_exclusive_scan<kRowNT>(eq_local, tmp, tot);
-  int cnt = 0;
-  for (int i = w0; i < w1; ++i) {
-    uint32_t e = eqmap[i];
-    uint32_t take = 0u;
-    while (e && eq_before < quota) {
-      const uint32_t low = e & (0u - e);
-      take |= low;
-      e ^= low;
-      ++eq_before;
-    }
-    const uint32_t bits = selmap[i] | take;
-    selmap[i] = bits;
-    cnt += __popc(bits);
-  }
-  int pos = block_exclusive_scan<kRowNT>(cnt, tmp, tot);
-  for (int i = w0; i < w1; ++i) {
-    uint32_t bits = selmap[i];
-    while (bits) {
-      const int b = __ffs(bits) - 1;
-      bits &= bits - 1;
-      if (pos < m) out[pos] = i * 32 + b;
-      ++pos;
-    }
-  }
-  for (int i = m + threadIdx.x; i < a.k; i += kRowNT) out[i] = -1;
+hipError_t set_lds(const void *kernel, size_t lds) {
+  if (lds <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
 }  // namespace
 
-int topk_slices(int rows, int max_ctx) {
+bool topk_sliced(int rows) { return rows < 256; }
+
+TopkLayout topk_layout(int rows, int max_ctx) {
+  TopkLayout L;
+  if (!topk_sliced(rows)) {
+    L.slices = 1;
+    L.slice_len = 0;
+    L.sel_seg = 0;
+    L.row_words = kTopkHdrWords;
+    return L;
+  }
   int s = (2048 + rows - 1) / rows;
   const int cap = (max_ctx + 4095) / 4096;
   if (s > cap) s = cap;
-  return s < 1 ? 1 : s;
+  if (s > kTopkMaxSlices) s = kTopkMaxSlices;
+  L.slices = s < 1 ? 1 : s;
+  L.slice_len = ((max_ctx + L.slices - 1) / L.slices + 63) & ~63;
+  L.sel_seg = L.slice_len < kTopkMaxK ? L.slice_len : kTopkMaxK;
+  L.row_words = kTopkRegions + (long long)L.slices * (L.sel_seg + 2ll * L.slice_len);
+  return L;
 }
-
-bool topk_sliced(int rows) { return rows < 256; }
 
 hipError_t launch_topk_zero(const TopkArgs &a, hipStream_t st) {
   if (a.rows <= 0) return hipSuccess;
@@ -432,21 +562,13 @@ hipError_t launch_topk_select(const TopkArgs &a, hipStream_t st) {
   const int Wmax = (a.sv.max_ctx + 31) / 32;
   if (topk_sliced(a.rows)) {
     hipLaunchKernelGGL(topk_collect_kernel, dim3(a.slices, a.rows), dim3(kNT), 0, st, a);
-    const size_t lds = (size_t)(2 * Wmax + kTopkBins + 2 * kLdsCap) * sizeof(uint32_t);
-    if (lds > 65536) {
-      const hipError_t e = hipFuncSetAttribute((const void *)topk_select_kernel<true>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(topk_select_kernel<true>, dim3(a.rows), dim3(kRowNT), lds, st, a);
+    const size_t lds = (size_t)(2 * Wmax + kTopkBins + 2 * kTieCap) * sizeof(uint32_t);
+    if (hipError_t e = set_lds((const void *)topk_select_sliced_kernel, lds)) return e;
+    hipLaunchKernelGGL(topk_select_sliced_kernel, dim3(a.rows), dim3(kRowNT), lds, st, a);
   } else {
     const size_t lds = (size_t)(2 * Wmax + kTopkBins + 2 * kLdsCap) * sizeof(uint32_t);
-    if (lds > 65536) {
-      const hipError_t e = hipFuncSetAttribute((const void *)topk_select_kernel<false>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(topk_select_kernel<false>, dim3(a.rows), dim3(kRowNT), lds, st, a);
+    if (hipError_t e = set_lds((const void *)topk_select_rows_kernel, lds)) return e;
+    hipLaunchKernelGGL(topk_select_rows_kernel, dim3(a.rows), dim3(kRowNT), lds, st, a);
   }
   return hipGetLastError();
 }
