@@ -108,15 +108,23 @@ def time_forward(B, torch, inp, steps, warmup):
                                      stage_events=ev)
     for _ in range(warmup):
         call()
-    stage = [make_events(torch, 4) for _ in range(steps)]
+    # Timed region 1, the step time: K steps back to back, nothing recorded in between.
     start, end = make_events(torch, 2)
     torch.cuda.synchronize()
     start.record()
     for i in range(steps):
-        call(stage[i])
+        call()
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
+    # Timed region 2, the stages: the same K steps with HIP events recorded by the
+    # library on its stream between the kernels (indexer | top-k | attention).
+    # Each event record costs a few microseconds, which is why region 1 has none.
+    stage = [make_events(torch, 4) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        call(stage[i])
+    torch.cuda.synchronize()
     st = [[stage[i][j].elapsed_time(stage[i][j + 1]) for j in range(3)] for i in range(steps)]
     mean = [sum(s[j] for s in st) / steps for j in range(3)]
     return total_ms / steps, mean

@@ -98,29 +98,34 @@ __device__ void find_digit(const uint32_t *hist, int nbins, int need, int *out, 
 // Ascending-position compaction of the selection: the bits of selmap, plus the
 // first `quota` bits of eqmap (ties at the threshold, lowest position first),
 // written to out[0, m); out[m, k) = -1.  Thread i owns words [i*wpt, (i+1)*wpt).
+// `quota` is block-uniform.
 template <int NT>
 __device__ void compact_selection(uint32_t *selmap, const uint32_t *eqmap, int W, int quota, int m, int k,
                                   int32_t *out, int *tmp) {
   const int wpt = (W + NT - 1) / NT;
   const int w0 = threadIdx.x * wpt;
   const int w1 = w0 + wpt < W ? w0 + wpt : W;
-  int eq_local = 0;
-  for (int i = w0; i < w1; ++i) eq_local += __popc(eqmap[i]);
   int tot;
-  int eq_before = block_exclusive_scan<NT>(eq_local, tmp, tot);
   int cnt = 0;
-  for (int i = w0; i < w1; ++i) {
-    uint32_t e = eqmap[i];
-    uint32_t take = 0u;
-    while (e && eq_before < quota) {
-      const uint32_t low = e & (0u - e);
-      take |= low;
-      e ^= low;
-      ++eq_before;
+  if (quota > 0) {
+    int eq_local = 0;
+    for (int i = w0; i < w1; ++i) eq_local += __popc(eqmap[i]);
+    int eq_before = block_exclusive_scan<NT>(eq_local, tmp, tot);
+    for (int i = w0; i < w1; ++i) {
+      uint32_t e = eqmap[i];
+      uint32_t take = 0u;
+      while (e && eq_before < quota) {
+        const uint32_t low = e & (0u - e);
+        take |= low;
+        e ^= low;
+        ++eq_before;
+      }
+      const uint32_t bits = selmap[i] | take;
+      selmap[i] = bits;
+      cnt += __popc(bits);
     }
-    const uint32_t bits = selmap[i] | take;
-    selmap[i] = bits;
-    cnt += __popc(bits);
+  } else {
+    for (int i = w0; i < w1; ++i) cnt += __popc(selmap[i]);
   }
   int pos = block_exclusive_scan<NT>(cnt, tmp, tot);
   for (int i = w0; i < w1; ++i) {
@@ -397,31 +402,48 @@ __global__ __launch_bounds__(kRowNT) void topk_select_sliced_kernel(TopkArgs a) 
   }
   __syncthreads();
   const int nt = (int)nties;
-  // Visit every tie of the second digit: from the LDS list, or from the slices'
-  // candidate lists again when it overflowed.
-  auto for_each_tie = [&](auto &&f) {
-    if (nt <= kTieCap) {
-      for (int i = threadIdx.x; i < nt; i += kRowNT) f(ties[2 * i], ties[2 * i + 1]);
-    } else {
-      for (int i = t0; i < ncand; i += tps) {
-        const uint2 e = *reinterpret_cast<const uint2 *>(scand + 2 * i);
-        const uint32_t lo = e.x & 0x1fffffu;
-        if (e.y < (uint32_t)n && (lo >> 10) == d2) f(lo, e.y);
+  int quota = 0;
+  if (nt <= 64) {
+    // Few ties (the usual case): wave 0 ranks them exactly in the order (low key
+    // bits descending, position ascending) and takes the first need3.
+    if (threadIdx.x < 64) {
+      const int i = threadIdx.x;
+      const uint32_t lo = i < nt ? ties[2 * i] : 0u, s = i < nt ? ties[2 * i + 1] : 0xffffffffu;
+      int rank = 0;
+      for (int j = 0; j < nt; ++j) {
+        const uint32_t lj = (uint32_t)__builtin_amdgcn_readlane((int)lo, j);
+        const uint32_t sj = (uint32_t)__builtin_amdgcn_readlane((int)s, j);
+        rank += (lj > lo || (lj == lo && sj < s)) ? 1 : 0;
       }
+      if (i < nt && rank < need3) atomicOr(&selmap[s >> 5], 1u << (s & 31));
     }
-  };
-  // ---- third digit key[9:0]
-  for (int i = threadIdx.x; i < 1024; i += kRowNT) h[i] = 0u;
-  __syncthreads();
-  for_each_tie([&](uint32_t lo, uint32_t) { atomicAdd(&h[lo & 1023u], 1u); });
-  __syncthreads();
-  find_digit<kRowNT>(h, 1024, need3, res + 4, tmp);
-  const uint32_t T = (d2 << 10) | (uint32_t)res[4];
-  const int quota = need3 - res[5];
-  for_each_tie([&](uint32_t lo, uint32_t s) {
-    if (lo > T) atomicOr(&selmap[s >> 5], 1u << (s & 31));
-    else if (lo == T) atomicOr(&eqmap[s >> 5], 1u << (s & 31));
-  });
+  } else {
+    // Visit every tie of the second digit: from the LDS list, or from the slices'
+    // candidate lists again when it overflowed.
+    auto for_each_tie = [&](auto &&f) {
+      if (nt <= kTieCap) {
+        for (int i = threadIdx.x; i < nt; i += kRowNT) f(ties[2 * i], ties[2 * i + 1]);
+      } else {
+        for (int i = t0; i < ncand; i += tps) {
+          const uint2 e = *reinterpret_cast<const uint2 *>(scand + 2 * i);
+          const uint32_t lo = e.x & 0x1fffffu;
+          if (e.y < (uint32_t)n && (lo >> 10) == d2) f(lo, e.y);
+        }
+      }
+    };
+    // ---- third digit key[9:0]
+    for (int i = threadIdx.x; i < 1024; i += kRowNT) h[i] = 0u;
+    __syncthreads();
+    for_each_tie([&](uint32_t lo, uint32_t) { atomicAdd(&h[lo & 1023u], 1u); });
+    __syncthreads();
+    find_digit<kRowNT>(h, 1024, need3, res + 4, tmp);
+    const uint32_t T = (d2 << 10) | (uint32_t)res[4];
+    quota = need3 - res[5];
+    for_each_tie([&](uint32_t lo, uint32_t s) {
+      if (lo > T) atomicOr(&selmap[s >> 5], 1u << (s & 31));
+      else if (lo == T) atomicOr(&eqmap[s >> 5], 1u << (s & 31));
+    });
+  }
   __syncthreads();
   compact_selection<kRowNT>(selmap, eqmap, W, quota, m, a.k, out, tmp);
 }
