@@ -305,6 +305,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
   // Stage the tile starting at key `base` into registers.
   uint4 stage[kPerThread];
   long long stage_slot[kPerThread];
+  float stage_scale[kPerThread];
   // A 64-key tile is one 64-token block: one uniform lookup gives its first slot.
   auto fetch = [&](int base) {
     const long long sl0 = a.sv.slot(0, base);
@@ -315,86 +316,117 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
       const long long sl = (sl0 >= 0 && base + key < nmax) ? sl0 + key : -1;
       stage_slot[i] = sl;
       stage[i] = sl >= 0 ? ld16(kbase + sl * Tr::kRowBytes + ch * 16) : make_uint4(0, 0, 0, 0);
+      if (DT == DSA_FP8_E4M3FN) stage_scale[i] = (sl >= 0 && ch == 0) ? a.k_scale[sl] : 0.f;
     }
   };
+  __shared__ int absent[2][kPrefillKeys];
+  __shared__ float kscale[2][kPrefillKeys];
   // Swizzled store: chunk ch of key `key` goes to slot ch ^ (key & 15) of its row (bf16),
-  // so the 16 lanes of one MFMA operand read touch 16 distinct bank groups.
+  // so the 16 lanes of one MFMA operand read touch 16 distinct bank groups.  The
+  // key's presence (and fp8 scale) go beside the tile.
   auto put = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
       const int c = threadIdx.x + i * 512;
       const int key = c / kChunks, ch = c % kChunks;
       tile[buf][key * kChunks + (ch ^ (key & (kChunks - 1)))] = stage[i];
+      if (ch == 0) {
+        absent[buf][key] = stage_slot[i] < 0;
+        if (DT == DSA_FP8_E4M3FN) kscale[buf][key] = stage_scale[i];
+      }
     }
   };
-  __shared__ int absent[2][kPrefillKeys];
   // first radix digit of the top-k: each wave owns its query row's bins
   __shared__ uint32_t wh[kPrefillQ][kTopkBins];
   const bool hist = a.hist_mode == 2;
   if (hist)
     for (int i = lane; i < kTopkBins; i += 64) wh[wv][i] = 0u;
 
+  // MFMAs of 32-key group nb of the tile in buffer bi (rows nb*32 + col) into
+  // (c0a, c1a), interleaved in program order with the ReLU-weighted head sum of
+  // the previous group's accumulators (p0a, p1a): each k-step's two MFMAs are
+  // followed by a slice of the reduction, and scheduling barriers keep that
+  // order, so the VALU work runs while the matrix core is busy.
+  auto mma_reduce = [&](int bi, int nb, f32x16 &c0a, f32x16 &c1a, const f32x16 &p0a,
+                        const f32x16 &p1a) -> float {
+    const int key = nb * 32 + col;
+    typename Tr::Op kb[Tr::kSteps];
+    const uint4 *trow = &tile[bi][key * kChunks];
+#pragma unroll
+    for (int ks = 0; ks < Tr::kSteps; ++ks) {
+      if constexpr (DT == DSA_BF16) {
+        const int ch = g * 8 + ks;
+        kb[ks] = __builtin_bit_cast(typename Tr::Op, trow[ch ^ (key & 15)]);
+      } else {
+        const int ch = g * 4 + ks * 2;
+        const uint4 lo = trow[ch ^ (key & 7)], hi = trow[(ch + 1) ^ (key & 7)];
+        typename Tr::Op o;
+        o[0] = lo.x; o[1] = lo.y; o[2] = lo.z; o[3] = lo.w;
+        o[4] = hi.x; o[5] = hi.y; o[6] = hi.z; o[7] = hi.w;
+        kb[ks] = o;
+      }
+    }
+    c0a = zero_vec<f32x16>();
+    c1a = zero_vec<f32x16>();
+    constexpr int kPerStep = 16 / Tr::kSteps;     // reduction elements (per block) per k-step
+    float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < Tr::kSteps; ++ks) {
+      c0a = Tr::mma(qa[0][ks], kb[ks], c0a);
+      c1a = Tr::mma(qa[1][ks], kb[ks], c1a);
+#pragma unroll
+      for (int e = 0; e < kPerStep; ++e) {
+        const int v = ks * kPerStep + e;
+        r0 = fmaf(wt[0][v], __int_as_float(max(__float_as_int(p0a[v]), 0)), r0);
+        r1 = fmaf(wt[1][v], __int_as_float(max(__float_as_int(p1a[v]), 0)), r1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const float rr = r0 + r1;
+    return rr + shfl_xor(rr, 32);
+  };
+  auto emit = [&](int s, float sc, bool gone, float kscl) {
+    if (g == 0 && s < n && row_ok) {
+      float v = neg_inf();
+      if (!gone) {
+        v = sc;
+        if (DT == DSA_FP8_E4M3FN) v *= kscl;
+      }
+      srow[s] = v;
+      if (hist) atomicAdd(&wh[wv][score_key(v) >> 21], 1u);
+    }
+  };
+
+  // Software pipeline over 32-key groups: while group i+1 is multiplied, group
+  // i is reduced and written.  The presence flags and scales of a group are read
+  // into registers before the barrier after which their buffer may be refilled.
   int buf = 0;
   if (nmax > 0) {
     fetch(0);
     put(0);
-    for (int i = 0; i < kPerThread; ++i) {
-      const int c = threadIdx.x + i * 512;
-      if (c % kChunks == 0) absent[0][c / kChunks] = stage_slot[i] < 0;
-    }
   }
   __syncthreads();
+  f32x16 A0 = zero_vec<f32x16>(), A1 = zero_vec<f32x16>(), B0 = zero_vec<f32x16>(), B1 = zero_vec<f32x16>();
+  (void)mma_reduce(0, 0, A0, A1, B0, B1);
+  bool goneA = absent[0][col] != 0;
+  float scaleA = DT == DSA_FP8_E4M3FN ? kscale[0][col] : 1.f;
   for (int base = 0; base < nmax; base += kPrefillKeys) {
     const bool more = base + kPrefillKeys < nmax;
     if (more) fetch(base + kPrefillKeys);
-    if (base < n) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int key = nb * 32 + col;
-        typename Tr::Op kb[Tr::kSteps];
-        const uint4 *trow = &tile[buf][key * kChunks];
-#pragma unroll
-        for (int ks = 0; ks < Tr::kSteps; ++ks) {
-          if constexpr (DT == DSA_BF16) {
-            const int ch = g * 8 + ks;
-            kb[ks] = __builtin_bit_cast(typename Tr::Op, trow[ch ^ (key & 15)]);
-          } else {
-            const int ch = g * 4 + ks * 2;
-            const uint4 lo = trow[ch ^ (key & 7)], hi = trow[(ch + 1) ^ (key & 7)];
-            typename Tr::Op o;
-            o[0] = lo.x; o[1] = lo.y; o[2] = lo.z; o[3] = lo.w;
-            o[4] = hi.x; o[5] = hi.y; o[6] = hi.z; o[7] = hi.w;
-            kb[ks] = o;
-          }
-        }
-        f32x16 c0a = zero_vec<f32x16>(), c1a = zero_vec<f32x16>();
-#pragma unroll
-        for (int ks = 0; ks < Tr::kSteps; ++ks) {
-          c0a = Tr::mma(qa[0][ks], kb[ks], c0a);
-          c1a = Tr::mma(qa[1][ks], kb[ks], c1a);
-        }
-        const float sc = head_reduce(c0a, c1a, wt);
-        const int s = base + key;
-        if (g == 0 && s < n && row_ok) {
-          float v = neg_inf();
-          if (!absent[buf][key]) {
-            v = sc;
-            if (DT == DSA_FP8_E4M3FN) v *= a.k_scale[a.sv.slot(0, base) + key];
-          }
-          srow[s] = v;
-          if (hist) atomicAdd(&wh[wv][score_key(v) >> 21], 1u);
-        }
-      }
-    }
-    if (more) {
-      put(buf ^ 1);
-      for (int i = 0; i < kPerThread; ++i) {
-        const int c = threadIdx.x + i * 512;
-        if (c % kChunks == 0) absent[buf ^ 1][c / kChunks] = stage_slot[i] < 0;
-      }
-    }
+    // group (base, 1) -> B while group (base, 0) in A is reduced
+    const float scA = mma_reduce(buf, 1, B0, B1, A0, A1);
+    const bool goneB = absent[buf][32 + col] != 0;
+    const float scaleB = DT == DSA_FP8_E4M3FN ? kscale[buf][32 + col] : 1.f;
+    emit(base + col, scA, goneA, scaleA);
+    if (more) put(buf ^ 1);
     __syncthreads();
     buf ^= 1;
+    // group (base + 64, 0) -> A while group (base, 1) in B is reduced (past the
+    // last tile this multiplies a stale buffer and the result is never used)
+    const float scB = mma_reduce(buf, 0, A0, A1, B0, B1);
+    goneA = absent[buf][col] != 0;
+    scaleA = DT == DSA_FP8_E4M3FN ? kscale[buf][col] : 1.f;
+    emit(base + 32 + col, scB, goneB, scaleB);
   }
   if (a.fill_masked && row_ok) {
     for (long long s = n + lane; s < a.ld; s += 64) srow[s] = neg_inf();
