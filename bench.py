@@ -245,23 +245,35 @@ def main():
         pin = generate(WORKLOADS[pname], "cuda")
         pms, pst = time_forward(B, torch, pin, 2, 1)
         pf_idx, pf_mla = algorithmic_flops(pin)
-        # the indexer alone over every query row, one launch
+        # each stage alone over every query row, one call each (the forward
+        # processes the rows in chunks; its stage events cover the first chunk)
         pb = B.problem_from_inputs(pin)
         sc = torch.empty((pin.num_q, pin.max_ctx), dtype=torch.float32, device="cuda")
-        B.index_scores(pb, pin.q_idx, pin.q_scale, pin.w, pin.k_cache, pin.k_scale, scores=sc)
-        e0, e1 = make_events(torch, 2)
-        e0.record()
-        B.index_scores(pb, pin.q_idx, pin.q_scale, pin.w, pin.k_cache, pin.k_scale, scores=sc)
-        e1.record()
-        torch.cuda.synchronize()
-        ims = e0.elapsed_time(e1)
+        idx = torch.empty((pin.num_q, pin.topk), dtype=torch.int32, device="cuda")
+        tws = torch.empty(B.workspace_size(B.OP_TOPK, pb), dtype=torch.uint8, device="cuda")
+        mws = torch.empty(max(1, B.workspace_size(B.OP_SPARSE_MLA, pb)), dtype=torch.uint8, device="cuda")
+        ops = [lambda: B.index_scores(pb, pin.q_idx, pin.q_scale, pin.w, pin.k_cache, pin.k_scale, scores=sc),
+               lambda: B.topk(pb, sc, idx=idx, ws=tws),
+               lambda: B.sparse_mla(pb, pin.sm_scale, pin.q, pin.kv_cache, idx, ws=mws)]
+        stage_ms = []
+        for op in ops:
+            op()
+            e0, e1 = make_events(torch, 2)
+            e0.record()
+            op()
+            e1.record()
+            torch.cuda.synchronize()
+            stage_ms.append(e0.elapsed_time(e1))
+        ims = stage_ms[0]
         result["prefill"] = {
             "workload": pname, "tokens_per_s": round(pin.num_q / (pms * 1e-3), 1), "ms_per_step": round(pms, 3),
-            "indexer_ms_all_rows": round(ims, 3),
+            "stage_ops_ms_all_rows": {"index_scores": round(stage_ms[0], 3), "topk": round(stage_ms[1], 3),
+                                      "sparse_mla": round(stage_ms[2], 3)},
             "indexer_mfma_frac": round(pf_idx / (ims * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
+            "attention_mfma_frac": round(pf_mla / (stage_ms[2] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
             "step_mfma_frac": round((pf_idx + pf_mla) / (pms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4)}
         log(f"prefill {pms:.2f} ms/step, indexer {ims:.2f} ms")
-        del pin, sc
+        del pin, sc, idx, tws, mws
         torch.cuda.empty_cache()
         inp = generate(wl, "cuda") if not args.no_cpu_baseline else None
     if not args.no_cpu_baseline:

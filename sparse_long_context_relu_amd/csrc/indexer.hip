@@ -269,12 +269,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // ------------------------------------------------------------------ prefill tiling
 
 constexpr int kPrefillQ = 8;     // queries (waves) per workgroup
-constexpr int kPrefillKeys = 64; // keys per LDS tile
 
 template <int DT>
 __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
   typedef IdxTraits<DT> Tr;
   constexpr int kChunks = Tr::kRowBytes / 16;           // 16-byte chunks per key row (16 or 8)
+  // keys per LDS tile: 64 for bf16 (a larger tile spills registers), 128 for
+  // e4m3fn (half the bytes per key, and twice the MFMA work per barrier)
+  constexpr int kPrefillKeys = DT == DSA_BF16 ? 64 : 128;
   constexpr int kTileChunks = kPrefillKeys * kChunks;   // chunks per tile
   constexpr int kPerThread = kTileChunks / 512;         // 2 (bf16) or 1 (fp8)
   __shared__ uint4 tile[2][kTileChunks];
@@ -306,14 +308,17 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
   uint4 stage[kPerThread];
   long long stage_slot[kPerThread];
   float stage_scale[kPerThread];
-  // A 64-key tile is one 64-token block: one uniform lookup gives its first slot.
+  // A tile covers whole 64-token blocks: one uniform lookup per block gives its first slot.
   auto fetch = [&](int base) {
-    const long long sl0 = a.sv.slot(0, base);
+    long long slb[kPrefillKeys / 64];
+#pragma unroll
+    for (int j = 0; j < kPrefillKeys / 64; ++j) slb[j] = base + 64 * j < nmax ? a.sv.slot(0, base + 64 * j) : -1;
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
       const int c = threadIdx.x + i * 512;
       const int key = c / kChunks, ch = c % kChunks;
-      const long long sl = (sl0 >= 0 && base + key < nmax) ? sl0 + key : -1;
+      const long long sl0 = slb[key >> 6];
+      const long long sl = (sl0 >= 0 && base + key < nmax) ? sl0 + (key & 63) : -1;
       stage_slot[i] = sl;
       stage[i] = sl >= 0 ? ld16(kbase + sl * Tr::kRowBytes + ch * 16) : make_uint4(0, 0, 0, 0);
       if (DT == DSA_FP8_E4M3FN) stage_scale[i] = (sl >= 0 && ch == 0) ? a.k_scale[sl] : 0.f;
@@ -380,6 +385,9 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
         r0 = fmaf(wt[0][v], __int_as_float(max(__float_as_int(p0a[v]), 0)), r0);
         r1 = fmaf(wt[1][v], __int_as_float(max(__float_as_int(p1a[v]), 0)), r1);
       }
+      // pin this slice of the reduction here (the compiler would otherwise hoist
+      // the whole reduction above the MFMAs it is meant to overlap)
+      asm volatile("" : "+v"(r0), "+v"(r1));
       __builtin_amdgcn_sched_barrier(0);
     }
     const float rr = r0 + r1;
@@ -406,27 +414,38 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
     put(0);
   }
   __syncthreads();
-  f32x16 A0 = zero_vec<f32x16>(), A1 = zero_vec<f32x16>(), B0 = zero_vec<f32x16>(), B1 = zero_vec<f32x16>();
-  (void)mma_reduce(0, 0, A0, A1, B0, B1);
-  bool goneA = absent[0][col] != 0;
-  float scaleA = DT == DSA_FP8_E4M3FN ? kscale[0][col] : 1.f;
+  constexpr int kGroups = kPrefillKeys / 32;             // 32-key groups per tile (even)
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = zero_vec<f32x16>();
+  bool gone[2];
+  float scl[2];
+  (void)mma_reduce(0, 0, acc[0][0], acc[0][1], acc[1][0], acc[1][1]);
+  gone[0] = absent[0][col] != 0;
+  scl[0] = DT == DSA_FP8_E4M3FN ? kscale[0][col] : 1.f;
   for (int base = 0; base < nmax; base += kPrefillKeys) {
     const bool more = base + kPrefillKeys < nmax;
     if (more) fetch(base + kPrefillKeys);
-    // group (base, 1) -> B while group (base, 0) in A is reduced
-    const float scA = mma_reduce(buf, 1, B0, B1, A0, A1);
-    const bool goneB = absent[buf][32 + col] != 0;
-    const float scaleB = DT == DSA_FP8_E4M3FN ? kscale[buf][32 + col] : 1.f;
-    emit(base + col, scA, goneA, scaleA);
+    // group nb -> acc[nb & 1] while group nb - 1 is reduced and written
+#pragma unroll
+    for (int nb = 1; nb < kGroups; ++nb) {
+      const int cur = nb & 1, prv = cur ^ 1;
+      const float sc = mma_reduce(buf, nb, acc[cur][0], acc[cur][1], acc[prv][0], acc[prv][1]);
+      gone[cur] = absent[buf][nb * 32 + col] != 0;
+      scl[cur] = DT == DSA_FP8_E4M3FN ? kscale[buf][nb * 32 + col] : 1.f;
+      emit(base + (nb - 1) * 32 + col, sc, gone[prv], scl[prv]);
+    }
     if (more) put(buf ^ 1);
     __syncthreads();
     buf ^= 1;
-    // group (base + 64, 0) -> A while group (base, 1) in B is reduced (past the
-    // last tile this multiplies a stale buffer and the result is never used)
-    const float scB = mma_reduce(buf, 0, A0, A1, B0, B1);
-    goneA = absent[buf][col] != 0;
-    scaleA = DT == DSA_FP8_E4M3FN ? kscale[buf][col] : 1.f;
-    emit(base + 32 + col, scB, goneB, scaleB);
+    // group 0 of the next tile -> acc[0] while the tile's last group (in acc[1])
+    // is reduced (past the last tile this multiplies a stale buffer, unused)
+    const float sc = mma_reduce(buf, 0, acc[0][0], acc[0][1], acc[1][0], acc[1][1]);
+    const bool last_gone = gone[1];
+    const float last_scl = scl[1];
+    gone[0] = absent[buf][col] != 0;
+    scl[0] = DT == DSA_FP8_E4M3FN ? kscale[buf][col] : 1.f;
+    emit(base + (kGroups - 1) * 32 + col, sc, last_gone, last_scl);
   }
   if (a.fill_masked && row_ok) {
     for (long long s = n + lane; s < a.ld; s += 64) srow[s] = neg_inf();
