@@ -36,7 +36,12 @@ constexpr int kDataChunks = kD * 2 / 16;      // 72
 constexpr int kRowChunks = kDataChunks + 2;   // row stride 1184 B
 constexpr int kRowStride = kRowChunks * 16;
 constexpr int kTileChunks = kR * kRowChunks;  // 2368
+// A tile buffer is padded to 40 whole 64-lane loads, five per wave, so every
+// load writes all of its lanes and every wave issues the same loads; the pad
+// receives copies of a valid row.
 constexpr int kWaveLoads = (kTileChunks + kThreads - 1) / kThreads;  // 5 direct loads per wave
+constexpr int kTileLoads = kWaveLoads * kWaves;                      // 40
+constexpr int kTileBufChunks = kTileLoads * 64;                      // 2560
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 constexpr int kKs = kD / 32;                  // 18 k-steps of the logits
 constexpr int kDb = kDv / 16;                 // 32 value-dim blocks
@@ -104,32 +109,33 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Issue the direct-to-LDS gather of split rows [j0, j0+32) into the tile at LDS
+// The direct-to-LDS gather of split rows [j0, j0+32) into the tile at LDS
 // address `tile`.  Position p of the tile is (row p/74, slot p%74) and holds data
 // chunk slot ^ swz(row) of that row; a wave's j-th load covers positions
-// (8 j + wv) 64 + [0, 64).  The pad chunks and
-// absent rows (slot -1) load a valid row (`fallback`), so every LDS byte the
-// MFMAs read is finite; absent rows are masked in the softmax.  `slots` holds
-// -1 past the split's last row, far enough for every lane's row.
-__device__ __forceinline__ void issue_tile(uint32_t tile, const uint8_t *kv, const int *slots, int j0,
-                                           int fallback, int wv, int lane) {
+// (8 j + wv) 64 + [0, 64).  The pad chunks and absent rows (slot -1) load a
+// valid row (`fallback`), so every LDS byte the MFMAs read is finite; absent
+// rows are masked in the softmax.  `slots` holds -1 past the split's last row,
+// far enough for every lane's row.
+struct TileLoads {
+  const uint8_t *src[kWaveLoads];   // this lane's source of each of the wave's loads
+};
+
+// Sources of this wave's loads of the tile of split rows [j0, j0+32): slot reads
+// first (independent LDS reads, one wait), then the addresses.  Rows past the
+// tile (the pad) read the slot list's -1 tail and load the fallback row.
+__device__ __forceinline__ TileLoads tile_loads(const uint8_t *kv, const int *slots, int j0, int fallback, int wv,
+                                                int lane) {
   // Recompute the per-lane coordinates on every call rather than keep them live
   // across the tile loop (the registers are needed by the MFMA operands).
   asm volatile("" : "+v"(lane));
   int p = wv * 64 + lane;
   int row = p / kRowChunks;
   int ch = p - row * kRowChunks;
+  int sl[kWaveLoads], dc[kWaveLoads];
 #pragma unroll
   for (int j = 0; j < kWaveLoads; ++j) {
-    const int base = (j * kWaves + wv) * 64;      // wave-uniform
-    if (base < kTileChunks) {
-      int sl = slots[j0 + row];
-      sl = sl < 0 ? fallback : sl;
-      const int dc = ch < kDataChunks ? ch ^ swz(row) : 0;
-      const uint8_t *src = kv + (long long)sl * (kD * 2) + dc * 16;
-      if (base + 64 <= kTileChunks || p < kTileChunks) lds_dma16(src, tile + base * 16);
-    }
-    // next load: p += 512 = 6 * 74 + 68
+    sl[j] = slots[j0 + row];
+    dc[j] = ch < kDataChunks ? ch ^ swz(row) : 0;
     p += kWaves * 64;
     row += (kWaves * 64) / kRowChunks;
     ch += (kWaves * 64) % kRowChunks;
@@ -138,6 +144,25 @@ __device__ __forceinline__ void issue_tile(uint32_t tile, const uint8_t *kv, con
       row += 1;
     }
   }
+  TileLoads t;
+#pragma unroll
+  for (int j = 0; j < kWaveLoads; ++j) {
+    const int s = sl[j] < 0 ? fallback : sl[j];
+    t.src[j] = kv + (long long)s * (kD * 2) + dc[j] * 16;
+  }
+  return t;
+}
+
+// The wave's j-th load of a tile into the buffer at LDS address `tile`.
+__device__ __forceinline__ void tile_load(const TileLoads &t, int j, uint32_t tile, int wv) {
+  lds_dma16(t.src[j], tile + (j * kWaves + wv) * 1024);
+}
+
+__device__ __forceinline__ void issue_tile(uint32_t tile, const uint8_t *kv, const int *slots, int j0,
+                                           int fallback, int wv, int lane) {
+  const TileLoads t = tile_loads(kv, slots, j0, fallback, wv, lane);
+#pragma unroll
+  for (int j = 0; j < kWaveLoads; ++j) tile_load(t, j, tile, wv);
 }
 
 // Logits, online softmax and value product for the tile at LDS address `tile`.
@@ -239,8 +264,8 @@ __device__ __forceinline__ void consume_tile(uint32_t tile, const int *slots, in
 }
 
 __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
-  __shared__ uint4 tiles[kBufs][kTileChunks];
-  __shared__ int slots[kMaxSplitRows + 2 * kR];
+  __shared__ uint4 tiles[kBufs][kTileBufChunks];
+  __shared__ int slots[kMaxSplitRows + 4 * kR];
   __shared__ int fallback;
 
   int sp, r;
@@ -263,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
   __syncthreads();
   // Slots of this split's rows (-1: absent, and past the last row), so the
   // gather depends on LDS only.
-  for (int j = threadIdx.x; j < ntiles * kR + kR; j += kThreads) {
+  for (int j = threadIdx.x; j < ntiles * kR + 3 * kR; j += kThreads) {
     int sl = -1;
     if (j < rows) {
       const int s = irow[i0 + j];
@@ -296,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
   const uint32_t pv_even = pv_row + (((vc >> 1)) ^ g) * 16;
   const uint32_t pv_odd = pv_row + ((2 + (vc >> 1)) ^ g) * 16;
   const uint32_t tile_lds = lds_addr(&tiles[0][0]);
-  constexpr uint32_t kTileBytes = kTileChunks * 16;
+  constexpr uint32_t kTileBytes = kTileBufChunks * 16;
   __syncthreads();
   const int fb = fallback;
 
