@@ -57,8 +57,9 @@ def algorithmic_flops(inp):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ("sparse_long_context_relu_amd/csrc/indexer.hip", "sparse_long_context_relu_amd/csrc/common.h",
-                  "sparse_long_context_relu_amd/csrc/kernels.h")
+KERNEL_SOURCES = ("sparse_long_context_relu_amd/csrc/indexer_decode.hip",
+                  "sparse_long_context_relu_amd/csrc/indexer_common.h",
+                  "sparse_long_context_relu_amd/csrc/common.h", "sparse_long_context_relu_amd/csrc/kernels.h")
 
 
 def kernel_source_hash():

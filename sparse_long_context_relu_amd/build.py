@@ -15,8 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libdsa.so")
-SOURCES = ["dsa_api.hip", "indexer.hip", "topk.hip", "sparse_mla.hip"]
-HEADERS = ["common.h", "kernels.h"]
+SOURCES = ["dsa_api.hip", "indexer.hip", "indexer_decode.hip", "topk.hip", "sparse_mla.hip"]
+HEADERS = ["common.h", "kernels.h", "indexer_common.h"]
 
 ARCH = "gfx950"
 CXXFLAGS = [

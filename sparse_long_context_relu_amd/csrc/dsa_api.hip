@@ -95,7 +95,7 @@ int mla_split_count(const dsa_dims *d, int rows) {
 long long mla_ws_bytes(const dsa_dims *d, int rows) {
   const int ns = mla_split_count(d, rows);
   if (ns <= 1) return 0;
-  return (long long)rows * ns * d->heads * (d->v_dim + 4) * (long long)sizeof(float);
+  return (long long)rows * ns * d->heads * ((long long)d->v_dim * 2 + 2 * (long long)sizeof(float));
 }
 
 long long topk_ws_bytes(int rows, int max_ctx) {
@@ -194,7 +194,7 @@ MlaArgs mla_args(const dsa_seqs *s, const dsa_dims *d, float sm_scale, const voi
   a.q_begin = q_begin;
   a.rows = rows;
   a.n_split = mla_split_count(d, rows);
-  a.part = reinterpret_cast<float *>(ws);
+  a.part = ws;
   return a;
 }
 

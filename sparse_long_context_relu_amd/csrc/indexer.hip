@@ -14,257 +14,11 @@
 //     share 64-key tiles staged through LDS.
 // e4m3fn: scores = k_scale(s) * sum_j (w_j q_scale_j) ReLU(q8_j . k8_s),
 // exact because ReLU(a x) = a ReLU(x) for a > 0.
-#include "kernels.h"
+//   (the decode tiling is in indexer_decode.hip)
+#include "indexer_common.h"
 
 namespace dsa {
 namespace {
-
-constexpr int kHeads = 64;
-constexpr int kDim = 128;
-constexpr int kDecodeChunk = 2048;  // keys per decode workgroup
-
-// ------------------------------------------------------------------ helpers
-
-template <int DT>
-struct IdxTraits;
-
-// bf16: 8 k-steps of 16; lane group g holds d = 64 g + 8 ks + [0, 8).
-template <>
-struct IdxTraits<DSA_BF16> {
-  static constexpr int kSteps = 8;
-  static constexpr int kRowBytes = kDim * 2;
-  typedef bf16x8 Op;
-  __device__ static Op load(const uint8_t *row, int g, int ks) {
-    return as_bf16x8(ld16(row + g * 128 + ks * 16));
-  }
-  __device__ static f32x16 mma(Op a, Op b, f32x16 c) { return mfma32_bf16(a, b, c); }
-};
-
-// e4m3fn: 2 k-steps of 64; lane group g holds d = 64 g + 32 ks + [0, 32).
-template <>
-struct IdxTraits<DSA_FP8_E4M3FN> {
-  static constexpr int kSteps = 2;
-  static constexpr int kRowBytes = kDim;
-  typedef i32x8 Op;
-  __device__ static Op load(const uint8_t *row, int g, int ks) {
-    const uint8_t *p = row + g * 64 + ks * 32;
-    uint4 lo = ld16(p), hi = ld16(p + 16);
-    Op o;
-    o[0] = lo.x; o[1] = lo.y; o[2] = lo.z; o[3] = lo.w;
-    o[4] = hi.x; o[5] = hi.y; o[6] = hi.z; o[7] = hi.w;
-    return o;
-  }
-  __device__ static f32x16 mma(Op a, Op b, f32x16 c) { return mfma32_fp8(a, b, c); }
-};
-
-// Weight of accumulator element v of head block hb for lane group g.
-__device__ __forceinline__ int acc_head(int hb, int v, int g) { return hb * 32 + 8 * (v >> 2) + 4 * g + (v & 3); }
-
-template <int DT>
-__device__ __forceinline__ void load_query(const IndexerArgs &a, int t, int col, int g,
-                                           typename IdxTraits<DT>::Op (&qa)[2][IdxTraits<DT>::kSteps],
-                                           float (&wt)[2][16]) {
-  typedef IdxTraits<DT> Tr;
-  const uint8_t *qrow = reinterpret_cast<const uint8_t *>(a.q_idx) + (long long)t * kHeads * Tr::kRowBytes;
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-    for (int ks = 0; ks < Tr::kSteps; ++ks) qa[hb][ks] = Tr::load(qrow + (hb * 32 + col) * Tr::kRowBytes, g, ks);
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int h = acc_head(hb, v, g);
-      float wv = a.w[(long long)t * kHeads + h];
-      if (DT == DSA_FP8_E4M3FN) wv *= a.q_scale[(long long)t * kHeads + h];
-      wt[hb][v] = wv;
-    }
-}
-
-// ReLU-weighted head sum of the two 32-head accumulator blocks for the key in
-// column l%32; the result is valid in every lane.
-__device__ __forceinline__ float head_reduce(const f32x16 &c0, const f32x16 &c1, const float (&wt)[2][16]) {
-  // ReLU as an integer max on the float's bits: non-negative floats are
-  // non-negative integers, negative floats (and -0.0) negative ones.
-  float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    p0 = fmaf(wt[0][v], __int_as_float(max(__float_as_int(c0[v]), 0)), p0);
-    p1 = fmaf(wt[1][v], __int_as_float(max(__float_as_int(c1[v]), 0)), p1);
-  }
-  float p = p0 + p1;
-  return p + shfl_xor(p, 32);
-}
-
-template <int DT>
-__device__ __forceinline__ float key_scale(const IndexerArgs &a, long long slot) {
-  if (DT == DSA_FP8_E4M3FN) return a.k_scale[slot];
-  return 1.f;
-}
-
-// ------------------------------------------------------------------ decode tiling
-//
-// Each wave owns 32-key tiles (kRowBytes * 32 contiguous bytes: a tile never
-// straddles a 64-token block).  It loads a tile with fully coalesced 16-byte
-// loads -- one instruction covers whole rows -- into registers one tile ahead,
-// stores it into a wave-private LDS buffer with the 16-byte chunks of row r
-// XOR-swizzled by r, and reads the MFMA operands (lane: key l%32, chunks of
-// k-group l/32) back from there without bank conflicts.
-
-constexpr int kDecodeWaves = 4;
-
-template <int DT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void indexer_decode_kernel(
-    IndexerArgs a) {
-  typedef IdxTraits<DT> Tr;
-  constexpr int kChunks = Tr::kRowBytes / 16;       // 16-byte chunks per key row (16 bf16, 8 fp8)
-  constexpr int kPer = 32 * kChunks / 64;           // chunks each lane loads per tile (8 or 4)
-  __shared__ uint4 wtile[kDecodeWaves][32 * kChunks];
-  __shared__ uint32_t lh[kTopkBins];
-
-  const int r = blockIdx.y;
-  const int t = a.q_begin + r;
-  const int n = a.sv.candidates(t);
-  const int b = a.sv.seq_of(t);
-  const int c0 = blockIdx.x * kDecodeChunk;
-  float *srow = a.scores + (long long)r * a.ld;
-  const long long cend = c0 + kDecodeChunk < a.ld ? c0 + kDecodeChunk : a.ld;
-  if (a.fill_masked) {
-    for (long long s = (c0 > n ? c0 : n) + threadIdx.x; s < cend; s += blockDim.x) srow[s] = neg_inf();
-  }
-  if (c0 >= n) return;
-  const int c1 = c0 + kDecodeChunk < n ? c0 + kDecodeChunk : n;
-
-  // first radix digit of the top-k, counted per workgroup and added to the row's bins
-  const bool hist = a.hist_mode == 1;
-  if (hist)
-    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
-  // Slot of the first key of each 64-token block of this chunk (-1: absent),
-  // read once, so a tile's lookup is an LDS read that never waits on the
-  // vector-memory counter (which also counts the score stores in flight).
-  __shared__ long long blk0[kDecodeChunk / 64];
-  if (threadIdx.x < kDecodeChunk / 64) {
-    const int s = c0 + threadIdx.x * 64;
-    blk0[threadIdx.x] = s < c1 ? a.sv.slot(b, s) : -1;
-  }
-  __syncthreads();
-
-  const int lane = lane_id();
-  const int wv = threadIdx.x >> 6;
-  const int g = lane >> 5, col = lane & 31;
-  typename Tr::Op qa[2][Tr::kSteps];
-  float wt[2][16];
-  load_query<DT>(a, t, col, g, qa, wt);
-
-  const uint8_t *kbase = reinterpret_cast<const uint8_t *>(a.k_cache);
-  uint4 *tile = wtile[wv];
-  // Coalesced fetch of the tile at key `base`: lane l takes chunk (i*64 + l) of
-  // the tile for i < kPer, i.e. row (i*64 + l) / kChunks.  A tile lies inside
-  // one 64-token block, so one wave-uniform lookup gives the slot of its first
-  // row and the others follow.  Rows past c1 or in an absent block load zeros.
-  auto tile_slot = [&](int base) -> long long {
-    const long long b0 = blk0[(base - c0) >> 6];
-    return b0 >= 0 ? b0 + (base & 63) : -1;
-  };
-  // Every lane always loads (absent rows read the chunk's first row instead) and
-  // `put` zeroes what is absent: no branches, and no register initialised
-  // before a load that might be skipped.
-  auto fetch = [&](int base, long long sl0, uint4 (&st)[kPer]) {
-    const long long first = sl0 >= 0 ? sl0 : 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int p = i * 64 + lane;
-      const int row = p / kChunks, ch = p % kChunks;
-      const int rr = base + row < c1 ? row : 0;
-      st[i] = ld16(kbase + (first + rr) * Tr::kRowBytes + ch * 16);
-    }
-  };
-  auto put = [&](const uint4 (&st)[kPer], int base, long long sl0) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int p = i * 64 + lane;
-      const int row = p / kChunks, ch = p % kChunks;
-      const bool ok = sl0 >= 0 && base + row < c1;
-      tile[row * kChunks + (ch ^ (row & (kChunks - 1)))] = ok ? st[i] : make_uint4(0, 0, 0, 0);
-    }
-  };
-  // Two tiles in flight per wave: stage A holds tile i+1 (loaded one tile ago),
-  // stage B receives tile i+2 while tile i is multiplied from LDS.  The loop is
-  // unrolled by two so the stages keep fixed registers.
-  constexpr int kStep = kDecodeWaves * 32;
-  uint4 sa[kPer], sb[kPer];
-  int base = c0 + wv * 32;
-  long long sl0 = -1, sla = -1, slb = -1;
-  if (base < c1) {
-    sl0 = tile_slot(base);
-    fetch(base, sl0, sa);
-    put(sa, base, sl0);
-  }
-  sla = base + kStep < c1 ? tile_slot(base + kStep) : -1;
-  fetch(base + kStep, sla, sa);
-  // Drain the query, weight and first-tile loads here, so that no wait for them
-  // lands inside the loop (where it would also wait for the prefetch).
-  __builtin_amdgcn_s_waitcnt(0);
-  // Scores of the tile resident in LDS (valid in every lane for key col).
-  auto consume = [&]() {
-    typename Tr::Op kb[Tr::kSteps];
-    const uint4 *trow = tile + col * kChunks;
-#pragma unroll
-    for (int ks = 0; ks < Tr::kSteps; ++ks) {
-      if constexpr (DT == DSA_BF16) {
-        kb[ks] = __builtin_bit_cast(typename Tr::Op, trow[(g * 8 + ks) ^ (col & 15)]);
-      } else {
-        const int ch = g * 4 + ks * 2;
-        const uint4 lo = trow[ch ^ (col & 7)], hi = trow[(ch + 1) ^ (col & 7)];
-        typename Tr::Op o;
-        o[0] = lo.x; o[1] = lo.y; o[2] = lo.z; o[3] = lo.w;
-        o[4] = hi.x; o[5] = hi.y; o[6] = hi.z; o[7] = hi.w;
-        kb[ks] = o;
-      }
-    }
-    f32x16 c0a = zero_vec<f32x16>(), c1a = zero_vec<f32x16>();
-#pragma unroll
-    for (int ks = 0; ks < Tr::kSteps; ++ks) {
-      c0a = Tr::mma(qa[0][ks], kb[ks], c0a);
-      c1a = Tr::mma(qa[1][ks], kb[ks], c1a);
-    }
-    return head_reduce(c0a, c1a, wt);
-  };
-  auto emit = [&](int tb, long long tsl, float sc) {
-    const int s = tb + col;
-    if (g == 0 && s < c1) {
-      const float v = tsl >= 0 ? sc * key_scale<DT>(a, tsl + col) : neg_inf();
-      srow[s] = v;
-      if (hist) atomicAdd(&lh[score_key(v) >> 21], 1u);
-    }
-  };
-  for (; base < c1; base += 2 * kStep) {
-    const int b1 = base + kStep, b2 = base + 2 * kStep, b3 = base + 3 * kStep;
-    // LDS: tile `base` (slot sl0); stage A: tile b1 (sla); tile b2 -> stage B.
-    // The fetch is unconditional (past c1 it reads slot 0 and is discarded), so
-    // the compiler's wait counts stay exact on every path.
-    slb = b2 < c1 ? tile_slot(b2) : -1;
-    fetch(b2, slb, sb);
-    float sc = consume();
-    put(sa, b1, sla);                              // the LDS reads above completed before the MFMAs
-    emit(base, sl0, sc);
-    if (b1 >= c1) break;
-    // LDS: tile b1; stage B: tile b2 (slb); tile b3 -> stage A
-    const long long s1 = sla;
-    sla = b3 < c1 ? tile_slot(b3) : -1;
-    fetch(b3, sla, sa);
-    sc = consume();
-    put(sb, b2, slb);                              // past c1 this stores zeros that are never read
-    emit(b1, s1, sc);
-    sl0 = slb;
-  }
-  if (hist) {
-    __syncthreads();
-    uint32_t *hrow = a.hist + (long long)r * a.hist_stride;
-    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x)
-      if (lh[i]) atomicAdd(&hrow[i], lh[i]);
-  }
-}
 
 // ------------------------------------------------------------------ prefill tiling
 
@@ -502,14 +256,8 @@ hipError_t launch_index_scores(const IndexerArgs &a, hipStream_t st) {
     return hipGetLastError();
   }
   const bool decode = a.sv.mode == DSA_DECODE;
-  if (decode) {
-    const long long span = a.fill_masked ? a.ld : a.sv.max_ctx;
-    dim3 grid((unsigned)((span + kDecodeChunk - 1) / kDecodeChunk), (unsigned)a.rows);
-    if (a.dtype == DSA_BF16)
-      hipLaunchKernelGGL(indexer_decode_kernel<DSA_BF16>, grid, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL(indexer_decode_kernel<DSA_FP8_E4M3FN>, grid, dim3(256), 0, st, a);
-  } else {
+  if (decode) return launch_index_decode(a, st);
+  {
     dim3 grid((unsigned)((a.rows + kPrefillQ - 1) / kPrefillQ));
     if (a.dtype == DSA_BF16)
       hipLaunchKernelGGL(indexer_prefill_kernel<DSA_BF16>, grid, dim3(512), 0, st, a);

@@ -57,7 +57,9 @@ struct MlaArgs {
   float *lse;
   int q_begin, rows;
   int n_split;
-  float *part;  // [rows, n_split, H, Dv + 4] when n_split > 1 (acc[Dv], max, sum, pad)
+  // when n_split > 1: the normalised split outputs, bf16 [rows, n_split, H, Dv],
+  // followed by their (running max in log2 units, sum) pairs, fp32 [rows, n_split, H, 2]
+  void *part;
 };
 
 // top-k workspace, per row, in 32-bit words.  Header (zeroed before every
@@ -85,6 +87,7 @@ int mla_splits(int rows, int k);
 size_t mla_f32_lds(int H, int D, int k);
 
 hipError_t launch_index_scores(const IndexerArgs &a, hipStream_t s);
+hipError_t launch_index_decode(const IndexerArgs &a, hipStream_t s);   // decode tiling of the above
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);         // zero + hist1 + select
 hipError_t launch_topk_zero(const TopkArgs &a, hipStream_t s);    // zero the per-row headers
 hipError_t launch_topk_select(const TopkArgs &a, hipStream_t s);  // collect + select (hist1 ready)

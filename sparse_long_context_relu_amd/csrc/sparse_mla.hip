@@ -97,6 +97,7 @@ __device__ __forceinline__ void lds_dma16(const void *gsrc, uint32_t m0) {
 // wait for vector-memory counts <= 0 / <= 4, leave the others free.
 constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitVm4 = 0x0F74;
+constexpr int kWaitLgkm0 = 0xC07F;   // LDS / scalar counts <= 0, vector memory left in flight
 constexpr int kBufs = 3;
 
 // Workgroup barrier without a memory fence: the fence of __syncthreads would
@@ -284,8 +285,20 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, g = lane >> 4;
 
+  // Q^T operands for this wave's heads: lane holds head 16 wv + col,
+  // dims 32 ks + 8 g + [0, 8).  Issued first, so that their latency overlaps
+  // the index and page-table loads of the slot translation below; the barriers
+  // up to the first tile wait for LDS work only and leave them in flight.
+  bf16x8 qb[kKs];
+  {
+    const uint8_t *qrow = reinterpret_cast<const uint8_t *>(a.q) + ((long long)t * kH + wv * 16 + col) * (kD * 2);
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) qb[ks] = as_bf16x8(ld16(qrow + ks * 64 + g * 16));
+  }
+
   if (threadIdx.x == 0) fallback = -1;
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  lds_barrier();
   // Slots of this split's rows (-1: absent, and past the last row), so the
   // gather depends on LDS only.
   for (int j = threadIdx.x; j < ntiles * kR + 3 * kR; j += kThreads) {
@@ -296,15 +309,6 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
       if (sl >= 0) atomicMax(&fallback, sl);
     }
     slots[j] = sl;
-  }
-
-  // Q^T operands for this wave's heads: lane holds head 16 wv + col,
-  // dims 32 ks + 8 g + [0, 8).
-  bf16x8 qb[kKs];
-  {
-    const uint8_t *qrow = reinterpret_cast<const uint8_t *>(a.q) + ((long long)t * kH + wv * 16 + col) * (kD * 2);
-#pragma unroll
-    for (int ks = 0; ks < kKs; ++ks) qb[ks] = as_bf16x8(ld16(qrow + ks * 64 + g * 16));
   }
 
   f32x4 acc[kDb];
@@ -322,7 +326,8 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
   const uint32_t pv_odd = pv_row + ((2 + (vc >> 1)) ^ g) * 16;
   const uint32_t tile_lds = lds_addr(&tiles[0][0]);
   constexpr uint32_t kTileBytes = kTileBufChunks * 16;
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  lds_barrier();
   const int fb = fallback;
 
   if (fb >= 0) {
@@ -355,85 +360,81 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
   const int h = wv * 16 + col;
   float l_tot = l_run + shfl_xor(l_run, 16);
   l_tot += shfl_xor(l_tot, 32);
-  if (a.n_split == 1) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t *orow = reinterpret_cast<uint16_t *>(a.out) + ((long long)t * kH + h) * kDv;
+  // One split: the output row.  Several: this split's normalised output in
+  // bf16 (a weighted mean of value rows, so within their range) and its
+  // (max, sum), merged by the combine kernel.
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const long long orow_i = a.n_split == 1 ? (long long)t * kH + h : ((long long)r * a.n_split + sp) * kH + h;
+  uint16_t *orow = reinterpret_cast<uint16_t *>(a.n_split == 1 ? a.out : a.part) + orow_i * kDv;
 #pragma unroll
-    for (int db = 0; db < kDb; ++db) {
-      const int d = db * 16 + 4 * g;
-      uint2 pk;
-      pk.x = (uint32_t)f32_to_bf16(acc[db][0] * inv) | ((uint32_t)f32_to_bf16(acc[db][1] * inv) << 16);
-      pk.y = (uint32_t)f32_to_bf16(acc[db][2] * inv) | ((uint32_t)f32_to_bf16(acc[db][3] * inv) << 16);
-      *reinterpret_cast<uint2 *>(orow + d) = pk;
-    }
-    if (a.lse != nullptr && g == 0)
-      a.lse[(long long)t * kH + h] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : neg_inf();
-  } else {
-    float *prow = a.part + (((long long)r * a.n_split + sp) * kH + h) * (kDv + 4);
-#pragma unroll
-    for (int db = 0; db < kDb; ++db) {
-      const int d = db * 16 + 4 * g;
-      *reinterpret_cast<float4 *>(prow + d) = make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
-    }
-    if (g == 0) {
-      prow[kDv] = m_run;
-      prow[kDv + 1] = l_tot;
+  for (int db = 0; db < kDb; ++db) {
+    const int d = db * 16 + 4 * g;
+    uint2 pk;
+    pk.x = pack_bf16x2(acc[db][0] * inv, acc[db][1] * inv);
+    pk.y = pack_bf16x2(acc[db][2] * inv, acc[db][3] * inv);
+    *reinterpret_cast<uint2 *>(orow + d) = pk;
+  }
+  if (g == 0) {
+    if (a.n_split == 1) {
+      if (a.lse != nullptr) a.lse[orow_i] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : neg_inf();
+    } else {
+      float2 *ml = reinterpret_cast<float2 *>(reinterpret_cast<uint16_t *>(a.part) +
+                                              (long long)a.rows * a.n_split * kH * kDv);
+      ml[orow_i] = make_float2(m_run, l_tot);
     }
   }
 }
 
 // Merge the split partials of one (query, head): one wave per head, each lane
-// owning 8 of the 512 value dims.  Lane s < n_split reads split s's running
-// maximum and sum; the loads of up to eight splits' accumulators are issued
-// together, and the weighted sum runs in split order.
+// owning 8 consecutive value dims.  Lane s < n_split reads split s's running
+// maximum and sum; split s weighs exp2(max_s - M) sum_s, normalised over the
+// splits.  The loads of up to eight splits are issued together, and the
+// weighted sum runs in split order.
 __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
   const int lane = lane_id();
   const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int r = blockIdx.y;
   const int t = a.q_begin + r;
   const int ns = a.n_split;
-  const long long stride = (long long)kH * (kDv + 4);
-  const float *base = a.part + ((long long)r * ns * kH + h) * (kDv + 4);
+  const uint16_t *po = reinterpret_cast<const uint16_t *>(a.part) + ((long long)r * ns * kH + h) * kDv + lane * 8;
+  const float2 *ml = reinterpret_cast<const float2 *>(reinterpret_cast<const uint16_t *>(a.part) +
+                                                      (long long)a.rows * ns * kH * kDv) +
+                     (long long)r * ns * kH + h;
   float ms = neg_inf(), ls = 0.f;
   if (lane < ns) {
-    ms = base[lane * stride + kDv];
-    ls = base[lane * stride + kDv + 1];
+    const float2 v = ml[(long long)lane * kH];
+    ms = v.x;
+    ls = v.y;
   }
   const float M = wave_max(ms);
-  const float w = ms == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-  const float L = wave_sum(w * ls);
+  const float w = ms == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(ms - M) * ls;
+  const float L = wave_sum(w);
   const float inv = L > 0.f ? 1.f / L : 0.f;
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < ns; s0 += 8) {
-    float4 v[8][2];
+    uint4 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (s0 + u < ns) {
-        const float *p = base + (s0 + u) * stride + lane * 4;
-        v[u][0] = *reinterpret_cast<const float4 *>(p);
-        v[u][1] = *reinterpret_cast<const float4 *>(p + kDv / 2);
-      }
+      if (s0 + u < ns) v[u] = *reinterpret_cast<const uint4 *>(po + (long long)(s0 + u) * kH * kDv);
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       if (s0 + u < ns) {
         const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), s0 + u));
+        const uint32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          o[4 * hf + 0] = fmaf(wu, v[u][hf].x, o[4 * hf + 0]);
-          o[4 * hf + 1] = fmaf(wu, v[u][hf].y, o[4 * hf + 1]);
-          o[4 * hf + 2] = fmaf(wu, v[u][hf].z, o[4 * hf + 2]);
-          o[4 * hf + 3] = fmaf(wu, v[u][hf].w, o[4 * hf + 3]);
+        for (int i = 0; i < 4; ++i) {
+          o[2 * i] = fmaf(wu, __builtin_bit_cast(float, x[i] << 16), o[2 * i]);
+          o[2 * i + 1] = fmaf(wu, __builtin_bit_cast(float, x[i] & 0xFFFF0000u), o[2 * i + 1]);
         }
       }
   }
-  uint16_t *orow = reinterpret_cast<uint16_t *>(a.out) + ((long long)t * kH + h) * kDv;
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    uint2 pk;
-    pk.x = (uint32_t)f32_to_bf16(o[4 * hf + 0] * inv) | ((uint32_t)f32_to_bf16(o[4 * hf + 1] * inv) << 16);
-    pk.y = (uint32_t)f32_to_bf16(o[4 * hf + 2] * inv) | ((uint32_t)f32_to_bf16(o[4 * hf + 3] * inv) << 16);
-    *reinterpret_cast<uint2 *>(orow + hf * (kDv / 2) + lane * 4) = pk;
-  }
+  uint16_t *orow = reinterpret_cast<uint16_t *>(a.out) + ((long long)t * kH + h) * kDv + lane * 8;
+  uint4 pk;
+  pk.x = pack_bf16x2(o[0] * inv, o[1] * inv);
+  pk.y = pack_bf16x2(o[2] * inv, o[3] * inv);
+  pk.z = pack_bf16x2(o[4] * inv, o[5] * inv);
+  pk.w = pack_bf16x2(o[6] * inv, o[7] * inv);
+  *reinterpret_cast<uint4 *>(orow) = pk;
   if (lane == 0 && a.lse != nullptr) a.lse[(long long)t * kH + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : neg_inf();
 }
 

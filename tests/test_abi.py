@@ -128,7 +128,7 @@ def test_topk_validation():
 def test_sparse_mla_validation():
     pb = _problem()
     need = B.workspace_size(B.OP_SPARSE_MLA, pb)
-    assert need == 2 * 32 * 128 * (512 + 4) * 4         # 2 queries x 32 splits of fp32 partials
+    assert need == 2 * 32 * 128 * (512 * 2 + 8)           # 2 queries x 32 splits: bf16 outputs, fp32 (max, sum)
     call = lambda pbx, ws=FAKE, nb=1 << 40, q=FAKE, sm=0.04: B.LIB.dsa_sparse_mla(
         ctypes.byref(pbx.seqs), ctypes.byref(pbx.dims), sm, q, FAKE, FAKE, FAKE, None, ws, nb, None)
     assert call(pb, q=None) == B.ERR_INVALID_ARG
