@@ -52,6 +52,14 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
+// v + v[lane ^ 32] in every lane, through the gfx950 half-wave swap (a VALU
+// op; no LDS round trip).  Lanes below 32 add v[l] + v[l + 32], the others
+// v[l - 32] + v[l]: the same sums as an exchange with lane ^ 32.
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));

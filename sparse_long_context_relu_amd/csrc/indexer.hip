@@ -60,39 +60,39 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
   const uint8_t *kbase = reinterpret_cast<const uint8_t *>(a.k_cache);
   // Stage the tile starting at key `base` into registers.
   uint4 stage[kPerThread];
-  long long stage_slot[kPerThread];
   float stage_scale[kPerThread];
-  // A tile covers whole 64-token blocks: one uniform lookup per block gives its first slot.
-  auto fetch = [&](int base) {
-    long long slb[kPrefillKeys / 64];
+  // A tile covers whole 64-token blocks: one uniform lookup per block gives its
+  // first slot, and whether the block is present at all (keys past nmax are
+  // never written out, so their presence does not matter).
+  constexpr int kBlocks = kPrefillKeys / 64;
+  auto fetch = [&](int base, bool (&ok)[kBlocks]) {
+    long long slb[kBlocks];
 #pragma unroll
-    for (int j = 0; j < kPrefillKeys / 64; ++j) slb[j] = base + 64 * j < nmax ? a.sv.slot(0, base + 64 * j) : -1;
+    for (int j = 0; j < kBlocks; ++j) {
+      slb[j] = base + 64 * j < nmax ? a.sv.slot(0, base + 64 * j) : -1;
+      ok[j] = slb[j] >= 0;
+    }
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
       const int c = threadIdx.x + i * 512;
       const int key = c / kChunks, ch = c % kChunks;
       const long long sl0 = slb[key >> 6];
       const long long sl = (sl0 >= 0 && base + key < nmax) ? sl0 + (key & 63) : -1;
-      stage_slot[i] = sl;
       stage[i] = sl >= 0 ? ld16(kbase + sl * Tr::kRowBytes + ch * 16) : make_uint4(0, 0, 0, 0);
       if (DT == DSA_FP8_E4M3FN) stage_scale[i] = (sl >= 0 && ch == 0) ? a.k_scale[sl] : 0.f;
     }
   };
-  __shared__ int absent[2][kPrefillKeys];
   __shared__ float kscale[2][kPrefillKeys];
   // Swizzled store: chunk ch of key `key` goes to slot ch ^ (key & 15) of its row (bf16),
   // so the 16 lanes of one MFMA operand read touch 16 distinct bank groups.  The
-  // key's presence (and fp8 scale) go beside the tile.
+  // fp8 key scales go beside the tile.
   auto put = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
       const int c = threadIdx.x + i * 512;
       const int key = c / kChunks, ch = c % kChunks;
       tile[buf][key * kChunks + (ch ^ (key & (kChunks - 1)))] = stage[i];
-      if (ch == 0) {
-        absent[buf][key] = stage_slot[i] < 0;
-        if (DT == DSA_FP8_E4M3FN) kscale[buf][key] = stage_scale[i];
-      }
+      if (DT == DSA_FP8_E4M3FN && ch == 0) kscale[buf][key] = stage_scale[i];
     }
   };
   // first radix digit of the top-k: each wave owns its query row's bins
@@ -144,8 +144,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
       asm volatile("" : "+v"(r0), "+v"(r1));
       __builtin_amdgcn_sched_barrier(0);
     }
-    const float rr = r0 + r1;
-    return rr + shfl_xor(rr, 32);
+    return sum_xor32(r0 + r1);
   };
   auto emit = [&](int s, float sc, bool gone, float kscl) {
     if (g == 0 && s < n && row_ok) {
@@ -160,11 +159,15 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
   };
 
   // Software pipeline over 32-key groups: while group i+1 is multiplied, group
-  // i is reduced and written.  The presence flags and scales of a group are read
-  // into registers before the barrier after which their buffer may be refilled.
+  // i is reduced and written.  The fp8 scales of a group are read into registers
+  // before the barrier after which their buffer may be refilled; block presence
+  // travels with the tile in wave-uniform flags.
   int buf = 0;
+  bool okc[kBlocks], okn[kBlocks];          // the tile in LDS / the tile being fetched
+#pragma unroll
+  for (int j = 0; j < kBlocks; ++j) okc[j] = okn[j] = true;
   if (nmax > 0) {
-    fetch(0);
+    fetch(0, okc);
     put(0);
   }
   __syncthreads();
@@ -172,22 +175,19 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = zero_vec<f32x16>();
-  bool gone[2];
   float scl[2];
   (void)mma_reduce(0, 0, acc[0][0], acc[0][1], acc[1][0], acc[1][1]);
-  gone[0] = absent[0][col] != 0;
   scl[0] = DT == DSA_FP8_E4M3FN ? kscale[0][col] : 1.f;
   for (int base = 0; base < nmax; base += kPrefillKeys) {
     const bool more = base + kPrefillKeys < nmax;
-    if (more) fetch(base + kPrefillKeys);
+    if (more) fetch(base + kPrefillKeys, okn);
     // group nb -> acc[nb & 1] while group nb - 1 is reduced and written
 #pragma unroll
     for (int nb = 1; nb < kGroups; ++nb) {
       const int cur = nb & 1, prv = cur ^ 1;
       const float sc = mma_reduce(buf, nb, acc[cur][0], acc[cur][1], acc[prv][0], acc[prv][1]);
-      gone[cur] = absent[buf][nb * 32 + col] != 0;
       scl[cur] = DT == DSA_FP8_E4M3FN ? kscale[buf][nb * 32 + col] : 1.f;
-      emit(base + (nb - 1) * 32 + col, sc, gone[prv], scl[prv]);
+      emit(base + (nb - 1) * 32 + col, sc, !okc[(nb - 1) >> 1], scl[prv]);
     }
     if (more) put(buf ^ 1);
     __syncthreads();
@@ -195,9 +195,10 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
     // group 0 of the next tile -> acc[0] while the tile's last group (in acc[1])
     // is reduced (past the last tile this multiplies a stale buffer, unused)
     const float sc = mma_reduce(buf, 0, acc[0][0], acc[0][1], acc[1][0], acc[1][1]);
-    const bool last_gone = gone[1];
+    const bool last_gone = !okc[kBlocks - 1];
     const float last_scl = scl[1];
-    gone[0] = absent[buf][col] != 0;
+#pragma unroll
+    for (int j = 0; j < kBlocks; ++j) okc[j] = okn[j];
     scl[0] = DT == DSA_FP8_E4M3FN ? kscale[buf][col] : 1.f;
     emit(base + (kGroups - 1) * 32 + col, sc, last_gone, last_scl);
   }
