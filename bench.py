@@ -97,7 +97,20 @@ def make_events(torch, count):
     return evs
 
 
-def time_forward(B, torch, inp, steps, warmup):
+def settle(torch, call, ms):
+    """Run `call` untimed for about `ms` of wall time.  The GPU raises its shader
+    clock over tens of milliseconds of sustained work; timing right after an
+    idle gap (input generation, a sync) would measure the ramp, not the step."""
+    if ms <= 0:
+        return
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(4):
+            call()
+        torch.cuda.synchronize()
+
+
+def time_forward(B, torch, inp, steps, warmup, settle_ms=0):
     pb = B.problem_from_inputs(inp)
     ws = torch.empty(B.workspace_size(B.OP_FORWARD, pb), dtype=torch.uint8, device="cuda")
     T, H, Dv, k = inp.num_q, inp.wl.heads, inp.wl.v_dim, inp.topk
@@ -107,6 +120,7 @@ def time_forward(B, torch, inp, steps, warmup):
     call = lambda ev=None: B.forward(pb, inp.q_idx, inp.q_scale, inp.w, inp.k_cache, inp.k_scale, inp.q,
                                      inp.kv_cache, inp.sm_scale, out=out, lse=lse, topk_idx=idx, ws=ws,
                                      stage_events=ev)
+    settle(torch, call, settle_ms)
     for _ in range(warmup):
         call()
     # Timed region 1, the step time: K steps back to back, nothing recorded in between.
@@ -172,6 +186,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--settle-ms", type=float, default=400.0,
+                    help="untimed run-in before each timed region, so the shader clock has settled")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurement")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -201,7 +217,7 @@ def main():
     inp = generate(wl, "cuda")
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
-    ms, stages = time_forward(B, torch, inp, args.steps, args.warmup)
+    ms, stages = time_forward(B, torch, inp, args.steps, args.warmup, args.settle_ms)
     tokens = inp.num_q
     value = tokens / (ms * 1e-3)
     idx_bytes, step_bytes = algorithmic_bytes(inp)
@@ -223,7 +239,8 @@ def main():
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "settle_ms": args.settle_ms, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak",
         "vs_baseline": None, "dtype": wl.mla_dtype if wl.index_dtype != "fp8" else "bf16+fp8",
         "data": "synthetic (seeded; no dataset or weights)",
         "config": {"workload": name, "mode": wl.mode, "batch": wl.num_seqs,
@@ -244,7 +261,7 @@ def main():
         del inp
         torch.cuda.empty_cache()
         pin = generate(WORKLOADS[pname], "cuda")
-        pms, pst = time_forward(B, torch, pin, 2, 1)
+        pms, pst = time_forward(B, torch, pin, 3, 1, args.settle_ms)
         pf_idx, pf_mla = algorithmic_flops(pin)
         # each stage alone over every query row, one call each (the forward
         # processes the rows in chunks; its stage events cover the first chunk)
@@ -258,13 +275,14 @@ def main():
                lambda: B.sparse_mla(pb, pin.sm_scale, pin.q, pin.kv_cache, idx, ws=mws)]
         stage_ms = []
         for op in ops:
-            op()
+            settle(torch, op, args.settle_ms / 2)
             e0, e1 = make_events(torch, 2)
             e0.record()
-            op()
+            for _ in range(3):
+                op()
             e1.record()
             torch.cuda.synchronize()
-            stage_ms.append(e0.elapsed_time(e1))
+            stage_ms.append(e0.elapsed_time(e1) / 3)
         ims = stage_ms[0]
         result["prefill"] = {
             "workload": pname, "tokens_per_s": round(pin.num_q / (pms * 1e-3), 1), "ms_per_step": round(pms, 3),
