@@ -16,6 +16,51 @@ typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 
 constexpr int kWave = 64;
 
+// ---------------------------------------------------------------- direct-to-LDS tiles
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// One 16-byte direct-to-LDS load: lane l's 16 bytes land at LDS address
+// m0 + 16 l (m0 wave-uniform); inactive lanes write nothing.  It returns
+// nothing in registers.  It is written out here because the compiler's wait
+// insertion cannot tell tile buffers apart and would otherwise stall the
+// consumer of one buffer on the loads still streaming into another; a kernel
+// using it waits for these loads itself (s_waitcnt vmcnt and a barrier) before
+// any wave reads the buffer they fill.  Vector-memory loads complete in issue
+// order, so vmcnt(n) means "all but this wave's n most recent loads landed"
+// (stores issued in between can only make such a wait stricter).
+__device__ __forceinline__ void lds_dma16(const void *gsrc, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0), "v"(gsrc)
+               : "memory", "m0");
+}
+
+// The 4-byte form: lane l's 4 bytes land at LDS address m0 + 4 l.
+__device__ __forceinline__ void lds_dma4(const void *gsrc, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(m0), "v"(gsrc)
+               : "memory", "m0");
+}
+
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kWaitVm0 = 0x0F70;      // vector-memory count <= 0, the others free
+__host__ __device__ constexpr int wait_vm(int n) { return 0x0F70 | n; }   // vmcnt <= n (n < 16)
+constexpr int kWaitLgkm0 = 0xC07F;    // LDS / scalar counts <= 0, vector memory left in flight
+
+// Workgroup barrier without a memory fence: the fence of __syncthreads would
+// also wait for the tile loads still streaming into the other buffers.  LDS
+// reads are complete once their values are used, and the direct-to-LDS writes
+// are covered by each wave's own s_waitcnt before it arrives here.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------- scalars
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }

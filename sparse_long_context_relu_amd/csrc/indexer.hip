@@ -11,7 +11,7 @@
 //     keys split into chunks across workgroups; each wave streams 32-key
 //     tiles straight from HBM into MFMA operand registers.
 //   * prefill tiling: 8 consecutive queries per workgroup (one per wave)
-//     share 64-key tiles staged through LDS.
+//     share 16 KB key tiles gathered straight into LDS, three deep.
 // e4m3fn: scores = k_scale(s) * sum_j (w_j q_scale_j) ReLU(q8_j . k8_s),
 // exact because ReLU(a x) = a ReLU(x) for a > 0.
 //   (the decode tiling is in indexer_decode.hip)
@@ -24,20 +24,37 @@ namespace {
 
 constexpr int kPrefillQ = 8;     // queries (waves) per workgroup
 
+// Slot of the first key of the 64-token block holding key `s` of sequence 0,
+// or -1 when the block is outside the pool.  `s` is wave-uniform; a paged
+// lookup goes through the scalar cache (the block table is read-only here), so
+// it never waits on the vector-memory counter that tracks the tile loads.
+__device__ __forceinline__ long long block_slot(const SeqView &sv, int s) {
+  if (sv.block_table == nullptr) return (long long)(s & ~63);
+  const __attribute__((address_space(4))) int32_t *bt =
+      (const __attribute__((address_space(4))) int32_t *)sv.block_table;
+  const int blk = bt[__builtin_amdgcn_readfirstlane(s >> 6)];
+  return (blk < 0 || blk >= sv.num_blocks) ? -1 : (long long)blk * 64;
+}
+
 template <int DT>
 __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
   typedef IdxTraits<DT> Tr;
   constexpr int kChunks = Tr::kRowBytes / 16;           // 16-byte chunks per key row (16 or 8)
-  // keys per LDS tile: 64 for bf16 (a larger tile spills registers), 128 for
-  // e4m3fn (half the bytes per key, and twice the MFMA work per barrier)
+  // keys per LDS tile: 64 for bf16, 128 for e4m3fn (the same 16 KB)
   constexpr int kPrefillKeys = DT == DSA_BF16 ? 64 : 128;
-  constexpr int kTileChunks = kPrefillKeys * kChunks;   // chunks per tile
-  constexpr int kPerThread = kTileChunks / 512;         // 2 (bf16) or 1 (fp8)
-  __shared__ uint4 tile[2][kTileChunks];
+  constexpr int kBlocks = kPrefillKeys / 64;            // 64-token blocks per tile
+  constexpr int kTileChunks = kPrefillKeys * kChunks;   // 1024 chunks per tile
+  constexpr int kLoads = kTileChunks / 512;             // direct loads per wave per tile (2)
+  constexpr bool kScaled = DT == DSA_FP8_E4M3FN;
+  constexpr int kWaveLoads = kLoads + (kScaled ? 1 : 0);   // + the key scales (fp8)
+  constexpr int kBufs = 3;                              // tiles tt+1, tt+2 stream in while tt is used
+  constexpr uint32_t kTileBytes = kTileChunks * 16;
+  __shared__ uint4 tile[kBufs][kTileChunks];
+  __shared__ float kscale[kBufs][kScaled ? kPrefillKeys : 1];
 
   const int grp = gridDim.x - 1 - blockIdx.x;           // longest rows first
   const int lane = lane_id();
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, col = lane & 31;
   const int r = grp * kPrefillQ + wv;
   const bool row_ok = r < a.rows;
@@ -51,55 +68,59 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
       nmax = ni > nmax ? ni : nmax;
     }
   }
+  nmax = __builtin_amdgcn_readfirstlane(nmax);
   float *srow = a.scores + (long long)(row_ok ? r : 0) * a.ld;
 
   typename Tr::Op qa[2][Tr::kSteps];
   float wt[2][16];
   load_query<DT>(a, t, col, g, qa, wt);
 
-  const uint8_t *kbase = reinterpret_cast<const uint8_t *>(a.k_cache);
-  // Stage the tile starting at key `base` into registers.
-  uint4 stage[kPerThread];
-  float stage_scale[kPerThread];
-  // A tile covers whole 64-token blocks: one uniform lookup per block gives its
-  // first slot, and whether the block is present at all (keys past nmax are
-  // never written out, so their presence does not matter).
-  constexpr int kBlocks = kPrefillKeys / 64;
-  auto fetch = [&](int base, bool (&ok)[kBlocks]) {
-    long long slb[kBlocks];
-#pragma unroll
-    for (int j = 0; j < kBlocks; ++j) {
-      slb[j] = base + 64 * j < nmax ? a.sv.slot(0, base + 64 * j) : -1;
-      ok[j] = slb[j] >= 0;
-    }
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int c = threadIdx.x + i * 512;
-      const int key = c / kChunks, ch = c % kChunks;
-      const long long sl0 = slb[key >> 6];
-      const long long sl = (sl0 >= 0 && base + key < nmax) ? sl0 + (key & 63) : -1;
-      stage[i] = sl >= 0 ? ld16(kbase + sl * Tr::kRowBytes + ch * 16) : make_uint4(0, 0, 0, 0);
-      if (DT == DSA_FP8_E4M3FN) stage_scale[i] = (sl >= 0 && ch == 0) ? a.k_scale[sl] : 0.f;
-    }
-  };
-  __shared__ float kscale[2][kPrefillKeys];
-  // Swizzled store: chunk ch of key `key` goes to slot ch ^ (key & 15) of its row (bf16),
-  // so the 16 lanes of one MFMA operand read touch 16 distinct bank groups.  The
-  // fp8 key scales go beside the tile.
-  auto put = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int c = threadIdx.x + i * 512;
-      const int key = c / kChunks, ch = c % kChunks;
-      tile[buf][key * kChunks + (ch ^ (key & (kChunks - 1)))] = stage[i];
-      if (DT == DSA_FP8_E4M3FN && ch == 0) kscale[buf][key] = stage_scale[i];
-    }
-  };
   // first radix digit of the top-k: each wave owns its query row's bins
   __shared__ uint32_t wh[kPrefillQ][kTopkBins];
   const bool hist = a.hist_mode == 2;
   if (hist)
     for (int i = lane; i < kTopkBins; i += 64) wh[wv][i] = 0u;
+
+  const uint8_t *kbase = reinterpret_cast<const uint8_t *>(a.k_cache);
+  const uint32_t tile_lds = lds_addr(&tile[0][0]);
+  const uint32_t scale_lds = lds_addr(&kscale[0][0]);
+  // Direct-to-LDS gather of the tile at key `base` (< nmax) into buffer `bi`.
+  // Position p of a tile holds data chunk (p % kChunks) ^ (key & (kChunks - 1))
+  // of key p / kChunks, so the 16 lanes of one MFMA operand read touch distinct
+  // bank groups; wave wv's j-th load fills positions (8 j + wv) 64 + [0, 64).
+  // Keys at or past nmax load the last valid key, absent blocks slot 0: every
+  // byte the MFMAs read is a finite cache entry, and neither is written out.
+  // Returns the block presence bits of the tile.
+  auto issue = [&](int base, int bi) -> uint32_t {
+    long long sl0[kBlocks];
+    uint32_t ok = 0;
+#pragma unroll
+    for (int j = 0; j < kBlocks; ++j) {
+      sl0[j] = base + 64 * j < nmax ? block_slot(a.sv, base + 64 * j) : -1;
+      ok |= (sl0[j] >= 0 ? 1u : 0u) << j;
+    }
+    const int last = nmax - 1 - base;                    // last valid key of the tile
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int p = (j * kPrefillQ + wv) * 64 + lane;
+      const int key = p / kChunks, ch = (p % kChunks) ^ (key & (kChunks - 1));
+      const int kk = key <= last ? key : last;
+      const long long b0 = sl0[kk >> 6];
+      const long long sl = b0 >= 0 ? b0 + (kk & 63) : 0;
+      lds_dma16(kbase + sl * Tr::kRowBytes + ch * 16, tile_lds + bi * kTileBytes + (j * kPrefillQ + wv) * 1024);
+    }
+    if constexpr (kScaled) {
+      // the 128 key scales, one per lane: wave wv's lanes 0..15 fetch keys 16 wv + lane
+      if (lane < 16) {
+        const int key = wv * 16 + lane;
+        const int kk = key <= last ? key : last;
+        const long long b0 = sl0[kk >> 6];
+        const long long sl = b0 >= 0 ? b0 + (kk & 63) : 0;
+        lds_dma4(a.k_scale + sl, scale_lds + bi * (kPrefillKeys * 4) + wv * 64);
+      }
+    }
+    return ok;
+  };
 
   // MFMAs of 32-key group nb of the tile in buffer bi (rows nb*32 + col) into
   // (c0a, c1a), interleaved in program order with the ReLU-weighted head sum of
@@ -151,56 +172,67 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
       float v = neg_inf();
       if (!gone) {
         v = sc;
-        if (DT == DSA_FP8_E4M3FN) v *= kscl;
+        if (kScaled) v *= kscl;
       }
       srow[s] = v;
       if (hist) atomicAdd(&wh[wv][score_key(v) >> 21], 1u);
     }
   };
 
-  // Software pipeline over 32-key groups: while group i+1 is multiplied, group
-  // i is reduced and written.  The fp8 scales of a group are read into registers
-  // before the barrier after which their buffer may be refilled; block presence
-  // travels with the tile in wave-uniform flags.
-  int buf = 0;
-  bool okc[kBlocks], okn[kBlocks];          // the tile in LDS / the tile being fetched
-#pragma unroll
-  for (int j = 0; j < kBlocks; ++j) okc[j] = okn[j] = true;
-  if (nmax > 0) {
-    fetch(0, okc);
-    put(0);
-  }
-  __syncthreads();
+  // Software pipeline over the 32-key groups of all tiles: while group i+1 is
+  // multiplied, group i is reduced and written.  Tile tt+2 is issued right after
+  // the barrier that opens tile tt, into the buffer of tile tt-1, which every
+  // wave has finished reading by then.  Block presence bits travel with the
+  // tile (3 buffers x kBlocks bits); fp8 key scales are read into registers one
+  // group ahead of their use.
   constexpr int kGroups = kPrefillKeys / 32;             // 32-key groups per tile (even)
+  const int ntiles = (nmax + kPrefillKeys - 1) / kPrefillKeys;
+  uint32_t okbits = 0;
+  if (ntiles > 0) okbits |= issue(0, 0);
+  // drain the query / weight loads (with tile 0) here, so that no wait for
+  // them lands inside the loop, where it would also wait for the prefetches
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  if (ntiles > 1) okbits |= issue(kPrefillKeys, 1) << kBlocks;
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = zero_vec<f32x16>();
-  float scl[2];
-  (void)mma_reduce(0, 0, acc[0][0], acc[0][1], acc[1][0], acc[1][1]);
-  scl[0] = DT == DSA_FP8_E4M3FN ? kscale[0][col] : 1.f;
-  for (int base = 0; base < nmax; base += kPrefillKeys) {
-    const bool more = base + kPrefillKeys < nmax;
-    if (more) fetch(base + kPrefillKeys, okn);
-    // group nb -> acc[nb & 1] while group nb - 1 is reduced and written
-#pragma unroll
-    for (int nb = 1; nb < kGroups; ++nb) {
-      const int cur = nb & 1, prv = cur ^ 1;
-      const float sc = mma_reduce(buf, nb, acc[cur][0], acc[cur][1], acc[prv][0], acc[prv][1]);
-      scl[cur] = DT == DSA_FP8_E4M3FN ? kscale[buf][nb * 32 + col] : 1.f;
-      emit(base + (nb - 1) * 32 + col, sc, !okc[(nb - 1) >> 1], scl[prv]);
+  float scl[2] = {1.f, 1.f};
+  bool gone_prev = false;
+  int bi = 0;
+  for (int tt = 0; tt < ntiles; ++tt) {
+    // this wave's loads of tile tt have landed once at most the loads of tile
+    // tt+1 are outstanding; the barrier then covers every wave's
+    if (tt + 1 < ntiles)
+      __builtin_amdgcn_s_waitcnt(wait_vm(kWaveLoads));
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    lds_barrier();
+    if (tt + 2 < ntiles) {
+      const int nb2 = bi == 0 ? 2 : bi - 1;              // (tt + 2) % 3
+      okbits = (okbits & ~(((1u << kBlocks) - 1) << (nb2 * kBlocks))) |
+               (issue((tt + 2) * kPrefillKeys, nb2) << (nb2 * kBlocks));
     }
-    if (more) put(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    // group 0 of the next tile -> acc[0] while the tile's last group (in acc[1])
-    // is reduced (past the last tile this multiplies a stale buffer, unused)
-    const float sc = mma_reduce(buf, 0, acc[0][0], acc[0][1], acc[1][0], acc[1][1]);
-    const bool last_gone = !okc[kBlocks - 1];
-    const float last_scl = scl[1];
+    const uint32_t okt = okbits >> (bi * kBlocks);
+    const int base = tt * kPrefillKeys;
 #pragma unroll
-    for (int j = 0; j < kBlocks; ++j) okc[j] = okn[j];
-    scl[0] = DT == DSA_FP8_E4M3FN ? kscale[buf][col] : 1.f;
-    emit(base + (kGroups - 1) * 32 + col, sc, last_gone, last_scl);
+    for (int nb = 0; nb < kGroups; ++nb) {
+      const int cur = nb & 1, prv = cur ^ 1;
+      const float sc = mma_reduce(bi, nb, acc[cur][0], acc[cur][1], acc[prv][0], acc[prv][1]);
+      if (kScaled) scl[cur] = kscale[bi][nb * 32 + col];
+      if (tt > 0 || nb > 0) emit(base + nb * 32 - 32 + col, sc, gone_prev, scl[prv]);
+      gone_prev = ((okt >> (nb >> 1)) & 1u) == 0;
+    }
+    bi = bi == 2 ? 0 : bi + 1;
+  }
+  if (ntiles > 0) {
+    // the last group (in acc[1], kGroups being even) is reduced alone
+    float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      p0 = fmaf(wt[0][v], __int_as_float(max(__float_as_int(acc[1][0][v]), 0)), p0);
+      p1 = fmaf(wt[1][v], __int_as_float(max(__float_as_int(acc[1][1][v]), 0)), p1);
+    }
+    emit(ntiles * kPrefillKeys - 32 + col, sum_xor32(p0 + p1), gone_prev, scl[1]);
   }
   if (a.fill_masked && row_ok) {
     for (long long s = n + lane; s < a.ld; s += 64) srow[s] = neg_inf();

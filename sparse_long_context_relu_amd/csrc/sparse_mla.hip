@@ -76,39 +76,7 @@ __device__ __forceinline__ void mla_block(const MlaArgs &a, int &sp, int &r) {
   sp = v - r * a.n_split;
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-
-// One 16-byte direct-to-LDS load: lane l's 16 bytes land at LDS address
-// m0 + 16 l (m0 wave-uniform).  It returns nothing in registers.  It is written
-// out here because the compiler's wait insertion cannot tell the two tile
-// buffers apart and would otherwise stall the consumer of one buffer on the
-// loads still streaming into the other; the kernel waits for these loads itself
-// (s_waitcnt vmcnt(0) and a barrier) before any wave reads the buffer they fill.
-__device__ __forceinline__ void lds_dma16(const void *gsrc, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(m0), "v"(gsrc)
-               : "memory", "m0");
-}
-
-// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8):
-// wait for vector-memory counts <= 0 / <= 4, leave the others free.
-constexpr int kWaitVm0 = 0x0F70;
-constexpr int kWaitVm4 = 0x0F74;
-constexpr int kWaitLgkm0 = 0xC07F;   // LDS / scalar counts <= 0, vector memory left in flight
 constexpr int kBufs = 3;
-
-// Workgroup barrier without a memory fence: the fence of __syncthreads would
-// also wait for the tile loads still streaming into the other buffers.  LDS
-// reads are complete once their values are used, and the direct-to-LDS writes
-// are covered by each wave's own s_waitcnt before it arrives here.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // The direct-to-LDS gather of split rows [j0, j0+32) into the tile at LDS
 // address `tile`.  Position p of the tile is (row p/74, slot p%74) and holds data
@@ -343,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
       // loads of tile tt+1 are outstanding; the barrier then covers every wave's,
       // and also orders every wave's reads of tile tt-1 before its buffer is refilled.
       if (tt + 1 < ntiles)
-        __builtin_amdgcn_s_waitcnt(kWaitVm4);
+        __builtin_amdgcn_s_waitcnt(wait_vm(4));
       else
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
       lds_barrier();
