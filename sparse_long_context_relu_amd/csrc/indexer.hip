@@ -24,6 +24,7 @@ namespace {
 
 constexpr int kPrefillQ = 8;     // queries (waves) per workgroup
 
+
 // Slot of the first key of the 64-token block holding key `s` of sequence 0,
 // or -1 when the block is outside the pool.  `s` is wave-uniform; a paged
 // lookup goes through the scalar cache (the block table is read-only here), so
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
   // drain the query / weight loads (with tile 0) here, so that no wait for
   // them lands inside the loop, where it would also wait for the prefetches
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  if (ntiles > 1) okbits |= issue(kPrefillKeys, 1) << kBlocks;
+  if (kBufs > 2 && ntiles > 1) okbits |= issue(kPrefillKeys, 1) << kBlocks;
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = zero_vec<f32x16>();
@@ -202,15 +203,15 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
   for (int tt = 0; tt < ntiles; ++tt) {
     // this wave's loads of tile tt have landed once at most the loads of tile
     // tt+1 are outstanding; the barrier then covers every wave's
-    if (tt + 1 < ntiles)
+    if (kBufs > 2 && tt + 1 < ntiles)
       __builtin_amdgcn_s_waitcnt(wait_vm(kWaveLoads));
     else
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
     lds_barrier();
-    if (tt + 2 < ntiles) {
-      const int nb2 = bi == 0 ? 2 : bi - 1;              // (tt + 2) % 3
+    if (tt + kBufs - 1 < ntiles) {
+      const int nb2 = bi == 0 ? kBufs - 1 : bi - 1;      // (tt + kBufs - 1) % kBufs
       okbits = (okbits & ~(((1u << kBlocks) - 1) << (nb2 * kBlocks))) |
-               (issue((tt + 2) * kPrefillKeys, nb2) << (nb2 * kBlocks));
+               (issue((tt + kBufs - 1) * kPrefillKeys, nb2) << (nb2 * kBlocks));
     }
     const uint32_t okt = okbits >> (bi * kBlocks);
     const int base = tt * kPrefillKeys;
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
       if (tt > 0 || nb > 0) emit(base + nb * 32 - 32 + col, sc, gone_prev, scl[prv]);
       gone_prev = ((okt >> (nb >> 1)) & 1u) == 0;
     }
-    bi = bi == 2 ? 0 : bi + 1;
+    bi = bi == kBufs - 1 ? 0 : bi + 1;
   }
   if (ntiles > 0) {
     // the last group (in acc[1], kGroups being even) is reduced alone
