@@ -105,6 +105,23 @@ __device__ __forceinline__ float sum_xor32(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48),
+// through the gfx950 row swaps (VALU ops; no LDS round trip).  The 16-lane swap
+// exchanges odd rows of one operand with even rows of the other, so with both
+// operands = v the pair holds (v[l], v[l ^ 16]) in every lane; the 32-lane swap
+// then does the same across the halves.
+__device__ __forceinline__ float max_over_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum_over_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return sum_xor32(__uint_as_float(a[0]) + __uint_as_float(a[1]));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));

@@ -147,6 +147,11 @@ __device__ __forceinline__ void consume_tile(uint32_t tile, const int *slots, in
   // (scheduling barriers keep the compiler from sinking the reads to their uses).
   constexpr int kBatch = 3;
   constexpr int kSteps = 2 * kKs / kBatch;
+  // Row presence of the tile, read before the logits so that its LDS latency
+  // is covered by them (row lane%32's slot; -1: absent).
+  const int lane = lane_id();
+  const int row_slot = slots[j0 + (lane & (kR - 1))];
+  __builtin_amdgcn_sched_barrier(0);
   f32x4 st[2] = {zero_vec<f32x4>(), zero_vec<f32x4>()};
   u32x4 fr[2][kBatch];
   auto read = [&](int i, int buf) {
@@ -171,8 +176,7 @@ __device__ __forceinline__ void consume_tile(uint32_t tile, const int *slots, in
 
   // ---- online softmax (base 2), one head per lane column.
   // Row validity of the tile as a wave-uniform mask (bit j: row j present).
-  const int lane = lane_id();
-  const uint32_t rowmask = (uint32_t)__ballot(lane < kR && slots[j0 + (lane & (kR - 1))] >= 0);
+  const uint32_t rowmask = (uint32_t)__ballot(lane < kR && row_slot >= 0);
   const uint32_t mine = rowmask >> (4 * g);     // bit v: row 4g+v; bit 16+v: row 16+4g+v
   float mx = neg_inf();
 #pragma unroll
@@ -182,8 +186,7 @@ __device__ __forceinline__ void consume_tile(uint32_t tile, const int *slots, in
       st[rb][v] = ((mine >> (16 * rb + v)) & 1u) ? st[rb][v] * scale2 : neg_inf();
       mx = fmaxf(mx, st[rb][v]);
     }
-  mx = fmaxf(mx, shfl_xor(mx, 16));
-  mx = fmaxf(mx, shfl_xor(mx, 32));
+  mx = max_over_rows(mx);
   if (__any(mx > m_run + kLazy)) {
     // raise the base of every head whose maximum moved (a head with no row yet
     // present keeps -inf and a zero accumulator)
@@ -326,8 +329,7 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
   }
 
   const int h = wv * 16 + col;
-  float l_tot = l_run + shfl_xor(l_run, 16);
-  l_tot += shfl_xor(l_tot, 32);
+  const float l_tot = sum_over_rows(l_run);
   // One split: the output row.  Several: this split's normalised output in
   // bf16 (a weighted mean of value rows, so within their range) and its
   // (max, sum), merged by the combine kernel.
