@@ -271,15 +271,40 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   lds_barrier();
   // Slots of this split's rows (-1: absent, and past the last row), so the
-  // gather depends on LDS only.
-  for (int j = threadIdx.x; j < ntiles * kR + 3 * kR; j += kThreads) {
-    int sl = -1;
-    if (j < rows) {
-      const int s = irow[i0 + j];
-      sl = (s >= 0 && s < n) ? (int)a.sv.slot(b, s) : -1;
-      if (sl >= 0) atomicMax(&fallback, sl);
+  // gather depends on LDS only.  All of a thread's positions are loaded first,
+  // then all of their block-table entries: two dependent latencies in all.
+  constexpr int kFill = (kMaxSplitRows + 4 * kR + kThreads - 1) / kThreads;
+  const int nfill = ntiles * kR + 3 * kR;
+  int pos[kFill];
+#pragma unroll
+  for (int u = 0; u < kFill; ++u) {
+    const int j = threadIdx.x + u * kThreads;
+    pos[u] = j < rows ? irow[i0 + j] : -1;
+  }
+  int sl[kFill];
+  if (a.sv.block_table == nullptr) {
+#pragma unroll
+    for (int u = 0; u < kFill; ++u)
+      sl[u] = (pos[u] >= 0 && pos[u] < n) ? (int)((long long)b * a.sv.max_seq_len + pos[u]) : -1;
+  } else {
+    // every lane loads (an invalid position reads the sequence's first entry),
+    // so the loads are issued back to back
+    const int32_t *bt = a.sv.block_table + (long long)b * a.sv.max_blocks;
+    int blk[kFill];
+#pragma unroll
+    for (int u = 0; u < kFill; ++u) blk[u] = bt[(pos[u] >= 0 && pos[u] < n) ? (pos[u] >> 6) : 0];
+#pragma unroll
+    for (int u = 0; u < kFill; ++u)
+      sl[u] = (pos[u] >= 0 && pos[u] < n && blk[u] >= 0 && blk[u] < a.sv.num_blocks) ? blk[u] * 64 + (pos[u] & 63)
+                                                                                     : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < kFill; ++u) {
+    const int j = threadIdx.x + u * kThreads;
+    if (j < nfill) {
+      slots[j] = sl[u];
+      if (sl[u] >= 0) atomicMax(&fallback, sl[u]);
     }
-    slots[j] = sl;
   }
 
   f32x4 acc[kDb];
@@ -310,11 +335,11 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
     if (ntiles > 1) issue_tile(tile_lds + kTileBytes, kv, slots, kR, fb, wv, lane);
     int cur = 0;
     for (int tt = 0; tt < ntiles; ++tt) {
-      // This wave's loads of tile tt have landed once at most the (four or five)
-      // loads of tile tt+1 are outstanding; the barrier then covers every wave's,
-      // and also orders every wave's reads of tile tt-1 before its buffer is refilled.
+      // This wave's loads of tile tt have landed once at most the loads of tile
+      // tt+1 are outstanding; the barrier then covers every wave's, and also
+      // orders every wave's reads of tile tt-1 before its buffer is refilled.
       if (tt + 1 < ntiles)
-        __builtin_amdgcn_s_waitcnt(wait_vm(4));
+        __builtin_amdgcn_s_waitcnt(wait_vm(kWaveLoads));
       else
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
       lds_barrier();
