@@ -33,6 +33,9 @@ Every step is the plain definition:
 5. eq. U in MQA mode: every head h attends over the selected latent rows c(s)
    with logits sm_scale * q(t,h) . c(s) over all D dims and values c(s)[:Dv];
    softmax; lse = max + ln(sum exp(z - max)).
+6. upstream of the indexer ("runs in FP8" [ZS 3.1]): per-row e4m3fn
+   quantisation with an fp32 scale, and the append of a new token's quantised
+   index key into the (paged) key cache.
 
 Readings where the pages are silent are stated at each function.
 """
@@ -290,3 +293,86 @@ def forward(inp: OracleInputs, rows=None, keep_scores: bool = False) -> dict:
     if keep_scores:
         res["scores"] = scores
     return res
+
+
+# --------------------------------------------------------------------------
+# 6. fp8 quantisation and key-cache append  ("runs in FP8" [ZS 3.1; BT (1)])
+# --------------------------------------------------------------------------
+
+E4M3FN_MAX = 448.0
+# codes 0x00..0x7E are the non-negative finite values, in increasing order
+_E4M3_POSITIVE = E4M3FN_TABLE[:0x7F]
+
+
+def encode_e4m3fn(y) -> np.ndarray:
+    """Nearest e4m3fn code to each finite value (|y| <= 448), ties to the even code.
+
+    Round to nearest, ties to even, is the IEEE default and the reading for a
+    format conversion the pages leave unstated.  The sign bit follows the sign
+    of y (-0.0 encodes as 0x80).  Works in float64, where every float32 input,
+    every e4m3fn value and every midpoint between neighbours is exact.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    if not np.all(np.isfinite(y)) or np.any(np.abs(y) > E4M3FN_MAX):
+        raise ValueError("encode_e4m3fn: inputs must be finite and within +-448 (clamp first)")
+    mag = np.abs(y)
+    hi = np.searchsorted(_E4M3_POSITIVE, mag, side="left")       # first value >= mag
+    hi = np.minimum(hi, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = mag - _E4M3_POSITIVE[lo]
+    d_hi = _E4M3_POSITIVE[hi] - mag
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(mag == _E4M3_POSITIVE[hi], hi, np.where(pick_hi, hi, lo)).astype(np.uint8)
+    return np.where(np.signbit(y), code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def quantize_fp8(x) -> tuple:
+    """Per-row e4m3fn quantisation of x [rows, n] (float32 values).
+
+    Reading (per-token fp32 scales): scale = amax(|x|) / 448, or 1 when the row
+    is all zeros; code = RNE(clamp(x / scale, -448, 448)).  The scale and the
+    quotient are float32 IEEE operations, the precision the quantised codes are
+    decided in.  Returns (codes uint8 [rows, n], scale float32 [rows]).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    _finite(x.astype(np.float64), "value to quantise")
+    amax = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
+    scale = np.where(amax > 0, amax / np.float32(E4M3FN_MAX), np.float32(1.0)).astype(np.float32)
+    y = (x / scale[:, None]).astype(np.float32)
+    y = np.clip(y, np.float32(-E4M3FN_MAX), np.float32(E4M3FN_MAX))
+    return encode_e4m3fn(y), scale
+
+
+def append_index_keys(mode: str, q_pos, block_table, block_size: int, k_new, k_cache, k_scale) -> tuple:
+    """Quantise the new index key of every query token and store it in the cache.
+
+    Token t belongs to sequence sequence_of(t) at position q_pos[t]; its key
+    k_new[t] (float32 values) is quantised per row as in quantize_fp8 and
+    written, with its scale, to that position's cache slot (through the block
+    table when paged).  Tokens whose position is negative or whose block is
+    outside the pool are skipped.  Returns updated copies (codes, scales).
+    """
+    cache = np.array(k_cache, copy=True)
+    scales = np.array(k_scale, copy=True)
+    codes, sc = quantize_fp8(k_new)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    for t in range(q_pos.shape[0]):
+        b = t if mode == "decode" else 0
+        pos = int(q_pos[t])
+        if pos < 0:
+            continue
+        if block_table is None:
+            if pos >= cache.shape[1]:
+                continue
+            cache[b, pos] = codes[t]
+            scales[b, pos] = sc[t]
+        else:
+            j = pos // block_size
+            if j >= block_table.shape[1]:
+                continue
+            blk = int(block_table[b, j])
+            if blk < 0 or blk >= cache.shape[0]:
+                continue
+            cache[blk, pos % block_size] = codes[t]
+            scales[blk, pos % block_size] = sc[t]
+    return cache, scales

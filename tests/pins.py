@@ -382,4 +382,91 @@ def pin_permutation_invariance(o):
     _close(a["lse"], b["lse"], 1e-12, "permuted lse")
 
 
+# ---------------------------------------------------------------- fp8 quantisation and append
+
+def pin_e4m3_encode_roundtrip(o):
+    """Every finite e4m3fn value encodes back to its own code (signed zeros included)."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = o.decode_e4m3fn(codes)
+    fin = np.isfinite(vals)
+    assert np.array_equal(o.encode_e4m3fn(vals[fin]), codes[fin]), "round trip"
+
+
+def pin_e4m3_encode_midpoints(o):
+    """Halfway between neighbouring codes the even code wins; just off the midpoint the nearer one."""
+    for c in range(0, 0x7E):
+        a, b = float(o.decode_e4m3fn(c)), float(o.decode_e4m3fn(c + 1))
+        mid = (a + b) / 2.0
+        even = c if c % 2 == 0 else c + 1
+        for sign, bit in ((1.0, 0), (-1.0, 0x80)):
+            got = o.encode_e4m3fn(np.array([sign * mid]))[0]
+            assert got == (even | bit), f"midpoint of codes {c:#x},{c + 1:#x}"
+            lo = o.encode_e4m3fn(np.array([sign * np.nextafter(mid, a)]))[0]
+            hi = o.encode_e4m3fn(np.array([sign * np.nextafter(mid, b)]))[0]
+            assert lo == (c | bit) and hi == ((c + 1) | bit), f"near the midpoint of {c:#x}"
+
+
+def pin_e4m3_encode_torch(o):
+    """Random float32 values in [-448, 448] (all binades) against torch's float8_e4m3fn cast."""
+    rng = np.random.default_rng(17)
+    mag = np.exp2(rng.uniform(-12.0, np.log2(448.0), 200000)).astype(np.float32)
+    y = np.where(rng.random(mag.shape) < 0.5, -mag, mag).astype(np.float32)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(o.encode_e4m3fn(y), ref), "encoder vs torch cast"
+
+
+def pin_quantize_golden(o):
+    """Hand-derived rows (tests/golden/quantize_hand.json)."""
+    g = _golden("quantize_hand.json")
+    for case in g["cases"]:
+        codes, scale = o.quantize_fp8(np.array([case["x"]], dtype=np.float32))
+        assert codes[0].tolist() == case["codes"], case["name"]
+        assert float(scale[0]) == case["scale"], case["name"]
+
+
+def pin_quantize_bounds(o):
+    """Per row: the largest magnitude maps to +-448, and dequantisation errs by at most half
+    the spacing of e4m3fn values around the code (times the scale)."""
+    rng = np.random.default_rng(23)
+    x = (rng.standard_normal((64, 128)) * np.exp2(rng.uniform(-20, 20, (64, 1)))).astype(np.float32)
+    codes, scale = o.quantize_fp8(x)
+    vals = o.decode_e4m3fn(codes)
+    assert np.all(np.max(np.abs(vals), axis=1) == 448.0)
+    mags = o.decode_e4m3fn(np.arange(0x7F, dtype=np.uint8))
+    y = x.astype(np.float64) / scale.astype(np.float64)[:, None]
+    # spacing of e4m3fn values on the side of the code where y lies
+    idx = np.searchsorted(mags, np.abs(vals))
+    up = np.abs(y) > np.abs(vals)
+    spacing = np.where(up, mags[np.minimum(idx + 1, 0x7E)] - mags[idx], mags[idx] - mags[np.maximum(idx - 1, 0)])
+    # the quotient itself is a float32: allow its own rounding on top of the half spacing
+    assert np.all(np.abs(vals - y) <= spacing / 2 + np.abs(y) * 2.0 ** -23), "rounding error bound"
+
+
+def pin_append_index_keys(o):
+    """Appending into a paged cache writes exactly the slots the block table names."""
+    bs, d = 4, 8
+    table = np.array([[2, 0, -1], [1, 3, 5]], dtype=np.int64)     # sequence 0: blocks 2, 0; sequence 1: 1, 3, 5
+    cache = np.full((6, bs, d), 0x11, dtype=np.uint8)
+    scale = np.full((6, bs), 7.0, dtype=np.float32)
+    rng = np.random.default_rng(5)
+    k_new = rng.standard_normal((2, d)).astype(np.float32)
+    # decode: token 0 -> sequence 0 at position 5 (block 0, offset 1); token 1 -> sequence 1 at position 10
+    # (table entry 2 = block 5, outside the 6-block pool? no: block 5 exists, offset 2)
+    c2, s2 = o.append_index_keys("decode", [5, 10], table, bs, k_new, cache, scale)
+    codes, sc = o.quantize_fp8(k_new)
+    changed = np.argwhere(np.any(c2 != cache, axis=2) | (s2 != scale))
+    assert sorted(map(tuple, changed.tolist())) == [(0, 1), (5, 2)], changed
+    assert np.array_equal(c2[0, 1], codes[0]) and s2[0, 1] == sc[0]
+    assert np.array_equal(c2[5, 2], codes[1]) and s2[5, 2] == sc[1]
+    # a negative position and an absent block are skipped
+    c3, s3 = o.append_index_keys("decode", [-1, 9], np.array([[2, 0, -1], [1, 3, -1]]), bs, k_new, cache, scale)
+    assert np.array_equal(c3, cache) and np.array_equal(s3, scale)
+    # contiguous cache [B, Lmax, d]: prefill tokens all belong to sequence 0
+    cc = np.zeros((1, 6, d), dtype=np.uint8)
+    cs = np.ones((1, 6), dtype=np.float32)
+    c4, s4 = o.append_index_keys("prefill", [0, 3], None, bs, k_new, cc, cs)
+    assert np.array_equal(c4[0, 0], codes[0]) and np.array_equal(c4[0, 3], codes[1])
+    assert np.all(c4[0, [1, 2, 4, 5]] == 0) and s4[0, 3] == sc[1]
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

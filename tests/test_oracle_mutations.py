@@ -99,6 +99,33 @@ def _bf16_truncated_low(bits):
     return b.view(np.float32).astype(np.float64)
 
 
+def _encode_ties_away(y):
+    y = np.asarray(y, dtype=np.float64)
+    pos = od.E4M3FN_TABLE[:0x7F]
+    mag = np.abs(y)
+    hi = np.minimum(np.searchsorted(pos, mag, side="left"), 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    code = np.where((pos[hi] - mag) <= (mag - pos[lo]), hi, lo).astype(np.uint8)
+    return np.where(np.signbit(y), code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def _encode_truncate(y):
+    y = np.asarray(y, dtype=np.float64)
+    pos = od.E4M3FN_TABLE[:0x7F]
+    mag = np.abs(y)
+    code = (np.searchsorted(pos, mag, side="right") - 1).astype(np.uint8)
+    return np.where(np.signbit(y), code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def _append_block_offset_dropped(mode, q_pos, block_table, block_size, k_new, k_cache, k_scale):
+    # stores every paged token at offset 0 of its block
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    if block_table is None:
+        return od.__dict__["_orig_append"](mode, q_pos, block_table, block_size, k_new, k_cache, k_scale)
+    return od.__dict__["_orig_append"](mode, q_pos - q_pos % block_size, block_table, block_size, k_new, k_cache,
+                                       k_scale)
+
+
 MUTATIONS = {
     "indexer_no_relu": ("index_scores", _no_relu),
     "indexer_relu_after_weight": ("index_scores", _relu_after_weight),
@@ -116,6 +143,10 @@ MUTATIONS = {
     "fp8_key_scale_dropped": ("query_index_operands", _fp8_no_kscale),
     "paged_ignores_block_table": ("gather_rows", _paged_ignores_table),
     "bf16_wrong_shift": ("decode_bf16", _bf16_truncated_low),
+    "fp8_ties_away_from_zero": ("encode_e4m3fn", _encode_ties_away),
+    "fp8_round_toward_zero": ("encode_e4m3fn", _encode_truncate),
+    "fp8_scale_uses_fnuz_max": ("E4M3FN_MAX", 240.0),
+    "append_block_offset_dropped": ("append_index_keys", _append_block_offset_dropped),
 }
 
 
@@ -124,6 +155,7 @@ def test_mutation_is_caught(name, monkeypatch):
     attr, repl = MUTATIONS[name]
     monkeypatch.setattr(od, "_orig_sparse_mla", od.sparse_mla, raising=False)
     monkeypatch.setattr(od, "_orig_query_index_operands", od.query_index_operands, raising=False)
+    monkeypatch.setattr(od, "_orig_append", od.append_index_keys, raising=False)
     monkeypatch.setattr(od, attr, repl)
     caught = []
     for pin in pins.ALL_PINS:
