@@ -200,6 +200,35 @@ int dsa_sparse_mla(const dsa_seqs *seqs, const dsa_dims *dims, float sm_scale, c
 int dsa_forward(const dsa_seqs *seqs, const dsa_dims *dims, const dsa_forward_args *args,
                 void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Upstream of step 1: per-row fp8 quantisation for an indexer that "runs in
+ * FP8" [ZS 3.1; BT (1)].  The pages fix neither scale nor rounding; the
+ * reading taken: for each row r of src [rows, len] (DSA_BF16 or DSA_F32),
+ *   scale[r]   = max_i |src[r,i]| / 448   (1 when the row is all zeros),
+ *   dst[r, i]  = e4m3fn code of clamp(src[r,i] / scale[r], -448, 448),
+ *                rounded to nearest, ties to even,
+ * both fp32 IEEE operations.  scale[r] is stored scale_repeat times, at
+ * scale[r * scale_repeat + j], j < scale_repeat: quantising indexer queries
+ * with one scale per token gives len = H_I * d_I, scale_repeat = H_I (the
+ * q_scale [T, H_I] layout); keys take len = d_I, scale_repeat = 1.
+ * dst [rows, len] bytes, scale [rows * scale_repeat] fp32, both owned by the
+ * caller.  src must be finite.  Supported: len % 4 == 0, len <= 65536,
+ * scale_repeat <= 1024.  No workspace. */
+int dsa_quantize_fp8(int64_t rows, int32_t len, int32_t src_dtype, const void *src, void *dst,
+                     float *scale, int32_t scale_repeat, hipStream_t stream);
+
+/* Append the new index key of every query token to an e4m3fn key cache
+ * [ZS 3.1 "runs in FP8"; the decode step upstream of the indexer].  Token t
+ * belongs to sequence t (decode) or 0 (prefill) at position q_pos[t]; its key
+ * k_new[t, 0..index_dim) (DSA_BF16 or DSA_F32, layout [T, index_dim]) is
+ * quantised as by dsa_quantize_fp8 (one scale per key) and written with its
+ * scale to that position's slot of k_cache / k_scale (the layouts of
+ * dsa_index_scores; through the block table when paged).  A token whose
+ * position is negative, past the contiguous slots or the table's columns, or
+ * in a block outside the pool is skipped.  Tokens must name distinct slots.
+ * Supported: index_dim % 4 == 0, index_dim <= 2048.  No workspace. */
+int dsa_append_index_keys(const dsa_seqs *seqs, int32_t index_dim, int32_t src_dtype, const void *k_new,
+                          void *k_cache, float *k_scale, hipStream_t stream);
+
 /* Static string naming a dsa_status value. */
 const char *dsa_status_string(int status);
 

@@ -23,7 +23,7 @@ OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_MLA, OP_FORWARD = 0, 1, 2, 3
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
 EXPORTS = ("dsa_workspace_size", "dsa_index_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward",
-           "dsa_status_string")
+           "dsa_quantize_fp8", "dsa_append_index_keys", "dsa_status_string")
 
 
 class DsaSeqs(ctypes.Structure):
@@ -70,6 +70,10 @@ def _load() -> ctypes.CDLL:
     lib.dsa_sparse_mla.restype = ctypes.c_int
     lib.dsa_forward.argtypes = [sp, dp, ctypes.POINTER(DsaForwardArgs), P, SZ, P]
     lib.dsa_forward.restype = ctypes.c_int
+    lib.dsa_quantize_fp8.argtypes = [I64, I32, I32, P, P, P, I32, P]
+    lib.dsa_quantize_fp8.restype = ctypes.c_int
+    lib.dsa_append_index_keys.argtypes = [sp, I32, I32, P, P, P, P]
+    lib.dsa_append_index_keys.restype = ctypes.c_int
     lib.dsa_status_string.argtypes = [ctypes.c_int]
     lib.dsa_status_string.restype = ctypes.c_char_p
     return lib
@@ -240,3 +244,28 @@ def forward_inputs(inp, ws=None, stage_events=None, **kw):
     pb = problem_from_inputs(inp)
     return forward(pb, inp.q_idx, inp.q_scale, inp.w, inp.k_cache, inp.k_scale, inp.q, inp.kv_cache,
                    inp.sm_scale, ws=ws, stage_events=stage_events, **kw)
+
+
+def quantize_fp8(src: torch.Tensor, scale_repeat: int = 1, dst=None, scale=None, stream=None):
+    """Per-row e4m3fn quantisation of src [..., len] (bf16 / fp32): returns (codes, scales).
+
+    codes has src's shape (torch.float8_e4m3fn); scales is [rows, scale_repeat] fp32."""
+    src = src.contiguous()
+    n = src.shape[-1]
+    rows = src.numel() // n if n else 0
+    if dst is None:
+        dst = torch.empty(src.shape, dtype=torch.float8_e4m3fn, device=src.device)
+    if scale is None:
+        scale = torch.empty((rows, scale_repeat), dtype=torch.float32, device=src.device)
+    st = LIB.dsa_quantize_fp8(rows, n, dtype_code(src), _ptr(src), _ptr(dst), _ptr(scale), scale_repeat,
+                              _stream(stream))
+    _check(st, "dsa_quantize_fp8")
+    return dst, scale
+
+
+def append_index_keys(pb: Problem, k_new: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tensor, stream=None):
+    """Quantise each query token's new index key and store it in the e4m3fn key cache (in place)."""
+    k_new = k_new.contiguous()
+    st = LIB.dsa_append_index_keys(ctypes.byref(pb.seqs), k_new.shape[-1], dtype_code(k_new), _ptr(k_new),
+                                   _ptr(k_cache), _ptr(k_scale), _stream(stream))
+    _check(st, "dsa_append_index_keys")

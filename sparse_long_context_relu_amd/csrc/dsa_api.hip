@@ -11,6 +11,10 @@ namespace {
 
 constexpr int kMaxCtx = 262144;
 constexpr long long kScoreBudget = 256ll << 20;  // bytes of score rows per prefill chunk
+constexpr int kQuantMaxLen = 65536;              // values per quantised row
+constexpr int kQuantMaxRepeat = 1024;            // copies of each row's scale
+constexpr long long kQuantMaxRows = 2147483647;  // one workgroup (or a quarter) per row
+constexpr int kAppendMaxDim = 2048;              // index key width for the append
 
 long long align256(long long x) { return (x + 255) & ~255ll; }
 
@@ -315,6 +319,43 @@ DSA_EXPORT int dsa_forward(const dsa_seqs *seqs, const dsa_dims *dims, const dsa
     if (timed && hipEventRecord(ev[3], stream) != hipSuccess) return DSA_ERR_HIP;
   }
   return DSA_OK;
+}
+
+DSA_EXPORT int dsa_quantize_fp8(int64_t rows, int32_t len, int32_t src_dtype, const void *src, void *dst,
+                                float *scale, int32_t scale_repeat, hipStream_t stream) {
+  if (rows < 0 || len < 1 || scale_repeat < 1) return DSA_ERR_INVALID_ARG;
+  if (src_dtype != DSA_BF16 && src_dtype != DSA_F32) return DSA_ERR_INVALID_ARG;
+  if (len % 4 != 0 || len > kQuantMaxLen || scale_repeat > kQuantMaxRepeat) return DSA_ERR_UNSUPPORTED;
+  if (rows == 0) return DSA_OK;
+  if (rows > kQuantMaxRows) return DSA_ERR_UNSUPPORTED;
+  if (src == nullptr || dst == nullptr || scale == nullptr) return DSA_ERR_INVALID_ARG;
+  QuantArgs a;
+  a.rows = rows;
+  a.len = len;
+  a.src_dtype = src_dtype;
+  a.scale_repeat = scale_repeat;
+  a.src = src;
+  a.dst = reinterpret_cast<uint8_t *>(dst);
+  a.scale = scale;
+  return hip_status(launch_fp8_quantize(a, stream));
+}
+
+DSA_EXPORT int dsa_append_index_keys(const dsa_seqs *seqs, int32_t index_dim, int32_t src_dtype,
+                                     const void *k_new, void *k_cache, float *k_scale, hipStream_t stream) {
+  if (int e = check_seqs(seqs)) return e;
+  if (index_dim < 1) return DSA_ERR_INVALID_ARG;
+  if (src_dtype != DSA_BF16 && src_dtype != DSA_F32) return DSA_ERR_INVALID_ARG;
+  if (index_dim % 4 != 0 || index_dim > kAppendMaxDim) return DSA_ERR_UNSUPPORTED;
+  if (seqs->num_q == 0) return DSA_OK;
+  if (k_new == nullptr || k_cache == nullptr || k_scale == nullptr) return DSA_ERR_INVALID_ARG;
+  AppendArgs a;
+  a.sv = view(seqs);
+  a.len = index_dim;
+  a.src_dtype = src_dtype;
+  a.src = k_new;
+  a.cache = reinterpret_cast<uint8_t *>(k_cache);
+  a.scale = k_scale;
+  return hip_status(launch_fp8_append(a, stream));
 }
 
 DSA_EXPORT const char *dsa_status_string(int status) {

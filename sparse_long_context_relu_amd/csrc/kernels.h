@@ -77,6 +77,25 @@ constexpr int kTopkHdrWords = 2 * kTopkBins + 64;
 constexpr int kTopkCounts = kTopkHdrWords;            // [2][kTopkMaxSlices]: selected, candidates
 constexpr int kTopkRegions = kTopkCounts + 2 * kTopkMaxSlices;
 
+// Per-row e4m3fn quantisation: src [rows, len] (bf16 / fp32) -> dst [rows, len]
+// codes and scale[rows * scale_repeat] (each row's scale repeated).
+struct QuantArgs {
+  long long rows;
+  int len, src_dtype, scale_repeat;
+  const void *src;
+  uint8_t *dst;
+  float *scale;
+};
+
+// Append of one new index key per query token into the e4m3fn key cache.
+struct AppendArgs {
+  SeqView sv;
+  int len, src_dtype;
+  const void *src;   // [T, len]
+  uint8_t *cache;    // key cache rows of len codes
+  float *scale;      // key scales, one per cache row
+};
+
 struct TopkLayout {
   int slices, slice_len, sel_seg;
   long long row_words;
@@ -92,5 +111,7 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t s);         // zero + hist
 hipError_t launch_topk_zero(const TopkArgs &a, hipStream_t s);    // zero the per-row headers
 hipError_t launch_topk_select(const TopkArgs &a, hipStream_t s);  // collect + select (hist1 ready)
 hipError_t launch_sparse_mla(const MlaArgs &a, hipStream_t s);
+hipError_t launch_fp8_quantize(const QuantArgs &a, hipStream_t s);
+hipError_t launch_fp8_append(const AppendArgs &a, hipStream_t s);
 
 }  // namespace dsa

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     text = open(B.HEADER_PATH).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_function():
@@ -163,6 +163,27 @@ def test_forward_validation_and_workspace():
     pf = B.make_problem(mode="prefill", q_pos=qp, max_ctx=65536, num_seqs=1, max_seq_len=65536,
                         index_dtype=B.FP8_E4M3FN)
     assert B.workspace_size(B.OP_FORWARD, pf) < (1 << 30)
+
+
+def test_quantize_and_append_validation():
+    """Host-side checks of the fp8 quantisation and key-append entry points (no launch)."""
+    L, P = B.LIB, ctypes.c_void_p
+    fake = P(0x1000)
+    assert L.dsa_quantize_fp8(-1, 128, B.BF16, fake, fake, fake, 1, None) == B.ERR_INVALID_ARG
+    assert L.dsa_quantize_fp8(4, 0, B.BF16, fake, fake, fake, 1, None) == B.ERR_INVALID_ARG
+    assert L.dsa_quantize_fp8(4, 128, B.FP8_E4M3FN, fake, fake, fake, 1, None) == B.ERR_INVALID_ARG
+    assert L.dsa_quantize_fp8(4, 130, B.BF16, fake, fake, fake, 1, None) == B.ERR_UNSUPPORTED
+    assert L.dsa_quantize_fp8(4, 128, B.BF16, fake, fake, fake, 2000, None) == B.ERR_UNSUPPORTED
+    assert L.dsa_quantize_fp8(4, 128, B.BF16, None, fake, fake, 1, None) == B.ERR_INVALID_ARG
+    assert L.dsa_quantize_fp8(0, 128, B.BF16, None, None, None, 1, None) == B.OK
+    q_pos = torch.zeros(2, dtype=torch.int32)
+    pb = B.make_problem(mode="decode", q_pos=q_pos, max_ctx=64, num_seqs=2, max_seq_len=64,
+                        index_dtype=B.FP8_E4M3FN, topk=64)
+    sp = ctypes.byref(pb.seqs)
+    assert L.dsa_append_index_keys(sp, 128, B.BF16, fake, fake, None, None) == B.ERR_INVALID_ARG
+    assert L.dsa_append_index_keys(sp, 126, B.BF16, fake, fake, fake, None) == B.ERR_UNSUPPORTED
+    assert L.dsa_append_index_keys(sp, 128, B.FP8_E4M3FN, fake, fake, fake, None) == B.ERR_INVALID_ARG
+    assert L.dsa_append_index_keys(None, 128, B.BF16, fake, fake, fake, None) == B.ERR_INVALID_ARG
 
 
 def test_status_strings():
