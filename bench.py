@@ -57,33 +57,32 @@ def algorithmic_flops(inp):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ("sparse_long_context_relu_amd/csrc/indexer_decode.hip",
-                  "sparse_long_context_relu_amd/csrc/indexer_common.h",
-                  "sparse_long_context_relu_amd/csrc/common.h", "sparse_long_context_relu_amd/csrc/kernels.h")
+KERNEL_ISA_FILE = os.path.join(ROOT, "sparse_long_context_relu_amd", "kernel_isa.json")
 
 
-def kernel_source_hash():
-    import hashlib
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
+def kernel_fingerprint(kernel):
+    """SHA-256 of the kernel's gfx950 assembly in the library as built (written by the build)."""
+    try:
+        with open(KERNEL_ISA_FILE) as f:
+            return json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
 
 
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` on `workload` from the committed counter
     runs (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a
     plain copy of known size), or None when there are none or the kernel's
-    sources changed since they were taken."""
+    machine code differs from the one the counters were taken on."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
+    fp = kernel_fingerprint(kernel + "<bf16>")
     for e in rec.get("entries", []):
         if e.get("kernel") == kernel and e.get("workload") == workload:
-            if e.get("source_sha256") != kernel_source_hash():
+            if fp is None or e.get("isa_sha256") != fp:
                 return None
             return int(e["traffic_bytes"])
     return None
@@ -110,16 +109,22 @@ def settle(torch, call, ms):
         torch.cuda.synchronize()
 
 
-def time_forward(B, torch, inp, steps, warmup, settle_ms=0):
+def time_forward(B, torch, inp, steps, warmup, settle_ms=0, prep=None):
     pb = B.problem_from_inputs(inp)
     ws = torch.empty(B.workspace_size(B.OP_FORWARD, pb), dtype=torch.uint8, device="cuda")
     T, H, Dv, k = inp.num_q, inp.wl.heads, inp.wl.v_dim, inp.topk
     out = torch.empty((T, H, Dv), dtype=inp.q.dtype, device="cuda")
     lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
     idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
-    call = lambda ev=None: B.forward(pb, inp.q_idx, inp.q_scale, inp.w, inp.k_cache, inp.k_scale, inp.q,
-                                     inp.kv_cache, inp.sm_scale, out=out, lse=lse, topk_idx=idx, ws=ws,
-                                     stage_events=ev)
+    fwd = lambda ev=None: B.forward(pb, inp.q_idx, inp.q_scale, inp.w, inp.k_cache, inp.k_scale, inp.q,
+                                    inp.kv_cache, inp.sm_scale, out=out, lse=lse, topk_idx=idx, ws=ws,
+                                    stage_events=ev)
+
+    def call(ev=None):
+        if prep is not None:       # work upstream of the forward that belongs to the step
+            prep()
+        fwd(ev)
+
     settle(torch, call, settle_ms)
     for _ in range(warmup):
         call()
@@ -190,6 +195,8 @@ def main():
                     help="untimed run-in before each timed region, so the shader clock has settled")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurement")
+    ap.add_argument("--no-fp8-decode", action="store_true", help="skip the secondary fp8-indexer decode measurement")
+    ap.add_argument("--fp8-workload", default="decode_128k_paged_fp8")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -255,10 +262,46 @@ def main():
         "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
     }
 
+    if not args.no_fp8_decode and wl.mode == "decode":
+        # The decode step with the indexer in e4m3fn: the new tokens' index queries and
+        # keys arrive in bf16, are quantised (dsa_quantize_fp8) and the keys appended
+        # to the paged fp8 cache (dsa_append_index_keys), then dsa_forward runs.
+        fname = args.fp8_workload
+        log(f"secondary: {fname}")
+        del inp
+        torch.cuda.empty_cache()
+        fin = generate(WORKLOADS[fname], "cuda")
+        T, HI, DI = fin.num_q, fin.wl.index_heads, fin.wl.index_dim
+        g = torch.Generator(device="cuda").manual_seed(1234)
+        q_new = torch.randn((T, HI * DI), device="cuda", generator=g).to(torch.bfloat16)
+        k_new = torch.randn((T, DI), device="cuda", generator=g).to(torch.bfloat16)
+        fpb = B.problem_from_inputs(fin)
+        q8 = fin.q_idx.view(T, HI * DI)
+
+        def prep():
+            B.quantize_fp8(q_new, scale_repeat=HI, dst=q8, scale=fin.q_scale)
+            B.append_index_keys(fpb, k_new, fin.k_cache, fin.k_scale)
+
+        fms, fst = time_forward(B, torch, fin, args.steps, args.warmup, args.settle_ms, prep=prep)
+        f_idx, f_step = algorithmic_bytes(fin)
+        f_quant = T * (HI * DI * 3 + HI * 4) + T * (DI * 3 + 4)      # bf16 in, e4m3 + scales out
+        result["fp8_decode"] = {
+            "workload": fname, "step": "quantise q_I + append k_I + dsa_forward",
+            "tokens_per_s": round(T / (fms * 1e-3), 1), "ms_per_step": round(fms, 4),
+            "stages_ms": {"indexer": round(fst[0], 4), "topk": round(fst[1], 4), "attention": round(fst[2], 4)},
+            "indexer_bytes_per_launch": f_idx,
+            "indexer_hbm_frac": round(f_idx / (fst[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "step_algorithmic_bytes": f_step + f_quant,
+            "step_hbm_frac": round((f_step + f_quant) / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"fp8 decode {fms:.3f} ms/step, indexer {fst[0]:.4f} ms")
+        del fin, q_new, k_new, q8
+        torch.cuda.empty_cache()
+        inp = generate(wl, "cuda") if (args.no_prefill and not args.no_cpu_baseline) else None
+
     if not args.no_prefill:
         pname = "prefill_16k_bf16"
         log(f"secondary: {pname}")
-        del inp
+        inp = None
         torch.cuda.empty_cache()
         pin = generate(WORKLOADS[pname], "cuda")
         pms, pst = time_forward(B, torch, pin, 3, 1, args.settle_ms)

@@ -4,6 +4,8 @@ Run ``python -m sparse_long_context_relu_amd.build`` (or call ``build()``).
 """
 from __future__ import annotations
 
+import hashlib
+import json
 import os
 import shutil
 import subprocess
@@ -17,6 +19,12 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libdsa.so")
 SOURCES = ["dsa_api.hip", "indexer.hip", "indexer_decode.hip", "topk.hip", "sparse_mla.hip", "quantize.hip"]
 HEADERS = ["common.h", "kernels.h", "indexer_common.h"]
+
+# Kernels whose machine code is fingerprinted at build time: a record measured
+# on one build (profiles/traffic.json) stays valid while the fingerprint matches.
+KERNEL_HASH_PATH = os.path.join(PKG, "kernel_isa.json")
+# record name -> (source, symbol fragment of the instance)
+HASHED_KERNELS = {"indexer_decode_kernel<bf16>": ("indexer_decode.hip", "indexer_decode_kernelILi1E")}
 
 ARCH = "gfx950"
 CXXFLAGS = [
@@ -60,7 +68,39 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}")
     os.replace(tmp, LIB_PATH)
+    write_kernel_hashes(cc)
     return LIB_PATH
+
+
+def kernel_isa_text(asm: str, kernel: str) -> str:
+    """The instructions of every function in `asm` whose symbol names `kernel`
+    (comments and the compilation-unit id dropped)."""
+    keep, inside = [], False
+    for line in asm.splitlines():
+        if line.startswith("_Z") and kernel in line and line.split(";")[0].rstrip().endswith(":"):
+            inside = True
+        elif inside and line.lstrip().startswith(".Lfunc_end"):
+            inside = False
+        if inside and not line.lstrip().startswith(";"):
+            keep.append(line.split(";")[0].rstrip())
+    return "\n".join(keep)
+
+
+def write_kernel_hashes(cc: str) -> dict:
+    """SHA-256 of the gfx950 assembly of each fingerprinted kernel, to kernel_isa.json."""
+    out = {}
+    for name, (src, kernel) in HASHED_KERNELS.items():
+        asm_path = os.path.join(BUILD_DIR, src + ".s")
+        subprocess.run([cc, *CXXFLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm_path],
+                       check=True, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+        with open(asm_path) as f:
+            text = kernel_isa_text(f.read(), kernel)
+        if not text:
+            raise RuntimeError(f"{kernel} not found in the assembly of {src}")
+        out[name] = hashlib.sha256(text.encode()).hexdigest()
+    with open(KERNEL_HASH_PATH, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
 
 
 def _wait(item, verbose):

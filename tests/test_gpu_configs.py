@@ -71,6 +71,7 @@ CASES = [
     ("prefill_16k_bf16", 24),
     ("decode_128k_paged_bf16", 6),
     ("decode_128k_exact_paged_bf16", 3),
+    ("decode_128k_paged_fp8", 4),
     ("prefill_64k_fp8", 10),
 ]
 

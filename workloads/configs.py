@@ -73,6 +73,10 @@ WORKLOADS = {
     "decode_128k_exact_paged_bf16": Workload(
         name="decode_128k_exact_paged_bf16", seed=4, mode="decode", num_seqs=32, length=131072,
         paged=True),
+    # The long-context decode with the indexer in e4m3fn (keys and queries with per-token fp32 scales).
+    "decode_128k_paged_fp8": Workload(
+        name="decode_128k_paged_fp8", seed=4, mode="decode", num_seqs=32, length=131072,
+        length_range=(32768, 131072), paged=True, index_dtype="fp8"),
     # Causal prefill of 65536 tokens, indexer in e4m3fn with per-token fp32 scales.
     "prefill_64k_fp8": Workload(
         name="prefill_64k_fp8", seed=5, mode="prefill", num_seqs=1, length=65536,
