@@ -11,6 +11,7 @@ namespace {
 
 constexpr int kMaxCtx = 262144;
 constexpr long long kScoreBudget = 256ll << 20;  // bytes of score rows per prefill chunk
+constexpr long long kMinChunkRows = 4096;        // query rows per prefill chunk, at least
 constexpr int kQuantMaxLen = 65536;              // values per quantised row
 constexpr int kQuantMaxRepeat = 1024;            // copies of each row's scale
 constexpr long long kQuantMaxRows = 2147483647;  // one workgroup (or a quarter) per row
@@ -106,11 +107,15 @@ long long topk_ws_bytes(int rows, int max_ctx) {
   return (long long)rows * topk_layout(rows, max_ctx).row_words * (long long)sizeof(uint32_t);
 }
 
+// Query rows per prefill chunk: as many as kScoreBudget bytes of score rows
+// hold, but never fewer than kMinChunkRows (the prefill indexer runs 8 rows per
+// workgroup, so a chunk must span the 256 CUs twice over; at long contexts that
+// takes more score memory than the budget: 1 GiB of rows at 64K).
 int forward_chunk_rows(const dsa_seqs *s) {
   if (s->mode == DSA_DECODE || s->num_q == 0) return s->num_q;
   long long rows = kScoreBudget / (score_ld(s) * 4);
   rows = rows / 8 * 8;
-  if (rows < 8) rows = 8;
+  if (rows < kMinChunkRows) rows = kMinChunkRows;
   return rows < s->num_q ? (int)rows : s->num_q;
 }
 

@@ -162,7 +162,8 @@ def test_forward_validation_and_workspace():
     qp = torch.arange(65536, dtype=torch.int32)
     pf = B.make_problem(mode="prefill", q_pos=qp, max_ctx=65536, num_seqs=1, max_seq_len=65536,
                         index_dtype=B.FP8_E4M3FN)
-    assert B.workspace_size(B.OP_FORWARD, pf) < (1 << 30)
+    ws64k = B.workspace_size(B.OP_FORWARD, pf)
+    assert (1 << 30) <= ws64k < (3 << 29)          # 4096-row chunks of 256 KiB score rows, not 16 GiB
 
 
 def test_quantize_and_append_validation():
