@@ -197,6 +197,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurement")
     ap.add_argument("--no-fp8-decode", action="store_true", help="skip the secondary fp8-indexer decode measurement")
     ap.add_argument("--fp8-workload", default="decode_128k_paged_fp8")
+    ap.add_argument("--no-exact-decode", action="store_true",
+                    help="skip the secondary decode line with every context exactly 128K tokens")
+    ap.add_argument("--exact-workload", default="decode_128k_exact_paged_bf16")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -262,41 +265,49 @@ def main():
         "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
     }
 
-    if not args.no_fp8_decode and wl.mode == "decode":
-        # The decode step with the indexer in e4m3fn: the new tokens' index queries and
-        # keys arrive in bf16, are quantised (dsa_quantize_fp8) and the keys appended
-        # to the paged fp8 cache (dsa_append_index_keys), then dsa_forward runs.
-        fname = args.fp8_workload
-        log(f"secondary: {fname}")
-        del inp
-        torch.cuda.empty_cache()
-        fin = generate(WORKLOADS[fname], "cuda")
-        T, HI, DI = fin.num_q, fin.wl.index_heads, fin.wl.index_dim
-        g = torch.Generator(device="cuda").manual_seed(1234)
-        q_new = torch.randn((T, HI * DI), device="cuda", generator=g).to(torch.bfloat16)
-        k_new = torch.randn((T, DI), device="cuda", generator=g).to(torch.bfloat16)
-        fpb = B.problem_from_inputs(fin)
-        q8 = fin.q_idx.view(T, HI * DI)
+    def decode_line(name, fp8_prep):
+        """Another decode workload through the same step (for e4m3fn indexing: the new
+        tokens' index queries and keys arrive in bf16 and are quantised with
+        dsa_quantize_fp8 and appended with dsa_append_index_keys inside the step)."""
+        log(f"secondary: {name}")
+        din = generate(WORKLOADS[name], "cuda")
+        T, HI, DI = din.num_q, din.wl.index_heads, din.wl.index_dim
+        prep, extra = None, 0
+        if fp8_prep:
+            g = torch.Generator(device="cuda").manual_seed(1234)
+            q_new = torch.randn((T, HI * DI), device="cuda", generator=g).to(torch.bfloat16)
+            k_new = torch.randn((T, DI), device="cuda", generator=g).to(torch.bfloat16)
+            dpb = B.problem_from_inputs(din)
+            q8 = din.q_idx.view(T, HI * DI)
 
-        def prep():
-            B.quantize_fp8(q_new, scale_repeat=HI, dst=q8, scale=fin.q_scale)
-            B.append_index_keys(fpb, k_new, fin.k_cache, fin.k_scale)
+            def prep():
+                B.quantize_fp8(q_new, scale_repeat=HI, dst=q8, scale=din.q_scale)
+                B.append_index_keys(dpb, k_new, din.k_cache, din.k_scale)
 
-        fms, fst = time_forward(B, torch, fin, args.steps, args.warmup, args.settle_ms, prep=prep)
-        f_idx, f_step = algorithmic_bytes(fin)
-        f_quant = T * (HI * DI * 3 + HI * 4) + T * (DI * 3 + 4)      # bf16 in, e4m3 + scales out
-        result["fp8_decode"] = {
-            "workload": fname, "step": "quantise q_I + append k_I + dsa_forward",
-            "tokens_per_s": round(T / (fms * 1e-3), 1), "ms_per_step": round(fms, 4),
-            "stages_ms": {"indexer": round(fst[0], 4), "topk": round(fst[1], 4), "attention": round(fst[2], 4)},
-            "indexer_bytes_per_launch": f_idx,
-            "indexer_hbm_frac": round(f_idx / (fst[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "step_algorithmic_bytes": f_step + f_quant,
-            "step_hbm_frac": round((f_step + f_quant) / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-        log(f"fp8 decode {fms:.3f} ms/step, indexer {fst[0]:.4f} ms")
-        del fin, q_new, k_new, q8
+            extra = T * (HI * DI * 3 + HI * 4) + T * (DI * 3 + 4)      # bf16 in, e4m3 + scales out
+        dms, dst = time_forward(B, torch, din, args.steps, args.warmup, args.settle_ms, prep=prep)
+        d_idx, d_step = algorithmic_bytes(din)
+        line = {"workload": name, "step": "quantise q_I + append k_I + dsa_forward" if fp8_prep else "dsa_forward",
+                "context_total": int((din.q_pos.long() + 1).sum()),
+                "tokens_per_s": round(T / (dms * 1e-3), 1), "ms_per_step": round(dms, 4),
+                "stages_ms": {"indexer": round(dst[0], 4), "topk": round(dst[1], 4), "attention": round(dst[2], 4)},
+                "indexer_bytes_per_launch": d_idx,
+                "indexer_hbm_frac": round(d_idx / (dst[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "step_algorithmic_bytes": d_step + extra,
+                "step_hbm_frac": round((d_step + extra) / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"{name}: {dms:.3f} ms/step, indexer {dst[0]:.4f} ms")
+        del din
         torch.cuda.empty_cache()
-        inp = generate(wl, "cuda") if (args.no_prefill and not args.no_cpu_baseline) else None
+        return line
+
+    if wl.mode == "decode" and not (args.no_exact_decode and args.no_fp8_decode):
+        inp = None
+        torch.cuda.empty_cache()
+        if not args.no_exact_decode:
+            # every sequence exactly 128K tokens (the 128K-context headline shape)
+            result["exact_128k_decode"] = decode_line(args.exact_workload, False)
+        if not args.no_fp8_decode:
+            result["fp8_decode"] = decode_line(args.fp8_workload, True)
 
     if not args.no_prefill:
         pname = "prefill_16k_bf16"
@@ -337,8 +348,10 @@ def main():
         log(f"prefill {pms:.2f} ms/step, indexer {ims:.2f} ms")
         del pin, sc, idx, tws, mws
         torch.cuda.empty_cache()
-        inp = generate(wl, "cuda") if not args.no_cpu_baseline else None
+        inp = None
     if not args.no_cpu_baseline:
+        if inp is None:
+            inp = generate(wl, "cuda")
         log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
