@@ -36,6 +36,8 @@ Every step is the plain definition:
 6. upstream of the indexer ("runs in FP8" [ZS 3.1]): per-row e4m3fn
    quantisation with an fp32 scale, and the append of a new token's quantised
    index key into the (paged) key cache.
+7. the dense MLA that DSA is measured against [ZS 3.4]: eq. U's attention
+   over every candidate s = 0..p, no indexer and no selection.
 
 Readings where the pages are silent are stated at each function.
 """
@@ -376,3 +378,35 @@ def append_index_keys(mode: str, q_pos, block_table, block_size: int, k_new, k_c
             cache[blk, pos % block_size] = codes[t]
             scales[blk, pos % block_size] = sc[t]
     return cache, scales
+
+
+# --------------------------------------------------------------------------
+# 7. dense MLA, the attention DSA is compared against  [ZS 3.4; LD, dense
+#    warm-up stage]
+# --------------------------------------------------------------------------
+
+def dense_attention(inp: OracleInputs, t: int) -> tuple:
+    """Dense MLA in MQA mode for query t: every head attends over every candidate.
+
+    The comparison the pages draw ([ZS 3.4]: DSA decodes a 128K context about
+    twice as cheaply as dense MLA; for short prompts DSA behaves as dense
+    attention) is against attention over all preceding tokens and the token
+    itself, s = 0..pos_t, with the same logits, softmax and values as eq. U.
+    Returns (out [H, v_dim], lse [H]).
+    """
+    n = candidate_count(inp, t)
+    b = sequence_of(inp, t)
+    q_t = _finite(decode(inp.q[t], inp.mla_dtype), "MLA query")
+    rows = _finite(decode(gather_rows(inp.kv_cache, inp, b, np.arange(n)), inp.mla_dtype), "latent row")
+    return sparse_mla(q_t, rows, inp.v_dim, inp.sm_scale)
+
+
+def dense_forward(inp: OracleInputs, rows=None) -> dict:
+    """dense_attention for the query rows ``rows`` (default: all): ``out`` [R, H, Dv], ``lse`` [R, H]."""
+    rows = list(range(inp.num_q)) if rows is None else [int(r) for r in rows]
+    H = inp.q.shape[1]
+    out = np.zeros((len(rows), H, inp.v_dim))
+    lse = np.zeros((len(rows), H))
+    for i, t in enumerate(rows):
+        out[i], lse[i] = dense_attention(inp, t)
+    return {"rows": rows, "out": out, "lse": lse}

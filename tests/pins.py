@@ -382,6 +382,64 @@ def pin_permutation_invariance(o):
     _close(a["lse"], b["lse"], 1e-12, "permuted lse")
 
 
+# ---------------------------------------------------------------- dense MLA
+
+def pin_dense_causal_sdpa(o):
+    """Dense MLA of a prefill equals torch's causal SDPA (diagonal included, the
+    library's own mask) over the whole [T, T] problem, lse included."""
+    T, H, D, Dv = 37, 3, 10, 6
+    wl = small_workload(mode="prefill", length=T, k=4, H=H, D=D, Dv=Dv)
+    oi = to_oracle(generate(wl, "cpu"))
+    res = o.dense_forward(oi)
+    kv = torch.from_numpy(oi.kv_cache[0, :T].astype(np.float64))
+    q = torch.from_numpy(oi.q.astype(np.float64)).permute(1, 0, 2).reshape(1, H, T, D)
+    k = kv.reshape(1, 1, T, D).expand(1, H, T, D)
+    v = kv[:, :Dv].contiguous().reshape(1, 1, T, Dv).expand(1, H, T, Dv)
+    want = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=oi.sm_scale)
+    _close(res["out"], want.reshape(H, T, Dv).permute(1, 0, 2).numpy(), 1e-12, "dense causal out")
+    logits = (q @ k.transpose(-1, -2)) * oi.sm_scale
+    causal = torch.ones(T, T, dtype=torch.bool).tril()
+    want_lse = torch.logsumexp(logits.masked_fill(~causal, -math.inf), dim=-1)
+    _close(res["lse"], want_lse.reshape(H, T).T.numpy(), 1e-12, "dense causal lse")
+
+
+def pin_dense_ragged_paged(o):
+    """Dense decode over ragged, paged contexts equals SDPA over each sequence's
+    first n_t tokens, taken from a contiguous copy of the same data; slots past
+    a sequence's length (NaN poison) are never read."""
+    rng = np.random.default_rng(16)
+    wl = small_workload(mode="decode", num_seqs=3, length=30, k=5, H=2, D=12, Dv=8)
+    oi = to_oracle(generate(wl, "cpu", lengths=[7, 30, 18]))
+    contiguous = oi.kv_cache.copy()
+    bs = 4
+    B, L = oi.kv_cache.shape[:2]
+    nb = (L + bs - 1) // bs
+    table = rng.permutation(B * nb).reshape(B, nb)
+    vc = np.full((B * nb, bs) + oi.kv_cache.shape[2:], np.nan, oi.kv_cache.dtype)
+    for b in range(B):
+        for s in range(L):
+            vc[table[b, s // bs], s % bs] = oi.kv_cache[b, s]
+    oi.block_table, oi.block_size, oi.kv_cache = table, bs, vc
+    res = o.dense_forward(oi)
+    for t in range(3):
+        n = int(oi.q_pos[t]) + 1
+        want_out, want_lse = _sdpa(oi.q[t].astype(float), contiguous[t, :n].astype(float), 8, oi.sm_scale,
+                                   np.ones(n, bool))
+        _close(res["out"][t], want_out, 1e-12, f"query {t} out")
+        _close(res["lse"][t], want_lse, 1e-12, f"query {t} lse")
+
+
+def pin_dense_equals_short_prompt_dsa(o):
+    """With k >= every n_t the DSA path selects every candidate, so its result is
+    the dense one (short prompts, zeroshot section 3.4)."""
+    wl = small_workload(mode="decode", num_seqs=4, length=20, k=32)
+    oi = to_oracle(generate(wl, "cpu", lengths=[1, 9, 20, 14]))
+    a = o.forward(oi)
+    d = o.dense_forward(oi)
+    _close(a["out"], d["out"], 1e-12, "short-prompt out")
+    _close(a["lse"], d["lse"], 1e-12, "short-prompt lse")
+
+
 # ---------------------------------------------------------------- fp8 quantisation and append
 
 def pin_e4m3_encode_roundtrip(o):

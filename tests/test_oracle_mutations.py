@@ -126,6 +126,28 @@ def _append_block_offset_dropped(mode, q_pos, block_table, block_size, k_new, k_
                                        k_scale)
 
 
+def _dense_with(shift):
+    def f(inp, t):
+        n = od.candidate_count(inp, t) + shift
+        b = od.sequence_of(inp, t)
+        q_t = od.decode(inp.q[t], inp.mla_dtype)
+        rows = od.decode(od.gather_rows(inp.kv_cache, inp, b, np.arange(max(n, 0))), inp.mla_dtype)
+        return od.sparse_mla(q_t, rows, inp.v_dim, inp.sm_scale)
+    return f
+
+
+def _dense_reversed_table(inp, t):
+    # reads each sequence's blocks in reverse table order
+    if inp.block_table is None:
+        return od.__dict__["_orig_dense"](inp, t)
+    saved = inp.block_table
+    inp.block_table = saved[:, ::-1]
+    try:
+        return od.__dict__["_orig_dense"](inp, t)
+    finally:
+        inp.block_table = saved
+
+
 MUTATIONS = {
     "indexer_no_relu": ("index_scores", _no_relu),
     "indexer_relu_after_weight": ("index_scores", _relu_after_weight),
@@ -147,6 +169,9 @@ MUTATIONS = {
     "fp8_round_toward_zero": ("encode_e4m3fn", _encode_truncate),
     "fp8_scale_uses_fnuz_max": ("E4M3FN_MAX", 240.0),
     "append_block_offset_dropped": ("append_index_keys", _append_block_offset_dropped),
+    "dense_excludes_self": ("dense_attention", _dense_with(-1)),
+    "dense_one_past_self": ("dense_attention", _dense_with(+1)),
+    "dense_reversed_block_table": ("dense_attention", _dense_reversed_table),
 }
 
 
@@ -156,6 +181,7 @@ def test_mutation_is_caught(name, monkeypatch):
     monkeypatch.setattr(od, "_orig_sparse_mla", od.sparse_mla, raising=False)
     monkeypatch.setattr(od, "_orig_query_index_operands", od.query_index_operands, raising=False)
     monkeypatch.setattr(od, "_orig_append", od.append_index_keys, raising=False)
+    monkeypatch.setattr(od, "_orig_dense", od.dense_attention, raising=False)
     monkeypatch.setattr(od, attr, repl)
     caught = []
     for pin in pins.ALL_PINS:
