@@ -150,6 +150,43 @@ def time_forward(B, torch, inp, steps, warmup, settle_ms=0, prep=None):
     return total_ms / steps, mean
 
 
+def time_op(torch, op, steps, warmup, settle_ms):
+    """Mean ms of `op` over `steps` back-to-back calls after a settle and `warmup` calls."""
+    settle(torch, op, settle_ms)
+    for _ in range(warmup):
+        op()
+    e0, e1 = make_events(torch, 2)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        op()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def dense_line(B, torch, inp, dsa_ms, steps, warmup, settle_ms):
+    """Dense MLA over every candidate (dsa_dense_mla: no indexer, no selection) on the
+    same inputs, against the DSA step time `dsa_ms`."""
+    wl = inp.wl
+    pb = B.problem_from_inputs(inp)
+    ws = torch.empty(max(1, B.workspace_size(B.OP_DENSE_MLA, pb)), dtype=torch.uint8, device="cuda")
+    T = inp.num_q
+    out = torch.empty((T, wl.heads, wl.v_dim), dtype=inp.q.dtype, device="cuda")
+    lse = torch.empty((T, wl.heads), dtype=torch.float32, device="cuda")
+    op = lambda: B.dense_mla(pb, inp.sm_scale, inp.q, inp.kv_cache, out=out, lse=lse, ws=ws)
+    ms = time_op(torch, op, steps, warmup, settle_ms)
+    n_total = int((inp.q_pos.to("cpu").long() + 1).sum())
+    e = ELEM[wl.mla_dtype]
+    flops = n_total * wl.heads * 2 * (wl.qk_dim + wl.v_dim)
+    nbytes = n_total * wl.qk_dim * e + T * wl.heads * (wl.qk_dim + wl.v_dim) * e
+    del ws, out, lse
+    return {"dense_mla_ms": round(ms, 4), "dsa_step_ms": round(dsa_ms, 4), "dense_over_dsa": round(ms / dsa_ms, 3),
+            "dense_tokens_per_s": round(T / (ms * 1e-3), 1), "dense_rows": n_total,
+            "dense_mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[wl.mla_dtype], 4),
+            "dense_hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(inp, seconds):
     """The float64 oracle, as it stands, on the queries of the timed batch, for a bounded time."""
     import numpy as np
@@ -200,6 +237,8 @@ def main():
     ap.add_argument("--no-exact-decode", action="store_true",
                     help="skip the secondary decode line with every context exactly 128K tokens")
     ap.add_argument("--exact-workload", default="decode_128k_exact_paged_bf16")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense-MLA comparison (attention over every candidate) on the same inputs")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -265,6 +304,12 @@ def main():
         "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
     }
 
+    dense = {}
+    if not args.no_dense:
+        log("dense MLA on the same inputs")
+        dense[name] = dense_line(B, torch, inp, ms, max(3, args.steps // 4), 1, args.settle_ms)
+        log(f"dense: {dense[name]['dense_mla_ms']:.3f} ms ({dense[name]['dense_over_dsa']:.2f}x the DSA step)")
+
     def decode_line(name, fp8_prep):
         """Another decode workload through the same step (for e4m3fn indexing: the new
         tokens' index queries and keys arrive in bf16 and are quantised with
@@ -296,6 +341,8 @@ def main():
                 "step_algorithmic_bytes": d_step + extra,
                 "step_hbm_frac": round((d_step + extra) / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         log(f"{name}: {dms:.3f} ms/step, indexer {dst[0]:.4f} ms")
+        if not args.no_dense and not fp8_prep:
+            dense[name] = dense_line(B, torch, din, dms, max(3, args.steps // 4), 1, args.settle_ms)
         del din
         torch.cuda.empty_cache()
         return line
@@ -346,9 +393,16 @@ def main():
             "attention_mfma_frac": round(pf_mla / (stage_ms[2] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
             "step_mfma_frac": round((pf_idx + pf_mla) / (pms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4)}
         log(f"prefill {pms:.2f} ms/step, indexer {ims:.2f} ms")
-        del pin, sc, idx, tws, mws
+        del sc, idx, tws, mws
+        torch.cuda.empty_cache()
+        if not args.no_dense:
+            dense[pname] = dense_line(B, torch, pin, pms, 2, 1, args.settle_ms)
+        del pin
         torch.cuda.empty_cache()
         inp = None
+    if dense:
+        # the comparison the pages draw: DSA against dense MLA over the same contexts
+        result["dense_comparison"] = dense
     if not args.no_cpu_baseline:
         if inp is None:
             inp = generate(wl, "cuda")

@@ -99,7 +99,8 @@ typedef enum dsa_op {
   DSA_OP_INDEX_SCORES = 0,
   DSA_OP_TOPK = 1,
   DSA_OP_SPARSE_MLA = 2,
-  DSA_OP_FORWARD = 3
+  DSA_OP_FORWARD = 3,
+  DSA_OP_DENSE_MLA = 4
 } dsa_op;
 
 /* Where each query sits and which cache rows it may read (host struct). */
@@ -196,9 +197,29 @@ int dsa_sparse_mla(const dsa_seqs *seqs, const dsa_dims *dims, float sm_scale, c
  * indexer, then token selection, then sparse attention].  Results equal
  * dsa_index_scores -> dsa_topk -> dsa_sparse_mla on the same inputs.
  * Prefill runs in query chunks so the score rows of a chunk stay on chip.
+ * Short prompts [ZS 3.4: DSA then behaves as dense attention]: when
+ * max_ctx <= k every query keeps all of its candidates whatever their
+ * scores, so the indexer and top-k are not run; the attention walks the
+ * candidate positions and the output bytes are the same.  topk_idx, if
+ * given, then receives 0..n_t-1 followed by -1.
  * Workspace: dsa_workspace_size(DSA_OP_FORWARD, ...). */
 int dsa_forward(const dsa_seqs *seqs, const dsa_dims *dims, const dsa_forward_args *args,
                 void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Dense MLA, the attention DSA is measured against [ZS 3.4: at a 128K context
+ * DSA decodes about twice as cheaply as dense MLA; LD: the dense warm-up
+ * stage keeps dense attention]: step 3 over EVERY candidate s = 0..q_pos[t]
+ * of each query, with no indexer and no selection.  Logits, softmax, output,
+ * lse and precision as dsa_sparse_mla; dims->topk and the indexer fields are
+ * not read.  bf16: each query's candidates are cut into up to 128 splits of
+ * at most 2048 rows, merged in split order; queries run in chunks whose split
+ * partials fit 1 GiB of workspace (so a decode batch is one chunk).
+ * Supported: bf16 H = 128, D = 576, Dv = 512 (max_ctx <= 262144); fp32
+ * H <= 16, D <= 128, max_ctx <= 1024.
+ * Workspace: dsa_workspace_size(DSA_OP_DENSE_MLA, ...). */
+int dsa_dense_mla(const dsa_seqs *seqs, const dsa_dims *dims, float sm_scale, const void *q,
+                  const void *kv_cache, void *out, float *lse, void *ws, size_t ws_bytes,
+                  hipStream_t stream);
 
 /* Upstream of step 1: per-row fp8 quantisation for an indexer that "runs in
  * FP8" [ZS 3.1; BT (1)].  The pages fix neither scale nor rounding; the

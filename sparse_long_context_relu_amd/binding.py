@@ -19,11 +19,11 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "dsa.h")
 
 F32, BF16, FP8_E4M3FN = 0, 1, 2
 PREFILL, DECODE = 0, 1
-OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_MLA, OP_FORWARD = 0, 1, 2, 3
+OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_MLA, OP_FORWARD, OP_DENSE_MLA = 0, 1, 2, 3, 4
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
 EXPORTS = ("dsa_workspace_size", "dsa_index_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward",
-           "dsa_quantize_fp8", "dsa_append_index_keys", "dsa_status_string")
+           "dsa_dense_mla", "dsa_quantize_fp8", "dsa_append_index_keys", "dsa_status_string")
 
 
 class DsaSeqs(ctypes.Structure):
@@ -70,6 +70,8 @@ def _load() -> ctypes.CDLL:
     lib.dsa_sparse_mla.restype = ctypes.c_int
     lib.dsa_forward.argtypes = [sp, dp, ctypes.POINTER(DsaForwardArgs), P, SZ, P]
     lib.dsa_forward.restype = ctypes.c_int
+    lib.dsa_dense_mla.argtypes = [sp, dp, ctypes.c_float, P, P, P, P, P, SZ, P]
+    lib.dsa_dense_mla.restype = ctypes.c_int
     lib.dsa_quantize_fp8.argtypes = [I64, I32, I32, P, P, P, I32, P]
     lib.dsa_quantize_fp8.restype = ctypes.c_int
     lib.dsa_append_index_keys.argtypes = [sp, I32, I32, P, P, P, P]
@@ -209,6 +211,20 @@ def sparse_mla(pb: Problem, sm_scale: float, q, kv_cache, topk_idx, out=None, ls
                             _ptr(kv_cache), _ptr(topk_idx), _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws),
                             _stream(stream))
     _check(st, "dsa_sparse_mla")
+    return out, lse
+
+
+def dense_mla(pb: Problem, sm_scale: float, q, kv_cache, out=None, lse=None, ws=None, want_lse: bool = True,
+              stream=None):
+    """Dense MLA over every candidate of each query: (out [T, H, Dv] in q's dtype, lse [T, H] fp32 or None)."""
+    if out is None:
+        out = torch.empty((pb.num_q, pb.dims.heads, pb.dims.v_dim), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((pb.num_q, pb.dims.heads), dtype=torch.float32, device=q.device)
+    ws = _workspace(OP_DENSE_MLA, pb, ws, q.device)
+    st = LIB.dsa_dense_mla(ctypes.byref(pb.seqs), ctypes.byref(pb.dims), float(sm_scale), _ptr(q),
+                           _ptr(kv_cache), _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream))
+    _check(st, "dsa_dense_mla")
     return out, lse
 
 

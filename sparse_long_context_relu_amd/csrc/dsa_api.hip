@@ -16,6 +16,8 @@ constexpr int kQuantMaxLen = 65536;              // values per quantised row
 constexpr int kQuantMaxRepeat = 1024;            // copies of each row's scale
 constexpr long long kQuantMaxRows = 2147483647;  // one workgroup (or a quarter) per row
 constexpr int kAppendMaxDim = 2048;              // index key width for the append
+constexpr long long kDenseWsBudget = 1ll << 30;  // bytes of split partials per dense query chunk
+constexpr int kDenseF32MaxCtx = 1024;            // fp32 dense lists live in one workgroup's LDS
 
 long long align256(long long x) { return (x + 255) & ~255ll; }
 
@@ -66,6 +68,22 @@ int check_mla_dims(const dsa_dims *d) {
     case DSA_F32:
       if (d->heads > 16 || d->qk_dim > 128 || d->topk > 1024)
         return DSA_ERR_UNSUPPORTED;
+      return DSA_OK;
+    case DSA_FP8_E4M3FN:
+      return DSA_ERR_UNSUPPORTED;
+    default:
+      return DSA_ERR_INVALID_ARG;
+  }
+}
+
+int check_dense_dims(const dsa_seqs *s, const dsa_dims *d) {
+  if (d == nullptr || d->heads < 1 || d->qk_dim < 1 || d->v_dim < 1 || d->v_dim > d->qk_dim)
+    return DSA_ERR_INVALID_ARG;
+  switch (d->mla_dtype) {
+    case DSA_BF16:
+      return (d->heads == 128 && d->qk_dim == 576 && d->v_dim == 512) ? DSA_OK : DSA_ERR_UNSUPPORTED;
+    case DSA_F32:
+      if (d->heads > 16 || d->qk_dim > 128 || s->max_ctx > kDenseF32MaxCtx) return DSA_ERR_UNSUPPORTED;
       return DSA_OK;
     case DSA_FP8_E4M3FN:
       return DSA_ERR_UNSUPPORTED;
@@ -133,6 +151,32 @@ ForwardLayout forward_layout(const dsa_seqs *s, const dsa_dims *d) {
   L.off_topk = L.off_idx + align256((long long)L.chunk * d->topk * 4);
   L.off_mla = L.off_topk + align256(topk_ws_bytes(L.chunk, s->max_ctx));
   L.total = L.off_mla + align256(mla_ws_bytes(d, L.chunk));
+  return L;
+}
+
+// Dense MLA: every query's list is its max_ctx candidate positions, cut into
+// n_split pieces of at most 2048; queries run in chunks whose split partials
+// fit kDenseWsBudget (one chunk when they all fit, and always for decode
+// batches of up to 64 queries at 128K).
+struct DenseLayout {
+  int chunk, n_split;
+  long long total;
+};
+
+DenseLayout dense_layout(const dsa_seqs *s, const dsa_dims *d) {
+  DenseLayout L;
+  const int T = s->num_q;
+  L.chunk = T;
+  L.n_split = d->mla_dtype == DSA_BF16 ? mla_dense_splits(T, s->max_ctx) : 1;
+  L.total = 0;
+  if (L.n_split > 1) {
+    const long long per_row = (long long)L.n_split * d->heads * ((long long)d->v_dim * 2 + 8);
+    if ((long long)T * per_row > kDenseWsBudget) {
+      const long long c = kDenseWsBudget / per_row;
+      L.chunk = c < 1 ? 1 : (int)c;
+    }
+    L.total = (long long)L.chunk * per_row;
+  }
   return L;
 }
 
@@ -204,6 +248,7 @@ MlaArgs mla_args(const dsa_seqs *s, const dsa_dims *d, float sm_scale, const voi
   a.rows = rows;
   a.n_split = mla_split_count(d, rows);
   a.part = ws;
+  a.dense = 0;
   return a;
 }
 
@@ -230,6 +275,9 @@ DSA_EXPORT size_t dsa_workspace_size(int op, const dsa_seqs *seqs, const dsa_dim
     case DSA_OP_FORWARD:
       if (check_index_dims(dims) != DSA_OK || check_mla_dims(dims) != DSA_OK) return 0;
       return (size_t)forward_layout(seqs, dims).total;
+    case DSA_OP_DENSE_MLA:
+      if (check_dense_dims(seqs, dims) != DSA_OK) return 0;
+      return (size_t)dense_layout(seqs, dims).total;
     default:
       return 0;
   }
@@ -294,12 +342,29 @@ DSA_EXPORT int dsa_forward(const dsa_seqs *seqs, const dsa_dims *dims, const dsa
   void *mla_ws = base + L.off_mla;
   hipEvent_t const *ev = reinterpret_cast<hipEvent_t const *>(args->stage_events);
 
+  // Short prompts: when no query has more than k candidates the selection is
+  // every candidate whatever the scores, so the indexer and the top-k are
+  // skipped and the attention walks the candidate positions directly (the
+  // same lists, split the same way, so the same bytes out).
+  const bool all_selected = seqs->max_ctx <= dims->topk;
   const int T = seqs->num_q;
   for (int c0 = 0; c0 < T; c0 += L.chunk) {
     const int rows = c0 + L.chunk < T ? L.chunk : T - c0;
     const bool timed = ev != nullptr && c0 == 0;
     int32_t *idx = args->topk_idx != nullptr ? args->topk_idx + (long long)c0 * dims->topk : idx_ws;
     TopkArgs ta = topk_args(seqs, dims->topk, scores, L.ld, idx, topk_ws, c0, rows);
+    if (all_selected) {
+      if (timed && hipEventRecord(ev[0], stream) != hipSuccess) return DSA_ERR_HIP;
+      if (timed && hipEventRecord(ev[1], stream) != hipSuccess) return DSA_ERR_HIP;
+      if (args->topk_idx != nullptr && launch_topk_all(ta, stream) != hipSuccess) return DSA_ERR_HIP;
+      if (timed && hipEventRecord(ev[2], stream) != hipSuccess) return DSA_ERR_HIP;
+      MlaArgs ma = mla_args(seqs, dims, args->sm_scale, args->q, args->kv_cache, nullptr, args->out, args->lse,
+                            mla_ws, c0, rows);
+      ma.dense = 1;
+      if (launch_sparse_mla(ma, stream) != hipSuccess) return DSA_ERR_HIP;
+      if (timed && hipEventRecord(ev[3], stream) != hipSuccess) return DSA_ERR_HIP;
+      continue;
+    }
     IndexerArgs ia = indexer_args(seqs, dims, args->q_idx, args->q_scale, args->w, args->k_cache,
                                   args->k_scale, scores, L.ld, c0, rows, 0);
     // The MFMA indexers count the top-k's first radix digit as they write the
@@ -322,6 +387,28 @@ DSA_EXPORT int dsa_forward(const dsa_seqs *seqs, const dsa_dims *dims, const dsa
                           mla_ws, c0, rows);
     if (launch_sparse_mla(ma, stream) != hipSuccess) return DSA_ERR_HIP;
     if (timed && hipEventRecord(ev[3], stream) != hipSuccess) return DSA_ERR_HIP;
+  }
+  return DSA_OK;
+}
+
+DSA_EXPORT int dsa_dense_mla(const dsa_seqs *seqs, const dsa_dims *dims, float sm_scale, const void *q,
+                             const void *kv_cache, void *out, float *lse, void *ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  if (int e = check_seqs(seqs)) return e;
+  if (int e = check_dense_dims(seqs, dims)) return e;
+  if (seqs->num_q == 0) return DSA_OK;
+  if (q == nullptr || kv_cache == nullptr || out == nullptr) return DSA_ERR_INVALID_ARG;
+  if (!(sm_scale == sm_scale)) return DSA_ERR_INVALID_ARG;
+  const DenseLayout L = dense_layout(seqs, dims);
+  if (int e = check_ws((size_t)L.total, ws, ws_bytes)) return e;
+  const int T = seqs->num_q;
+  for (int c0 = 0; c0 < T; c0 += L.chunk) {
+    const int rows = c0 + L.chunk < T ? L.chunk : T - c0;
+    MlaArgs a = mla_args(seqs, dims, sm_scale, q, kv_cache, nullptr, out, lse, ws, c0, rows);
+    a.dense = 1;
+    a.k = seqs->max_ctx;
+    a.n_split = L.n_split;
+    if (launch_sparse_mla(a, stream) != hipSuccess) return DSA_ERR_HIP;
   }
   return DSA_OK;
 }

@@ -52,7 +52,11 @@ struct MlaArgs {
   float sm_scale;
   const void *q;
   const void *kv;
-  const int32_t *idx;  // [rows, k]
+  const int32_t *idx;  // [rows, k]; unused when dense
+  // dense: entry j of query t's list is position j itself (present while
+  // j < n_t), for j < k; idx is not read.  k then only sets how the lists are
+  // split.  A split with no position writes no partial.
+  int dense;
   void *out;
   float *lse;
   int q_begin, rows;
@@ -103,6 +107,8 @@ struct TopkLayout {
 TopkLayout topk_layout(int rows, int max_ctx);
 bool topk_sliced(int rows);
 int mla_splits(int rows, int k);
+int mla_dense_splits(int rows, int span);   // splits of a dense list of `span` entries
+constexpr int kMlaMaxSplits = 128;
 size_t mla_f32_lds(int H, int D, int k);
 
 hipError_t launch_index_scores(const IndexerArgs &a, hipStream_t s);
@@ -110,7 +116,8 @@ hipError_t launch_index_decode(const IndexerArgs &a, hipStream_t s);   // decode
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);         // zero + hist1 + select
 hipError_t launch_topk_zero(const TopkArgs &a, hipStream_t s);    // zero the per-row headers
 hipError_t launch_topk_select(const TopkArgs &a, hipStream_t s);  // collect + select (hist1 ready)
-hipError_t launch_sparse_mla(const MlaArgs &a, hipStream_t s);
+hipError_t launch_topk_all(const TopkArgs &a, hipStream_t s);     // every candidate (all n_t <= k)
+hipError_t launch_sparse_mla(const MlaArgs &a, hipStream_t s);     // also the dense lists
 hipError_t launch_fp8_quantize(const QuantArgs &a, hipStream_t s);
 hipError_t launch_fp8_append(const AppendArgs &a, hipStream_t s);
 

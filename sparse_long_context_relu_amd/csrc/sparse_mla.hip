@@ -245,11 +245,15 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
   const int t = a.q_begin + r;
   const int n = a.sv.candidates(t);
   const int b = a.sv.seq_of(t);
-  const int32_t *irow = a.idx + (long long)r * a.k;
+  const int32_t *irow = a.dense ? nullptr : a.idx + (long long)r * a.k;
   const int len = split_len(a.k, a.n_split);
   const int i0 = sp * len;
-  const int i1 = i0 + len < a.k ? i0 + len : a.k;
+  int i1 = i0 + len < a.k ? i0 + len : a.k;
+  if (a.dense && i1 > n) i1 = n;              // dense lists end at the last candidate
   const int rows = i1 > i0 ? i1 - i0 : 0;
+  // A dense split past the last candidate has nothing to merge; the combine
+  // reads only the splits that hold a position.
+  if (a.dense && rows == 0 && a.n_split > 1) return;
   const int ntiles = (rows + kR - 1) / kR;
 
   const int lane = lane_id();
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
 #pragma unroll
   for (int u = 0; u < kFill; ++u) {
     const int j = threadIdx.x + u * kThreads;
-    pos[u] = j < rows ? irow[i0 + j] : -1;
+    pos[u] = j < rows ? (a.dense ? i0 + j : irow[i0 + j]) : -1;
   }
   int sl[kFill];
   if (a.sv.block_table == nullptr) {
@@ -381,40 +385,56 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
 }
 
 // Merge the split partials of one (query, head): one wave per head, each lane
-// owning 8 consecutive value dims.  Lane s < n_split reads split s's running
-// maximum and sum; split s weighs exp2(max_s - M) sum_s, normalised over the
-// splits.  The loads of up to eight splits are issued together, and the
-// weighted sum runs in split order.
+// owning 8 consecutive value dims.  Lanes s and s + 64 read the running maximum
+// and sum of splits s and s + 64 (up to 128 splits); split s weighs
+// exp2(max_s - M) sum_s, normalised over the splits.  The loads of up to eight
+// splits are issued together, and the weighted sum runs in split order.  A
+// dense list merges only the splits that hold a position.
 __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
   const int lane = lane_id();
   const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int r = blockIdx.y;
   const int t = a.q_begin + r;
   const int ns = a.n_split;
+  int nm = ns;
+  if (a.dense) {
+    const int len = split_len(a.k, ns);
+    const int n = a.sv.candidates(t);
+    nm = n <= 0 ? 0 : (n + len - 1) / len;
+    if (nm > ns) nm = ns;
+  }
   const uint16_t *po = reinterpret_cast<const uint16_t *>(a.part) + ((long long)r * ns * kH + h) * kDv + lane * 8;
   const float2 *ml = reinterpret_cast<const float2 *>(reinterpret_cast<const uint16_t *>(a.part) +
                                                       (long long)a.rows * ns * kH * kDv) +
                      (long long)r * ns * kH + h;
-  float ms = neg_inf(), ls = 0.f;
-  if (lane < ns) {
+  float ms0 = neg_inf(), ls0 = 0.f, ms1 = neg_inf(), ls1 = 0.f;
+  if (lane < nm) {
     const float2 v = ml[(long long)lane * kH];
-    ms = v.x;
-    ls = v.y;
+    ms0 = v.x;
+    ls0 = v.y;
   }
-  const float M = wave_max(ms);
-  const float w = ms == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(ms - M) * ls;
-  const float L = wave_sum(w);
+  if (lane + 64 < nm) {
+    const float2 v = ml[(long long)(lane + 64) * kH];
+    ms1 = v.x;
+    ls1 = v.y;
+  }
+  const float M = wave_max(fmaxf(ms0, ms1));
+  const float w0 = ms0 == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(ms0 - M) * ls0;
+  const float w1 = ms1 == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(ms1 - M) * ls1;
+  const float L = wave_sum(w0 + w1);
   const float inv = L > 0.f ? 1.f / L : 0.f;
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < ns; s0 += 8) {
+  for (int s0 = 0; s0 < nm; s0 += 8) {
+    const float w = s0 < 64 ? w0 : w1;
     uint4 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (s0 + u < ns) v[u] = *reinterpret_cast<const uint4 *>(po + (long long)(s0 + u) * kH * kDv);
+      if (s0 + u < nm) v[u] = *reinterpret_cast<const uint4 *>(po + (long long)(s0 + u) * kH * kDv);
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (s0 + u < ns) {
-        const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), s0 + u));
+      if (s0 + u < nm) {
+        const float wu =
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), (s0 + u) & 63));
         const uint32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -448,10 +468,10 @@ __global__ __launch_bounds__(256) void mla_f32_kernel(MlaArgs a) {
   const int b = a.sv.seq_of(t);
   const float *q = reinterpret_cast<const float *>(a.q) + (long long)t * H * D;
   const float *kv = reinterpret_cast<const float *>(a.kv);
-  const int32_t *irow = a.idx + (long long)r * K;
+  const int32_t *irow = a.dense ? nullptr : a.idx + (long long)r * K;
   for (int i = threadIdx.x; i < H * D; i += blockDim.x) qs[i] = q[i];
   for (int j = threadIdx.x; j < K; j += blockDim.x) {
-    const int s = irow[j];
+    const int s = a.dense ? j : irow[j];
     slots[j] = (s >= 0 && s < n) ? a.sv.slot(b, s) : -1;
   }
   __syncthreads();
@@ -509,6 +529,15 @@ int mla_splits(int rows, int k) {
   int cap = (k + 2 * kR - 1) / (2 * kR);
   if (s > cap) s = cap;
   return s < 1 ? 1 : s;
+}
+
+// A dense list of `span` entries: splits of at most kMaxSplitRows entries (the
+// slot list of a workgroup), and at least as many as fill the chip.
+int mla_dense_splits(int rows, int span) {
+  int s = (span + kMaxSplitRows - 1) / kMaxSplitRows;
+  const int fill = mla_splits(rows, span);
+  if (s < fill) s = fill;
+  return s > kMlaMaxSplits ? kMlaMaxSplits : s;
 }
 
 size_t mla_f32_lds(int H, int D, int k) {

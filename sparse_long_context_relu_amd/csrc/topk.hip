@@ -544,6 +544,16 @@ __global__ __launch_bounds__(kRowNT) void topk_select_rows_kernel(TopkArgs a) {
   compact_selection<kRowNT>(selmap, eqmap, W, quota, m, a.k, out, tmp);
 }
 
+// The selection when no query has more than k candidates: every candidate, in
+// ascending position order, then -1.
+__global__ __launch_bounds__(256) void topk_all_kernel(TopkArgs a) {
+  const int r = blockIdx.y;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= a.k) return;
+  const int n = a.sv.candidates(a.q_begin + r);
+  a.idx[(long long)r * a.k + j] = j < n ? j : -1;
+}
+
 hipError_t set_lds(const void *kernel, size_t lds) {
   if (lds <= 65536) return hipSuccess;
   return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -592,6 +602,12 @@ hipError_t launch_topk_select(const TopkArgs &a, hipStream_t st) {
     if (hipError_t e = set_lds((const void *)topk_select_rows_kernel, lds)) return e;
     hipLaunchKernelGGL(topk_select_rows_kernel, dim3(a.rows), dim3(kRowNT), lds, st, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_all(const TopkArgs &a, hipStream_t st) {
+  if (a.rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_all_kernel, dim3((a.k + 255) / 256, a.rows), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

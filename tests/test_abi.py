@@ -143,6 +143,40 @@ def test_sparse_mla_validation():
     assert call(pb4) == B.ERR_INVALID_ARG
 
 
+def test_dense_mla_validation_and_workspace():
+    """Dense MLA: host checks and the split / chunk workspace (no launch)."""
+    call = lambda pbx, ws=FAKE, nb=1 << 40, q=FAKE, sm=0.04: B.LIB.dsa_dense_mla(
+        ctypes.byref(pbx.seqs), ctypes.byref(pbx.dims), sm, q, FAKE, FAKE, None, ws, nb, None)
+    per_split = 128 * (512 * 2 + 8)                      # bf16 head outputs + fp32 (max, sum) per split
+    # decode, 32 x 128K: 64 splits of 2048 rows, one chunk
+    pb = _problem(q_pos=torch.full((32,), 131071, dtype=torch.int32), max_ctx=131072, num_seqs=32,
+                  max_seq_len=131072)
+    need = B.workspace_size(B.OP_DENSE_MLA, pb)
+    assert need == 32 * 64 * per_split
+    assert call(pb, q=None) == B.ERR_INVALID_ARG
+    assert call(pb, sm=float("nan")) == B.ERR_INVALID_ARG
+    assert call(pb, ws=None, nb=0) == B.ERR_WORKSPACE
+    assert call(pb, nb=need - 1) == B.ERR_WORKSPACE
+    # the top-k size is not read
+    pb.dims.topk = 0
+    assert B.workspace_size(B.OP_DENSE_MLA, pb) == need
+    # prefill, 16K: 8 splits per query, query chunks bounded by 1 GiB of partials
+    pf = B.make_problem(mode="prefill", q_pos=torch.arange(16384, dtype=torch.int32), max_ctx=16384, num_seqs=1,
+                        max_seq_len=16384)
+    ws16k = B.workspace_size(B.OP_DENSE_MLA, pf)
+    assert ws16k == (1 << 30) // (8 * per_split) * (8 * per_split)
+    # short contexts with many queries need no splits
+    short = B.make_problem(mode="prefill", q_pos=torch.arange(512, dtype=torch.int32), max_ctx=512, num_seqs=1,
+                           max_seq_len=512)
+    assert B.workspace_size(B.OP_DENSE_MLA, short) == 0
+    assert call(_problem(heads=64)) == B.ERR_UNSUPPORTED
+    assert call(_problem(mla_dtype=B.FP8_E4M3FN)) == B.ERR_UNSUPPORTED
+    f32 = dict(mla_dtype=B.F32, heads=8, qk_dim=80, v_dim=64)
+    assert call(_problem(**f32)) == B.ERR_UNSUPPORTED     # fp32 lists are limited to 1024 candidates
+    small = _problem(q_pos=torch.tensor([255, 100], dtype=torch.int32), max_ctx=256, max_seq_len=256, **f32)
+    assert B.workspace_size(B.OP_DENSE_MLA, small) == 0
+
+
 def test_forward_validation_and_workspace():
     pb = _problem()
     need = B.workspace_size(B.OP_FORWARD, pb)
