@@ -51,37 +51,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (c0 >= n) return;
   const int c1 = c0 + kDecodeChunk < n ? c0 + kDecodeChunk : n;
 
-  // first radix digit of the top-k, counted per workgroup and added to the row's bins
-  const bool hist = a.hist_mode == 1;
-  if (hist)
-    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
-  // Slot of the first key of each 64-token block of this chunk (-1: absent),
-  // read once, so a tile's lookup is an LDS read that never waits on the
-  // vector-memory counter (which also counts the score stores in flight).
-  __shared__ long long blk0[kDecodeChunk / 64];
-  if (threadIdx.x < kDecodeChunk / 64) {
-    const int s = c0 + threadIdx.x * 64;
-    blk0[threadIdx.x] = s < c1 ? a.sv.slot(b, s) : -1;
-  }
-  __syncthreads();
-
   const int lane = lane_id();
   const int wv = threadIdx.x >> 6;
   const int g = lane >> 5, col = lane & 31;
+  // Start-up, ordered so that the first tiles are in flight after one
+  // block-table latency: the query operands and weights are loaded first (the
+  // oldest loads), then the block-table entries of the chunk for the LDS copy
+  // used from the third tile on, then the wave's first two tiles, whose slots
+  // come straight from the table through the scalar cache.
   typename Tr::Op qa[2][Tr::kSteps];
   float wt[2][16];
   load_query<DT>(a, t, col, g, qa, wt);
+  // Slot of the first key of each 64-token block of this chunk (-1: absent),
+  // kept in LDS, so a tile's lookup in the loop is an LDS read that never waits
+  // on the vector-memory counter (which also counts the score stores in flight).
+  // Only the raw entry is loaded here; it is checked after the tile loads are
+  // issued, so that no wait is placed before them.
+  __shared__ long long blk0[kDecodeChunk / 64];
+  const int my_s = c0 + (int)threadIdx.x * 64;
+  const bool my_fill = threadIdx.x < kDecodeChunk / 64 && my_s < c1;
+  int my_raw = 0;
+  if (my_fill && a.sv.block_table != nullptr)
+    my_raw = a.sv.block_table[(long long)b * a.sv.max_blocks + (my_s >> 6)];
 
   const uint8_t *kbase = reinterpret_cast<const uint8_t *>(a.k_cache);
   uint4 *tile = wtile[wv];
-  // Coalesced fetch of the tile at key `base`: lane l takes chunk (i*64 + l) of
-  // the tile for i < kPer, i.e. row (i*64 + l) / kChunks.  A tile lies inside
-  // one 64-token block, so one wave-uniform lookup gives the slot of its first
-  // row and the others follow.  Rows past c1 or in an absent block load zeros.
   auto tile_slot = [&](int base) -> long long {
     const long long b0 = blk0[(base - c0) >> 6];
     return b0 >= 0 ? b0 + (base & 63) : -1;
   };
+  // The same lookup for the wave's first two tiles, before the LDS copy exists:
+  // both block-table entries are read at once, wave-uniformly, through the
+  // scalar cache (a tile past the chunk reads the chunk's first entry and is
+  // marked absent).
+  auto first_slots = [&](int bA, int bB, long long &sA, long long &sB) {
+    if (a.sv.block_table == nullptr) {
+      sA = bA < c1 ? (long long)b * a.sv.max_seq_len + bA : -1;
+      sB = bB < c1 ? (long long)b * a.sv.max_seq_len + bB : -1;
+      return;
+    }
+    const __attribute__((address_space(4))) int32_t *bt =
+        (const __attribute__((address_space(4))) int32_t *)(a.sv.block_table + (long long)b * a.sv.max_blocks);
+    const int kA = bt[__builtin_amdgcn_readfirstlane((bA < c1 ? bA : c0) >> 6)];
+    const int kB = bt[__builtin_amdgcn_readfirstlane((bB < c1 ? bB : c0) >> 6)];
+    sA = (bA < c1 && kA >= 0 && kA < a.sv.num_blocks) ? (long long)kA * 64 + (bA & 63) : -1;
+    sB = (bB < c1 && kB >= 0 && kB < a.sv.num_blocks) ? (long long)kB * 64 + (bB & 63) : -1;
+  };
+  // Coalesced fetch of the tile at key `base`: lane l takes chunk (i*64 + l) of
+  // the tile for i < kPer, i.e. row (i*64 + l) / kChunks.  A tile lies inside
+  // one 64-token block, so one wave-uniform lookup gives the slot of its first
+  // row and the others follow.  Rows past c1 or in an absent block load zeros.
   // Every lane always loads (absent rows read the chunk's first row instead) and
   // `put` zeroes what is absent: no branches, and no register initialised
   // before a load that might be skipped.
@@ -110,17 +129,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int kStep = kDecodeWaves * 32;
   uint4 sa[kPer], sb[kPer];
   int base = c0 + wv * 32;
-  long long sl0 = -1, sla = -1, slb = -1;
-  if (base < c1) {
-    sl0 = tile_slot(base);
-    fetch(base, sl0, sa);
-    put(sa, base, sl0);
+  long long sl0, sla, slb = -1;
+  first_slots(base, base + kStep, sl0, sla);
+  fetch(base, sl0, sb);                            // tile 0, through stage B
+  fetch(base + kStep, sla, sa);                    // tile 1
+  // first radix digit of the top-k, counted per workgroup and added to the row's bins
+  const bool hist = a.hist_mode == 1;
+  if (hist)
+    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
+  if (threadIdx.x < kDecodeChunk / 64) {
+    long long v = -1;
+    if (my_fill) {
+      if (a.sv.block_table == nullptr)
+        v = (long long)b * a.sv.max_seq_len + my_s;
+      else if (my_raw >= 0 && my_raw < a.sv.num_blocks)
+        v = (long long)my_raw * 64;
+    }
+    blk0[threadIdx.x] = v;
   }
-  sla = base + kStep < c1 ? tile_slot(base + kStep) : -1;
-  fetch(base + kStep, sla, sa);
-  // Drain the query, weight and first-tile loads here, so that no wait for them
-  // lands inside the loop (where it would also wait for the prefetch).
-  __builtin_amdgcn_s_waitcnt(0);
+  // LDS-only barrier: the tile loads stay in flight across it.
+  lds_barrier();
+  // The query, weight and table loads and tile 0 have landed once at most the
+  // loads of tile 1 are outstanding; draining them here keeps every wait for
+  // them out of the loop (where it would also wait for the prefetch).
+  __builtin_amdgcn_s_waitcnt(wait_vm(kPer));
+  put(sb, base, sl0);
   // Scores of the tile resident in LDS (valid in every lane for key col).
   auto consume = [&]() {
     typename Tr::Op kb[Tr::kSteps];
