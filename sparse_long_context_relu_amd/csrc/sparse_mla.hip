@@ -260,17 +260,6 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, g = lane >> 4;
 
-  // Q^T operands for this wave's heads: lane holds head 16 wv + col,
-  // dims 32 ks + 8 g + [0, 8).  Issued first, so that their latency overlaps
-  // the index and page-table loads of the slot translation below; the barriers
-  // up to the first tile wait for LDS work only and leave them in flight.
-  bf16x8 qb[kKs];
-  {
-    const uint8_t *qrow = reinterpret_cast<const uint8_t *>(a.q) + ((long long)t * kH + wv * 16 + col) * (kD * 2);
-#pragma unroll
-    for (int ks = 0; ks < kKs; ++ks) qb[ks] = as_bf16x8(ld16(qrow + ks * 64 + g * 16));
-  }
-
   if (threadIdx.x == 0) fallback = -1;
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   lds_barrier();
@@ -301,6 +290,17 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
     for (int u = 0; u < kFill; ++u)
       sl[u] = (pos[u] >= 0 && pos[u] < n && blk[u] >= 0 && blk[u] < a.sv.num_blocks) ? blk[u] * 64 + (pos[u] & 63)
                                                                                      : -1;
+  }
+  // Q^T operands for this wave's heads: lane holds head 16 wv + col,
+  // dims 32 ks + 8 g + [0, 8).  Issued only now: vector-memory waits are in
+  // order, so query loads issued before the index and page-table loads would
+  // be drained by the waits for those.  From here they stream in with the
+  // first tile; the barriers up to it wait for LDS work only.
+  bf16x8 qb[kKs];
+  {
+    const uint8_t *qrow = reinterpret_cast<const uint8_t *>(a.q) + ((long long)t * kH + wv * 16 + col) * (kD * 2);
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) qb[ks] = as_bf16x8(ld16(qrow + ks * 64 + g * 16));
   }
 #pragma unroll
   for (int u = 0; u < kFill; ++u) {
