@@ -10,7 +10,9 @@ Sources (the pages this follows; cited below by tag):
 * [ZS]  "DeepSeek V3.2: How Far Can Open Models Go If You Actually Try?"
         (zeroshot.it.com) -- section 3.1: the indexer score equation (eq. I),
         the selection-then-attention equation (eq. U) and the MQA-mode note;
-        section 3.4: short prompts behave like dense masked attention.
+        section 3.3: Stage 1, the dense warm-up in which the indexer is trained
+        with a KL loss against the dense attention; section 3.4: short
+        prompts behave like dense masked attention.
 * [LD]  "DeepSeek-V3.2: Pushing the Frontier of Open Large Language Models"
         (papers.lunadong.com summary) -- System Modules (indexer scores the
         preceding tokens; a top-k operation selects; MLA in MQA mode attends),
@@ -38,6 +40,9 @@ Every step is the plain definition:
    index key into the (paged) key cache.
 7. the dense MLA that DSA is measured against [ZS 3.4]: eq. U's attention
    over every candidate s = 0..p, no indexer and no selection.
+8. the indexer's warm-up objective [ZS 3.3 Stage 1; LD Objective Functions]: the KL divergence
+   between the head-aggregated, L1-normalised dense attention distribution
+   and softmax(I), and its gradient into q_I, w and k_I.
 
 Readings where the pages are silent are stated at each function.
 """
@@ -410,3 +415,102 @@ def dense_forward(inp: OracleInputs, rows=None) -> dict:
     for i, t in enumerate(rows):
         out[i], lse[i] = dense_attention(inp, t)
     return {"rows": rows, "out": out, "lse": lse}
+
+
+# --------------------------------------------------------------------------
+# 8. the indexer's warm-up loss, L_I = sum_t KL(p_t || softmax(I_t)), and its
+#    gradient into the indexer's inputs  [ZS 3.3, Stage 1 (dense warm-up);
+#    LD Modeling, Objective Functions]
+# --------------------------------------------------------------------------
+
+def attention_distribution(inp: OracleInputs, t: int) -> np.ndarray:
+    """p_t over the candidates s = 0..pos_t: the dense attention probabilities of
+    every head, summed over heads and L1-normalised.
+
+    Reading of the target [LD Objective Functions]: the main attention's
+    softmax weights (eq. U over every candidate) are added over the H heads
+    and divided by their total, which is H; float64 [n_t].
+    """
+    n = candidate_count(inp, t)
+    if n == 0:
+        return np.zeros(0)
+    b = sequence_of(inp, t)
+    q_t = _finite(decode(inp.q[t], inp.mla_dtype), "MLA query")
+    rows = _finite(decode(gather_rows(inp.kv_cache, inp, b, np.arange(n)), inp.mla_dtype), "latent row")
+    z = inp.sm_scale * (q_t @ rows.T)                          # [H, n]
+    a = np.exp(z - z.max(axis=1, keepdims=True))
+    a /= a.sum(axis=1, keepdims=True)                          # softmax per head
+    agg = a.sum(axis=0)                                        # aggregate over heads
+    return agg / agg.sum()                                     # L1 normalisation
+
+
+def kl_rows(scores: np.ndarray, p: np.ndarray) -> tuple:
+    """KL(p || softmax(I)) of one query and its gradient with respect to I.
+
+    scores I [n] and target p [n] (sums to 1).  loss = sum_s p_s (log p_s -
+    log softmax(I)_s), a term with p_s = 0 contributing 0; dloss/dI =
+    softmax(I) - p (p does not depend on I).  Returns (loss, grad [n]).
+    """
+    I = np.asarray(scores, dtype=np.float64)
+    p = np.asarray(p, dtype=np.float64)
+    if I.shape[0] == 0:
+        return 0.0, np.zeros(0)
+    m = I.max()
+    lse = m + math.log(np.exp(I - m).sum())
+    log_q = I - lse
+    nz = p > 0
+    loss = float(np.sum(p[nz] * (np.log(p[nz]) - log_q[nz])))
+    return loss, np.exp(log_q) - p
+
+
+def index_scores_backward(q_t: np.ndarray, w_t: np.ndarray, keys: np.ndarray, grad: np.ndarray) -> tuple:
+    """Gradient of eq. I for one query, given dL/dI(s) for its candidates.
+
+    With x_js = q_j . k_s and I_s = sum_j w_j ReLU(x_js):
+      dL/dw_j = sum_s g_s ReLU(x_js)
+      dL/dq_j = sum_s g_s w_j [x_js > 0] k_s
+      dL/dk_s = sum_j g_s w_j [x_js > 0] q_j
+    Reading: ReLU'(0) = 0.  Returns (dq [H_I, d_I], dw [H_I], dk [n, d_I]).
+    """
+    x = q_t @ keys.T                                           # [H_I, n]
+    on = x > 0
+    gm = grad[None, :] * w_t[:, None] * on                     # [H_I, n]
+    dw = (grad[None, :] * np.maximum(x, 0.0)).sum(axis=1)
+    dq = gm @ keys
+    dk = gm.T @ q_t
+    return dq, dw, dk
+
+
+def indexer_kl_loss(inp: OracleInputs, rows=None) -> dict:
+    """Loss and gradients of the warm-up objective over query rows ``rows``.
+
+    Per query: I_t from eq. I over its candidates, p_t from
+    attention_distribution, (loss_t, g_t) from kl_rows, then
+    index_scores_backward.  Key gradients of every query are added into
+    ``dk``, shaped like the key cache (one row per cache slot).  Returns
+    ``loss`` [R] (the per-query terms; L_I is their sum), ``grad_scores``
+    (list of g_t), ``dq`` [R, H_I, d_I], ``dw`` [R, H_I] and ``dk``.
+    """
+    rows = list(range(inp.num_q)) if rows is None else [int(r) for r in rows]
+    H_I, d_I = inp.q_idx.shape[1], inp.q_idx.shape[2]
+    loss = np.zeros(len(rows))
+    dq = np.zeros((len(rows), H_I, d_I))
+    dw = np.zeros((len(rows), H_I))
+    dk = np.zeros(inp.k_cache.shape[:-1] + (d_I,))
+    grads = []
+    for i, t in enumerate(rows):
+        q_t, w_t, keys = query_index_operands(inp, t)
+        I = index_scores(q_t, w_t, keys)
+        p = attention_distribution(inp, t)
+        loss[i], g = kl_rows(I, p)
+        grads.append(g)
+        dq[i], dw[i], dk_t = index_scores_backward(q_t, w_t, keys, g)
+        b = sequence_of(inp, t)
+        n = candidate_count(inp, t)
+        pos = np.arange(n)
+        if inp.block_table is None:
+            dk[b, pos] += dk_t
+        else:
+            blocks = np.asarray(inp.block_table[b], dtype=np.int64)[pos // inp.block_size]
+            np.add.at(dk, (blocks, pos % inp.block_size), dk_t)
+    return {"rows": rows, "loss": loss, "grad_scores": grads, "dq": dq, "dw": dw, "dk": dk}

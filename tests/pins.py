@@ -440,6 +440,179 @@ def pin_dense_equals_short_prompt_dsa(o):
     _close(a["lse"], d["lse"], 1e-12, "short-prompt lse")
 
 
+# ---------------------------------------------------------------- indexer warm-up loss
+
+def pin_attention_distribution_torch(o):
+    """p_t equals the head mean of torch's float64 softmax over each query's causal
+    candidates (ragged paged decode, NaN poison past each length), and sums to 1."""
+    wl = small_workload(mode="decode", num_seqs=3, length=30, k=5, H=3, D=12, Dv=8)
+    oi = to_oracle(generate(wl, "cpu", lengths=[7, 30, 18]))
+    for t in range(3):
+        n = int(oi.q_pos[t]) + 1
+        q = torch.from_numpy(oi.q[t].astype(np.float64))
+        kv = torch.from_numpy(oi.kv_cache[t, :n].astype(np.float64))
+        want = torch.softmax(oi.sm_scale * (q @ kv.T), dim=-1).mean(dim=0).numpy()
+        got = o.attention_distribution(oi, t)
+        _close(got, want, 1e-12, f"query {t} distribution")
+        assert abs(got.sum() - 1.0) < 1e-12
+
+
+def pin_kl_rows_torch(o):
+    """kl_rows equals torch's kl_div(log_softmax(I), p, sum) and its gradient equals
+    torch autograd's, zeros in p included."""
+    rng = np.random.default_rng(21)
+    for n in (1, 2, 9, 40):
+        I = rng.normal(size=n) * 3
+        p = rng.random(n) ** 3
+        p[rng.random(n) < 0.3] = 0.0
+        if p.sum() == 0:
+            p[0] = 1.0
+        p /= p.sum()
+        It = torch.tensor(I, dtype=torch.float64, requires_grad=True)
+        lt = torch.nn.functional.kl_div(torch.log_softmax(It, dim=0), torch.tensor(p), reduction="sum")
+        lt.backward()
+        loss, g = o.kl_rows(I, p)
+        _close(loss, lt.item(), 1e-12, f"n={n} loss")
+        _close(g, It.grad.numpy(), 1e-12, f"n={n} grad")
+
+
+def pin_kl_rows_zero_at_match(o):
+    """I = log p + c (any c) is a perfect match: loss 0 and gradient 0."""
+    rng = np.random.default_rng(22)
+    p = rng.random(12)
+    p /= p.sum()
+    for c in (0.0, 5.0, -40.0):
+        loss, g = o.kl_rows(np.log(p) + c, p)
+        assert abs(loss) < 1e-12 and np.max(np.abs(g)) < 1e-12, c
+
+
+def pin_index_scores_backward_autograd(o):
+    """dq, dw, dk of eq. I equal torch autograd of sum_s g_s I_s (float64, mixed-sign
+    weights)."""
+    rng = np.random.default_rng(23)
+    for H_I, d_I, n in ((1, 3, 4), (3, 5, 7), (4, 8, 33)):
+        q = rng.normal(size=(H_I, d_I))
+        w = rng.normal(size=H_I)
+        k = rng.normal(size=(n, d_I))
+        g = rng.normal(size=n)
+        qt, wt, kt = (torch.tensor(x, requires_grad=True) for x in (q, w, k))
+        I = (wt[:, None] * torch.relu(qt @ kt.T)).sum(dim=0)
+        (I * torch.tensor(g)).sum().backward()
+        dq, dw, dk = o.index_scores_backward(q, w, k, g)
+        _close(dq, qt.grad.numpy(), 1e-12, "dq")
+        _close(dw, wt.grad.numpy(), 1e-12, "dw")
+        _close(dk, kt.grad.numpy(), 1e-12, "dk")
+
+
+def _kl_workload():
+    wl = small_workload(mode="prefill", length=14, k=4, H_I=3, d_I=8, H=2, D=12, Dv=8, w_high=1.0)
+    return to_oracle(generate(wl, "cpu"))
+
+
+def pin_indexer_kl_loss_finite_differences(o):
+    """Central differences of the summed loss (inputs moved by 2^-10, exact in
+    float32) match the analytic gradients into w, q_I and k_I; q/k entries are
+    used only where no q.k term lies within reach of the ReLU kink."""
+    oi = _kl_workload()
+    res = o.indexer_kl_loss(oi)
+    h = 2.0 ** -10
+
+    def total(field, idx, delta):
+        arr = getattr(oi, field)
+        old = arr[idx]
+        arr[idx] = np.float32(old + delta)
+        try:
+            return float(o.indexer_kl_loss(oi)["loss"].sum())
+        finally:
+            arr[idx] = old
+
+    def fd(field, idx):
+        return (total(field, idx, h) - total(field, idx, -h)) / (2 * h)
+
+    rng = np.random.default_rng(24)
+    for _ in range(6):                                     # w: eq. I is linear in w
+        t, j = int(rng.integers(0, 14)), int(rng.integers(0, 3))
+        _close(fd("w", (t, j)), res["dw"][t, j], 1e-5, f"dw[{t},{j}]")
+    q = oi.q_idx.astype(np.float64)
+    k = oi.k_cache[0].astype(np.float64)
+    checked = 0
+    for t in range(3, 14):
+        for j in range(3):
+            x = q[t, j] @ k[: t + 1].T
+            if np.min(np.abs(x)) < 0.05:
+                continue
+            d = int(rng.integers(0, 8))
+            _close(fd("q_idx", (t, j, d)), res["dq"][t, j, d], 1e-5, f"dq[{t},{j},{d}]")
+            checked += 1
+            break
+    assert checked >= 4
+    checked = 0
+    for s in range(14):
+        x = q[s:, :, :] @ k[s]
+        if np.min(np.abs(x)) < 0.05:
+            continue
+        d = int(rng.integers(0, 8))
+        _close(fd("k_cache", (0, s, d)), res["dk"][0, s, d], 1e-5, f"dk[{s},{d}]")
+        checked += 1
+    assert checked >= 4
+
+
+def pin_indexer_kl_loss_autograd(o):
+    """The whole objective against torch autograd in float64: p from torch's softmax
+    over the latent rows, the loss from torch's kl_div, gradients by autograd."""
+    oi = _kl_workload()
+    res = o.indexer_kl_loss(oi)
+    T = oi.num_q
+    q = torch.tensor(oi.q_idx.astype(np.float64), requires_grad=True)
+    w = torch.tensor(oi.w.astype(np.float64), requires_grad=True)
+    k = torch.tensor(oi.k_cache[0].astype(np.float64), requires_grad=True)
+    qm = torch.tensor(oi.q.astype(np.float64))
+    kv = torch.tensor(oi.kv_cache[0].astype(np.float64))
+    total = 0.0
+    for t in range(T):
+        n = t + 1
+        p = torch.softmax(oi.sm_scale * (qm[t] @ kv[:n].T), dim=-1).mean(dim=0)
+        I = (w[t][:, None] * torch.relu(q[t] @ k[:n].T)).sum(dim=0)
+        lt = torch.nn.functional.kl_div(torch.log_softmax(I, dim=0), p, reduction="sum")
+        _close(res["loss"][t], lt.item(), 1e-12, f"loss[{t}]")
+        total = total + lt
+    total.backward()
+    _close(res["dq"], q.grad.numpy(), 1e-11, "dq")
+    _close(res["dw"], w.grad.numpy(), 1e-11, "dw")
+    _close(res["dk"][0, :T], k.grad.numpy(), 1e-11, "dk")
+
+
+def pin_indexer_kl_paged_poison(o):
+    """Ragged paged decode with NaN poison past each length: finite results, and the
+    key gradients land only in slots the block table names for valid positions."""
+    rng = np.random.default_rng(25)
+    wl = small_workload(mode="decode", num_seqs=3, length=29, k=6)
+    oi = to_oracle(generate(wl, "cpu", lengths=[29, 13, 21]))
+    ref = o.indexer_kl_loss(oi)
+    bs = 4
+    B, L = oi.kv_cache.shape[:2]
+    nb = (L + bs - 1) // bs
+    table = rng.permutation(B * nb).reshape(B, nb)
+    kc = np.full((B * nb, bs) + oi.k_cache.shape[2:], np.nan, oi.k_cache.dtype)
+    vc = np.full((B * nb, bs) + oi.kv_cache.shape[2:], np.nan, oi.kv_cache.dtype)
+    for b in range(B):
+        for s in range(L):
+            kc[table[b, s // bs], s % bs] = oi.k_cache[b, s]
+            vc[table[b, s // bs], s % bs] = oi.kv_cache[b, s]
+    oi.block_table, oi.block_size, oi.k_cache, oi.kv_cache = table, bs, kc, vc
+    res = o.indexer_kl_loss(oi)
+    for key in ("loss", "dq", "dw"):
+        assert np.all(np.isfinite(res[key])), key
+        _close(res[key], ref[key], 1e-12, key)
+    for b, n in enumerate((29, 13, 21)):
+        for s in range(L):
+            got = res["dk"][table[b, s // bs], s % bs]
+            if s < n:
+                _close(got, ref["dk"][b, s], 1e-12, f"dk seq {b} pos {s}")
+            else:
+                assert np.all(got == 0), f"dk written past the length: seq {b} pos {s}"
+
+
 # ---------------------------------------------------------------- fp8 quantisation and append
 
 def pin_e4m3_encode_roundtrip(o):

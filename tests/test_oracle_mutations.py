@@ -148,6 +148,52 @@ def _dense_reversed_table(inp, t):
         inp.block_table = saved
 
 
+def _dist_unnormalised(inp, t):
+    return od.__dict__["_orig_dist"](inp, t) * inp.q.shape[1]
+
+
+def _dist_first_head(inp, t):
+    n = od.candidate_count(inp, t)
+    b = od.sequence_of(inp, t)
+    q_t = od.decode(inp.q[t], inp.mla_dtype)[:1]
+    rows = od.decode(od.gather_rows(inp.kv_cache, inp, b, np.arange(n)), inp.mla_dtype)
+    z = inp.sm_scale * (q_t @ rows.T)
+    a = np.exp(z - z.max(axis=1, keepdims=True))
+    return (a / a.sum(axis=1, keepdims=True))[0]
+
+
+def _kl_grad_sign(scores, p):
+    loss, g = od.__dict__["_orig_kl"](scores, p)
+    return loss, -g
+
+
+def _kl_reversed(scores, p):
+    # KL(softmax(I) || p)
+    I = np.asarray(scores, float)
+    q = np.exp(I - I.max())
+    q /= q.sum()
+    p = np.asarray(p, float)
+    loss = float(np.sum(q * (np.log(q) - np.log(np.maximum(p, 1e-300)))))
+    return loss, od.__dict__["_orig_kl"](scores, p)[1]
+
+
+def _bwd_relu_value(q, w, keys, grad):
+    x = q @ keys.T
+    gm = grad[None, :] * w[:, None] * np.maximum(x, 0.0)
+    return gm @ keys, (grad[None, :] * np.maximum(x, 0.0)).sum(axis=1), gm.T @ q
+
+
+def _bwd_dk_no_weight(q, w, keys, grad):
+    dq, dw, _ = od.__dict__["_orig_bwd"](q, w, keys, grad)
+    gm = grad[None, :] * (q @ keys.T > 0)
+    return dq, dw, gm.T @ q
+
+
+def _bwd_dw_unmasked(q, w, keys, grad):
+    dq, _, dk = od.__dict__["_orig_bwd"](q, w, keys, grad)
+    return dq, (grad[None, :] * (q @ keys.T)).sum(axis=1), dk
+
+
 MUTATIONS = {
     "indexer_no_relu": ("index_scores", _no_relu),
     "indexer_relu_after_weight": ("index_scores", _relu_after_weight),
@@ -172,6 +218,13 @@ MUTATIONS = {
     "dense_excludes_self": ("dense_attention", _dense_with(-1)),
     "dense_one_past_self": ("dense_attention", _dense_with(+1)),
     "dense_reversed_block_table": ("dense_attention", _dense_reversed_table),
+    "kl_target_not_normalised": ("attention_distribution", _dist_unnormalised),
+    "kl_target_first_head_only": ("attention_distribution", _dist_first_head),
+    "kl_gradient_sign_flipped": ("kl_rows", _kl_grad_sign),
+    "kl_direction_reversed": ("kl_rows", _kl_reversed),
+    "bwd_relu_value_as_mask": ("index_scores_backward", _bwd_relu_value),
+    "bwd_dk_without_weight": ("index_scores_backward", _bwd_dk_no_weight),
+    "bwd_dw_without_relu": ("index_scores_backward", _bwd_dw_unmasked),
 }
 
 
@@ -182,6 +235,9 @@ def test_mutation_is_caught(name, monkeypatch):
     monkeypatch.setattr(od, "_orig_query_index_operands", od.query_index_operands, raising=False)
     monkeypatch.setattr(od, "_orig_append", od.append_index_keys, raising=False)
     monkeypatch.setattr(od, "_orig_dense", od.dense_attention, raising=False)
+    monkeypatch.setattr(od, "_orig_dist", od.attention_distribution, raising=False)
+    monkeypatch.setattr(od, "_orig_kl", od.kl_rows, raising=False)
+    monkeypatch.setattr(od, "_orig_bwd", od.index_scores_backward, raising=False)
     monkeypatch.setattr(od, attr, repl)
     caught = []
     for pin in pins.ALL_PINS:
