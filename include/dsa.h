@@ -100,7 +100,8 @@ typedef enum dsa_op {
   DSA_OP_TOPK = 1,
   DSA_OP_SPARSE_MLA = 2,
   DSA_OP_FORWARD = 3,
-  DSA_OP_DENSE_MLA = 4
+  DSA_OP_DENSE_MLA = 4,
+  DSA_OP_ATTENTION_PROBS = 5
 } dsa_op;
 
 /* Where each query sits and which cache rows it may read (host struct). */
@@ -220,6 +221,33 @@ int dsa_forward(const dsa_seqs *seqs, const dsa_dims *dims, const dsa_forward_ar
 int dsa_dense_mla(const dsa_seqs *seqs, const dsa_dims *dims, float sm_scale, const void *q,
                   const void *kv_cache, void *out, float *lse, void *ws, size_t ws_bytes,
                   hipStream_t stream);
+
+/* The indexer's warm-up target [ZS 3.3, Stage 1: the main attention stays
+ * dense and the indexer learns its distribution; LD Modeling, Objective
+ * Functions: the dense attention aggregated over heads, L1-normalised].
+ * For every query t and candidate s = 0..q_pos[t]:
+ *   probs[t, s] = (1/H) sum_h softmax_s(sm_scale * q[t,h,:] . c(s))
+ * (each head's weights sum to 1, so dividing the head sum by H is its L1
+ * normalisation); probs[t, s] = 0 for q_pos[t] < s < ld_probs.  lse, if not
+ * NULL, receives each head's log-sum-exp [T, H] (as dsa_dense_mla's).  Two
+ * passes of the attention kernel over every candidate: the log-sum-exp, then
+ * the weights; bf16 operands, fp32 arithmetic and output.  ld_probs >=
+ * max_ctx.  Supported: bf16 H = 128, D = 576, Dv = 512.
+ * Workspace: dsa_workspace_size(DSA_OP_ATTENTION_PROBS, ...). */
+int dsa_attention_probs(const dsa_seqs *seqs, const dsa_dims *dims, float sm_scale, const void *q,
+                        const void *kv_cache, float *probs, int64_t ld_probs, float *lse, void *ws,
+                        size_t ws_bytes, hipStream_t stream);
+
+/* One KL term of the warm-up objective per query [ZS 3.3:
+ * L_I = sum_t KL(p_t || softmax(I_t))], and its gradient with respect to the
+ * scores.  scores [T, ld] holds I (e.g. from dsa_index_scores) on entry and
+ * dL/dI = softmax(I_t) - p_t on return (0 for s > q_pos[t]); probs [T, ld]
+ * holds p (e.g. from dsa_attention_probs).  loss[t] = sum_s p (log p - log
+ * softmax(I)_s) over the candidates with p > 0 (L_I is the sum over t).  A
+ * score of -inf (absent key) has softmax weight 0.  fp32; deterministic.  No
+ * workspace. */
+int dsa_indexer_kl(const dsa_seqs *seqs, float *scores, const float *probs, int64_t ld, float *loss,
+                   hipStream_t stream);
 
 /* Upstream of step 1: per-row fp8 quantisation for an indexer that "runs in
  * FP8" [ZS 3.1; BT (1)].  The pages fix neither scale nor rounding; the

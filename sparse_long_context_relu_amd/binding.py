@@ -19,11 +19,12 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "dsa.h")
 
 F32, BF16, FP8_E4M3FN = 0, 1, 2
 PREFILL, DECODE = 0, 1
-OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_MLA, OP_FORWARD, OP_DENSE_MLA = 0, 1, 2, 3, 4
+OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_MLA, OP_FORWARD, OP_DENSE_MLA, OP_ATTENTION_PROBS = 0, 1, 2, 3, 4, 5
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
 EXPORTS = ("dsa_workspace_size", "dsa_index_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward",
-           "dsa_dense_mla", "dsa_quantize_fp8", "dsa_append_index_keys", "dsa_status_string")
+           "dsa_dense_mla", "dsa_attention_probs", "dsa_indexer_kl", "dsa_quantize_fp8", "dsa_append_index_keys",
+           "dsa_status_string")
 
 
 class DsaSeqs(ctypes.Structure):
@@ -72,6 +73,10 @@ def _load() -> ctypes.CDLL:
     lib.dsa_forward.restype = ctypes.c_int
     lib.dsa_dense_mla.argtypes = [sp, dp, ctypes.c_float, P, P, P, P, P, SZ, P]
     lib.dsa_dense_mla.restype = ctypes.c_int
+    lib.dsa_attention_probs.argtypes = [sp, dp, ctypes.c_float, P, P, P, I64, P, P, SZ, P]
+    lib.dsa_attention_probs.restype = ctypes.c_int
+    lib.dsa_indexer_kl.argtypes = [sp, P, P, I64, P, P]
+    lib.dsa_indexer_kl.restype = ctypes.c_int
     lib.dsa_quantize_fp8.argtypes = [I64, I32, I32, P, P, P, I32, P]
     lib.dsa_quantize_fp8.restype = ctypes.c_int
     lib.dsa_append_index_keys.argtypes = [sp, I32, I32, P, P, P, P]
@@ -226,6 +231,31 @@ def dense_mla(pb: Problem, sm_scale: float, q, kv_cache, out=None, lse=None, ws=
                            _ptr(kv_cache), _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream))
     _check(st, "dsa_dense_mla")
     return out, lse
+
+
+def attention_probs(pb: Problem, sm_scale: float, q, kv_cache, probs=None, ld: Optional[int] = None, lse=None,
+                    ws=None, stream=None):
+    """Head-aggregated dense attention distribution: (probs [T, ld] fp32, lse [T, H] fp32 or None)."""
+    ld = pb.seqs.max_ctx if ld is None else ld
+    if probs is None:
+        probs = torch.empty((pb.num_q, ld), dtype=torch.float32, device=q.device)
+    ws = _workspace(OP_ATTENTION_PROBS, pb, ws, q.device)
+    st = LIB.dsa_attention_probs(ctypes.byref(pb.seqs), ctypes.byref(pb.dims), float(sm_scale), _ptr(q),
+                                 _ptr(kv_cache), _ptr(probs), int(probs.stride(0)), _ptr(lse), _ptr(ws), _nbytes(ws),
+                                 _stream(stream))
+    _check(st, "dsa_attention_probs")
+    return probs, lse
+
+
+def indexer_kl(pb: Problem, scores: torch.Tensor, probs: torch.Tensor, loss=None, stream=None):
+    """KL rows: scores (I) is overwritten by dL/dI; returns loss [T] fp32."""
+    assert scores.stride(0) == probs.stride(0) and scores.stride(1) == 1 and probs.stride(1) == 1
+    if loss is None:
+        loss = torch.empty(pb.num_q, dtype=torch.float32, device=scores.device)
+    st = LIB.dsa_indexer_kl(ctypes.byref(pb.seqs), _ptr(scores), _ptr(probs), int(scores.stride(0)), _ptr(loss),
+                            _stream(stream))
+    _check(st, "dsa_indexer_kl")
+    return loss
 
 
 def forward(pb: Problem, q_idx, q_scale, w, k_cache, k_scale, q, kv_cache, sm_scale: float, out=None,

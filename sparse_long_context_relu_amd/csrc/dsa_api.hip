@@ -180,6 +180,35 @@ DenseLayout dense_layout(const dsa_seqs *s, const dsa_dims *d) {
   return L;
 }
 
+// Warm-up target: per-head log-sum-exp of every query (kept in the workspace
+// unless the caller asks for it), then the head-aggregated weights.  The lse
+// pass's split partials are fp32 (max, sum) pairs; queries run in chunks
+// whose partials fit kDenseWsBudget.
+struct ProbsLayout {
+  int chunk, n_split;
+  long long off_part, total;
+};
+
+ProbsLayout probs_layout(const dsa_seqs *s, const dsa_dims *d) {
+  ProbsLayout L;
+  const int T = s->num_q;
+  L.n_split = mla_dense_splits(T, s->max_ctx);
+  const long long per_row = L.n_split > 1 ? (long long)L.n_split * d->heads * 8 : 0;
+  L.chunk = T;
+  if (per_row > 0 && (long long)T * per_row > kDenseWsBudget) {
+    const long long c = kDenseWsBudget / per_row;
+    L.chunk = c < 1 ? 1 : (int)c;
+  }
+  L.off_part = align256((long long)T * d->heads * 4);
+  L.total = L.off_part + align256((long long)L.chunk * per_row);
+  return L;
+}
+
+int check_probs_dims(const dsa_seqs *s, const dsa_dims *d) {
+  if (int e = check_dense_dims(s, d)) return e;
+  return d->mla_dtype == DSA_BF16 ? DSA_OK : DSA_ERR_UNSUPPORTED;
+}
+
 int check_ws(size_t need, const void *ws, size_t ws_bytes) {
   if (need == 0) return DSA_OK;
   if (ws == nullptr || ws_bytes < need) return DSA_ERR_WORKSPACE;
@@ -249,6 +278,9 @@ MlaArgs mla_args(const dsa_seqs *s, const dsa_dims *d, float sm_scale, const voi
   a.n_split = mla_split_count(d, rows);
   a.part = ws;
   a.dense = 0;
+  a.mode = 0;
+  a.probs = nullptr;
+  a.ld = 0;
   return a;
 }
 
@@ -278,6 +310,9 @@ DSA_EXPORT size_t dsa_workspace_size(int op, const dsa_seqs *seqs, const dsa_dim
     case DSA_OP_DENSE_MLA:
       if (check_dense_dims(seqs, dims) != DSA_OK) return 0;
       return (size_t)dense_layout(seqs, dims).total;
+    case DSA_OP_ATTENTION_PROBS:
+      if (check_probs_dims(seqs, dims) != DSA_OK) return 0;
+      return (size_t)probs_layout(seqs, dims).total;
     default:
       return 0;
   }
@@ -411,6 +446,52 @@ DSA_EXPORT int dsa_dense_mla(const dsa_seqs *seqs, const dsa_dims *dims, float s
     if (launch_sparse_mla(a, stream) != hipSuccess) return DSA_ERR_HIP;
   }
   return DSA_OK;
+}
+
+DSA_EXPORT int dsa_attention_probs(const dsa_seqs *seqs, const dsa_dims *dims, float sm_scale, const void *q,
+                                   const void *kv_cache, float *probs, int64_t ld_probs, float *lse, void *ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  if (int e = check_seqs(seqs)) return e;
+  if (int e = check_probs_dims(seqs, dims)) return e;
+  if (seqs->num_q == 0) return DSA_OK;
+  if (q == nullptr || kv_cache == nullptr || probs == nullptr || ld_probs < seqs->max_ctx) return DSA_ERR_INVALID_ARG;
+  if (!(sm_scale == sm_scale)) return DSA_ERR_INVALID_ARG;
+  const ProbsLayout L = probs_layout(seqs, dims);
+  if (int e = check_ws((size_t)L.total, ws, ws_bytes)) return e;
+  uint8_t *base = reinterpret_cast<uint8_t *>(ws);
+  float *lse_buf = lse != nullptr ? lse : reinterpret_cast<float *>(base);
+  void *part = base + L.off_part;
+  const int T = seqs->num_q;
+  for (int c0 = 0; c0 < T; c0 += L.chunk) {
+    const int rows = c0 + L.chunk < T ? L.chunk : T - c0;
+    MlaArgs a = mla_args(seqs, dims, sm_scale, q, kv_cache, nullptr, nullptr, lse_buf, part, c0, rows);
+    a.dense = 1;
+    a.k = seqs->max_ctx;
+    a.n_split = L.n_split;
+    a.mode = 1;
+    if (launch_sparse_mla(a, stream) != hipSuccess) return DSA_ERR_HIP;
+    a.mode = 2;
+    a.probs = probs + (long long)c0 * ld_probs;
+    a.ld = ld_probs;
+    if (launch_sparse_mla(a, stream) != hipSuccess) return DSA_ERR_HIP;
+  }
+  return DSA_OK;
+}
+
+DSA_EXPORT int dsa_indexer_kl(const dsa_seqs *seqs, float *scores, const float *probs, int64_t ld, float *loss,
+                              hipStream_t stream) {
+  if (int e = check_seqs(seqs)) return e;
+  if (seqs->num_q == 0) return DSA_OK;
+  if (scores == nullptr || probs == nullptr || loss == nullptr || ld < seqs->max_ctx) return DSA_ERR_INVALID_ARG;
+  KlArgs a;
+  a.sv = view(seqs);
+  a.q_begin = 0;
+  a.rows = seqs->num_q;
+  a.scores = scores;
+  a.probs = probs;
+  a.ld = ld;
+  a.loss = loss;
+  return hip_status(launch_indexer_kl(a, stream));
 }
 
 DSA_EXPORT int dsa_quantize_fp8(int64_t rows, int32_t len, int32_t src_dtype, const void *src, void *dst,

@@ -57,6 +57,13 @@ struct MlaArgs {
   // j < n_t), for j < k; idx is not read.  k then only sets how the lists are
   // split.  A split with no position writes no partial.
   int dense;
+  // 0: attention (out, lse); 1: lse only (bf16, dense lists; split partials are
+  // fp32 (max, sum) pairs [rows, n_split, H, 2] in part); 2: the softmax
+  // weights given lse (input), summed over heads and divided by H, written to
+  // probs[r * ld + position] (bf16, dense lists; 0 past the last candidate)
+  int mode;
+  float *probs;
+  long long ld;
   void *out;
   float *lse;
   int q_begin, rows;
@@ -100,6 +107,16 @@ struct AppendArgs {
   float *scale;      // key scales, one per cache row
 };
 
+// Per-query KL rows of the indexer's warm-up objective.
+struct KlArgs {
+  SeqView sv;
+  int q_begin, rows;
+  float *scores;        // [rows, ld]: I in, dL/dI out (0 past the last candidate)
+  const float *probs;   // [rows, ld]: the target distribution
+  long long ld;
+  float *loss;          // [T]: indexed by query
+};
+
 struct TopkLayout {
   int slices, slice_len, sel_seg;
   long long row_words;
@@ -118,6 +135,7 @@ hipError_t launch_topk_zero(const TopkArgs &a, hipStream_t s);    // zero the pe
 hipError_t launch_topk_select(const TopkArgs &a, hipStream_t s);  // collect + select (hist1 ready)
 hipError_t launch_topk_all(const TopkArgs &a, hipStream_t s);     // every candidate (all n_t <= k)
 hipError_t launch_sparse_mla(const MlaArgs &a, hipStream_t s);     // also the dense lists
+hipError_t launch_indexer_kl(const KlArgs &a, hipStream_t s);
 hipError_t launch_fp8_quantize(const QuantArgs &a, hipStream_t s);
 hipError_t launch_fp8_append(const AppendArgs &a, hipStream_t s);
 

@@ -134,14 +134,33 @@ __device__ __forceinline__ void issue_tile(uint32_t tile, const uint8_t *kv, con
   for (int j = 0; j < kWaveLoads; ++j) tile_load(t, j, tile, wv);
 }
 
-// Logits, online softmax and value product for the tile at LDS address `tile`.
+// Sum over the 16 lanes of a row of the wave (the 16 heads of a lane group),
+// in every lane of the row: two quad swaps, then the half-row and row mirrors.
+__device__ __forceinline__ float sum16(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+  return x;
+}
+
+// What a pass over the rows computes.
+constexpr int kModeAttn = 0;    // softmax attention: output rows and lse
+constexpr int kModeLse = 1;     // the logits' log-sum-exp per head only
+constexpr int kModeProbs = 2;   // softmax weights given the lse, summed over the heads
+
+// Logits, then per mode: online softmax and value product (attention), online
+// softmax only (lse), or the normalised weights summed over this wave's heads
+// into `psum` (probs; 32 rows, needs the head's lse in base 2 as `lse2`).
 //
 // The operand reads are issued ahead of the MFMAs that consume them (fixed
 // instruction groups below), so several LDS reads are in flight while the
 // matrix core works.
+template <int kMode>
 __device__ __forceinline__ void consume_tile(uint32_t tile, const int *slots, int j0, const bf16x8 (&qb)[kKs],
                                              f32x4 (&acc)[kDb], float &m_run, float &l_run, float scale2,
-                                             uint32_t qk_off, uint32_t pv_even, uint32_t pv_odd, int g) {
+                                             uint32_t qk_off, uint32_t pv_even, uint32_t pv_odd, int g,
+                                             float lse2, float *prow) {
   // ---- S^T for 32 rows x this wave's 16 heads.  The 36 operand reads go in
   // batches of kBatch, each batch issued before the MFMAs of the previous one
   // (scheduling barriers keep the compiler from sinking the reads to their uses).
@@ -178,6 +197,22 @@ __device__ __forceinline__ void consume_tile(uint32_t tile, const int *slots, in
   // Row validity of the tile as a wave-uniform mask (bit j: row j present).
   const uint32_t rowmask = (uint32_t)__ballot(lane < kR && row_slot >= 0);
   const uint32_t mine = rowmask >> (4 * g);     // bit v: row 4g+v; bit 16+v: row 16+4g+v
+  if constexpr (kMode == kModeProbs) {
+    // weight of each present row for this lane's head, summed over the 16 heads
+    float e[8];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        e[rb * 4 + v] = sum16(((mine >> (16 * rb + v)) & 1u) ? __builtin_amdgcn_exp2f(st[rb][v] * scale2 - lse2) : 0.f);
+    // lane with column c < 8 keeps row 16 (c / 4) + 4 g + c % 4
+    const int c = lane & 15;
+    float mine_e = e[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mine_e = c == i ? e[i] : mine_e;
+    if (c < 8) prow[16 * (c >> 2) + 4 * g + (c & 3)] = mine_e;
+    return;
+  }
   float mx = neg_inf();
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
@@ -193,10 +228,12 @@ __device__ __forceinline__ void consume_tile(uint32_t tile, const int *slots, in
     const float m_new = fmaxf(m_run, mx);
     const float alpha = m_run == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
     l_run *= alpha;
+    if constexpr (kMode == kModeAttn) {
 #pragma unroll
-    for (int db = 0; db < kDb; ++db)
+      for (int db = 0; db < kDb; ++db)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[db][v] *= alpha;
+        for (int v = 0; v < 4; ++v) acc[db][v] *= alpha;
+    }
     m_run = m_new;
   }
   // exponent base 0 while the head has seen nothing: -inf - 0 stays -inf (weight 0)
@@ -212,6 +249,7 @@ __device__ __forceinline__ void consume_tile(uint32_t tile, const int *slots, in
       pb[rb * 4 + v] = (__bf16)pv;
     }
   l_run += psum;
+  if constexpr (kMode == kModeLse) return;
   // ---- O^T += V^T . P^T.  k-slots 0..3 = tile rows 4g+e, 4..7 = rows 16+4g+e (e = 0..3),
   // matching the rows this lane holds in P^T.  Lane 4e+c of group g points the
   // transpose read at row 4g+e (resp. 16+4g+e), dims d0+4c..d0+4c+3, and receives
@@ -235,10 +273,13 @@ __device__ __forceinline__ void consume_tile(uint32_t tile, const int *slots, in
   __builtin_amdgcn_sched_group_barrier(0x008, kAheadV, 1);
 }
 
+template <int kMode>
 __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
   __shared__ uint4 tiles[kBufs][kTileBufChunks];
   __shared__ int slots[kMaxSplitRows + 4 * kR];
   __shared__ int fallback;
+  // probs: each wave's head sums of the last two tiles' rows
+  __shared__ float psums[kMode == kModeProbs ? 2 : 1][kMode == kModeProbs ? kWaves : 1][kR];
 
   int sp, r;
   mla_block(a, sp, r);
@@ -251,9 +292,16 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
   int i1 = i0 + len < a.k ? i0 + len : a.k;
   if (a.dense && i1 > n) i1 = n;              // dense lists end at the last candidate
   const int rows = i1 > i0 ? i1 - i0 : 0;
+  if constexpr (kMode == kModeProbs) {
+    // positions of this split past the query's last candidate (and, for the
+    // last split, up to the row's end) hold 0
+    float *prow = a.probs + (long long)r * a.ld;
+    const long long z0 = i0 + rows, z1 = sp + 1 == a.n_split ? a.ld : (i0 + len < a.ld ? i0 + len : a.ld);
+    for (long long s = z0 + threadIdx.x; s < z1; s += kThreads) prow[s] = 0.f;
+  }
   // A dense split past the last candidate has nothing to merge; the combine
   // reads only the splits that hold a position.
-  if (a.dense && rows == 0 && a.n_split > 1) return;
+  if (a.dense && rows == 0 && (a.n_split > 1 || kMode == kModeProbs)) return;
   const int ntiles = (rows + kR - 1) / kR;
 
   const int lane = lane_id();
@@ -326,6 +374,19 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
   const uint32_t pv_odd = pv_row + ((2 + (vc >> 1)) ^ g) * 16;
   const uint32_t tile_lds = lds_addr(&tiles[0][0]);
   constexpr uint32_t kTileBytes = kTileBufChunks * 16;
+  // probs: this lane's head's log-sum-exp in base 2
+  const float lse2 = kMode == kModeProbs ? a.lse[(long long)t * kH + wv * 16 + col] * kLog2e : 0.f;
+  // probs: the normalised weights of tile tt's rows, summed over every head in a
+  // fixed order (wave 0, after the barrier that follows the tile)
+  auto write_probs = [&](int tt) {
+    if (lane < kR) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) v += psums[tt & 1][w][lane];
+      const int j = tt * kR + lane;
+      if (j < rows) a.probs[(long long)r * a.ld + i0 + j] = v * (1.f / kH);
+    }
+  };
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   lds_barrier();
   const int fb = fallback;
@@ -342,23 +403,46 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
       // This wave's loads of tile tt have landed once at most the loads of tile
       // tt+1 are outstanding; the barrier then covers every wave's, and also
       // orders every wave's reads of tile tt-1 before its buffer is refilled.
+      // (probs: the head sums of tile tt-1 written to LDS are complete as well)
+      constexpr int kLgkm = kMode == kModeProbs ? 0x0F00 : 0;
       if (tt + 1 < ntiles)
-        __builtin_amdgcn_s_waitcnt(wait_vm(kWaveLoads));
+        __builtin_amdgcn_s_waitcnt(wait_vm(kWaveLoads) & ~kLgkm);
       else
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0 & ~kLgkm);
       lds_barrier();
       if (tt + 2 < ntiles) {
         const int nb = cur == 0 ? 2 : cur - 1;     // (tt + 2) % 3
         issue_tile(tile_lds + nb * kTileBytes, kv, slots, (tt + 2) * kR, fb, wv, lane);
       }
-      consume_tile(tile_lds + cur * kTileBytes, slots, tt * kR, qb, acc, m_run, l_run, scale2, qk_off, pv_even,
-                   pv_odd, g);
+      if (kMode == kModeProbs && tt > 0 && wv == 0) write_probs(tt - 1);
+      consume_tile<kMode>(tile_lds + cur * kTileBytes, slots, tt * kR, qb, acc, m_run, l_run, scale2, qk_off,
+                          pv_even, pv_odd, g, lse2, &psums[kMode == kModeProbs ? (tt & 1) : 0][wv][0]);
       cur = cur == 2 ? 0 : cur + 1;
     }
+  }
+  if constexpr (kMode == kModeProbs) {
+    if (fb >= 0 && ntiles > 0) {
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      lds_barrier();
+      if (wv == 0) write_probs(ntiles - 1);
+    } else {
+      for (int j = threadIdx.x; j < rows; j += kThreads) a.probs[(long long)r * a.ld + i0 + j] = 0.f;  // none present
+    }
+    return;
   }
 
   const int h = wv * 16 + col;
   const float l_tot = sum_over_rows(l_run);
+  if constexpr (kMode == kModeLse) {
+    if (g == 0) {
+      if (a.n_split == 1) {
+        if (a.lse != nullptr) a.lse[(long long)t * kH + h] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : neg_inf();
+      } else {
+        reinterpret_cast<float2 *>(a.part)[((long long)r * a.n_split + sp) * kH + h] = make_float2(m_run, l_tot);
+      }
+    }
+    return;
+  }
   // One split: the output row.  Several: this split's normalised output in
   // bf16 (a weighted mean of value rows, so within their range) and its
   // (max, sum), merged by the combine kernel.
@@ -451,6 +535,32 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
   pk.w = pack_bf16x2(o[6] * inv, o[7] * inv);
   *reinterpret_cast<uint4 *>(orow) = pk;
   if (lane == 0 && a.lse != nullptr) a.lse[(long long)t * kH + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : neg_inf();
+}
+
+// lse pass with several splits: one thread per (query, head) merges the
+// splits' (max, sum) pairs in split order.
+__global__ __launch_bounds__(256) void mla_lse_combine_kernel(MlaArgs a) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)a.rows * kH) return;
+  const int r = (int)(i / kH), h = (int)(i % kH);
+  const int t = a.q_begin + r;
+  const int ns = a.n_split;
+  int nm = ns;
+  if (a.dense) {
+    const int len = split_len(a.k, ns);
+    const int n = a.sv.candidates(t);
+    nm = n <= 0 ? 0 : (n + len - 1) / len;
+    if (nm > ns) nm = ns;
+  }
+  const float2 *ml = reinterpret_cast<const float2 *>(a.part) + (long long)r * ns * kH + h;
+  float M = neg_inf();
+  for (int s = 0; s < nm; ++s) M = fmaxf(M, ml[(long long)s * kH].x);
+  float L = 0.f;
+  for (int s = 0; s < nm; ++s) {
+    const float2 v = ml[(long long)s * kH];
+    if (v.x != neg_inf()) L += __builtin_amdgcn_exp2f(v.x - M) * v.y;
+  }
+  a.lse[(long long)t * kH + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : neg_inf();
 }
 
 // fp32, small shapes (H <= 16, D <= 128, k <= 1024): one workgroup per query,
@@ -556,8 +666,18 @@ hipError_t launch_sparse_mla(const MlaArgs &a, hipStream_t st) {
     hipLaunchKernelGGL(mla_f32_kernel, dim3(a.rows), dim3(256), lds, st, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(mla_bf16_kernel, dim3(a.n_split * a.rows), dim3(kThreads), 0, st, a);
-  if (a.n_split > 1) hipLaunchKernelGGL(mla_combine_kernel, dim3(kH / 4, a.rows), dim3(256), 0, st, a);
+  const dim3 grid(a.n_split * a.rows);
+  if (a.mode == kModeLse) {
+    hipLaunchKernelGGL(mla_bf16_kernel<kModeLse>, grid, dim3(kThreads), 0, st, a);
+    if (a.n_split > 1)
+      hipLaunchKernelGGL(mla_lse_combine_kernel, dim3((unsigned)(((long long)a.rows * kH + 255) / 256)), dim3(256), 0,
+                         st, a);
+  } else if (a.mode == kModeProbs) {
+    hipLaunchKernelGGL(mla_bf16_kernel<kModeProbs>, grid, dim3(kThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(mla_bf16_kernel<kModeAttn>, grid, dim3(kThreads), 0, st, a);
+    if (a.n_split > 1) hipLaunchKernelGGL(mla_combine_kernel, dim3(kH / 4, a.rows), dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 

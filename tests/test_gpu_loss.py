@@ -1,0 +1,108 @@
+"""The indexer's warm-up objective on the GPU, through the C ABI, against the oracle:
+the head-aggregated dense attention distribution, the per-query KL rows with
+their score gradient, and the gradients into q_I, w and k_I.
+
+Tolerances (the pages state none for this path; derived from the arithmetic):
+the target distribution is exp(z - lse) with fp32 logits of exact bf16
+products, so its entries agree to 2e-3 of the row's largest weight and in L1
+distance; the KL rows are fp32 over at most 2^18 terms, checked to 1e-4
+relative on the same fp32 inputs; gradients that pass through a bf16 MFMA
+operand (the masked, weighted score gradient) agree to 2e-2 relative RMS."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.helpers import to_oracle, to_oracle_rows
+from tests.test_gpu_ops import B, DEV, _say, big_dims
+from workloads import generate
+
+pytestmark = pytest.mark.gpu
+
+
+def _probs(inp, ld=None):
+    pb = B().problem_from_inputs(inp)
+    lse = torch.empty((inp.num_q, inp.wl.heads), dtype=torch.float32, device=DEV)
+    probs, _ = B().attention_probs(pb, inp.sm_scale, inp.q, inp.kv_cache, ld=ld, lse=lse)
+    torch.cuda.synchronize()
+    return probs, lse
+
+
+def check_distribution(got, want, what):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, what
+    if want.size == 0:
+        return
+    err = np.abs(got - want)
+    assert err.max() <= 2e-3 * want.max(), f"{what}: max err {err.max():.3e} vs max p {want.max():.3e}"
+    assert err.sum() <= 2e-3, f"{what}: L1 distance {err.sum():.3e}"
+
+
+PROB_CASES = [
+    ("decode_paged_ragged", big_dims(mode="decode", num_seqs=4, length=5000, k=64, paged=True), [5000, 1, 64, 2049], 1.0),
+    ("decode_sharp", big_dims(mode="decode", num_seqs=2, length=4100, k=64), [4100, 1300], 1200.0),
+    ("decode_long_128_splits", big_dims(mode="decode", num_seqs=1, length=140000, k=64), [140000], 1.0),
+    ("prefill_one_split", big_dims(mode="prefill", length=300, k=64), None, 1.0),
+    ("prefill_two_splits", big_dims(mode="prefill", length=2600, k=64, prefill_q_start=2450), None, 1.0),
+]
+
+
+@pytest.mark.parametrize("name,wl,lengths,qmul", PROB_CASES, ids=[c[0] for c in PROB_CASES])
+def test_attention_probs(name, wl, lengths, qmul):
+    _say("attention_probs", name)
+    inp = generate(wl, DEV, lengths=lengths)
+    if qmul != 1.0:
+        inp.q = (inp.q.float() * qmul).to(inp.q.dtype)
+    ld = inp.max_ctx + 37
+    probs, lse = _probs(inp, ld=ld)
+    pg, lg = probs.cpu().numpy(), lse.cpu().numpy()
+    oi = to_oracle(inp)
+    for t in range(inp.num_q):
+        n = int(inp.q_pos[t]) + 1
+        check_distribution(pg[t, :n], oracle.attention_distribution(oi, t), f"{name} row {t}")
+        assert np.all(pg[t, n:] == 0), f"{name} row {t}: entries past the candidates"
+        _, l_ref = oracle.dense_attention(oi, t)
+        assert np.max(np.abs(lg[t] - l_ref)) <= 2e-3, f"{name} row {t}: lse"
+
+
+def _kl_inputs(wl, lengths=None):
+    inp = generate(wl, DEV, lengths=lengths)
+    pb = B().problem_from_inputs(inp)
+    scores = B().index_scores(pb, inp.q_idx, inp.q_scale, inp.w, inp.k_cache, inp.k_scale)
+    probs, _ = _probs(inp, ld=scores.stride(0))
+    return inp, pb, scores, probs
+
+
+KL_CASES = [
+    ("decode_paged_ragged", big_dims(mode="decode", num_seqs=3, length=5000, k=64, paged=True), [5000, 1, 3001]),
+    ("prefill", big_dims(mode="prefill", length=700, k=64)),
+]
+
+
+@pytest.mark.parametrize("name,wl,lengths", [c + (None,) if len(c) == 2 else c for c in KL_CASES],
+                         ids=[c[0] for c in KL_CASES])
+def test_indexer_kl_rows(name, wl, lengths):
+    """The KL kernel against the oracle's kl_rows on the same fp32 scores and target,
+    then the loss end to end against the oracle's objective."""
+    _say("indexer_kl", name)
+    inp, pb, scores, probs = _kl_inputs(wl, lengths)
+    I = scores.cpu().numpy().astype(np.float64)
+    P = probs.cpu().numpy().astype(np.float64)
+    loss = B().indexer_kl(pb, scores, probs)
+    torch.cuda.synchronize()
+    G, L = scores.cpu().numpy(), loss.cpu().numpy()
+    oi = to_oracle(inp)
+    for t in range(inp.num_q):
+        n = int(inp.q_pos[t]) + 1
+        l_ref, g_ref = oracle.kl_rows(I[t, :n], P[t, :n])
+        assert abs(L[t] - l_ref) <= 1e-4 * max(abs(l_ref), 1e-3), f"{name} row {t}: loss {L[t]} vs {l_ref}"
+        assert np.max(np.abs(G[t, :n] - g_ref)) <= 1e-5 * max(np.abs(g_ref).max(), 1e-6), f"{name} row {t}: grad"
+        assert np.all(G[t, n:] == 0), f"{name} row {t}: gradient past the candidates"
+    rows = list(range(inp.num_q)) if inp.mode == "decode" else [0, 1, 350, inp.num_q - 1]
+    oi, local = to_oracle_rows(inp, rows)
+    ref = oracle.indexer_kl_loss(oi, local)
+    for i, t in enumerate(rows):
+        assert abs(L[t] - ref["loss"][i]) <= 1e-3 * max(abs(ref["loss"][i]), 1e-3), f"{name} row {t}: end to end"
