@@ -101,7 +101,8 @@ typedef enum dsa_op {
   DSA_OP_SPARSE_MLA = 2,
   DSA_OP_FORWARD = 3,
   DSA_OP_DENSE_MLA = 4,
-  DSA_OP_ATTENTION_PROBS = 5
+  DSA_OP_ATTENTION_PROBS = 5,
+  DSA_OP_INDEXER_BACKWARD = 6
 } dsa_op;
 
 /* Where each query sits and which cache rows it may read (host struct). */
@@ -248,6 +249,26 @@ int dsa_attention_probs(const dsa_seqs *seqs, const dsa_dims *dims, float sm_sca
  * workspace. */
 int dsa_indexer_kl(const dsa_seqs *seqs, float *scores, const float *probs, int64_t ld, float *loss,
                    hipStream_t stream);
+
+/* Gradient of step 1 for the warm-up objective [ZS 3.3; the indexer is the
+ * only part trained in Stage 1]: given dL/dI in grad_scores [T, ld] (e.g.
+ * from dsa_indexer_kl), with x_js = q_idx[t,j,:] . k(s) over the candidates
+ * s = 0..q_pos[t]:
+ *   dw[t, j]        = sum_s g(t,s) ReLU(x_js)
+ *   dq_idx[t, j, :] = sum_s g(t,s) w[t,j] [x_js > 0] k(s)
+ *   dk(s)           = sum_t sum_j g(t,s) w[t,j] [x_js > 0] q_idx[t,j,:]
+ * (ReLU'(0) = 0).  dq_idx [T, H_I, d_I] and dw [T, H_I] fp32; dk fp32 in the
+ * key cache's layout (contiguous [B, max_seq_len, d_I] or paged
+ * [num_blocks, block_size, d_I]): the rows of positions 0..max_ctx-1 of
+ * sequence 0 (prefill) or 0..q_pos[t] of sequence t (decode) are written,
+ * 0 where no query sees the key; other rows are left as they are.  The
+ * products run on bf16 MFMA (the masked, weighted score gradient rounded to
+ * bf16 as an operand) with fp32 accumulation; split partials are summed in a
+ * fixed order (deterministic).  Supported: bf16 indexer, H_I = 64, d_I = 128.
+ * Workspace: dsa_workspace_size(DSA_OP_INDEXER_BACKWARD, ...). */
+int dsa_indexer_backward(const dsa_seqs *seqs, const dsa_dims *dims, const void *q_idx, const float *w,
+                         const void *k_cache, const float *grad_scores, int64_t ld, float *dq_idx,
+                         float *dw, float *dk, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Upstream of step 1: per-row fp8 quantisation for an indexer that "runs in
  * FP8" [ZS 3.1; BT (1)].  The pages fix neither scale nor rounding; the

@@ -19,11 +19,12 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "dsa.h")
 
 F32, BF16, FP8_E4M3FN = 0, 1, 2
 PREFILL, DECODE = 0, 1
-OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_MLA, OP_FORWARD, OP_DENSE_MLA, OP_ATTENTION_PROBS = 0, 1, 2, 3, 4, 5
+(OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_MLA, OP_FORWARD, OP_DENSE_MLA, OP_ATTENTION_PROBS,
+ OP_INDEXER_BACKWARD) = 0, 1, 2, 3, 4, 5, 6
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
 EXPORTS = ("dsa_workspace_size", "dsa_index_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward",
-           "dsa_dense_mla", "dsa_attention_probs", "dsa_indexer_kl", "dsa_quantize_fp8", "dsa_append_index_keys",
+           "dsa_dense_mla", "dsa_attention_probs", "dsa_indexer_kl", "dsa_indexer_backward", "dsa_quantize_fp8", "dsa_append_index_keys",
            "dsa_status_string")
 
 
@@ -77,6 +78,8 @@ def _load() -> ctypes.CDLL:
     lib.dsa_attention_probs.restype = ctypes.c_int
     lib.dsa_indexer_kl.argtypes = [sp, P, P, I64, P, P]
     lib.dsa_indexer_kl.restype = ctypes.c_int
+    lib.dsa_indexer_backward.argtypes = [sp, dp, P, P, P, P, I64, P, P, P, P, SZ, P]
+    lib.dsa_indexer_backward.restype = ctypes.c_int
     lib.dsa_quantize_fp8.argtypes = [I64, I32, I32, P, P, P, I32, P]
     lib.dsa_quantize_fp8.restype = ctypes.c_int
     lib.dsa_append_index_keys.argtypes = [sp, I32, I32, P, P, P, P]
@@ -256,6 +259,25 @@ def indexer_kl(pb: Problem, scores: torch.Tensor, probs: torch.Tensor, loss=None
                             _stream(stream))
     _check(st, "dsa_indexer_kl")
     return loss
+
+
+def indexer_backward(pb: Problem, q_idx, w, k_cache, grad_scores, dq=None, dw=None, dk=None, ws=None, stream=None):
+    """Gradients of the indexer scores: (dq [T, H_I, d_I], dw [T, H_I], dk like k_cache) in fp32.
+    dk defaults to zeros (rows no query sees stay 0)."""
+    dev = q_idx.device
+    T, HI, DI = q_idx.shape
+    if dq is None:
+        dq = torch.empty((T, HI, DI), dtype=torch.float32, device=dev)
+    if dw is None:
+        dw = torch.empty((T, HI), dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.zeros(tuple(k_cache.shape), dtype=torch.float32, device=dev)
+    ws = _workspace(OP_INDEXER_BACKWARD, pb, ws, dev)
+    st = LIB.dsa_indexer_backward(ctypes.byref(pb.seqs), ctypes.byref(pb.dims), _ptr(q_idx), _ptr(w), _ptr(k_cache),
+                                  _ptr(grad_scores), int(grad_scores.stride(0)), _ptr(dq), _ptr(dw), _ptr(dk),
+                                  _ptr(ws), _nbytes(ws), _stream(stream))
+    _check(st, "dsa_indexer_backward")
+    return dq, dw, dk
 
 
 def forward(pb: Problem, q_idx, q_scale, w, k_cache, k_scale, q, kv_cache, sm_scale: float, out=None,

@@ -209,6 +209,44 @@ int check_probs_dims(const dsa_seqs *s, const dsa_dims *d) {
   return d->mla_dtype == DSA_BF16 ? DSA_OK : DSA_ERR_UNSUPPORTED;
 }
 
+// Indexer backward: dq key-split partials (few queries only) and dk query-split
+// partials (prefill), the latter bounded by kDenseWsBudget.
+struct BwdLayout {
+  int q_splits, k_qsplits, q_per_split;
+  long long off_k, total;
+};
+
+constexpr long long kBwdQPartBytes = (64ll * 128 + 64) * 4;
+
+BwdLayout bwd_layout(const dsa_seqs *s) {
+  BwdLayout L;
+  const int T = s->num_q;
+  L.q_splits = bwd_q_splits(T, s->max_ctx);
+  const long long qpart = L.q_splits > 1 ? (long long)T * L.q_splits * kBwdQPartBytes : 0;
+  L.off_k = align256(qpart);
+  L.k_qsplits = 1;
+  L.q_per_split = T;
+  long long kpart = 0;
+  if (s->mode == DSA_PREFILL) {
+    const long long nkb = (s->max_ctx + kBwdKeysPerBlock - 1) / kBwdKeysPerBlock;
+    const long long per_split = nkb * kBwdKeysPerBlock * 128 * 4;
+    long long want = (T + 511) / 512;                     // 512 queries per split
+    long long cap = kDenseWsBudget / per_split;
+    if (cap < 1) cap = 1;
+    L.k_qsplits = (int)(want < cap ? want : cap);
+    L.q_per_split = (T + L.k_qsplits - 1) / L.k_qsplits;
+    kpart = (long long)L.k_qsplits * per_split;
+  }
+  L.total = L.off_k + align256(kpart);
+  return L;
+}
+
+int check_bwd_dims(const dsa_dims *d) {
+  if (d == nullptr) return DSA_ERR_INVALID_ARG;
+  if (d->index_dtype != DSA_BF16 || d->index_heads != 64 || d->index_dim != 128) return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
+}
+
 int check_ws(size_t need, const void *ws, size_t ws_bytes) {
   if (need == 0) return DSA_OK;
   if (ws == nullptr || ws_bytes < need) return DSA_ERR_WORKSPACE;
@@ -313,6 +351,9 @@ DSA_EXPORT size_t dsa_workspace_size(int op, const dsa_seqs *seqs, const dsa_dim
     case DSA_OP_ATTENTION_PROBS:
       if (check_probs_dims(seqs, dims) != DSA_OK) return 0;
       return (size_t)probs_layout(seqs, dims).total;
+    case DSA_OP_INDEXER_BACKWARD:
+      if (check_bwd_dims(dims) != DSA_OK) return 0;
+      return (size_t)bwd_layout(seqs).total;
     default:
       return 0;
   }
@@ -492,6 +533,39 @@ DSA_EXPORT int dsa_indexer_kl(const dsa_seqs *seqs, float *scores, const float *
   a.ld = ld;
   a.loss = loss;
   return hip_status(launch_indexer_kl(a, stream));
+}
+
+DSA_EXPORT int dsa_indexer_backward(const dsa_seqs *seqs, const dsa_dims *dims, const void *q_idx, const float *w,
+                                    const void *k_cache, const float *grad_scores, int64_t ld, float *dq_idx,
+                                    float *dw, float *dk, void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (int e = check_seqs(seqs)) return e;
+  if (int e = check_bwd_dims(dims)) return e;
+  if (seqs->num_q == 0) return DSA_OK;
+  if (q_idx == nullptr || w == nullptr || k_cache == nullptr || grad_scores == nullptr || ld < seqs->max_ctx)
+    return DSA_ERR_INVALID_ARG;
+  if (dq_idx == nullptr || dw == nullptr || dk == nullptr) return DSA_ERR_INVALID_ARG;
+  const BwdLayout L = bwd_layout(seqs);
+  if (int e = check_ws((size_t)L.total, ws, ws_bytes)) return e;
+  BwdArgs a;
+  a.sv = view(seqs);
+  a.q_begin = 0;
+  a.rows = seqs->num_q;
+  a.q_idx = q_idx;
+  a.w = w;
+  a.k_cache = k_cache;
+  a.grad = grad_scores;
+  a.ld = ld;
+  a.dq = dq_idx;
+  a.dw = dw;
+  a.dk = dk;
+  a.span = seqs->max_ctx;
+  a.n_split = L.q_splits;
+  a.q_per_split = L.q_per_split;
+  a.part = reinterpret_cast<float *>(ws);
+  if (launch_indexer_bwd_q(a, stream) != hipSuccess) return DSA_ERR_HIP;
+  a.n_split = L.k_qsplits;
+  a.part = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(ws) + L.off_k);
+  return hip_status(launch_indexer_bwd_k(a, stream));
 }
 
 DSA_EXPORT int dsa_quantize_fp8(int64_t rows, int32_t len, int32_t src_dtype, const void *src, void *dst,

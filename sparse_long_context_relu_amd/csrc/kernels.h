@@ -117,6 +117,24 @@ struct KlArgs {
   float *loss;          // [T]: indexed by query
 };
 
+// Gradient of the indexer scores into q_I, w and k_I (bf16 indexer operands).
+struct BwdArgs {
+  SeqView sv;
+  int q_begin, rows;        // query rows of this launch (grad row r = query q_begin + r)
+  const void *q_idx;        // [T, 64, 128] bf16
+  const float *w;           // [T, 64]
+  const void *k_cache;      // key cache, bf16 rows of 128
+  const float *grad;        // [rows, ld]: dL/dI
+  long long ld;
+  float *dq;                // [T, 64, 128]
+  float *dw;                // [T, 64]
+  float *dk;                // key cache layout, fp32 rows of 128
+  int span;                 // dq: list length the splits cut (max_ctx)
+  int n_split;              // dq: key splits per query; dk: query splits
+  int q_per_split;          // dk: queries per split (prefill)
+  float *part;              // split partials
+};
+
 struct TopkLayout {
   int slices, slice_len, sel_seg;
   long long row_words;
@@ -136,6 +154,10 @@ hipError_t launch_topk_select(const TopkArgs &a, hipStream_t s);  // collect + s
 hipError_t launch_topk_all(const TopkArgs &a, hipStream_t s);     // every candidate (all n_t <= k)
 hipError_t launch_sparse_mla(const MlaArgs &a, hipStream_t s);     // also the dense lists
 hipError_t launch_indexer_kl(const KlArgs &a, hipStream_t s);
+hipError_t launch_indexer_bwd_q(const BwdArgs &a, hipStream_t s);   // dq, dw (+ split merge)
+hipError_t launch_indexer_bwd_k(const BwdArgs &a, hipStream_t s);   // dk (+ split merge)
+constexpr int kBwdKeysPerBlock = 128;                                // keys per dk workgroup
+int bwd_q_splits(int rows, int span);                                // dq key splits per query
 hipError_t launch_fp8_quantize(const QuantArgs &a, hipStream_t s);
 hipError_t launch_fp8_append(const AppendArgs &a, hipStream_t s);
 

@@ -6,8 +6,11 @@ Tolerances (the pages state none for this path; derived from the arithmetic):
 the target distribution is exp(z - lse) with fp32 logits of exact bf16
 products, so its entries agree to 2e-3 of the row's largest weight and in L1
 distance; the KL rows are fp32 over at most 2^18 terms, checked to 1e-4
-relative on the same fp32 inputs; gradients that pass through a bf16 MFMA
-operand (the masked, weighted score gradient) agree to 2e-2 relative RMS."""
+relative on the same fp32 inputs.  For a given score gradient, dw (fp32
+throughout) agrees to 1e-4 relative RMS and dq, dk, which take the masked,
+weighted score gradient as a bf16 MFMA operand (2^-9 relative rounding), to
+1e-2; end to end, where the two sides' score gradients differ as well, 1e-3
+and 2e-2."""
 import math
 
 import numpy as np
@@ -106,3 +109,76 @@ def test_indexer_kl_rows(name, wl, lengths):
     ref = oracle.indexer_kl_loss(oi, local)
     for i, t in enumerate(rows):
         assert abs(L[t] - ref["loss"][i]) <= 1e-3 * max(abs(ref["loss"][i]), 1e-3), f"{name} row {t}: end to end"
+
+
+def _rel_rms(got, want):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    nrm = np.linalg.norm(want)
+    return np.linalg.norm(got - want) / nrm if nrm > 0 else np.linalg.norm(got)
+
+
+BWD_CASES = [
+    ("prefill_700", big_dims(mode="prefill", length=700, k=64), None),                    # 2 query splits for dk
+    ("prefill_few_rows", big_dims(mode="prefill", length=2600, k=64, prefill_q_start=2450), None),   # dq key splits
+    ("decode_paged_ragged", big_dims(mode="decode", num_seqs=3, length=5000, k=64, paged=True), [5000, 1, 3001]),
+    ("decode_contig", big_dims(mode="decode", num_seqs=2, length=2100, k=64), [2100, 64]),
+]
+
+
+@pytest.mark.parametrize("name,wl,lengths", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_indexer_backward(name, wl, lengths):
+    """dq, dw, dk for a given score gradient (seeded random) against the oracle's
+    index_scores_backward on the same values; dk rows no query sees stay 0."""
+    _say("indexer_backward", name)
+    inp = generate(wl, DEV, lengths=lengths)
+    pb = B().problem_from_inputs(inp)
+    gen = torch.Generator(device=DEV).manual_seed(7)
+    ld = inp.max_ctx + 3
+    grad = torch.randn((inp.num_q, ld), device=DEV, generator=gen, dtype=torch.float32) * 1e-3
+    dq, dw, dk = B().indexer_backward(pb, inp.q_idx, inp.w, inp.k_cache, grad)
+    torch.cuda.synchronize()
+    G = grad.cpu().numpy().astype(np.float64)
+    oi = to_oracle(inp)
+    dk_ref = np.zeros(dk.shape, dtype=np.float64)
+    dqg, dwg, dkg = dq.cpu().numpy(), dw.cpu().numpy(), dk.cpu().numpy()
+    dq_ref = np.zeros(dqg.shape)
+    dw_ref = np.zeros(dwg.shape)
+    for t in range(inp.num_q):
+        q_t, w_t, keys = oracle.query_index_operands(oi, t)
+        n = keys.shape[0]
+        dq_ref[t], dw_ref[t], dk_t = oracle.index_scores_backward(q_t, w_t, keys, G[t, :n])
+        b = oracle.sequence_of(oi, t)
+        pos = np.arange(n)
+        if oi.block_table is None:
+            dk_ref[b, pos] += dk_t
+        else:
+            blocks = np.asarray(oi.block_table[b], dtype=np.int64)[pos // oi.block_size]
+            np.add.at(dk_ref, (blocks, pos % oi.block_size), dk_t)
+    assert _rel_rms(dwg, dw_ref) <= 1e-4, f"{name}: dw rel RMS {_rel_rms(dwg, dw_ref):.3e}"
+    assert _rel_rms(dqg, dq_ref) <= 1e-2, f"{name}: dq rel RMS {_rel_rms(dqg, dq_ref):.3e}"
+    assert _rel_rms(dkg, dk_ref) <= 1e-2, f"{name}: dk rel RMS {_rel_rms(dkg, dk_ref):.3e}"
+    for t in range(inp.num_q):
+        assert _rel_rms(dqg[t], dq_ref[t]) <= 2e-2, f"{name}: dq row {t}"
+    # rows of keys nobody sees are untouched (zeros from the default output)
+    seen = np.abs(dk_ref).sum(axis=-1) > 0
+    assert np.all(dkg[~seen] == 0) or np.all(np.abs(dkg[~seen]) <= 1e-12), f"{name}: dk written where unseen"
+
+
+def test_indexer_objective_end_to_end():
+    """probs -> index scores -> KL -> backward on the GPU, against the oracle's whole
+    objective (loss per query, dq, dw, dk)."""
+    _say("indexer objective end to end")
+    inp = generate(big_dims(mode="prefill", length=600, k=64), DEV)
+    pb = B().problem_from_inputs(inp)
+    scores = B().index_scores(pb, inp.q_idx, inp.q_scale, inp.w, inp.k_cache, inp.k_scale)
+    probs, _ = _probs(inp, ld=scores.stride(0))
+    loss = B().indexer_kl(pb, scores, probs)
+    dq, dw, dk = B().indexer_backward(pb, inp.q_idx, inp.w, inp.k_cache, scores)
+    torch.cuda.synchronize()
+    ref = oracle.indexer_kl_loss(to_oracle(inp))
+    lg = loss.cpu().numpy()
+    assert np.max(np.abs(lg - ref["loss"]) / np.maximum(np.abs(ref["loss"]), 1e-3)) <= 1e-3
+    assert _rel_rms(dw.cpu().numpy(), ref["dw"]) <= 1e-3
+    assert _rel_rms(dq.cpu().numpy(), ref["dq"]) <= 2e-2
+    assert _rel_rms(dk.cpu().numpy(), ref["dk"]) <= 2e-2
