@@ -187,6 +187,51 @@ def dense_line(B, torch, inp, dsa_ms, steps, warmup, settle_ms):
             "dense_hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def warmup_objective_line(B, torch, inp, steps, settle_ms):
+    """The indexer's warm-up objective (dsa_indexer_kl_loss with the backward) on
+    the prefill inputs: step time, stage times and their matrix-core fractions."""
+    wl = inp.wl
+    pb = B.problem_from_inputs(inp)
+    ws = torch.empty(B.workspace_size(B.OP_INDEXER_KL_LOSS, pb), dtype=torch.uint8, device="cuda")
+    T = inp.num_q
+    loss = torch.empty(T, dtype=torch.float32, device="cuda")
+    dq = torch.empty((T, wl.index_heads, wl.index_dim), dtype=torch.float32, device="cuda")
+    dw = torch.empty((T, wl.index_heads), dtype=torch.float32, device="cuda")
+    dk = torch.zeros(tuple(inp.k_cache.shape), dtype=torch.float32, device="cuda")
+    # The frozen dense attention of the warm-up runs anyway and returns each head's
+    # log-sum-exp; the objective's target then needs one pass over the rows.
+    _, lse = B.dense_mla(pb, inp.sm_scale, inp.q, inp.kv_cache)
+    call = lambda ev=None, given=True: B.indexer_kl_loss(pb, inp.q_idx, inp.w, inp.k_cache, inp.q, inp.kv_cache,
+                                                         inp.sm_scale, lse=lse if given else None, loss=loss, dq=dq,
+                                                         dw=dw, dk=dk, ws=ws, stage_events=ev)
+    ms = time_op(torch, call, steps, 1, settle_ms)
+    ms_self = time_op(torch, lambda: call(given=False), steps, 1, 0)
+    evs = [make_events(torch, 5) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        call(evs[i])
+    torch.cuda.synchronize()
+    st = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps for j in range(4)]
+    pairs = int((inp.q_pos.to("cpu").long() + 1).sum())
+    peak = MFMA_PEAK_TFLOPS["bf16"]
+    f_probs = pairs * wl.heads * 2 * wl.qk_dim                     # the logits of the weights pass
+    f_scores = pairs * wl.index_heads * 2 * wl.index_dim
+    f_bwd = 4 * pairs * wl.index_heads * 2 * wl.index_dim           # q.k again and the dq product; the same for dk
+    kl_bytes = T * ((inp.max_ctx + 63) // 64 * 64) * 4 * 3
+    frac = lambda f, t: round(f / (t * 1e-3) / 1e12 / peak, 4)
+    del ws, loss, dq, dw, dk, lse
+    return {"workload": wl.name,
+            "step": "dsa_indexer_kl_loss (target from the dense attention's lse, scores, KL, backward)",
+            "ms_per_step": round(ms, 3), "queries_per_s": round(T / (ms * 1e-3), 1),
+            "self_contained_ms_per_step": round(ms_self, 3),
+            "stages_ms": {"target_probs": round(st[0], 3), "scores": round(st[1], 3), "kl_rows": round(st[2], 3),
+                          "backward": round(st[3], 3)},
+            "mfma_frac": {"target_probs": frac(f_probs, st[0]), "scores": frac(f_scores, st[1]),
+                          "backward": frac(f_bwd, st[3])},
+            "kl_rows_hbm_frac": round(kl_bytes / (st[2] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "step_mfma_frac": frac(f_probs + f_scores + f_bwd, ms)}
+
+
 def cpu_baseline(inp, seconds):
     """The float64 oracle, as it stands, on the queries of the timed batch, for a bounded time."""
     import numpy as np
@@ -239,6 +284,8 @@ def main():
     ap.add_argument("--exact-workload", default="decode_128k_exact_paged_bf16")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense-MLA comparison (attention over every candidate) on the same inputs")
+    ap.add_argument("--no-warmup-objective", action="store_true",
+                    help="skip the indexer warm-up objective (loss and backward) on the prefill inputs")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -397,6 +444,10 @@ def main():
         torch.cuda.empty_cache()
         if not args.no_dense:
             dense[pname] = dense_line(B, torch, pin, pms, 2, 1, args.settle_ms)
+        if not args.no_warmup_objective:
+            log("indexer warm-up objective on the prefill inputs")
+            result["warmup_objective"] = warmup_objective_line(B, torch, pin, 2, args.settle_ms)
+            log(f"warm-up objective: {result['warmup_objective']['ms_per_step']:.2f} ms")
         del pin
         torch.cuda.empty_cache()
         inp = None

@@ -102,7 +102,8 @@ typedef enum dsa_op {
   DSA_OP_FORWARD = 3,
   DSA_OP_DENSE_MLA = 4,
   DSA_OP_ATTENTION_PROBS = 5,
-  DSA_OP_INDEXER_BACKWARD = 6
+  DSA_OP_INDEXER_BACKWARD = 6,
+  DSA_OP_INDEXER_KL_LOSS = 7
 } dsa_op;
 
 /* Where each query sits and which cache rows it may read (host struct). */
@@ -151,6 +152,27 @@ typedef struct dsa_forward_args {
    * (decode always runs as one chunk); NULL records nothing */
   void *const *stage_events;
 } dsa_forward_args;
+
+/* Inputs and outputs of dsa_indexer_kl_loss (host struct of device pointers). */
+typedef struct dsa_kl_args {
+  const void *q_idx;     /* [T, H_I, d_I] bf16: the indexer (trained) */
+  const float *w;        /* [T, H_I] */
+  const void *k_cache;   /* indexer key cache, bf16 */
+  const void *q;         /* [T, H, D] bf16: the main attention (frozen) */
+  const void *kv_cache;  /* latent cache, bf16 */
+  float sm_scale;        /* softmax scale of the main attention */
+  int32_t reserved;      /* must be 0 */
+  const float *lse;      /* [T, H]: the main attention's per-head lse (e.g. from
+                            dsa_dense_mla), or NULL to compute it */
+  float *loss;           /* [T]: KL term of each query (L_I is their sum) */
+  float *dq_idx;         /* [T, H_I, d_I] fp32, or NULL: no backward */
+  float *dw;             /* [T, H_I] fp32 (NULL with dq_idx) */
+  float *dk;             /* key cache layout, fp32 (NULL with dq_idx) */
+  /* optional host array of 5 hipEvent_t recorded on `stream` at the start and
+   * after the target distribution, the scores, the KL rows and the backward;
+   * NULL records nothing */
+  void *const *stage_events;
+} dsa_kl_args;
 
 /* Bytes of workspace the given entry point needs for these shapes (0 when
  * none).  op is a dsa_op.  Returns 0 as well for invalid arguments; the
@@ -229,15 +251,17 @@ int dsa_dense_mla(const dsa_seqs *seqs, const dsa_dims *dims, float sm_scale, co
  * For every query t and candidate s = 0..q_pos[t]:
  *   probs[t, s] = (1/H) sum_h softmax_s(sm_scale * q[t,h,:] . c(s))
  * (each head's weights sum to 1, so dividing the head sum by H is its L1
- * normalisation); probs[t, s] = 0 for q_pos[t] < s < ld_probs.  lse, if not
- * NULL, receives each head's log-sum-exp [T, H] (as dsa_dense_mla's).  Two
- * passes of the attention kernel over every candidate: the log-sum-exp, then
- * the weights; bf16 operands, fp32 arithmetic and output.  ld_probs >=
+ * normalisation); probs[t, s] = 0 for q_pos[t] < s < ld_probs.  lse [T, H]
+ * holds each head's log-sum-exp: with lse_given = 0 it is computed first (a
+ * pass of the attention kernel over every candidate) and stored there unless
+ * lse is NULL; with lse_given = 1 the caller's values are used, e.g. the lse
+ * that dsa_dense_mla returns for the frozen dense attention.  The weights take
+ * one more pass; bf16 operands, fp32 arithmetic and output.  ld_probs >=
  * max_ctx.  Supported: bf16 H = 128, D = 576, Dv = 512.
  * Workspace: dsa_workspace_size(DSA_OP_ATTENTION_PROBS, ...). */
 int dsa_attention_probs(const dsa_seqs *seqs, const dsa_dims *dims, float sm_scale, const void *q,
-                        const void *kv_cache, float *probs, int64_t ld_probs, float *lse, void *ws,
-                        size_t ws_bytes, hipStream_t stream);
+                        const void *kv_cache, float *probs, int64_t ld_probs, float *lse, int32_t lse_given,
+                        void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* One KL term of the warm-up objective per query [ZS 3.3:
  * L_I = sum_t KL(p_t || softmax(I_t))], and its gradient with respect to the
@@ -269,6 +293,18 @@ int dsa_indexer_kl(const dsa_seqs *seqs, float *scores, const float *probs, int6
 int dsa_indexer_backward(const dsa_seqs *seqs, const dsa_dims *dims, const void *q_idx, const float *w,
                          const void *k_cache, const float *grad_scores, int64_t ld, float *dq_idx,
                          float *dw, float *dk, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* The indexer's warm-up objective in one call [ZS 3.3 Stage 1; LD Objective
+ * Functions]: dsa_attention_probs (target p, from args->lse when given),
+ * dsa_index_scores (I),
+ * dsa_indexer_kl (loss and dL/dI) and, when dq_idx is not NULL,
+ * dsa_indexer_backward, with the same contracts and results.  Scores and
+ * target are kept in the workspace ([T, ld] fp32 each, ld = max_ctx rounded
+ * up to 64).  Supported: bf16 indexer (H_I = 64, d_I = 128) and bf16 MLA
+ * (H = 128, D = 576, Dv = 512).
+ * Workspace: dsa_workspace_size(DSA_OP_INDEXER_KL_LOSS, ...). */
+int dsa_indexer_kl_loss(const dsa_seqs *seqs, const dsa_dims *dims, const dsa_kl_args *args, void *ws,
+                        size_t ws_bytes, hipStream_t stream);
 
 /* Upstream of step 1: per-row fp8 quantisation for an indexer that "runs in
  * FP8" [ZS 3.1; BT (1)].  The pages fix neither scale nor rounding; the

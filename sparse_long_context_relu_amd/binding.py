@@ -20,11 +20,12 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "dsa.h")
 F32, BF16, FP8_E4M3FN = 0, 1, 2
 PREFILL, DECODE = 0, 1
 (OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_MLA, OP_FORWARD, OP_DENSE_MLA, OP_ATTENTION_PROBS,
- OP_INDEXER_BACKWARD) = 0, 1, 2, 3, 4, 5, 6
+ OP_INDEXER_BACKWARD, OP_INDEXER_KL_LOSS) = 0, 1, 2, 3, 4, 5, 6, 7
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
 EXPORTS = ("dsa_workspace_size", "dsa_index_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward",
-           "dsa_dense_mla", "dsa_attention_probs", "dsa_indexer_kl", "dsa_indexer_backward", "dsa_quantize_fp8", "dsa_append_index_keys",
+           "dsa_dense_mla", "dsa_attention_probs", "dsa_indexer_kl", "dsa_indexer_backward", "dsa_indexer_kl_loss",
+           "dsa_quantize_fp8", "dsa_append_index_keys",
            "dsa_status_string")
 
 
@@ -48,6 +49,14 @@ class DsaForwardArgs(ctypes.Structure):
                 ("kv_cache", ctypes.c_void_p), ("sm_scale", ctypes.c_float), ("reserved", ctypes.c_int32),
                 ("topk_idx", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
                 ("stage_events", ctypes.c_void_p)]
+
+
+class DsaKlArgs(ctypes.Structure):
+    _fields_ = [("q_idx", ctypes.c_void_p), ("w", ctypes.c_void_p), ("k_cache", ctypes.c_void_p),
+                ("q", ctypes.c_void_p), ("kv_cache", ctypes.c_void_p), ("sm_scale", ctypes.c_float),
+                ("reserved", ctypes.c_int32), ("lse", ctypes.c_void_p), ("loss", ctypes.c_void_p),
+                ("dq_idx", ctypes.c_void_p),
+                ("dw", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("stage_events", ctypes.c_void_p)]
 
 
 class DsaError(RuntimeError):
@@ -74,12 +83,14 @@ def _load() -> ctypes.CDLL:
     lib.dsa_forward.restype = ctypes.c_int
     lib.dsa_dense_mla.argtypes = [sp, dp, ctypes.c_float, P, P, P, P, P, SZ, P]
     lib.dsa_dense_mla.restype = ctypes.c_int
-    lib.dsa_attention_probs.argtypes = [sp, dp, ctypes.c_float, P, P, P, I64, P, P, SZ, P]
+    lib.dsa_attention_probs.argtypes = [sp, dp, ctypes.c_float, P, P, P, I64, P, I32, P, SZ, P]
     lib.dsa_attention_probs.restype = ctypes.c_int
     lib.dsa_indexer_kl.argtypes = [sp, P, P, I64, P, P]
     lib.dsa_indexer_kl.restype = ctypes.c_int
     lib.dsa_indexer_backward.argtypes = [sp, dp, P, P, P, P, I64, P, P, P, P, SZ, P]
     lib.dsa_indexer_backward.restype = ctypes.c_int
+    lib.dsa_indexer_kl_loss.argtypes = [sp, dp, ctypes.POINTER(DsaKlArgs), P, SZ, P]
+    lib.dsa_indexer_kl_loss.restype = ctypes.c_int
     lib.dsa_quantize_fp8.argtypes = [I64, I32, I32, P, P, P, I32, P]
     lib.dsa_quantize_fp8.restype = ctypes.c_int
     lib.dsa_append_index_keys.argtypes = [sp, I32, I32, P, P, P, P]
@@ -237,14 +248,16 @@ def dense_mla(pb: Problem, sm_scale: float, q, kv_cache, out=None, lse=None, ws=
 
 
 def attention_probs(pb: Problem, sm_scale: float, q, kv_cache, probs=None, ld: Optional[int] = None, lse=None,
-                    ws=None, stream=None):
-    """Head-aggregated dense attention distribution: (probs [T, ld] fp32, lse [T, H] fp32 or None)."""
+                    lse_given: bool = False, ws=None, stream=None):
+    """Head-aggregated dense attention distribution: (probs [T, ld] fp32, lse [T, H] fp32 or None).
+    With lse_given, lse holds the per-head log-sum-exp already (e.g. from dense_mla)."""
     ld = pb.seqs.max_ctx if ld is None else ld
     if probs is None:
         probs = torch.empty((pb.num_q, ld), dtype=torch.float32, device=q.device)
     ws = _workspace(OP_ATTENTION_PROBS, pb, ws, q.device)
     st = LIB.dsa_attention_probs(ctypes.byref(pb.seqs), ctypes.byref(pb.dims), float(sm_scale), _ptr(q),
-                                 _ptr(kv_cache), _ptr(probs), int(probs.stride(0)), _ptr(lse), _ptr(ws), _nbytes(ws),
+                                 _ptr(kv_cache), _ptr(probs), int(probs.stride(0)), _ptr(lse), int(lse_given),
+                                 _ptr(ws), _nbytes(ws),
                                  _stream(stream))
     _check(st, "dsa_attention_probs")
     return probs, lse
@@ -278,6 +291,32 @@ def indexer_backward(pb: Problem, q_idx, w, k_cache, grad_scores, dq=None, dw=No
                                   _ptr(ws), _nbytes(ws), _stream(stream))
     _check(st, "dsa_indexer_backward")
     return dq, dw, dk
+
+
+def indexer_kl_loss(pb: Problem, q_idx, w, k_cache, q, kv_cache, sm_scale: float, backward: bool = True,
+                    lse=None, loss=None, dq=None, dw=None, dk=None, ws=None, stage_events=None, stream=None):
+    """The warm-up objective in one call: (loss [T], dq, dw, dk), the gradients None when backward is False."""
+    dev = q_idx.device
+    T, HI, DI = q_idx.shape
+    if loss is None:
+        loss = torch.empty(T, dtype=torch.float32, device=dev)
+    if backward:
+        dq = torch.empty((T, HI, DI), dtype=torch.float32, device=dev) if dq is None else dq
+        dw = torch.empty((T, HI), dtype=torch.float32, device=dev) if dw is None else dw
+        dk = torch.zeros(tuple(k_cache.shape), dtype=torch.float32, device=dev) if dk is None else dk
+    ws = _workspace(OP_INDEXER_KL_LOSS, pb, ws, dev)
+    ev_arr = None
+    if stage_events is not None:
+        assert len(stage_events) == 5
+        ev_arr = (ctypes.c_void_p * 5)(*[e.cuda_event for e in stage_events])
+    args = DsaKlArgs(q_idx=_ptr(q_idx), w=_ptr(w), k_cache=_ptr(k_cache), q=_ptr(q), kv_cache=_ptr(kv_cache),
+                     sm_scale=float(sm_scale), reserved=0, lse=_ptr(lse), loss=_ptr(loss), dq_idx=_ptr(dq) if backward else None,
+                     dw=_ptr(dw) if backward else None, dk=_ptr(dk) if backward else None,
+                     stage_events=None if ev_arr is None else ctypes.cast(ev_arr, ctypes.c_void_p))
+    st = LIB.dsa_indexer_kl_loss(ctypes.byref(pb.seqs), ctypes.byref(pb.dims), ctypes.byref(args), _ptr(ws),
+                                 _nbytes(ws), _stream(stream))
+    _check(st, "dsa_indexer_kl_loss")
+    return (loss, dq, dw, dk) if backward else (loss, None, None, None)
 
 
 def forward(pb: Problem, q_idx, q_scale, w, k_cache, k_scale, q, kv_cache, sm_scale: float, out=None,

@@ -247,6 +247,21 @@ int check_bwd_dims(const dsa_dims *d) {
   return DSA_OK;
 }
 
+struct KlLossLayout {
+  long long ld, off_probs, off_ws, total;
+};
+
+KlLossLayout kl_loss_layout(const dsa_seqs *s, const dsa_dims *d) {
+  KlLossLayout L;
+  L.ld = score_ld(s);
+  const long long rowbytes = align256((long long)s->num_q * L.ld * 4);
+  L.off_probs = rowbytes;
+  L.off_ws = 2 * rowbytes;
+  const long long a = probs_layout(s, d).total, b = bwd_layout(s).total;
+  L.total = L.off_ws + (a > b ? a : b);
+  return L;
+}
+
 int check_ws(size_t need, const void *ws, size_t ws_bytes) {
   if (need == 0) return DSA_OK;
   if (ws == nullptr || ws_bytes < need) return DSA_ERR_WORKSPACE;
@@ -354,6 +369,9 @@ DSA_EXPORT size_t dsa_workspace_size(int op, const dsa_seqs *seqs, const dsa_dim
     case DSA_OP_INDEXER_BACKWARD:
       if (check_bwd_dims(dims) != DSA_OK) return 0;
       return (size_t)bwd_layout(seqs).total;
+    case DSA_OP_INDEXER_KL_LOSS:
+      if (check_bwd_dims(dims) != DSA_OK || check_probs_dims(seqs, dims) != DSA_OK) return 0;
+      return (size_t)kl_loss_layout(seqs, dims).total;
     default:
       return 0;
   }
@@ -490,13 +508,14 @@ DSA_EXPORT int dsa_dense_mla(const dsa_seqs *seqs, const dsa_dims *dims, float s
 }
 
 DSA_EXPORT int dsa_attention_probs(const dsa_seqs *seqs, const dsa_dims *dims, float sm_scale, const void *q,
-                                   const void *kv_cache, float *probs, int64_t ld_probs, float *lse, void *ws,
-                                   size_t ws_bytes, hipStream_t stream) {
+                                   const void *kv_cache, float *probs, int64_t ld_probs, float *lse,
+                                   int32_t lse_given, void *ws, size_t ws_bytes, hipStream_t stream) {
   if (int e = check_seqs(seqs)) return e;
   if (int e = check_probs_dims(seqs, dims)) return e;
   if (seqs->num_q == 0) return DSA_OK;
   if (q == nullptr || kv_cache == nullptr || probs == nullptr || ld_probs < seqs->max_ctx) return DSA_ERR_INVALID_ARG;
   if (!(sm_scale == sm_scale)) return DSA_ERR_INVALID_ARG;
+  if (lse_given != 0 && (lse_given != 1 || lse == nullptr)) return DSA_ERR_INVALID_ARG;
   const ProbsLayout L = probs_layout(seqs, dims);
   if (int e = check_ws((size_t)L.total, ws, ws_bytes)) return e;
   uint8_t *base = reinterpret_cast<uint8_t *>(ws);
@@ -509,8 +528,10 @@ DSA_EXPORT int dsa_attention_probs(const dsa_seqs *seqs, const dsa_dims *dims, f
     a.dense = 1;
     a.k = seqs->max_ctx;
     a.n_split = L.n_split;
-    a.mode = 1;
-    if (launch_sparse_mla(a, stream) != hipSuccess) return DSA_ERR_HIP;
+    if (!lse_given) {
+      a.mode = 1;
+      if (launch_sparse_mla(a, stream) != hipSuccess) return DSA_ERR_HIP;
+    }
     a.mode = 2;
     a.probs = probs + (long long)c0 * ld_probs;
     a.ld = ld_probs;
@@ -566,6 +587,49 @@ DSA_EXPORT int dsa_indexer_backward(const dsa_seqs *seqs, const dsa_dims *dims, 
   a.n_split = L.k_qsplits;
   a.part = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(ws) + L.off_k);
   return hip_status(launch_indexer_bwd_k(a, stream));
+}
+
+DSA_EXPORT int dsa_indexer_kl_loss(const dsa_seqs *seqs, const dsa_dims *dims, const dsa_kl_args *args, void *ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  if (int e = check_seqs(seqs)) return e;
+  if (int e = check_bwd_dims(dims)) return e;
+  if (int e = check_probs_dims(seqs, dims)) return e;
+  if (args == nullptr || args->reserved != 0) return DSA_ERR_INVALID_ARG;
+  if (seqs->num_q == 0) return DSA_OK;
+  if (args->q_idx == nullptr || args->w == nullptr || args->k_cache == nullptr || args->q == nullptr ||
+      args->kv_cache == nullptr || args->loss == nullptr)
+    return DSA_ERR_INVALID_ARG;
+  const bool bwd = args->dq_idx != nullptr;
+  if (bwd && (args->dw == nullptr || args->dk == nullptr)) return DSA_ERR_INVALID_ARG;
+  if (!(args->sm_scale == args->sm_scale)) return DSA_ERR_INVALID_ARG;
+  const KlLossLayout L = kl_loss_layout(seqs, dims);
+  if (int e = check_ws((size_t)L.total, ws, ws_bytes)) return e;
+  uint8_t *base = reinterpret_cast<uint8_t *>(ws);
+  float *scores = reinterpret_cast<float *>(base);
+  float *probs = reinterpret_cast<float *>(base + L.off_probs);
+  void *sub = base + L.off_ws;
+  const size_t sub_bytes = ws_bytes - (size_t)L.off_ws;
+  hipEvent_t const *ev = reinterpret_cast<hipEvent_t const *>(args->stage_events);
+  auto mark = [&](int i) { return ev == nullptr || hipEventRecord(ev[i], stream) == hipSuccess; };
+  if (!mark(0)) return DSA_ERR_HIP;
+  if (int e = dsa_attention_probs(seqs, dims, args->sm_scale, args->q, args->kv_cache, probs, L.ld,
+                                  const_cast<float *>(args->lse), args->lse != nullptr ? 1 : 0, sub, sub_bytes,
+                                  stream))
+    return e;
+  if (!mark(1)) return DSA_ERR_HIP;
+  if (int e = dsa_index_scores(seqs, dims, args->q_idx, nullptr, args->w, args->k_cache, nullptr, scores, L.ld,
+                               stream))
+    return e;
+  if (!mark(2)) return DSA_ERR_HIP;
+  if (int e = dsa_indexer_kl(seqs, scores, probs, L.ld, args->loss, stream)) return e;
+  if (!mark(3)) return DSA_ERR_HIP;
+  if (bwd) {
+    if (int e = dsa_indexer_backward(seqs, dims, args->q_idx, args->w, args->k_cache, scores, L.ld, args->dq_idx,
+                                     args->dw, args->dk, sub, sub_bytes, stream))
+      return e;
+  }
+  if (!mark(4)) return DSA_ERR_HIP;
+  return DSA_OK;
 }
 
 DSA_EXPORT int dsa_quantize_fp8(int64_t rows, int32_t len, int32_t src_dtype, const void *src, void *dst,

@@ -44,9 +44,12 @@ int main(void) {
   printf("dsa_seqs %zu\\n", sizeof(dsa_seqs));
   printf("dsa_dims %zu\\n", sizeof(dsa_dims));
   printf("dsa_forward_args %zu\\n", sizeof(dsa_forward_args));
+  printf("dsa_kl_args %zu\\n", sizeof(dsa_kl_args));
   P(dsa_seqs, q_pos) P(dsa_seqs, block_table) P(dsa_seqs, max_blocks) P(dsa_seqs, max_seq_len)
   P(dsa_dims, mla_dtype)
   P(dsa_forward_args, sm_scale) P(dsa_forward_args, topk_idx) P(dsa_forward_args, stage_events)
+  P(dsa_kl_args, sm_scale) P(dsa_kl_args, lse) P(dsa_kl_args, loss) P(dsa_kl_args, dk)
+  P(dsa_kl_args, stage_events)
   return 0;
 }
 """)
@@ -58,10 +61,12 @@ int main(void) {
     assert int(got["dsa_seqs"]) == ctypes.sizeof(B.DsaSeqs)
     assert int(got["dsa_dims"]) == ctypes.sizeof(B.DsaDims)
     assert int(got["dsa_forward_args"]) == ctypes.sizeof(B.DsaForwardArgs)
+    assert int(got["dsa_kl_args"]) == ctypes.sizeof(B.DsaKlArgs)
     for key, v in got.items():
         if "." in key:
             struct, field = key.split(".")
-            cls = {"dsa_seqs": B.DsaSeqs, "dsa_dims": B.DsaDims, "dsa_forward_args": B.DsaForwardArgs}[struct]
+            cls = {"dsa_seqs": B.DsaSeqs, "dsa_dims": B.DsaDims, "dsa_forward_args": B.DsaForwardArgs,
+                   "dsa_kl_args": B.DsaKlArgs}[struct]
             assert getattr(cls, field).offset == int(v), key
 
 
@@ -175,6 +180,52 @@ def test_dense_mla_validation_and_workspace():
     assert call(_problem(**f32)) == B.ERR_UNSUPPORTED     # fp32 lists are limited to 1024 candidates
     small = _problem(q_pos=torch.tensor([255, 100], dtype=torch.int32), max_ctx=256, max_seq_len=256, **f32)
     assert B.workspace_size(B.OP_DENSE_MLA, small) == 0
+
+
+def test_warmup_objective_validation_and_workspace():
+    """Host checks and workspace sizes of the indexer warm-up entry points (no launch)."""
+    L = B.LIB
+    qp = torch.arange(4096, dtype=torch.int32)
+    pf = B.make_problem(mode="prefill", q_pos=qp, max_ctx=4096, num_seqs=1, max_seq_len=4096)
+    sp, dp = ctypes.byref(pf.seqs), ctypes.byref(pf.dims)
+    # probs: lse of every (query, head) + the lse pass's 2 splits of (max, sum) pairs
+    assert B.workspace_size(B.OP_ATTENTION_PROBS, pf) == 4096 * 128 * 4 + 4096 * 2 * 128 * 8
+    assert L.dsa_attention_probs(sp, dp, 0.04, None, FAKE, FAKE, 4096, None, 0, FAKE, 1 << 40, None) == B.ERR_INVALID_ARG
+    assert L.dsa_attention_probs(sp, dp, 0.04, FAKE, FAKE, FAKE, 4000, None, 0, FAKE, 1 << 40, None) == B.ERR_INVALID_ARG
+    assert L.dsa_attention_probs(sp, dp, 0.04, FAKE, FAKE, FAKE, 4096, None, 1, FAKE, 1 << 40, None) == B.ERR_INVALID_ARG
+    assert L.dsa_attention_probs(sp, dp, 0.04, FAKE, FAKE, FAKE, 4096, None, 0, None, 0, None) == B.ERR_WORKSPACE
+    f32 = B.make_problem(mode="prefill", q_pos=qp[:256], max_ctx=256, num_seqs=1, max_seq_len=256,
+                         mla_dtype=B.F32, heads=8, qk_dim=80, v_dim=64)
+    assert L.dsa_attention_probs(ctypes.byref(f32.seqs), ctypes.byref(f32.dims), 0.04, FAKE, FAKE, FAKE, 256, None,
+                                 0, FAKE, 1 << 40, None) == B.ERR_UNSUPPORTED
+    # KL rows: no workspace
+    assert L.dsa_indexer_kl(sp, None, FAKE, 4096, FAKE, None) == B.ERR_INVALID_ARG
+    assert L.dsa_indexer_kl(sp, FAKE, FAKE, 100, FAKE, None) == B.ERR_INVALID_ARG
+    # backward: dk partials of 8 query splits (512 queries each) x 32 key blocks x 128 keys x 128 dims
+    assert B.workspace_size(B.OP_INDEXER_BACKWARD, pf) == 8 * 32 * 128 * 128 * 4
+    bw = lambda **kw: L.dsa_indexer_backward(sp, dp, *[kw.get(k, FAKE) for k in ("q", "w", "k", "g")], 4096,
+                                             *[kw.get(k, FAKE) for k in ("dq", "dw", "dk")], FAKE, 1 << 40, None)
+    assert bw(dk=None) == B.ERR_INVALID_ARG and bw(g=None) == B.ERR_INVALID_ARG
+    fp8 = B.make_problem(mode="prefill", q_pos=qp, max_ctx=4096, num_seqs=1, max_seq_len=4096,
+                         index_dtype=B.FP8_E4M3FN)
+    assert L.dsa_indexer_backward(ctypes.byref(fp8.seqs), ctypes.byref(fp8.dims), FAKE, FAKE, FAKE, FAKE, 4096, FAKE,
+                                  FAKE, FAKE, FAKE, 1 << 40, None) == B.ERR_UNSUPPORTED
+    # decode: dq key splits (2 per query at 4096 candidates), no dk partials
+    dc = B.make_problem(mode="decode", q_pos=torch.full((4,), 4095, dtype=torch.int32), max_ctx=4096, num_seqs=4,
+                        max_seq_len=4096)
+    assert B.workspace_size(B.OP_INDEXER_BACKWARD, dc) == 4 * 2 * (64 * 128 + 64) * 4
+    # the fused objective: scores and target rows, then the larger of the two sub-workspaces
+    need = B.workspace_size(B.OP_INDEXER_KL_LOSS, pf)
+    assert need == 2 * 4096 * 4096 * 4 + max(B.workspace_size(B.OP_ATTENTION_PROBS, pf),
+                                             B.workspace_size(B.OP_INDEXER_BACKWARD, pf))
+    args = B.DsaKlArgs(q_idx=FAKE, w=FAKE, k_cache=FAKE, q=FAKE, kv_cache=FAKE, sm_scale=0.04, loss=FAKE, dq_idx=FAKE,
+                       dw=FAKE, dk=None)
+    call = lambda nb: L.dsa_indexer_kl_loss(sp, dp, ctypes.byref(args), FAKE, nb, None)
+    assert call(need) == B.ERR_INVALID_ARG                      # dq without dk
+    args.dk = FAKE
+    assert call(need - 1) == B.ERR_WORKSPACE
+    args.reserved = 1
+    assert call(need) == B.ERR_INVALID_ARG
 
 
 def test_forward_validation_and_workspace():

@@ -71,6 +71,24 @@ def test_attention_probs(name, wl, lengths, qmul):
         assert np.max(np.abs(lg[t] - l_ref)) <= 2e-3, f"{name} row {t}: lse"
 
 
+def test_attention_probs_given_lse():
+    """The target from the lse that dsa_dense_mla returns (one pass instead of two)."""
+    _say("attention_probs given lse")
+    inp = generate(big_dims(mode="prefill", length=2600, k=64, prefill_q_start=2450), DEV)
+    pb = B().problem_from_inputs(inp)
+    _, lse = B().dense_mla(pb, inp.sm_scale, inp.q, inp.kv_cache)
+    probs, _ = B().attention_probs(pb, inp.sm_scale, inp.q, inp.kv_cache, lse=lse, lse_given=True)
+    own, _ = _probs(inp)
+    torch.cuda.synchronize()
+    oi = to_oracle(inp)
+    pg = probs.cpu().numpy()
+    assert np.max(np.abs(pg - own.cpu().numpy())) <= 1e-6
+    for t in (0, 75, inp.num_q - 1):
+        n = int(inp.q_pos[t]) + 1
+        oi_rows, local = to_oracle_rows(inp, [t])
+        check_distribution(pg[t, :n], oracle.attention_distribution(oi_rows, local[0]), f"given lse row {t}")
+
+
 def _kl_inputs(wl, lengths=None):
     inp = generate(wl, DEV, lengths=lengths)
     pb = B().problem_from_inputs(inp)
@@ -182,3 +200,49 @@ def test_indexer_objective_end_to_end():
     assert _rel_rms(dw.cpu().numpy(), ref["dw"]) <= 1e-3
     assert _rel_rms(dq.cpu().numpy(), ref["dq"]) <= 2e-2
     assert _rel_rms(dk.cpu().numpy(), ref["dk"]) <= 2e-2
+
+
+def test_indexer_objective_full_size():
+    """The fused objective on the 16K-token prefill the benchmark times: sampled query
+    rows (loss end to end; dq, dw for the GPU's own score gradient) and sampled keys
+    (dk summed over every query that sees the key) against the oracle."""
+    from workloads import WORKLOADS, raw_numpy
+    _say("indexer objective full size", "prefill_16k_bf16")
+    inp = generate(WORKLOADS["prefill_16k_bf16"], DEV)
+    pb = B().problem_from_inputs(inp)
+    ws = torch.empty(B().workspace_size(B().OP_INDEXER_KL_LOSS, pb), dtype=torch.uint8, device=DEV)
+    loss, dq, dw, dk = B().indexer_kl_loss(pb, inp.q_idx, inp.w, inp.k_cache, inp.q, inp.kv_cache, inp.sm_scale,
+                                           ws=ws)
+    torch.cuda.synchronize()
+    T = inp.num_q
+    ld = (inp.max_ctx + 63) // 64 * 64
+    grad = ws[: T * ld * 4].view(torch.float32).view(T, ld)
+    assert torch.isfinite(loss).all() and torch.isfinite(dq).all() and torch.isfinite(dk).all()
+    rows = [0, 1, 2047, 2048, 9000, T - 1]
+    oi, local = to_oracle_rows(inp, rows)
+    ref = oracle.indexer_kl_loss(oi, local)
+    L, G = loss.cpu().numpy(), grad[rows].cpu().numpy().astype(np.float64)
+    for i, t in enumerate(rows):
+        assert abs(L[t] - ref["loss"][i]) <= 1e-3 * max(abs(ref["loss"][i]), 1e-3), f"row {t}: loss"
+        q_t, w_t, keys = oracle.query_index_operands(oi, local[i])
+        n = keys.shape[0]
+        dq_ref, dw_ref, _ = oracle.index_scores_backward(q_t, w_t, keys, G[i, :n])
+        assert _rel_rms(dw[t].cpu().numpy(), dw_ref) <= 1e-4, f"row {t}: dw"
+        assert _rel_rms(dq[t].cpu().numpy(), dq_ref) <= 1e-2, f"row {t}: dq"
+    # dk of sampled keys from every query's gradient column, in chunks of queries
+    keys_s = [0, 5, 8000, T - 1]
+    kc = oracle.decode_bf16(raw_numpy(inp.k_cache[0, :T]))
+    qpos = raw_numpy(inp.q_pos).astype(np.int64)
+    wv = raw_numpy(inp.w).astype(np.float64)
+    gcols = grad[:, keys_s].cpu().numpy().astype(np.float64)
+    dk_ref = np.zeros((len(keys_s), 128))
+    for c0 in range(0, T, 1024):
+        qc = oracle.decode_bf16(raw_numpy(inp.q_idx[c0:c0 + 1024]))              # [c, 64, 128]
+        for j, s in enumerate(keys_s):
+            x = qc @ kc[s]                                                        # [c, 64]
+            seen = (qpos[c0:c0 + 1024] >= s)[:, None]
+            gm = gcols[c0:c0 + 1024, j][:, None] * wv[c0:c0 + 1024] * (x > 0) * seen
+            dk_ref[j] += np.einsum("ch,chd->d", gm, qc)
+    dkg = dk[0, keys_s].cpu().numpy()
+    for j, s in enumerate(keys_s):
+        assert _rel_rms(dkg[j], dk_ref[j]) <= 2e-2, f"key {s}: dk rel RMS {_rel_rms(dkg[j], dk_ref[j]):.3e}"
