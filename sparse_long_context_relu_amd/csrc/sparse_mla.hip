@@ -68,8 +68,8 @@ __device__ __forceinline__ int split_len(int k, int n_split) {
 // Block order: the splits of one query are placed on the same XCD (workgroups
 // are dealt to the 8 XCDs round-robin by linear id), so its query rows are
 // fetched from HBM once and then served by that XCD's L2.
-__device__ __forceinline__ void mla_block(const MlaArgs &a, int &sp, int &r) {
-  const int total = a.n_split * a.rows;
+__device__ __forceinline__ void mla_block(const MlaArgs &a, int groups, int &sp, int &r) {
+  const int total = a.n_split * groups;
   int v = blockIdx.x;
   if ((total & 7) == 0) v = (v & 7) * (total >> 3) + (v >> 3);
   r = v / a.n_split;
@@ -151,16 +151,20 @@ constexpr int kModeProbs = 2;   // softmax weights given the lse, summed over th
 
 // Logits, then per mode: online softmax and value product (attention), online
 // softmax only (lse), or the normalised weights summed over this wave's heads
-// into `psum` (probs; 32 rows, needs the head's lse in base 2 as `lse2`).
+// (probs; 32 rows into prow + q kWaves kR, given each head's lse in base 2).
+// The lse and probs passes serve kQ queries of one sequence from each tile:
+// every operand read feeds kQ MFMAs, and query q sees the tile's first
+// nrow[q] - j0 rows.
 //
 // The operand reads are issued ahead of the MFMAs that consume them (fixed
 // instruction groups below), so several LDS reads are in flight while the
 // matrix core works.
-template <int kMode>
-__device__ __forceinline__ void consume_tile(uint32_t tile, const int *slots, int j0, const bf16x8 (&qb)[kKs],
-                                             f32x4 (&acc)[kDb], float &m_run, float &l_run, float scale2,
-                                             uint32_t qk_off, uint32_t pv_even, uint32_t pv_odd, int g,
-                                             float lse2, float *prow) {
+template <int kMode, int kQ>
+__device__ __forceinline__ void consume_tile(uint32_t tile, const int *slots, int j0, const bf16x8 (&qb)[kQ][kKs],
+                                             f32x4 (&acc)[kDb], float (&m_run)[kQ], float (&l_run)[kQ],
+                                             float scale2, uint32_t qk_off, uint32_t pv_even, uint32_t pv_odd, int g,
+                                             const float (&lse2)[kQ], const int (&nrow)[kQ], float *prow) {
+  static_assert(kMode != kModeAttn || kQ == 1, "attention serves one query per workgroup");
   // ---- S^T for 32 rows x this wave's 16 heads.  The 36 operand reads go in
   // batches of kBatch, each batch issued before the MFMAs of the previous one
   // (scheduling barriers keep the compiler from sinking the reads to their uses).
@@ -171,7 +175,9 @@ __device__ __forceinline__ void consume_tile(uint32_t tile, const int *slots, in
   const int lane = lane_id();
   const int row_slot = slots[j0 + (lane & (kR - 1))];
   __builtin_amdgcn_sched_barrier(0);
-  f32x4 st[2] = {zero_vec<f32x4>(), zero_vec<f32x4>()};
+  f32x4 st[kQ][2];
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) st[q][0] = st[q][1] = zero_vec<f32x4>();
   u32x4 fr[2][kBatch];
   auto read = [&](int i, int buf) {
 #pragma unroll
@@ -187,15 +193,20 @@ __device__ __forceinline__ void consume_tile(uint32_t tile, const int *slots, in
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int q = i * kBatch + u, ks = q >> 1, rb = q & 1;
-      st[rb] = mfma16_bf16(__builtin_bit_cast(bf16x8, fr[i & 1][u]), qb[ks], st[rb]);
+      const int k = i * kBatch + u, ks = k >> 1, rb = k & 1;
+#pragma unroll
+      for (int q = 0; q < kQ; ++q)
+        st[q][rb] = mfma16_bf16(__builtin_bit_cast(bf16x8, fr[i & 1][u]), qb[q][ks], st[q][rb]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
   // ---- online softmax (base 2), one head per lane column.
   // Row validity of the tile as a wave-uniform mask (bit j: row j present).
-  const uint32_t rowmask = (uint32_t)__ballot(lane < kR && row_slot >= 0);
+  const uint32_t rowmask =
+      (uint32_t)__ballot(lane < kR && row_slot >= 0 && (kQ == 1 || j0 + (lane & (kR - 1)) < nrow[q]));
   const uint32_t mine = rowmask >> (4 * g);     // bit v: row 4g+v; bit 16+v: row 16+4g+v
   if constexpr (kMode == kModeProbs) {
     // weight of each present row for this lane's head, summed over the 16 heads
@@ -204,52 +215,53 @@ __device__ __forceinline__ void consume_tile(uint32_t tile, const int *slots, in
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        e[rb * 4 + v] = sum16(((mine >> (16 * rb + v)) & 1u) ? __builtin_amdgcn_exp2f(st[rb][v] * scale2 - lse2) : 0.f);
+        e[rb * 4 + v] =
+            sum16(((mine >> (16 * rb + v)) & 1u) ? __builtin_amdgcn_exp2f(st[q][rb][v] * scale2 - lse2[q]) : 0.f);
     // lane with column c < 8 keeps row 16 (c / 4) + 4 g + c % 4
     const int c = lane & 15;
     float mine_e = e[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) mine_e = c == i ? e[i] : mine_e;
-    if (c < 8) prow[16 * (c >> 2) + 4 * g + (c & 3)] = mine_e;
-    return;
+    if (c < 8) prow[q * kWaves * kR + 16 * (c >> 2) + 4 * g + (c & 3)] = mine_e;
+    continue;
   }
   float mx = neg_inf();
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      st[rb][v] = ((mine >> (16 * rb + v)) & 1u) ? st[rb][v] * scale2 : neg_inf();
-      mx = fmaxf(mx, st[rb][v]);
+      st[q][rb][v] = ((mine >> (16 * rb + v)) & 1u) ? st[q][rb][v] * scale2 : neg_inf();
+      mx = fmaxf(mx, st[q][rb][v]);
     }
   mx = max_over_rows(mx);
-  if (__any(mx > m_run + kLazy)) {
+  if (__any(mx > m_run[q] + kLazy)) {
     // raise the base of every head whose maximum moved (a head with no row yet
     // present keeps -inf and a zero accumulator)
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = m_run == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    l_run *= alpha;
+    const float m_new = fmaxf(m_run[q], mx);
+    const float alpha = m_run[q] == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(m_run[q] - m_new);
+    l_run[q] *= alpha;
     if constexpr (kMode == kModeAttn) {
 #pragma unroll
       for (int db = 0; db < kDb; ++db)
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[db][v] *= alpha;
     }
-    m_run = m_new;
+    m_run[q] = m_new;
   }
   // exponent base 0 while the head has seen nothing: -inf - 0 stays -inf (weight 0)
-  const float base = m_run == neg_inf() ? 0.f : m_run;
+  const float base = m_run[q] == neg_inf() ? 0.f : m_run[q];
   bf16x8 pb;
   float psum = 0.f;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const float pv = __builtin_amdgcn_exp2f(st[rb][v] - base);
+      const float pv = __builtin_amdgcn_exp2f(st[q][rb][v] - base);
       psum += pv;
       pb[rb * 4 + v] = (__bf16)pv;
     }
-  l_run += psum;
-  if constexpr (kMode == kModeLse) return;
+  l_run[q] += psum;
+  if constexpr (kMode == kModeLse) continue;
   // ---- O^T += V^T . P^T.  k-slots 0..3 = tile rows 4g+e, 4..7 = rows 16+4g+e (e = 0..3),
   // matching the rows this lane holds in P^T.  Lane 4e+c of group g points the
   // transpose read at row 4g+e (resp. 16+4g+e), dims d0+4c..d0+4c+3, and receives
@@ -271,33 +283,54 @@ __device__ __forceinline__ void consume_tile(uint32_t tile, const int *slots, in
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, kAheadV, 1);
+  }
 }
 
-template <int kMode>
+// One workgroup per (group of kQ query rows, split of their lists); kQ > 1
+// only for the lse and probs passes of a prefill (dense lists of sequence 0,
+// one tile serving every query of the group).
+template <int kMode, int kQ>
 __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
   __shared__ uint4 tiles[kBufs][kTileBufChunks];
   __shared__ int slots[kMaxSplitRows + 4 * kR];
   __shared__ int fallback;
-  // probs: each wave's head sums of the last two tiles' rows
-  __shared__ float psums[kMode == kModeProbs ? 2 : 1][kMode == kModeProbs ? kWaves : 1][kR];
+  // probs: each wave's head sums of the last two tiles' rows, per query
+  __shared__ float psums[kMode == kModeProbs ? 2 : 1][kMode == kModeProbs ? kQ * kWaves * kR : 1];
 
-  int sp, r;
-  mla_block(a, sp, r);
+  int sp, rg;
+  mla_block(a, (a.rows + kQ - 1) / kQ, sp, rg);
+  const int r = rg * kQ;                      // first row of the group
   const int t = a.q_begin + r;
-  const int n = a.sv.candidates(t);
   const int b = a.sv.seq_of(t);
+  // rows of the group past the launch's last row see nothing and write nothing
+  int nq[kQ];
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) nq[q] = r + q < a.rows ? a.sv.candidates(t + q) : 0;
+  int n = nq[0];
+#pragma unroll
+  for (int q = 1; q < kQ; ++q) n = nq[q] > n ? nq[q] : n;
   const int32_t *irow = a.dense ? nullptr : a.idx + (long long)r * a.k;
   const int len = split_len(a.k, a.n_split);
   const int i0 = sp * len;
   int i1 = i0 + len < a.k ? i0 + len : a.k;
   if (a.dense && i1 > n) i1 = n;              // dense lists end at the last candidate
   const int rows = i1 > i0 ? i1 - i0 : 0;
+  int nrow[kQ];                               // list entries (from the split's start) each query sees
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    const int e = (i1 < nq[q] ? i1 : nq[q]) - i0;
+    nrow[q] = e > 0 ? e : 0;
+  }
   if constexpr (kMode == kModeProbs) {
-    // positions of this split past the query's last candidate (and, for the
+    // positions of this split past each query's last candidate (and, for the
     // last split, up to the row's end) hold 0
-    float *prow = a.probs + (long long)r * a.ld;
-    const long long z0 = i0 + rows, z1 = sp + 1 == a.n_split ? a.ld : (i0 + len < a.ld ? i0 + len : a.ld);
-    for (long long s = z0 + threadIdx.x; s < z1; s += kThreads) prow[s] = 0.f;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      if (r + q >= a.rows) break;
+      float *prow = a.probs + (long long)(r + q) * a.ld;
+      const long long z0 = i0 + nrow[q], z1 = sp + 1 == a.n_split ? a.ld : (i0 + len < a.ld ? i0 + len : a.ld);
+      for (long long s = z0 + threadIdx.x; s < z1; s += kThreads) prow[s] = 0.f;
+    }
   }
   // A dense split past the last candidate has nothing to merge; the combine
   // reads only the splits that hold a position.
@@ -344,11 +377,13 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
   // order, so query loads issued before the index and page-table loads would
   // be drained by the waits for those.  From here they stream in with the
   // first tile; the barriers up to it wait for LDS work only.
-  bf16x8 qb[kKs];
-  {
-    const uint8_t *qrow = reinterpret_cast<const uint8_t *>(a.q) + ((long long)t * kH + wv * 16 + col) * (kD * 2);
+  bf16x8 qb[kQ][kKs];
 #pragma unroll
-    for (int ks = 0; ks < kKs; ++ks) qb[ks] = as_bf16x8(ld16(qrow + ks * 64 + g * 16));
+  for (int q = 0; q < kQ; ++q) {
+    const int tq = r + q < a.rows ? t + q : t;
+    const uint8_t *qrow = reinterpret_cast<const uint8_t *>(a.q) + ((long long)tq * kH + wv * 16 + col) * (kD * 2);
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) qb[q][ks] = as_bf16x8(ld16(qrow + ks * 64 + g * 16));
   }
 #pragma unroll
   for (int u = 0; u < kFill; ++u) {
@@ -362,7 +397,12 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
   f32x4 acc[kDb];
 #pragma unroll
   for (int db = 0; db < kDb; ++db) acc[db] = zero_vec<f32x4>();
-  float m_run = neg_inf(), l_run = 0.f;
+  float m_run[kQ], l_run[kQ];
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    m_run[q] = neg_inf();
+    l_run[q] = 0.f;
+  }
   const float scale2 = a.sm_scale * kLog2e;
   const uint8_t *kv = reinterpret_cast<const uint8_t *>(a.kv);
   // per-lane LDS byte offsets: the logit operand (row col, data chunk 4 ks + g)
@@ -374,17 +414,23 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
   const uint32_t pv_odd = pv_row + ((2 + (vc >> 1)) ^ g) * 16;
   const uint32_t tile_lds = lds_addr(&tiles[0][0]);
   constexpr uint32_t kTileBytes = kTileBufChunks * 16;
-  // probs: this lane's head's log-sum-exp in base 2
-  const float lse2 = kMode == kModeProbs ? a.lse[(long long)t * kH + wv * 16 + col] * kLog2e : 0.f;
+  // probs: this lane's head's log-sum-exp in base 2, per query
+  float lse2[kQ];
+#pragma unroll
+  for (int q = 0; q < kQ; ++q)
+    lse2[q] = kMode == kModeProbs && r + q < a.rows ? a.lse[(long long)(t + q) * kH + wv * 16 + col] * kLog2e : 0.f;
   // probs: the normalised weights of tile tt's rows, summed over every head in a
   // fixed order (wave 0, after the barrier that follows the tile)
   auto write_probs = [&](int tt) {
     if (lane < kR) {
-      float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) v += psums[tt & 1][w][lane];
       const int j = tt * kR + lane;
-      if (j < rows) a.probs[(long long)r * a.ld + i0 + j] = v * (1.f / kH);
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) v += psums[tt & 1][(q * kWaves + w) * kR + lane];
+        if (j < nrow[q]) a.probs[(long long)(r + q) * a.ld + i0 + j] = v * (1.f / kH);
+      }
     }
   };
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -415,8 +461,9 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
         issue_tile(tile_lds + nb * kTileBytes, kv, slots, (tt + 2) * kR, fb, wv, lane);
       }
       if (kMode == kModeProbs && tt > 0 && wv == 0) write_probs(tt - 1);
-      consume_tile<kMode>(tile_lds + cur * kTileBytes, slots, tt * kR, qb, acc, m_run, l_run, scale2, qk_off,
-                          pv_even, pv_odd, g, lse2, &psums[kMode == kModeProbs ? (tt & 1) : 0][wv][0]);
+      consume_tile<kMode, kQ>(tile_lds + cur * kTileBytes, slots, tt * kR, qb, acc, m_run, l_run, scale2, qk_off,
+                              pv_even, pv_odd, g, lse2, nrow,
+                              &psums[kMode == kModeProbs ? (tt & 1) : 0][kMode == kModeProbs ? wv * kR : 0]);
       cur = cur == 2 ? 0 : cur + 1;
     }
   }
@@ -426,23 +473,31 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
       lds_barrier();
       if (wv == 0) write_probs(ntiles - 1);
     } else {
-      for (int j = threadIdx.x; j < rows; j += kThreads) a.probs[(long long)r * a.ld + i0 + j] = 0.f;  // none present
+#pragma unroll
+      for (int q = 0; q < kQ; ++q)                // none present: every weight is 0
+        for (int j = threadIdx.x; j < nrow[q]; j += kThreads) a.probs[(long long)(r + q) * a.ld + i0 + j] = 0.f;
     }
     return;
   }
 
   const int h = wv * 16 + col;
-  const float l_tot = sum_over_rows(l_run);
   if constexpr (kMode == kModeLse) {
-    if (g == 0) {
-      if (a.n_split == 1) {
-        if (a.lse != nullptr) a.lse[(long long)t * kH + h] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : neg_inf();
-      } else {
-        reinterpret_cast<float2 *>(a.part)[((long long)r * a.n_split + sp) * kH + h] = make_float2(m_run, l_tot);
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const float lq = sum_over_rows(l_run[q]);
+      if (g == 0 && r + q < a.rows) {
+        if (a.n_split == 1) {
+          if (a.lse != nullptr)
+            a.lse[(long long)(t + q) * kH + h] = lq > 0.f ? (m_run[q] + __log2f(lq)) * kLn2 : neg_inf();
+        } else {
+          reinterpret_cast<float2 *>(a.part)[((long long)(r + q) * a.n_split + sp) * kH + h] =
+              make_float2(m_run[q], lq);
+        }
       }
     }
     return;
   }
+  const float l_tot = sum_over_rows(l_run[0]);
   // One split: the output row.  Several: this split's normalised output in
   // bf16 (a weighted mean of value rows, so within their range) and its
   // (max, sum), merged by the combine kernel.
@@ -459,11 +514,11 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
   }
   if (g == 0) {
     if (a.n_split == 1) {
-      if (a.lse != nullptr) a.lse[orow_i] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : neg_inf();
+      if (a.lse != nullptr) a.lse[orow_i] = l_tot > 0.f ? (m_run[0] + __log2f(l_tot)) * kLn2 : neg_inf();
     } else {
       float2 *ml = reinterpret_cast<float2 *>(reinterpret_cast<uint16_t *>(a.part) +
                                               (long long)a.rows * a.n_split * kH * kDv);
-      ml[orow_i] = make_float2(m_run, l_tot);
+      ml[orow_i] = make_float2(m_run[0], l_tot);
     }
   }
 }
@@ -667,15 +722,24 @@ hipError_t launch_sparse_mla(const MlaArgs &a, hipStream_t st) {
     return hipGetLastError();
   }
   const dim3 grid(a.n_split * a.rows);
+  // the lse and probs passes of a prefill serve two queries from each tile
+  const bool pair = a.dense && a.sv.mode == DSA_PREFILL && a.rows > 1;
+  const dim3 grid2(a.n_split * ((a.rows + 1) / 2));
   if (a.mode == kModeLse) {
-    hipLaunchKernelGGL(mla_bf16_kernel<kModeLse>, grid, dim3(kThreads), 0, st, a);
+    if (pair)
+      hipLaunchKernelGGL((mla_bf16_kernel<kModeLse, 2>), grid2, dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((mla_bf16_kernel<kModeLse, 1>), grid, dim3(kThreads), 0, st, a);
     if (a.n_split > 1)
       hipLaunchKernelGGL(mla_lse_combine_kernel, dim3((unsigned)(((long long)a.rows * kH + 255) / 256)), dim3(256), 0,
                          st, a);
   } else if (a.mode == kModeProbs) {
-    hipLaunchKernelGGL(mla_bf16_kernel<kModeProbs>, grid, dim3(kThreads), 0, st, a);
+    if (pair)
+      hipLaunchKernelGGL((mla_bf16_kernel<kModeProbs, 2>), grid2, dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((mla_bf16_kernel<kModeProbs, 1>), grid, dim3(kThreads), 0, st, a);
   } else {
-    hipLaunchKernelGGL(mla_bf16_kernel<kModeAttn>, grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((mla_bf16_kernel<kModeAttn, 1>), grid, dim3(kThreads), 0, st, a);
     if (a.n_split > 1) hipLaunchKernelGGL(mla_combine_kernel, dim3(kH / 4, a.rows), dim3(256), 0, st, a);
   }
   return hipGetLastError();

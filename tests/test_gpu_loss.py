@@ -49,6 +49,8 @@ PROB_CASES = [
     ("decode_sharp", big_dims(mode="decode", num_seqs=2, length=4100, k=64), [4100, 1300], 1200.0),
     ("decode_long_128_splits", big_dims(mode="decode", num_seqs=1, length=140000, k=64), [140000], 1.0),
     ("prefill_one_split", big_dims(mode="prefill", length=300, k=64), None, 1.0),
+    ("prefill_odd_rows", big_dims(mode="prefill", length=301, k=64), None, 1.0),     # last query pair has one row
+    ("prefill_odd_rows_sharp", big_dims(mode="prefill", length=2500, k=64, prefill_q_start=2187), None, 900.0),
     ("prefill_two_splits", big_dims(mode="prefill", length=2600, k=64, prefill_q_start=2450), None, 1.0),
 ]
 
