@@ -432,10 +432,49 @@ def main():
             torch.cuda.synchronize()
             stage_ms.append(e0.elapsed_time(e1) / 3)
         ims = stage_ms[0]
+        # The stages as the fused forward runs them: one dsa_forward per query
+        # chunk of the full call (dsa_forward_chunk_rows), each bracketed by its
+        # stage events.  Unlike the standalone ops above, the fused path writes no
+        # -inf over the masked upper triangle and keeps a chunk's scores in its
+        # workspace.
+        piece = B.forward_chunk_rows(pb)
+        T = pin.num_q
+        fws = torch.empty(B.workspace_size(B.OP_FORWARD, pb), dtype=torch.uint8, device="cuda")
+        pout = torch.empty((T, pin.wl.heads, pin.wl.v_dim), dtype=pin.q.dtype, device="cuda")
+        pidx = torch.empty((T, pin.topk), dtype=torch.int32, device="cuda")
+        pieces = []
+        for c0 in range(0, T, piece):
+            c1 = min(T, c0 + piece)
+            pbc = B.make_problem(mode="prefill", q_pos=pin.q_pos[c0:c1], max_ctx=pin.max_ctx, num_seqs=pin.num_seqs,
+                                 block_table=pin.block_table, num_blocks=pin.num_blocks, max_seq_len=pin.max_seq_len,
+                                 index_heads=pin.wl.index_heads, index_dim=pin.wl.index_dim, topk=pin.topk,
+                                 heads=pin.wl.heads, qk_dim=pin.wl.qk_dim, v_dim=pin.wl.v_dim,
+                                 index_dtype=B.dtype_code(pin.q_idx), mla_dtype=B.dtype_code(pin.q))
+            pieces.append((pbc, c0, c1))
+        run_piece = lambda pbc, c0, c1, ev=None: B.forward(
+            pbc, pin.q_idx[c0:c1], None if pin.q_scale is None else pin.q_scale[c0:c1], pin.w[c0:c1], pin.k_cache,
+            pin.k_scale, pin.q[c0:c1], pin.kv_cache, pin.sm_scale, out=pout[c0:c1], topk_idx=pidx[c0:c1],
+            want_lse=False, ws=fws, stage_events=ev)
+        settle(torch, lambda: [run_piece(*pc) for pc in pieces], args.settle_ms / 2)
+        fused = [0.0, 0.0, 0.0]
+        reps = 2
+        for _ in range(reps):
+            evs = [make_events(torch, 4) for _ in pieces]
+            torch.cuda.synchronize()
+            for pc, ev in zip(pieces, evs):
+                run_piece(*pc, ev=ev)
+            torch.cuda.synchronize()
+            for ev in evs:
+                for j in range(3):
+                    fused[j] += ev[j].elapsed_time(ev[j + 1]) / reps
+        del fws, pout, pidx
         result["prefill"] = {
             "workload": pname, "tokens_per_s": round(pin.num_q / (pms * 1e-3), 1), "ms_per_step": round(pms, 3),
             "stage_ops_ms_all_rows": {"index_scores": round(stage_ms[0], 3), "topk": round(stage_ms[1], 3),
                                       "sparse_mla": round(stage_ms[2], 3)},
+            "fused_stages_ms": {"indexer": round(fused[0], 3), "topk": round(fused[1], 3), "attention": round(fused[2], 3)},
+            "indexer_mfma_frac_fused": round(pf_idx / (fused[0] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
+            "attention_mfma_frac_fused": round(pf_mla / (fused[2] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
             "indexer_mfma_frac": round(pf_idx / (ims * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
             "attention_mfma_frac": round(pf_mla / (stage_ms[2] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
             "step_mfma_frac": round((pf_idx + pf_mla) / (pms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4)}

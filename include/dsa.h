@@ -230,6 +230,11 @@ int dsa_sparse_mla(const dsa_seqs *seqs, const dsa_dims *dims, float sm_scale, c
 int dsa_forward(const dsa_seqs *seqs, const dsa_dims *dims, const dsa_forward_args *args,
                 void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Query rows per chunk that dsa_forward processes at a time for these shapes
+ * (all num_q rows for decode), so a caller can time or split work the way the
+ * call runs it.  0 for invalid arguments.  Host only; launches nothing. */
+int64_t dsa_forward_chunk_rows(const dsa_seqs *seqs, const dsa_dims *dims);
+
 /* Dense MLA, the attention DSA is measured against [ZS 3.4: at a 128K context
  * DSA decodes about twice as cheaply as dense MLA; LD: the dense warm-up
  * stage keeps dense attention]: step 3 over EVERY candidate s = 0..q_pos[t]

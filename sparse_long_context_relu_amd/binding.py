@@ -24,7 +24,7 @@ PREFILL, DECODE = 0, 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
 EXPORTS = ("dsa_workspace_size", "dsa_index_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward",
-           "dsa_dense_mla", "dsa_attention_probs", "dsa_indexer_kl", "dsa_indexer_backward", "dsa_indexer_kl_loss",
+           "dsa_dense_mla", "dsa_attention_probs", "dsa_indexer_kl", "dsa_indexer_backward", "dsa_indexer_kl_loss", "dsa_forward_chunk_rows",
            "dsa_quantize_fp8", "dsa_append_index_keys",
            "dsa_status_string")
 
@@ -91,6 +91,8 @@ def _load() -> ctypes.CDLL:
     lib.dsa_indexer_backward.restype = ctypes.c_int
     lib.dsa_indexer_kl_loss.argtypes = [sp, dp, ctypes.POINTER(DsaKlArgs), P, SZ, P]
     lib.dsa_indexer_kl_loss.restype = ctypes.c_int
+    lib.dsa_forward_chunk_rows.argtypes = [sp, dp]
+    lib.dsa_forward_chunk_rows.restype = ctypes.c_int64
     lib.dsa_quantize_fp8.argtypes = [I64, I32, I32, P, P, P, I32, P]
     lib.dsa_quantize_fp8.restype = ctypes.c_int
     lib.dsa_append_index_keys.argtypes = [sp, I32, I32, P, P, P, P]
@@ -168,6 +170,11 @@ def problem_from_inputs(inp, topk: Optional[int] = None) -> Problem:
                         max_seq_len=inp.max_seq_len, index_heads=wl.index_heads, index_dim=wl.index_dim,
                         topk=inp.topk if topk is None else topk, heads=wl.heads, qk_dim=wl.qk_dim,
                         v_dim=wl.v_dim, index_dtype=dtype_code(inp.q_idx), mla_dtype=dtype_code(inp.q))
+
+
+def forward_chunk_rows(pb: Problem) -> int:
+    """Query rows per chunk of dsa_forward for this problem."""
+    return int(LIB.dsa_forward_chunk_rows(ctypes.byref(pb.seqs), ctypes.byref(pb.dims)))
 
 
 def workspace_size(op: int, pb: Problem) -> int:

@@ -11,7 +11,7 @@ namespace {
 
 constexpr int kMaxCtx = 262144;
 constexpr long long kScoreBudget = 256ll << 20;  // bytes of score rows per prefill chunk
-constexpr long long kMinChunkRows = 4096;        // query rows per prefill chunk, at least
+constexpr long long kMinChunkRows = 8192;        // query rows per prefill chunk, at least
 constexpr int kQuantMaxLen = 65536;              // values per quantised row
 constexpr int kQuantMaxRepeat = 1024;            // copies of each row's scale
 constexpr long long kQuantMaxRows = 2147483647;  // one workgroup (or a quarter) per row
@@ -127,8 +127,9 @@ long long topk_ws_bytes(int rows, int max_ctx) {
 
 // Query rows per prefill chunk: as many as kScoreBudget bytes of score rows
 // hold, but never fewer than kMinChunkRows (the prefill indexer runs 8 rows per
-// workgroup, so a chunk must span the 256 CUs twice over; at long contexts that
-// takes more score memory than the budget: 1 GiB of rows at 64K).
+// workgroup; each chunk's launches end in a ragged tail, so chunks span the 256
+// CUs several times over; at long contexts that takes more score memory than
+// the budget: 2 GiB of rows at 64K).
 int forward_chunk_rows(const dsa_seqs *s) {
   if (s->mode == DSA_DECODE || s->num_q == 0) return s->num_q;
   long long rows = kScoreBudget / (score_ld(s) * 4);
@@ -375,6 +376,11 @@ DSA_EXPORT size_t dsa_workspace_size(int op, const dsa_seqs *seqs, const dsa_dim
     default:
       return 0;
   }
+}
+
+DSA_EXPORT int64_t dsa_forward_chunk_rows(const dsa_seqs *seqs, const dsa_dims *dims) {
+  if (check_seqs(seqs) != DSA_OK || check_index_dims(dims) != DSA_OK || check_mla_dims(dims) != DSA_OK) return 0;
+  return forward_chunk_rows(seqs);
 }
 
 DSA_EXPORT int dsa_index_scores(const dsa_seqs *seqs, const dsa_dims *dims, const void *q_idx,

@@ -248,7 +248,9 @@ def test_forward_validation_and_workspace():
     pf = B.make_problem(mode="prefill", q_pos=qp, max_ctx=65536, num_seqs=1, max_seq_len=65536,
                         index_dtype=B.FP8_E4M3FN)
     ws64k = B.workspace_size(B.OP_FORWARD, pf)
-    assert (1 << 30) <= ws64k < (3 << 29)          # 4096-row chunks of 256 KiB score rows, not 16 GiB
+    assert (2 << 30) <= ws64k < (5 << 29)          # 8192-row chunks of 256 KiB score rows, not 16 GiB
+    assert B.forward_chunk_rows(pf) == 8192
+    assert B.forward_chunk_rows(pb) == 2           # decode: every query in one chunk
 
 
 def test_quantize_and_append_validation():
