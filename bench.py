@@ -190,6 +190,61 @@ def fused_prefill_stages(B, torch, pin, settle_ms, reps=2):
     return fused
 
 
+def measured_ceilings(torch):
+    """Ceilings measured with library kernels next to the vendor peaks: a streaming
+    read (a reduction over 4 GiB) and a large bf16 GEMM (8192^3)."""
+    x = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+    a = torch.randn((8192, 8192), device="cuda").to(torch.bfloat16)
+    b = torch.randn((8192, 8192), device="cuda").to(torch.bfloat16)
+    y = torch.empty_like(x)
+    read_ms = time_op(torch, lambda: x.sum(), 10, 3, 100)
+    copy_ms = time_op(torch, lambda: y.copy_(x), 10, 3, 100)
+    gemm_ms = time_op(torch, lambda: torch.matmul(a, b), 10, 3, 200)
+    gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
+    res = {"hbm_copy_gbs": round(gbs(2 * x.numel() * 4, copy_ms), 1),
+           "hbm_copy_frac_of_spec": round(gbs(2 * x.numel() * 4, copy_ms) / HBM_PEAK_GBS, 4),
+           "hbm_reduce_read_gbs": round(gbs(x.numel() * 4, read_ms), 1),
+           "bf16_gemm_tflops": round(2 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
+           "bf16_gemm_frac_of_spec": round(2 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
+           "how": "device copy of 4 GiB (read + write bytes); torch sum over the same 4 GiB; torch.matmul of two "
+                  "8192x8192 bf16 matrices"}
+    del x, y, a, b
+    torch.cuda.empty_cache()
+    return res
+
+
+def fp8_index_quality(B, torch, inp):
+    """The e4m3fn indexer against the bf16 one on the same data (reported, not
+    gated): q_I and k_I of a bf16 workload quantised per token with
+    dsa_quantize_fp8, then scores and top-k of both compared."""
+    T, HI, DI = inp.q_idx.shape
+    pb16 = B.problem_from_inputs(inp)
+    s16 = B.index_scores(pb16, inp.q_idx, None, inp.w, inp.k_cache, None)
+    i16 = B.topk(pb16, s16)
+    q8, qs = B.quantize_fp8(inp.q_idx.reshape(T, HI * DI), scale_repeat=HI)
+    k8, ks = B.quantize_fp8(inp.k_cache.reshape(-1, DI))
+    pb8 = B.make_problem(mode=inp.mode, q_pos=inp.q_pos, max_ctx=inp.max_ctx, num_seqs=inp.num_seqs,
+                         block_table=inp.block_table, num_blocks=inp.num_blocks, max_seq_len=inp.max_seq_len,
+                         index_heads=HI, index_dim=DI, topk=inp.topk, index_dtype=B.FP8_E4M3FN)
+    s8 = B.index_scores(pb8, q8.view(T, HI, DI).view(torch.float8_e4m3fn), qs.view(T, HI), inp.w,
+                        k8.view(inp.k_cache.shape).view(torch.float8_e4m3fn), ks.view(inp.k_cache.shape[:-1]))
+    i8 = B.topk(pb8, s8)
+    torch.cuda.synchronize()
+    n = (inp.q_pos.long() + 1)
+    valid = torch.arange(s16.shape[1], device="cuda")[None, :] < n[:, None]
+    rel = ((s8 - s16).abs() / s16.abs().clamp_min(1e-30))[valid]
+    recall = []
+    for r in range(T):
+        a, b = i16[r], i8[r]
+        a, b = a[a >= 0], b[b >= 0]
+        recall.append(torch.isin(b, a).float().mean().item() if a.numel() else 1.0)
+    return {"workload": inp.wl.name, "score_rel_err_median": round(rel.median().item(), 5),
+            "score_rel_err_p99": round(torch.quantile(rel[::max(1, rel.numel() // 1000000)].float(), 0.99).item(), 5),
+            "topk_recall_mean": round(sum(recall) / len(recall), 4), "topk_recall_min": round(min(recall), 4),
+            "how": "per-token amax/448 scales (dsa_quantize_fp8), e4m3fn indexer vs the bf16 indexer on the same "
+                   "bf16 data; recall = share of the fp8 selection inside the bf16 selection"}
+
+
 def time_op(torch, op, steps, warmup, settle_ms):
     """Mean ms of `op` over `steps` back-to-back calls after a settle and `warmup` calls."""
     settle(torch, op, settle_ms)
@@ -326,6 +381,8 @@ def main():
                     help="skip the dense-MLA comparison (attention over every candidate) on the same inputs")
     ap.add_argument("--no-warmup-objective", action="store_true",
                     help="skip the indexer warm-up objective (loss and backward) on the prefill inputs")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the measured ceilings and the fp8 indexing-quality report")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -394,6 +451,10 @@ def main():
         "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
     }
 
+    if wl.mode == "decode" and wl.index_dtype == "bf16" and not args.no_extras:
+        log("fp8 indexing quality against bf16 on the same inputs")
+        result["fp8_index_quality"] = fp8_index_quality(B, torch, inp)
+        torch.cuda.empty_cache()
     dense = {}
     if not args.no_dense:
         log("dense MLA on the same inputs")
@@ -476,6 +537,18 @@ def main():
             stage_ms.append(e0.elapsed_time(e1) / 3)
         ims = stage_ms[0]
         fused = fused_prefill_stages(B, torch, pin, args.settle_ms / 2)
+        planted = None
+        if pin.planted is not None:
+            # share of planted keys among the selected positions of the rows
+            # that select (n > k), against their share among those rows' candidates
+            mark = torch.zeros(pin.max_ctx, dtype=torch.bool, device="cuda")
+            mark[pin.planted] = True
+            rows_sel = (pin.q_pos.long() + 1) > pin.topk
+            sel = idx[rows_sel]
+            cum = torch.cumsum(mark.long(), 0)
+            planted = {"share_in_topk": round(mark[sel.long()].float().mean().item(), 4),
+                       "share_in_candidates": round((cum[pin.q_pos.long()[rows_sel]].float() /
+                                                     (pin.q_pos.long()[rows_sel] + 1).float()).mean().item(), 4)}
         result["prefill"] = {
             "workload": pname, "tokens_per_s": round(pin.num_q / (pms * 1e-3), 1), "ms_per_step": round(pms, 3),
             "stage_ops_ms_all_rows": {"index_scores": round(stage_ms[0], 3), "topk": round(stage_ms[1], 3),
@@ -485,7 +558,8 @@ def main():
             "attention_mfma_frac_fused": round(pf_mla / (fused[2] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
             "indexer_mfma_frac": round(pf_idx / (ims * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
             "attention_mfma_frac": round(pf_mla / (stage_ms[2] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
-            "step_mfma_frac": round((pf_idx + pf_mla) / (pms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4)}
+            "step_mfma_frac": round((pf_idx + pf_mla) / (pms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
+            "planted_keys": planted}
         log(f"prefill {pms:.2f} ms/step, indexer {ims:.2f} ms")
         del sc, idx, tws, mws
         torch.cuda.empty_cache()
@@ -501,6 +575,11 @@ def main():
     if dense:
         # the comparison the pages draw: DSA against dense MLA over the same contexts
         result["dense_comparison"] = dense
+    if not args.no_extras:
+        inp = None
+        torch.cuda.empty_cache()
+        log("measured ceilings")
+        result["measured_ceilings"] = measured_ceilings(torch)
     if not args.no_cpu_baseline:
         if inp is None:
             inp = generate(wl, "cuda")
