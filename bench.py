@@ -387,7 +387,7 @@ def main():
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path is data-parallel across sequences; sharding is described, not built)", file=sys.stderr)
         sys.exit(2)
 
