@@ -248,3 +248,28 @@ def test_indexer_objective_full_size():
     dkg = dk[0, keys_s].cpu().numpy()
     for j, s in enumerate(keys_s):
         assert _rel_rms(dkg[j], dk_ref[j]) <= 2e-2, f"key {s}: dk rel RMS {_rel_rms(dkg[j], dk_ref[j]):.3e}"
+
+
+def test_indexer_objective_edge_cases():
+    """A query with no candidates and one with a single candidate: loss 0, zero gradients
+    (one candidate: p = softmax(I) = [1]); a full row next to them matches the oracle."""
+    _say("indexer objective edge cases")
+    inp = generate(big_dims(mode="decode", num_seqs=3, length=3000, k=64, paged=True), DEV, lengths=[3000, 1, 2000])
+    inp.q_pos[2] = -1
+    pb = B().problem_from_inputs(inp)
+    dk0 = torch.full(tuple(inp.k_cache.shape), 7.0, dtype=torch.float32, device=DEV)
+    loss, dq, dw, dk = B().indexer_kl_loss(pb, inp.q_idx, inp.w, inp.k_cache, inp.q, inp.kv_cache, inp.sm_scale,
+                                           dk=dk0)
+    torch.cuda.synchronize()
+    L = loss.cpu().numpy()
+    assert L[1] == 0.0 and L[2] == 0.0
+    assert torch.all(dq[1:] == 0) and torch.all(dw[1:] == 0)
+    # the sequence without a query sees no key: its slots keep their contents
+    bt = inp.block_table[2]
+    for blk in bt[: (2000 + 63) // 64].tolist():
+        assert torch.all(dk[blk] == 7.0)
+    # the single candidate's slot is written with 0
+    assert torch.all(dk[int(inp.block_table[1, 0]), 0] == 0)
+    ref = oracle.indexer_kl_loss(to_oracle(inp), [0])
+    assert abs(L[0] - ref["loss"][0]) <= 1e-3 * abs(ref["loss"][0])
+    assert _rel_rms(dq[0].cpu().numpy(), ref["dq"][0]) <= 2e-2
