@@ -50,6 +50,7 @@ __device__ __forceinline__ void lds_dma4(const void *gsrc, uint32_t m0) {
 constexpr int kWaitVm0 = 0x0F70;      // vector-memory count <= 0, the others free
 __host__ __device__ constexpr int wait_vm(int n) { return 0x0F70 | n; }   // vmcnt <= n (n < 16)
 constexpr int kWaitLgkm0 = 0xC07F;    // LDS / scalar counts <= 0, vector memory left in flight
+constexpr int kWaitNone = 0xCF7F;     // every count at its maximum: no wait
 
 // Workgroup barrier without a memory fence: the fence of __syncthreads would
 // also wait for the tile loads still streaming into the other buffers.  LDS

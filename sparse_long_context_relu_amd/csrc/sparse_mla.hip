@@ -134,6 +134,36 @@ __device__ __forceinline__ void issue_tile(uint32_t tile, const uint8_t *kv, con
   for (int j = 0; j < kWaveLoads; ++j) tile_load(t, j, tile, wv);
 }
 
+// The same gather issued by half of the waves (h = wave index within the half,
+// twice the loads each: load j covers positions (4 j + h) 64 + [0, 64)).  The
+// passes without a value product alternate the halves from tile to tile: each
+// tile's issue burst then stalls only four waves, while the other four go on
+// with their logits.
+constexpr int kHalfWaves = kWaves / 2;
+constexpr int kHalfLoads = kTileLoads / kHalfWaves;   // 10
+__device__ __forceinline__ void issue_tile_half(uint32_t tile, const uint8_t *kv, const int *slots, int j0,
+                                                int fallback, int h, int lane) {
+  asm volatile("" : "+v"(lane));
+  // two batches of five: slot reads, then the loads
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    constexpr int kB = kHalfLoads / 2;
+    int sl[kB], dc[kB];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const int p = ((b * kB + j) * kHalfWaves + h) * 64 + lane;
+      const int row = p / kRowChunks, ch = p - row * kRowChunks;
+      sl[j] = slots[j0 + row];
+      dc[j] = ch < kDataChunks ? ch ^ swz(row) : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const int src = sl[j] < 0 ? fallback : sl[j];
+      lds_dma16(kv + (long long)src * (kD * 2) + dc[j] * 16, tile + ((b * kB + j) * kHalfWaves + h) * 1024);
+    }
+  }
+}
+
 // Sum over the 16 lanes of a row of the wave (the 16 heads of a lane group),
 // in every lane of the row: two quad swaps, then the half-row and row mirrors.
 __device__ __forceinline__ float sum16(float x) {
@@ -439,11 +469,21 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
 
   if (fb >= 0) {
     // Three tile buffers: tiles tt+1 and tt+2 stream in while tile tt is used.
-    issue_tile(tile_lds, kv, slots, 0, fb, wv, lane);
+    // tile tt's gather: every wave (attention), or half (tt even: waves 0-3, odd: 4-7)
+    constexpr bool kHalf = kMode != kModeAttn;
+    const int half = wv / kHalfWaves, hw = wv % kHalfWaves;
+    auto issue = [&](uint32_t buf, int tt) {
+      if constexpr (kHalf) {
+        if ((tt & 1) == half) issue_tile_half(buf, kv, slots, tt * kR, fb, hw, lane);
+      } else {
+        issue_tile(buf, kv, slots, tt * kR, fb, wv, lane);
+      }
+    };
+    issue(tile_lds, 0);
     // Drain the query operand loads (with tile 0) here, so that no wait for them
     // is placed inside the loop, where it would also wait for the prefetches.
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    if (ntiles > 1) issue_tile(tile_lds + kTileBytes, kv, slots, kR, fb, wv, lane);
+    if (ntiles > 1) issue(tile_lds + kTileBytes, 1);
     int cur = 0;
     for (int tt = 0; tt < ntiles; ++tt) {
       // This wave's loads of tile tt have landed once at most the loads of tile
@@ -451,14 +491,15 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
       // orders every wave's reads of tile tt-1 before its buffer is refilled.
       // (probs: the head sums of tile tt-1 written to LDS are complete as well)
       constexpr int kLgkm = kMode == kModeProbs ? 0x0F00 : 0;
-      if (tt + 1 < ntiles)
-        __builtin_amdgcn_s_waitcnt(wait_vm(kWaveLoads) & ~kLgkm);
-      else
+      // (halves: a wave's only outstanding loads are of its own half's tile, tt or tt+1)
+      if (kHalf ? (tt & 1) == half : tt + 1 >= ntiles)
         __builtin_amdgcn_s_waitcnt(kWaitVm0 & ~kLgkm);
+      else
+        __builtin_amdgcn_s_waitcnt((kHalf ? kWaitNone : wait_vm(kWaveLoads)) & ~kLgkm);
       lds_barrier();
       if (tt + 2 < ntiles) {
         const int nb = cur == 0 ? 2 : cur - 1;     // (tt + 2) % 3
-        issue_tile(tile_lds + nb * kTileBytes, kv, slots, (tt + 2) * kR, fb, wv, lane);
+        issue(tile_lds + nb * kTileBytes, tt + 2);
       }
       if (kMode == kModeProbs && tt > 0 && wv == 0) write_probs(tt - 1);
       consume_tile<kMode, kQ>(tile_lds + cur * kTileBytes, slots, tt * kR, qb, acc, m_run, l_run, scale2, qk_off,
