@@ -65,12 +65,24 @@ __device__ __forceinline__ int split_len(int k, int n_split) {
   return (len + kR - 1) / kR * kR;
 }
 
-// Block order: the splits of one query are placed on the same XCD (workgroups
-// are dealt to the 8 XCDs round-robin by linear id), so its query rows are
-// fetched from HBM once and then served by that XCD's L2.
+// Block order.  Workgroups are dealt to the 8 XCDs round-robin by linear id,
+// and each XCD has its own L2.
+//   * Dense prefill lists: every query reads the same rows 0..t, so the
+//     workgroups that run together on one XCD take the same split of
+//     different queries (XCD x serves groups x, x+8, ..., split after split).
+//     Their tiles then come from one 2048-row range of the cache, which that
+//     L2 holds, instead of from every split's range at once.
+//   * Otherwise the splits of one query are placed on the same XCD, so its
+//     query rows are fetched once and then served by that XCD's L2.
 __device__ __forceinline__ void mla_block(const MlaArgs &a, int groups, int &sp, int &r) {
   const int total = a.n_split * groups;
   int v = blockIdx.x;
+  if (a.dense && a.sv.mode == DSA_PREFILL && (groups & 7) == 0) {
+    const int per_xcd = groups >> 3, k = v >> 3;
+    sp = k / per_xcd;
+    r = (k - sp * per_xcd) * 8 + (v & 7);
+    return;
+  }
   if ((total & 7) == 0) v = (v & 7) * (total >> 3) + (v >> 3);
   r = v / a.n_split;
   sp = v - r * a.n_split;
