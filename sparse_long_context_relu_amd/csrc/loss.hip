@@ -160,6 +160,7 @@ __global__ __launch_bounds__(256) void indexer_bwd_q_kernel(BwdArgs a) {
   }
   const float wh = a.w[(long long)t * kBwdHeads + h];
   const float *grow = a.grad + (long long)r * a.ld + i0;
+  const bool gvec = ((uintptr_t)grow & 15) == 0;
   const uint8_t *kbase = reinterpret_cast<const uint8_t *>(a.k_cache);
 
   // Tile tt holds candidates i0 + tt*32 .. + 31 (inside one 64-token block).
@@ -176,13 +177,19 @@ __global__ __launch_bounds__(256) void indexer_bwd_q_kernel(BwdArgs a) {
       const bool ok = sn >= 0 && tt * kBwdR + row < nk;
       pf[u] = ld16(kbase + (ok ? sn + row : 0) * kBwdRowBytes + ch * 16);
     }
+    // rows 16 rb + 4 g + [0, 4): one 16-byte load each where the gradient row
+    // is 16-byte aligned (kr is a multiple of 4), element loads otherwise
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 2; ++rb) {
+      const int kr = tt * kBwdR + 16 * rb + 4 * g;
+      if (gvec && kr + 3 < nk) {
+        const float4 v4 = *reinterpret_cast<const float4 *>(grow + kr);
+        gn[rb * 4 + 0] = v4.x; gn[rb * 4 + 1] = v4.y; gn[rb * 4 + 2] = v4.z; gn[rb * 4 + 3] = v4.w;
+      } else {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int kr = tt * kBwdR + 16 * rb + 4 * g + v;
-        gn[rb * 4 + v] = kr < nk ? grow[kr] : 0.f;
+        for (int v = 0; v < 4; ++v) gn[rb * 4 + v] = kr + v < nk ? grow[kr + v] : 0.f;
       }
+    }
   };
   auto put = [&](int buf, int tt) {
 #pragma unroll
