@@ -582,10 +582,30 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
 // exp2(max_s - M) sum_s, normalised over the splits.  The loads of up to eight
 // splits are issued together, and the weighted sum runs in split order.  A
 // dense list merges only the splits that hold a position.
+// The combine's (query, head group) of workgroup blockIdx.x, placed on the XCD
+// whose workgroups wrote that query's split partials (mla_block), so that the
+// partials are read from that XCD's L2.
+__device__ __forceinline__ void combine_block(const MlaArgs &a, int &r, int &hg) {
+  constexpr int kGroups = kH / 4;
+  const int v = blockIdx.x;
+  if ((a.rows & 7) == 0) {
+    const int x = v & 7, k = v >> 3;
+    hg = k % kGroups;
+    if (a.dense && a.sv.mode == DSA_PREFILL)
+      r = (k / kGroups) * 8 + x;                  // XCD x: queries x, x+8, ...
+    else
+      r = x * (a.rows >> 3) + k / kGroups;        // XCD x: a contiguous eighth of the queries
+    return;
+  }
+  r = v / kGroups;
+  hg = v - r * kGroups;
+}
+
 __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
   const int lane = lane_id();
-  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int r = blockIdx.y;
+  int r, hg;
+  combine_block(a, r, hg);
+  const int h = hg * 4 + (threadIdx.x >> 6);
   const int t = a.q_begin + r;
   const int ns = a.n_split;
   int nm = ns;
@@ -793,7 +813,7 @@ hipError_t launch_sparse_mla(const MlaArgs &a, hipStream_t st) {
       hipLaunchKernelGGL((mla_bf16_kernel<kModeProbs, 1>), grid, dim3(kThreads), 0, st, a);
   } else {
     hipLaunchKernelGGL((mla_bf16_kernel<kModeAttn, 1>), grid, dim3(kThreads), 0, st, a);
-    if (a.n_split > 1) hipLaunchKernelGGL(mla_combine_kernel, dim3(kH / 4, a.rows), dim3(256), 0, st, a);
+    if (a.n_split > 1) hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(kH / 4) * (unsigned)a.rows), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
