@@ -161,11 +161,15 @@ def gather_rows(cache: np.ndarray, inp: OracleInputs, b: int, positions: np.ndar
 
 
 def gather_scales(scale: np.ndarray, inp: OracleInputs, b: int, positions: np.ndarray) -> np.ndarray:
+    """fp32 key scales of sequence ``b`` at logical ``positions``: one scale per
+    cache slot, addressed exactly like the key rows (``gather_rows``)."""
     positions = np.asarray(positions, dtype=np.int64)
     if inp.block_table is None:
         return scale[b][positions]
     bs = inp.block_size
     blocks = np.asarray(inp.block_table[b], dtype=np.int64)[positions // bs]
+    if np.any(blocks < 0) or np.any(blocks >= scale.shape[0]):
+        raise ValueError("block table entry out of range for a candidate position")
     return scale[blocks, positions % bs]
 
 

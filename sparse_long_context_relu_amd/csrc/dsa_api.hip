@@ -143,15 +143,28 @@ struct ForwardLayout {
   long long ld, off_scores, off_idx, off_topk, off_mla, total;
 };
 
+// Every chunk of a call starts its regions at the same offsets, and a region's
+// size depends on the chunk's row count: a short last chunk takes the sliced
+// top-k layout (longer rows) and splits its attention rows (partials that a
+// full chunk does not have).  Each region is therefore sized for the larger of
+// the full chunk and the tail chunk.
 ForwardLayout forward_layout(const dsa_seqs *s, const dsa_dims *d) {
   ForwardLayout L;
   L.chunk = forward_chunk_rows(s);
   L.ld = score_ld(s);
+  const int tail = L.chunk > 0 ? s->num_q % L.chunk : 0;
+  long long topk_b = topk_ws_bytes(L.chunk, s->max_ctx);
+  long long mla_b = mla_ws_bytes(d, L.chunk);
+  if (tail > 0) {
+    const long long tt = topk_ws_bytes(tail, s->max_ctx), tm = mla_ws_bytes(d, tail);
+    topk_b = tt > topk_b ? tt : topk_b;
+    mla_b = tm > mla_b ? tm : mla_b;
+  }
   L.off_scores = 0;
   L.off_idx = align256(L.ld * L.chunk * 4);
   L.off_topk = L.off_idx + align256((long long)L.chunk * d->topk * 4);
-  L.off_mla = L.off_topk + align256(topk_ws_bytes(L.chunk, s->max_ctx));
-  L.total = L.off_mla + align256(mla_ws_bytes(d, L.chunk));
+  L.off_mla = L.off_topk + align256(topk_b);
+  L.total = L.off_mla + align256(mla_b);
   return L;
 }
 

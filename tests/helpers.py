@@ -34,11 +34,11 @@ def to_oracle(inp) -> OracleInputs:
 def small_workload(mode="prefill", length=40, num_seqs=1, H_I=3, d_I=8, k=6, H=2, D=12, Dv=8,
                    index_dtype="f32", mla_dtype="f32", paged=False, seed=11, length_range=None,
                    w_high=1.0, qkv_std=None, prefill_q_start=0, planted_frac=0.0,
-                   block_size=64) -> Workload:
+                   block_size=64, w_low=0.0) -> Workload:
     return Workload(name="small", seed=seed, mode=mode, num_seqs=num_seqs, length=length,
                     length_range=length_range, paged=paged, block_size=block_size,
                     index_heads=H_I, index_dim=d_I, topk=k, heads=H, qk_dim=D, v_dim=Dv,
-                    index_dtype=index_dtype, mla_dtype=mla_dtype, w_high=w_high,
+                    index_dtype=index_dtype, mla_dtype=mla_dtype, w_high=w_high, w_low=w_low,
                     qkv_std=(1.0 / math.sqrt(D)) if qkv_std is None else qkv_std,
                     sm_scale=1.0 / math.sqrt(D), prefill_q_start=prefill_q_start,
                     planted_frac=planted_frac)

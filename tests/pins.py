@@ -347,6 +347,37 @@ def pin_paged_equals_contiguous(o):
         assert np.array_equal(a[key], b_[key]), key
 
 
+def pin_paged_fp8_equals_contiguous(o):
+    """An e4m3fn indexer's key codes *and* their per-token fp32 scales re-laid into
+    permuted 4-token blocks give identical scores, selections, outputs and lse.
+    The scales are first spread over [1/4, 4] per token, so a scale read from the
+    wrong slot, or not read, changes the scores."""
+    rng = np.random.default_rng(16)
+    wl = small_workload(mode="decode", num_seqs=3, length=37, k=5, index_dtype="fp8")
+    oi = to_oracle(generate(wl, "cpu", lengths=[37, 11, 26]))
+    assert oi.index_dtype == "fp8" and oi.k_scale is not None
+    oi.k_scale = (oi.k_scale * rng.uniform(0.25, 4.0, oi.k_scale.shape)).astype(np.float32)
+    a = o.forward(oi, keep_scores=True)
+    bs = 4
+    B, L = oi.kv_cache.shape[:2]
+    nb = (L + bs - 1) // bs
+    table = rng.permutation(B * nb).reshape(B, nb)
+    kc = np.full((B * nb, bs) + oi.k_cache.shape[2:], 0x7F, oi.k_cache.dtype)     # e4m3fn NaN codes
+    ks = np.full((B * nb, bs), np.nan, np.float32)
+    vc = np.full((B * nb, bs) + oi.kv_cache.shape[2:], np.nan, oi.kv_cache.dtype)
+    for b in range(B):
+        for s in range(L):
+            kc[table[b, s // bs], s % bs] = oi.k_cache[b, s]
+            ks[table[b, s // bs], s % bs] = oi.k_scale[b, s]
+            vc[table[b, s // bs], s % bs] = oi.kv_cache[b, s]
+    oi.block_table, oi.block_size, oi.k_cache, oi.k_scale, oi.kv_cache = table, bs, kc, ks, vc
+    b_ = o.forward(oi, keep_scores=True)
+    for key in ("idx", "out", "lse"):
+        assert np.array_equal(a[key], b_[key]), key
+    for t in range(3):
+        assert np.array_equal(a["scores"][t], b_["scores"][t]), f"scores of query {t}"
+
+
 def pin_prefill_row_equals_decode(o):
     """Prefill row t equals a decode step whose context is the first t+1 tokens."""
     wl = small_workload(mode="prefill", length=30, k=7)

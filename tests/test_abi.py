@@ -278,3 +278,31 @@ def test_status_strings():
     for s in (B.OK, B.ERR_INVALID_ARG, B.ERR_UNSUPPORTED, B.ERR_WORKSPACE, B.ERR_HIP):
         assert B.status_string(s).startswith("DSA_")
     assert "unknown" in B.status_string(12345)
+
+
+@pytest.mark.parametrize("T", [8292, 8192 + 255, 65791, 131327, 16384 + 1])
+def test_forward_workspace_covers_ragged_tail_chunk(T):
+    """A prefill whose last query chunk is short (T mod chunk in [1, 255]) runs that
+    chunk with the sliced top-k layout and split attention rows, both larger per row
+    than a full chunk's.  Every chunk starts its regions at the same offsets, so the
+    forward workspace must hold, after the score and index regions of a full chunk,
+    the larger top-k region and the larger split-partial region of the two chunk
+    sizes (each taken from the standalone ops' workspace sizes, which use the same
+    layouts)."""
+    a256 = lambda x: (x + 255) // 256 * 256
+    qp = torch.arange(T, dtype=torch.int32)
+    pf = B.make_problem(mode="prefill", q_pos=qp, max_ctx=T, num_seqs=1, max_seq_len=T)
+    chunk = B.forward_chunk_rows(pf)
+    tail = T % chunk
+    assert chunk == 8192 and 0 < tail < 256
+    need = B.workspace_size(B.OP_FORWARD, pf)
+
+    def part(rows):
+        p = B.make_problem(mode="prefill", q_pos=qp[T - rows:], max_ctx=T, num_seqs=1, max_seq_len=T)
+        return B.workspace_size(B.OP_TOPK, p), B.workspace_size(B.OP_SPARSE_MLA, p)
+
+    (tk_full, ml_full), (tk_tail, ml_tail) = part(chunk), part(tail)
+    assert ml_tail > ml_full == 0          # only the short chunk splits its attention rows
+    ld = (T + 63) // 64 * 64
+    want = a256(ld * chunk * 4) + a256(chunk * 2048 * 4) + a256(max(tk_full, tk_tail)) + a256(max(ml_full, ml_tail))
+    assert need >= want, (need, want)

@@ -108,3 +108,45 @@ def test_workload_full_size(name, extra):
         m = min(inp.topk, n)
         o_ref, l_ref = oracle.query_attention(oi, li, ig[t, :m])
         check_attention(og[t], lg[t], o_ref, l_ref, OUT_TOL[inp.wl.mla_dtype], f"{name} row {t}")
+
+
+RAGGED_CASES = [
+    # T = 8192 + 100: one full query chunk, then a 100-row chunk (sliced top-k, split attention rows)
+    ("prefill_8292_bf16", dict(mode="prefill", length=8292, k=2048)),
+    # T = 8192 + 255 with the e4m3fn indexer and a paged cache
+    ("prefill_8447_fp8_paged", dict(mode="prefill", length=8447, k=2048, index_dtype="fp8", paged=True)),
+]
+
+
+@pytest.mark.parametrize("name,kw", RAGGED_CASES, ids=[c[0] for c in RAGGED_CASES])
+def test_prefill_ragged_tail_chunk(name, kw):
+    """A prefill whose last query chunk is short runs it with its own top-k and
+    attention layouts inside the workspace sized by dsa_workspace_size: every row
+    equals the staged ops bit for bit and passes the certificate, and sampled rows
+    on both sides of the chunk boundary match the oracle."""
+    from tests.test_gpu_ops import big_dims
+    _say("ragged tail chunk", name)
+    inp = generate(big_dims(**kw), DEV)
+    pb = B().problem_from_inputs(inp)
+    assert B().forward_chunk_rows(pb) == 8192 and 0 < inp.num_q % 8192 < 256
+    out, lse, idx = B().forward_inputs(inp)
+    scores = B().index_scores(pb, inp.q_idx, inp.q_scale, inp.w, inp.k_cache, inp.k_scale)
+    idx2 = B().topk(pb, scores)
+    out2, lse2 = B().sparse_mla(pb, inp.sm_scale, inp.q, inp.kv_cache, idx2)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2), "fused selection differs from the staged ops"
+    certificate_all_rows(scores, idx, inp.q_pos, inp.topk)
+    # the staged attention runs every row in one launch (other splits): within tolerance
+    assert torch.max(torch.abs(out.float() - out2.float())).item() <= 2e-2
+    T = inp.num_q
+    rows = [0, 2048, 8191, 8192, 8193, T - 2, T - 1]
+    oi, local = to_oracle_rows(inp, rows)
+    sc_h = scores[rows].cpu().numpy()
+    ig, og, lg = idx.cpu().numpy(), out.float().cpu().numpy(), lse.cpu().numpy()
+    for i, t in enumerate(rows):
+        ref = oracle.query_index_scores(oi, local[i])
+        n = ref.shape[0]
+        check_scores(sc_h[i][:n], ref, SCORE_TOL[inp.wl.index_dtype], f"{name} row {t}")
+        check_topk_row_e2e(ig[t], ref, inp.topk, f"{name} row {t}")
+        o_ref, l_ref = oracle.query_attention(oi, local[i], ig[t, :min(inp.topk, n)])
+        check_attention(og[t], lg[t], o_ref, l_ref, OUT_TOL["bf16"], f"{name} row {t}")

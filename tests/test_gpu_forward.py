@@ -42,6 +42,14 @@ FORWARD_CASES = [
     ("prefill", dict(mode="prefill", length=2600, k=2048, prefill_q_start=2000), None),
     ("prefill_fp8", dict(mode="prefill", length=2300, k=2048, prefill_q_start=2030, index_dtype="fp8"), None),
     ("prefill_short_k", dict(mode="prefill", length=700, k=100), None),
+    # mixed-sign head weights: rows of negative and positive scores through the fused top-k
+    ("decode_paged_mixed_w", dict(mode="decode", num_seqs=3, length=7000, k=2048, paged=True, w_low=-1 / 8),
+     [7000, 2050, 4096]),
+    ("decode_paged_fp8_mixed_w", dict(mode="decode", num_seqs=3, length=6000, k=2048, paged=True,
+                                      index_dtype="fp8", w_low=-1 / 8), [6000, 3000, 2100]),
+    ("prefill_mixed_w", dict(mode="prefill", length=2500, k=2048, prefill_q_start=2040, w_low=-1 / 8), None),
+    ("prefill_fp8_mixed_w", dict(mode="prefill", length=2400, k=2048, prefill_q_start=2100, index_dtype="fp8",
+                                 w_low=-1 / 8), None),
 ]
 
 

@@ -10,7 +10,9 @@ relative on the same fp32 inputs.  For a given score gradient, dw (fp32
 throughout) agrees to 1e-4 relative RMS and dq, dk, which take the masked,
 weighted score gradient as a bf16 MFMA operand (2^-9 relative rounding), to
 1e-2; end to end, where the two sides' score gradients differ as well, 1e-3
-and 2e-2."""
+and 2e-2.  Beside these norm gates every element of dq, dw and dk is checked
+against a bound derived from the same arithmetic (``_bwd_with_bounds``), for
+the score gradient the GPU used."""
 import math
 
 import numpy as np
@@ -131,6 +133,49 @@ def test_indexer_kl_rows(name, wl, lengths):
         assert abs(L[t] - ref["loss"][i]) <= 1e-3 * max(abs(ref["loss"][i]), 1e-3), f"{name} row {t}: end to end"
 
 
+def _bwd_with_bounds(q_t, w_t, keys, g):
+    """The oracle's dq, dw, dk of one query for the score gradient g, with a bound on
+    each element's error that follows from the kernels' arithmetic:
+
+    * x = q . k is an fp32 MFMA sum of exact bf16 products, off by at most
+      eps = 2^-16 * sum_d |q_d k_d| (a 256x margin over fp32 rounding of 128 terms);
+      where |x| <= eps the GPU's ReLU mask may differ from the oracle's, and such a
+      term may be wholly present or absent (it is added to the bound in full).
+    * G = g w [x > 0] enters the dq and dk products as a bf16 operand: relative
+      rounding 2^-9, bounded here by 2^-8; the fp32 accumulation of N terms adds at
+      most N 2^-23 of the sum of their magnitudes.
+    * dw = sum_s g ReLU(x) is fp32 throughout, and ReLU is continuous, so a mask
+      flip costs at most |g| eps.
+
+    Returns (dq, dw, dk, dq_bound, dw_bound, dk_bound) for this query; the dk
+    terms carry the N used (heads x keys for dq, heads for one query's dk)."""
+    x = q_t @ keys.T                                             # [H_I, n]
+    eps = 2.0 ** -16 * (np.abs(q_t) @ np.abs(keys).T)
+    amb = np.abs(x) <= eps
+    on = x > 0
+    H_I, n = x.shape
+    gm = np.abs(g)[None, :] * np.abs(w_t)[:, None]               # |g w| per (head, key)
+    dq, dw, dk = oracle.index_scores_backward(q_t, w_t, keys, g)
+    a_on = (gm * on) @ np.abs(keys)                              # sum of |G k| over the keys
+    a_amb = (gm * amb) @ np.abs(keys)
+    dq_b = (2.0 ** -8 + n * 2.0 ** -23) * a_on + a_amb
+    dw_b = (np.abs(g)[None, :] * eps).sum(axis=1) + n * 2.0 ** -23 * (np.abs(g)[None, :] * np.maximum(x, 0)).sum(axis=1)
+    k_on = (gm * on).T @ np.abs(q_t)                             # [n, d_I]
+    k_amb = (gm * amb).T @ np.abs(q_t)
+    dk_b = (2.0 ** -8) * k_on + k_amb
+    return dq, dw, dk, dq_b, dw_b, dk_b, k_on
+
+
+def _check_within(got, want, bound, what):
+    """Element-wise |got - want| <= bound (+ a 1e-30 floor for exact zeros)."""
+    got = np.asarray(got, dtype=np.float64)
+    d = np.abs(got - want) - bound - 1e-30
+    if np.any(d > 0):
+        i = np.unravel_index(np.argmax(d), d.shape)
+        raise AssertionError(f"{what}: {int((d > 0).sum())} elements outside the bound; worst at {i}: "
+                             f"got {got[i]:.6e} want {want[i]:.6e} bound {bound[i]:.3e}")
+
+
 def _rel_rms(got, want):
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
@@ -161,20 +206,31 @@ def test_indexer_backward(name, wl, lengths):
     G = grad.cpu().numpy().astype(np.float64)
     oi = to_oracle(inp)
     dk_ref = np.zeros(dk.shape, dtype=np.float64)
+    dk_bnd = np.zeros(dk.shape, dtype=np.float64)
+    dk_mag = np.zeros(dk.shape, dtype=np.float64)
+    dk_cnt = np.zeros(dk.shape[:-1], dtype=np.float64)
     dqg, dwg, dkg = dq.cpu().numpy(), dw.cpu().numpy(), dk.cpu().numpy()
     dq_ref = np.zeros(dqg.shape)
     dw_ref = np.zeros(dwg.shape)
     for t in range(inp.num_q):
         q_t, w_t, keys = oracle.query_index_operands(oi, t)
         n = keys.shape[0]
-        dq_ref[t], dw_ref[t], dk_t = oracle.index_scores_backward(q_t, w_t, keys, G[t, :n])
+        dq_ref[t], dw_ref[t], dk_t, dq_b, dw_b, dk_b, k_on = _bwd_with_bounds(q_t, w_t, keys, G[t, :n])
+        _check_within(dqg[t], dq_ref[t], dq_b, f"{name}: dq of query {t}")
+        _check_within(dwg[t], dw_ref[t], dw_b, f"{name}: dw of query {t}")
         b = oracle.sequence_of(oi, t)
         pos = np.arange(n)
         if oi.block_table is None:
-            dk_ref[b, pos] += dk_t
+            where = (np.full(n, b), pos)
         else:
             blocks = np.asarray(oi.block_table[b], dtype=np.int64)[pos // oi.block_size]
-            np.add.at(dk_ref, (blocks, pos % oi.block_size), dk_t)
+            where = (blocks, pos % oi.block_size)
+        np.add.at(dk_ref, where, dk_t)
+        np.add.at(dk_bnd, where, dk_b)
+        np.add.at(dk_mag, where, k_on)
+        np.add.at(dk_cnt, where, float(q_t.shape[0]))
+    # fp32 accumulation over every (query, head) term of a key
+    _check_within(dkg, dk_ref, dk_bnd + dk_cnt[..., None] * 2.0 ** -23 * dk_mag, f"{name}: dk")
     assert _rel_rms(dwg, dw_ref) <= 1e-4, f"{name}: dw rel RMS {_rel_rms(dwg, dw_ref):.3e}"
     assert _rel_rms(dqg, dq_ref) <= 1e-2, f"{name}: dq rel RMS {_rel_rms(dqg, dq_ref):.3e}"
     assert _rel_rms(dkg, dk_ref) <= 1e-2, f"{name}: dk rel RMS {_rel_rms(dkg, dk_ref):.3e}"
@@ -196,12 +252,22 @@ def test_indexer_objective_end_to_end():
     loss = B().indexer_kl(pb, scores, probs)
     dq, dw, dk = B().indexer_backward(pb, inp.q_idx, inp.w, inp.k_cache, scores)
     torch.cuda.synchronize()
-    ref = oracle.indexer_kl_loss(to_oracle(inp))
+    oi = to_oracle(inp)
+    ref = oracle.indexer_kl_loss(oi)
     lg = loss.cpu().numpy()
     assert np.max(np.abs(lg - ref["loss"]) / np.maximum(np.abs(ref["loss"]), 1e-3)) <= 1e-3
     assert _rel_rms(dw.cpu().numpy(), ref["dw"]) <= 1e-3
     assert _rel_rms(dq.cpu().numpy(), ref["dq"]) <= 2e-2
     assert _rel_rms(dk.cpu().numpy(), ref["dk"]) <= 2e-2
+    # element by element, for the score gradient the GPU computed (written over the scores)
+    G = scores.cpu().numpy().astype(np.float64)
+    dqg, dwg = dq.cpu().numpy(), dw.cpu().numpy()
+    for t in range(inp.num_q):
+        q_t, w_t, keys = oracle.query_index_operands(oi, t)
+        n = keys.shape[0]
+        dq_r, dw_r, _, dq_b, dw_b, _, _ = _bwd_with_bounds(q_t, w_t, keys, G[t, :n])
+        _check_within(dqg[t], dq_r, dq_b, f"end to end: dq of query {t}")
+        _check_within(dwg[t], dw_r, dw_b, f"end to end: dw of query {t}")
 
 
 def test_indexer_objective_full_size():
@@ -228,9 +294,11 @@ def test_indexer_objective_full_size():
         assert abs(L[t] - ref["loss"][i]) <= 1e-3 * max(abs(ref["loss"][i]), 1e-3), f"row {t}: loss"
         q_t, w_t, keys = oracle.query_index_operands(oi, local[i])
         n = keys.shape[0]
-        dq_ref, dw_ref, _ = oracle.index_scores_backward(q_t, w_t, keys, G[i, :n])
+        dq_ref, dw_ref, _, dq_b, dw_b, _, _ = _bwd_with_bounds(q_t, w_t, keys, G[i, :n])
         assert _rel_rms(dw[t].cpu().numpy(), dw_ref) <= 1e-4, f"row {t}: dw"
         assert _rel_rms(dq[t].cpu().numpy(), dq_ref) <= 1e-2, f"row {t}: dq"
+        _check_within(dq[t].cpu().numpy(), dq_ref, dq_b, f"row {t}: dq")
+        _check_within(dw[t].cpu().numpy(), dw_ref, dw_b, f"row {t}: dw")
     # dk of sampled keys from every query's gradient column, in chunks of queries
     keys_s = [0, 5, 8000, T - 1]
     kc = oracle.decode_bf16(raw_numpy(inp.k_cache[0, :T]))
@@ -238,16 +306,26 @@ def test_indexer_objective_full_size():
     wv = raw_numpy(inp.w).astype(np.float64)
     gcols = grad[:, keys_s].cpu().numpy().astype(np.float64)
     dk_ref = np.zeros((len(keys_s), 128))
+    dk_bnd = np.zeros((len(keys_s), 128))
+    dk_mag = np.zeros((len(keys_s), 128))
+    dk_cnt = np.zeros(len(keys_s))
     for c0 in range(0, T, 1024):
         qc = oracle.decode_bf16(raw_numpy(inp.q_idx[c0:c0 + 1024]))              # [c, 64, 128]
         for j, s in enumerate(keys_s):
             x = qc @ kc[s]                                                        # [c, 64]
+            eps = 2.0 ** -16 * (np.abs(qc) @ np.abs(kc[s]))
             seen = (qpos[c0:c0 + 1024] >= s)[:, None]
-            gm = gcols[c0:c0 + 1024, j][:, None] * wv[c0:c0 + 1024] * (x > 0) * seen
+            gw = gcols[c0:c0 + 1024, j][:, None] * wv[c0:c0 + 1024] * seen
+            gm = gw * (x > 0)
             dk_ref[j] += np.einsum("ch,chd->d", gm, qc)
+            k_on = np.einsum("ch,chd->d", np.abs(gm), np.abs(qc))
+            dk_mag[j] += k_on
+            dk_bnd[j] += 2.0 ** -8 * k_on + np.einsum("ch,chd->d", np.abs(gw) * (np.abs(x) <= eps), np.abs(qc))
+            dk_cnt[j] += 64 * int(seen.sum())
     dkg = dk[0, keys_s].cpu().numpy()
     for j, s in enumerate(keys_s):
         assert _rel_rms(dkg[j], dk_ref[j]) <= 2e-2, f"key {s}: dk rel RMS {_rel_rms(dkg[j], dk_ref[j]):.3e}"
+        _check_within(dkg[j], dk_ref[j], dk_bnd[j] + dk_cnt[j] * 2.0 ** -23 * dk_mag[j], f"key {s}: dk")
 
 
 def test_indexer_objective_edge_cases():

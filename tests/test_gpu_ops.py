@@ -3,6 +3,7 @@
 Sizes span several tiles with ragged tails; every case prints its name first
 so a failing run names it."""
 import math
+import zlib
 
 import numpy as np
 import pytest
@@ -42,6 +43,13 @@ INDEXER_CASES = [
     ("prefill_fp8", dict(mode="prefill", length=301, k=64, index_dtype="fp8"), None),
     ("decode_paged_fp8", dict(mode="decode", num_seqs=3, length=2500, k=64, paged=True, index_dtype="fp8"),
      [2500, 7, 1300]),
+    # mixed-sign head weights: scores of either sign, negative ReLU-weighted heads
+    ("decode_paged_bf16_mixed_w", dict(mode="decode", num_seqs=3, length=4100, k=64, paged=True, w_low=-1 / 8),
+     [4100, 300, 2049]),
+    ("prefill_bf16_mixed_w", dict(mode="prefill", length=290, k=64, w_low=-1 / 8), None),
+    ("decode_paged_fp8_mixed_w", dict(mode="decode", num_seqs=3, length=2600, k=64, paged=True, index_dtype="fp8",
+                                      w_low=-1 / 8), [2600, 33, 1999]),
+    ("prefill_fp8_mixed_w", dict(mode="prefill", length=310, k=64, index_dtype="fp8", w_low=-1 / 8), None),
     ("prefill_f32", dict(mode="prefill", length=200, k=16, H_I=4, d_I=32, H=8, D=80, Dv=64,
                          index_dtype="f32", mla_dtype="f32", qkv_std=1 / math.sqrt(80), w_high=1.0), None),
     ("decode_f32_paged", dict(mode="decode", num_seqs=3, length=700, k=16, H_I=4, d_I=32, H=8, D=80, Dv=64,
@@ -106,7 +114,7 @@ TOPK_CASES = [
 @pytest.mark.parametrize("name,rows,n_max,k,kind,mode", TOPK_CASES, ids=[c[0] for c in TOPK_CASES])
 def test_topk_isolated_bit_exact(name, rows, n_max, k, kind, mode):
     _say("topk", name)
-    rng = np.random.default_rng(abs(hash(name)) % (2 ** 31))
+    rng = np.random.default_rng(zlib.crc32(name.encode()))      # the same rows in every process
     x = _topk_rows(rows, n_max, kind, rng)
     if mode == "decode":
         pos = rng.integers(0, n_max, size=rows)

@@ -94,6 +94,22 @@ def _paged_ignores_table(cache, inp, b, positions):
     return cache[b * nb + positions // bs, positions % bs]
 
 
+def _paged_scales_ignore_table(scale, inp, b, positions):
+    positions = np.asarray(positions, dtype=np.int64)
+    if inp.block_table is None:
+        return scale[b][positions]
+    bs = inp.block_size
+    nb = inp.block_table.shape[1]
+    return scale[b * nb + positions // bs, positions % bs]
+
+
+def _paged_scales_all_one(scale, inp, b, positions):
+    positions = np.asarray(positions, dtype=np.int64)
+    if inp.block_table is None:
+        return scale[b][positions]
+    return np.ones(positions.shape[0], np.float32)
+
+
 def _bf16_truncated_low(bits):
     b = np.asarray(bits).astype(np.uint16).astype(np.uint32) << np.uint32(15)
     return b.view(np.float32).astype(np.float64)
@@ -210,6 +226,8 @@ MUTATIONS = {
     "e4m3_exponent_bias_8": ("E4M3FN_TABLE", _bias8_table()),
     "fp8_key_scale_dropped": ("query_index_operands", _fp8_no_kscale),
     "paged_ignores_block_table": ("gather_rows", _paged_ignores_table),
+    "paged_scales_ignore_block_table": ("gather_scales", _paged_scales_ignore_table),
+    "paged_scales_all_one": ("gather_scales", _paged_scales_all_one),
     "bf16_wrong_shift": ("decode_bf16", _bf16_truncated_low),
     "fp8_ties_away_from_zero": ("encode_e4m3fn", _encode_ties_away),
     "fp8_round_toward_zero": ("encode_e4m3fn", _encode_truncate),

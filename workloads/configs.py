@@ -36,7 +36,8 @@ class Workload:
     v_dim: int = 512               # Dv
     index_dtype: str = "bf16"      # "f32" | "bf16" | "fp8"
     mla_dtype: str = "bf16"        # "f32" | "bf16"
-    w_high: float = 1.0 / 8.0      # w ~ U(0, w_high)
+    w_high: float = 1.0 / 8.0      # w ~ U(w_low, w_high)
+    w_low: float = 0.0             # below 0: mixed-sign head weights (the indexer accepts any real w)
     qkv_std: float = 1.0 / 24.0    # q and latent cache ~ N(0, 1) * qkv_std
     sm_scale: float = 1.0 / math.sqrt(576.0)
     planted_frac: float = 0.0      # fraction of key positions shifted along one shared direction

@@ -7,7 +7,8 @@ Recipe (the same bytes feed the HIP library and the CPU oracle):
    prefill: ``q_start .. L-1``) and, for a paged cache, a random permutation
    of the block pool assigned to the sequences in order.
 2. Then, in this order: indexer queries ``q_I ~ N(0,1)``, indexer keys
-   ``k_I ~ N(0,1)``, head weights ``w ~ U(0, w_high)``, MLA queries
+   ``k_I ~ N(0,1)``, head weights ``w ~ U(w_low, w_high)`` (``w_low`` is 0
+   unless a test asks for mixed signs), MLA queries
    ``q ~ N(0,1)*std``, latent cache ``c ~ N(0,1)*std`` -- all drawn in fp32
    from one ``torch.Generator`` seeded with the workload seed.
 3. Planted keys (prefill only): ``round(frac*L)`` positions drawn without
@@ -138,7 +139,8 @@ def generate(wl: Workload, device="cpu", seed: Optional[int] = None,
     # 2. values, fixed order
     q_idx = torch.randn((T, H_I, d_I), generator=g, device=device, dtype=torch.float32)
     k_idx = torch.randn((slots, d_I), generator=g, device=device, dtype=torch.float32)
-    w = torch.rand((T, H_I), generator=g, device=device, dtype=torch.float32) * wl.w_high
+    u = torch.rand((T, H_I), generator=g, device=device, dtype=torch.float32)
+    w = u * wl.w_high if wl.w_low == 0.0 else wl.w_low + u * (wl.w_high - wl.w_low)
     q = torch.randn((T, H, D), generator=g, device=device, dtype=torch.float32) * wl.qkv_std
     kv = torch.randn((slots, D), generator=g, device=device, dtype=torch.float32) * wl.qkv_std
 
