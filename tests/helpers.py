@@ -85,14 +85,25 @@ OUT_TOL = {"f32": 1e-4, "bf16": 2e-2}
 NEAR_TIE = 1e-3
 
 
-def check_scores(gpu_row, ora_row, tol, what=""):
-    """|I_gpu - I_oracle| <= tol * |I_oracle| (+ a 1e-6 * mean|I| floor for exact zeros)."""
+def score_magnitude(oi, t):
+    """sum_j |w(t,j)| ReLU(q(t,j) . k(s)) over query t's candidates: the size of the
+    terms whose signed sum is I(t,s).  It equals |I(t,s)| when every weight is
+    non-negative; with mixed-sign weights the sum can cancel to far below its terms,
+    and a relative tolerance is then taken against this magnitude instead."""
+    q_t, w_t, keys = _oracle.query_index_operands(oi, t)
+    return np.abs(w_t) @ np.maximum(q_t @ keys.T, 0.0)
+
+
+def check_scores(gpu_row, ora_row, tol, what="", scale=None):
+    """|I_gpu - I_oracle| <= tol * |I_oracle| (+ a 1e-6 * mean|I| floor for exact zeros);
+    with ``scale`` (score_magnitude), tol * scale in place of tol * |I_oracle|."""
     g = np.asarray(gpu_row, dtype=np.float64)
     o = np.asarray(ora_row, dtype=np.float64)
     assert g.shape == o.shape, what
-    floor = 1e-6 * (np.mean(np.abs(o)) if o.size else 0.0)
-    bad = np.abs(g - o) > tol * np.abs(o) + floor
-    assert not bad.any(), f"{what}: {bad.sum()} scores off, worst rel {np.max(np.abs(g - o) / (np.abs(o) + floor + 1e-300)):.3e}"
+    ref = np.abs(o) if scale is None else np.asarray(scale, dtype=np.float64)
+    floor = 1e-6 * (np.mean(ref) if o.size else 0.0)
+    bad = np.abs(g - o) > tol * ref + floor
+    assert not bad.any(), f"{what}: {bad.sum()} scores off, worst rel {np.max(np.abs(g - o) / (ref + floor + 1e-300)):.3e}"
 
 
 def check_topk_row_exact(gpu_row, scores_f32, k, what=""):
@@ -105,9 +116,10 @@ def check_topk_row_exact(gpu_row, scores_f32, k, what=""):
     assert np.array_equal(got[:m], want), f"{what}: selection differs ({np.setdiff1d(got[:m], want)[:5]})"
 
 
-def check_topk_row_e2e(gpu_row, ora_scores, k, what=""):
+def check_topk_row_e2e(gpu_row, ora_scores, k, what="", scale=None):
     """End-to-end top-k: same size, ascending, in range; any swap against the oracle's
-    selection lies within NEAR_TIE relative of the oracle's k-th score.  Returns #swaps."""
+    selection lies within NEAR_TIE relative of the oracle's k-th score (with ``scale``,
+    score_magnitude, relative to the k-th position's magnitude).  Returns #swaps."""
     n = ora_scores.shape[0]
     m = min(k, n)
     got = np.asarray(gpu_row)
@@ -120,10 +132,11 @@ def check_topk_row_e2e(gpu_row, ora_scores, k, what=""):
         assert g.shape[0] == n
         return 0
     tau = ora_scores[o[-1]]
+    band = NEAR_TIE * (abs(tau) if scale is None else float(scale[o[-1]]))
     diff = np.setxor1d(g, o)
     if diff.size:
         dev = np.abs(ora_scores[diff] - tau)
-        assert np.all(dev <= NEAR_TIE * abs(tau)), f"{what}: swap outside the near-tie band ({dev.max():.3e} vs tau {tau:.4e})"
+        assert np.all(dev <= band), f"{what}: swap outside the near-tie band ({dev.max():.3e} vs tau {tau:.4e})"
     return diff.size // 2
 
 

@@ -8,7 +8,8 @@ import pytest
 import torch
 
 import oracle
-from tests.helpers import (OUT_TOL, check_attention, check_topk_row_e2e, small_workload, to_oracle)
+from tests.helpers import (OUT_TOL, check_attention, check_topk_row_e2e, score_magnitude, small_workload,
+                           to_oracle)
 from tests.test_gpu_ops import B, DEV, _say, big_dims
 from workloads import generate
 
@@ -27,7 +28,8 @@ def check_all_rows(inp, out, lse, idx, name):
     swaps = 0
     for t in range(inp.num_q):
         scores = oracle.query_index_scores(oi, t)
-        swaps += check_topk_row_e2e(ig[t], scores, inp.topk, f"{name} row {t}")
+        scale = score_magnitude(oi, t) if inp.wl.w_low < 0 else None
+        swaps += check_topk_row_e2e(ig[t], scores, inp.topk, f"{name} row {t}", scale=scale)
         m = min(inp.topk, scores.shape[0])
         o_ref, l_ref = oracle.query_attention(oi, t, ig[t, :m])
         check_attention(og[t], lg[t], o_ref, l_ref, OUT_TOL[inp.wl.mla_dtype], f"{name} row {t}")
