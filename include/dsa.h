@@ -26,7 +26,9 @@
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
  *     null stream).  The library never synchronises, never allocates device
  *     memory and keeps no state between calls; callers own every buffer,
- *     including the workspace sized by dsa_workspace_size().
+ *     including the workspace sized by dsa_workspace_size().  The one
+ *     exception is dsa_forward_noalloc, whose scratch is a static device
+ *     array of the library (see there).
  *   - Arguments are checked on the host before any launch; a failed check
  *     returns a negative dsa_status and launches nothing.  A launch failure
  *     returns DSA_ERR_HIP.  No C++ exception crosses the ABI.
@@ -87,7 +89,8 @@ typedef enum dsa_status {
   DSA_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent shape */
   DSA_ERR_UNSUPPORTED = -2, /* valid but outside the supported shapes/types */
   DSA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
-  DSA_ERR_HIP = -4          /* a kernel launch failed */
+  DSA_ERR_HIP = -4,         /* a kernel launch failed */
+  DSA_ERR_SCRATCH_LIMIT = -5 /* dsa_forward_noalloc: the problem needs more than its static scratch */
 } dsa_status;
 
 typedef enum dsa_mode {
@@ -229,6 +232,23 @@ int dsa_sparse_mla(const dsa_seqs *seqs, const dsa_dims *dims, float sm_scale, c
  * Workspace: dsa_workspace_size(DSA_OP_FORWARD, ...). */
 int dsa_forward(const dsa_seqs *seqs, const dsa_dims *dims, const dsa_forward_args *args,
                 void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* dsa_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same computation, kernels and results as dsa_forward, with the workspace
+ * taken from a static device array of the library: 128 MiB on each GPU,
+ * reserved when the library's code object is loaded on that GPU and held
+ * until the process ends.  The array of the current device (hipGetDevice) is
+ * used, so `stream` must belong to it.  The call allocates nothing (no
+ * hipMalloc, no library allocation).  A problem whose
+ * dsa_workspace_size(DSA_OP_FORWARD, ...) exceeds 128 MiB is rejected on the
+ * host with DSA_ERR_SCRATCH_LIMIT and launches nothing; 128 MiB holds, e.g.,
+ * a decode of 32 sequences at 128K context, or a prefill of 2048 tokens.
+ * Every call on one GPU shares that GPU's array (the kernels clear what must
+ * start at zero on every call), so calls that overlap on one GPU -- on
+ * different streams, or from different host threads -- race; order them. */
+int dsa_forward_noalloc(const dsa_seqs *seqs, const dsa_dims *dims, const dsa_forward_args *args,
+                        hipStream_t stream);
 
 /* Query rows per chunk that dsa_forward processes at a time for these shapes
  * (all num_q rows for decode), so a caller can time or split work the way the

@@ -21,9 +21,10 @@ F32, BF16, FP8_E4M3FN = 0, 1, 2
 PREFILL, DECODE = 0, 1
 (OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_MLA, OP_FORWARD, OP_DENSE_MLA, OP_ATTENTION_PROBS,
  OP_INDEXER_BACKWARD, OP_INDEXER_KL_LOSS) = 0, 1, 2, 3, 4, 5, 6, 7
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH_LIMIT = 0, -1, -2, -3, -4, -5
 
 EXPORTS = ("dsa_workspace_size", "dsa_index_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward",
+           "dsa_forward_noalloc",
            "dsa_dense_mla", "dsa_attention_probs", "dsa_indexer_kl", "dsa_indexer_backward", "dsa_indexer_kl_loss", "dsa_forward_chunk_rows",
            "dsa_quantize_fp8", "dsa_append_index_keys",
            "dsa_status_string")
@@ -81,6 +82,8 @@ def _load() -> ctypes.CDLL:
     lib.dsa_sparse_mla.restype = ctypes.c_int
     lib.dsa_forward.argtypes = [sp, dp, ctypes.POINTER(DsaForwardArgs), P, SZ, P]
     lib.dsa_forward.restype = ctypes.c_int
+    lib.dsa_forward_noalloc.argtypes = [sp, dp, ctypes.POINTER(DsaForwardArgs), P]
+    lib.dsa_forward_noalloc.restype = ctypes.c_int
     lib.dsa_dense_mla.argtypes = [sp, dp, ctypes.c_float, P, P, P, P, P, SZ, P]
     lib.dsa_dense_mla.restype = ctypes.c_int
     lib.dsa_attention_probs.argtypes = [sp, dp, ctypes.c_float, P, P, P, I64, P, I32, P, SZ, P]
@@ -350,6 +353,19 @@ def forward(pb: Problem, q_idx, q_scale, w, k_cache, k_scale, q, kv_cache, sm_sc
     st = LIB.dsa_forward(ctypes.byref(pb.seqs), ctypes.byref(pb.dims), ctypes.byref(args), _ptr(ws),
                          _nbytes(ws), _stream(stream))
     _check(st, "dsa_forward")
+    return out, lse, topk_idx
+
+
+def forward_noalloc(pb: Problem, q_idx, q_scale, w, k_cache, k_scale, q, kv_cache, sm_scale: float, out, lse=None,
+                    topk_idx=None, stream=None):
+    """dsa_forward_noalloc: dsa_forward with the library's static scratch (no workspace
+    argument; the caller passes every output)."""
+    args = DsaForwardArgs(q_idx=_ptr(q_idx), q_scale=_ptr(q_scale), w=_ptr(w), k_cache=_ptr(k_cache),
+                          k_scale=_ptr(k_scale), q=_ptr(q), kv_cache=_ptr(kv_cache),
+                          sm_scale=float(sm_scale), reserved=0, topk_idx=_ptr(topk_idx), out=_ptr(out),
+                          lse=_ptr(lse), stage_events=None)
+    st = LIB.dsa_forward_noalloc(ctypes.byref(pb.seqs), ctypes.byref(pb.dims), ctypes.byref(args), _stream(stream))
+    _check(st, "dsa_forward_noalloc")
     return out, lse, topk_idx
 
 

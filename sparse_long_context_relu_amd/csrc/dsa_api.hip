@@ -1,11 +1,20 @@
 // C ABI of the DSA forward path: host-side argument checks, workspace carving
 // and kernel orchestration on the caller's stream.  See include/dsa.h for the
 // contract of every entry point.
+#include <mutex>
+
 #include "kernels.h"
 
 #define DSA_EXPORT extern "C" __attribute__((visibility("default")))
 
 using namespace dsa;
+
+// Scratch memory of dsa_forward_noalloc: one array per GPU, held from the
+// library's load until the process ends.  In host code `scratch` names a host
+// stand-in, not device memory; its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is passed on.
+constexpr size_t kNoallocScratchBytes = 128ull << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
 
 namespace {
 
@@ -276,6 +285,25 @@ KlLossLayout kl_loss_layout(const dsa_seqs *s, const dsa_dims *d) {
   return L;
 }
 
+// Device address of `scratch` on the current device, looked up on the first
+// call per device and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_on_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DSA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return DSA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
 int check_ws(size_t need, const void *ws, size_t ws_bytes) {
   if (need == 0) return DSA_OK;
   if (ws == nullptr || ws_bytes < need) return DSA_ERR_WORKSPACE;
@@ -434,8 +462,9 @@ DSA_EXPORT int dsa_sparse_mla(const dsa_seqs *seqs, const dsa_dims *dims, float 
   return hip_status(launch_sparse_mla(a, stream));
 }
 
-DSA_EXPORT int dsa_forward(const dsa_seqs *seqs, const dsa_dims *dims, const dsa_forward_args *args,
-                           void *ws, size_t ws_bytes, hipStream_t stream) {
+namespace {
+
+int check_forward(const dsa_seqs *seqs, const dsa_dims *dims, const dsa_forward_args *args) {
   if (int e = check_seqs(seqs)) return e;
   if (int e = check_index_dims(dims)) return e;
   if (int e = check_mla_dims(dims)) return e;
@@ -445,6 +474,15 @@ DSA_EXPORT int dsa_forward(const dsa_seqs *seqs, const dsa_dims *dims, const dsa
     return e;
   if (args->q == nullptr || args->kv_cache == nullptr || args->out == nullptr) return DSA_ERR_INVALID_ARG;
   if (!(args->sm_scale == args->sm_scale)) return DSA_ERR_INVALID_ARG;
+  return DSA_OK;
+}
+
+}  // namespace
+
+DSA_EXPORT int dsa_forward(const dsa_seqs *seqs, const dsa_dims *dims, const dsa_forward_args *args,
+                           void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (int e = check_forward(seqs, dims, args)) return e;
+  if (seqs->num_q == 0) return DSA_OK;
   const ForwardLayout L = forward_layout(seqs, dims);
   if (int e = check_ws((size_t)L.total, ws, ws_bytes)) return e;
 
@@ -502,6 +540,16 @@ DSA_EXPORT int dsa_forward(const dsa_seqs *seqs, const dsa_dims *dims, const dsa
     if (timed && hipEventRecord(ev[3], stream) != hipSuccess) return DSA_ERR_HIP;
   }
   return DSA_OK;
+}
+
+DSA_EXPORT int dsa_forward_noalloc(const dsa_seqs *seqs, const dsa_dims *dims, const dsa_forward_args *args,
+                                   hipStream_t stream) {
+  if (int e = check_forward(seqs, dims, args)) return e;
+  if (seqs->num_q == 0) return DSA_OK;
+  if ((size_t)forward_layout(seqs, dims).total > kNoallocScratchBytes) return DSA_ERR_SCRATCH_LIMIT;
+  void *ptr = nullptr;
+  if (int e = scratch_on_current_device(&ptr)) return e;
+  return dsa_forward(seqs, dims, args, ptr, kNoallocScratchBytes, stream);
 }
 
 DSA_EXPORT int dsa_dense_mla(const dsa_seqs *seqs, const dsa_dims *dims, float sm_scale, const void *q,
@@ -695,6 +743,8 @@ DSA_EXPORT const char *dsa_status_string(int status) {
     case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: shape or type not supported";
     case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
     case DSA_ERR_HIP: return "DSA_ERR_HIP: kernel launch failed";
+    case DSA_ERR_SCRATCH_LIMIT:
+      return "DSA_ERR_SCRATCH_LIMIT: the problem needs more than the 128 MiB static scratch of dsa_forward_noalloc";
     default: return "unknown dsa_status";
   }
 }

@@ -306,3 +306,24 @@ def test_forward_workspace_covers_ragged_tail_chunk(T):
     ld = (T + 63) // 64 * 64
     want = a256(ld * chunk * 4) + a256(chunk * 2048 * 4) + a256(max(tk_full, tk_tail)) + a256(max(ml_full, ml_tail))
     assert need >= want, (need, want)
+
+
+def test_forward_noalloc_rejects_problems_over_its_scratch():
+    """dsa_forward_noalloc checks its arguments like dsa_forward, then rejects on the
+    host a problem whose forward workspace exceeds the 128 MiB static scratch (no
+    launch; no device is touched by these calls)."""
+    assert B.status_string(B.ERR_SCRATCH_LIMIT).startswith("DSA_ERR_SCRATCH_LIMIT")
+    big = B.make_problem(mode="decode", q_pos=torch.full((128,), 131071, dtype=torch.int32), max_ctx=131072,
+                         num_seqs=128, max_seq_len=131072)
+    assert B.workspace_size(B.OP_FORWARD, big) > (128 << 20)
+    args = B.DsaForwardArgs(q_idx=FAKE, w=FAKE, k_cache=FAKE, q=FAKE, kv_cache=FAKE, sm_scale=0.04, out=FAKE)
+    call = lambda pb: B.LIB.dsa_forward_noalloc(ctypes.byref(pb.seqs), ctypes.byref(pb.dims), ctypes.byref(args), None)
+    assert call(big) == B.ERR_SCRATCH_LIMIT
+    args.out = None
+    assert call(big) == B.ERR_INVALID_ARG                 # argument checks come first
+    args.out = FAKE
+    pb = _problem(q_pos=torch.zeros(0, dtype=torch.int32))
+    assert call(pb) == B.OK                               # nothing to do, nothing launched
+    fits = B.make_problem(mode="decode", q_pos=torch.full((32,), 131071, dtype=torch.int32), max_ctx=131072,
+                          num_seqs=32, max_seq_len=131072)
+    assert B.workspace_size(B.OP_FORWARD, fits) <= (128 << 20)   # the 128K decode batch fits
