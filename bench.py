@@ -7,6 +7,14 @@ long-context decode batch: 32 sequences, context ~ U[32768, 131072], paged
 64-token blocks, k = 2048, H_I = 64, d_I = 128, H = 128, D = 576, Dv = 512,
 bf16.  Prints one JSON line (stdout); progress goes to stderr.
 
+Every timed region cycles through several seeded input sets, enough that two
+steps on the same set are separated by at least twice the 256 MB MALL of other
+inputs: no step reads what an earlier step left in the last-level cache.
+Secondary lines: every context exactly 128K, the e4m3fn indexer (quantise +
+append + forward), 16 x 8K contiguous decode, the 16K bf16 prefill and the 64K
+prefill with the e4m3fn indexer, dense MLA on the same inputs, the indexer's
+warm-up objective, measured ceilings, and the float64 oracle on the host.
+
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 """
 from __future__ import annotations
@@ -109,31 +117,57 @@ def settle(torch, call, ms):
         torch.cuda.synchronize()
 
 
-def time_forward(B, torch, inp, steps, warmup, settle_ms=0, prep=None):
-    pb = B.problem_from_inputs(inp)
-    ws = torch.empty(B.workspace_size(B.OP_FORWARD, pb), dtype=torch.uint8, device="cuda")
-    T, H, Dv, k = inp.num_q, inp.wl.heads, inp.wl.v_dim, inp.topk
-    out = torch.empty((T, H, Dv), dtype=inp.q.dtype, device="cuda")
+MALL_BYTES = 256 << 20          # MI355X Infinity Cache (last-level, shared by the XCDs)
+
+
+def rotation_sets(step_bytes):
+    """Input sets a timed region cycles through, so that between two steps on the same
+    set at least twice the MALL's capacity of other inputs has been read: no step
+    finds its inputs left in the last-level cache by the step before it."""
+    return int(min(8, max(2, 1 + math.ceil(2 * MALL_BYTES / max(step_bytes, 1)))))
+
+
+def make_sets(generate, wl, n):
+    """n seeded input sets of workload wl (set 0 is the canonical seed)."""
+    return [generate(wl, "cuda", seed=wl.seed + 7919 * j) for j in range(n)]
+
+
+def time_forward(B, torch, inps, steps, warmup, settle_ms=0, preps=None):
+    """Step time and stage times of dsa_forward, cycling through the input sets
+    `inps` (step i uses set i mod len(inps)); `preps[j]` is work upstream of the
+    forward on set j that belongs to the step."""
+    inps = inps if isinstance(inps, (list, tuple)) else [inps]
+    inp0 = inps[0]
+    pbs = [B.problem_from_inputs(x) for x in inps]
+    ws = torch.empty(max(B.workspace_size(B.OP_FORWARD, pb) for pb in pbs), dtype=torch.uint8, device="cuda")
+    T, H, Dv, k = inp0.num_q, inp0.wl.heads, inp0.wl.v_dim, inp0.topk
+    out = torch.empty((T, H, Dv), dtype=inp0.q.dtype, device="cuda")
     lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
     idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
-    fwd = lambda ev=None: B.forward(pb, inp.q_idx, inp.q_scale, inp.w, inp.k_cache, inp.k_scale, inp.q,
-                                    inp.kv_cache, inp.sm_scale, out=out, lse=lse, topk_idx=idx, ws=ws,
-                                    stage_events=ev)
 
-    def call(ev=None):
-        if prep is not None:       # work upstream of the forward that belongs to the step
-            prep()
-        fwd(ev)
+    def call(i=0, ev=None):
+        j = i % len(inps)
+        x = inps[j]
+        if preps is not None and preps[j] is not None:    # work upstream of the forward that belongs to the step
+            preps[j]()
+        B.forward(pbs[j], x.q_idx, x.q_scale, x.w, x.k_cache, x.k_scale, x.q, x.kv_cache, x.sm_scale, out=out,
+                  lse=lse, topk_idx=idx, ws=ws, stage_events=ev)
 
-    settle(torch, call, settle_ms)
-    for _ in range(warmup):
-        call()
+    n_settle = [0]
+
+    def settle_call():
+        call(n_settle[0])
+        n_settle[0] += 1
+
+    settle(torch, settle_call, settle_ms)
+    for i in range(warmup):
+        call(i)
     # Timed region 1, the step time: K steps back to back, nothing recorded in between.
     start, end = make_events(torch, 2)
     torch.cuda.synchronize()
     start.record()
     for i in range(steps):
-        call()
+        call(i)
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
@@ -143,11 +177,59 @@ def time_forward(B, torch, inp, steps, warmup, settle_ms=0, prep=None):
     stage = [make_events(torch, 4) for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
-        call(stage[i])
+        call(i, stage[i])
     torch.cuda.synchronize()
     st = [[stage[i][j].elapsed_time(stage[i][j + 1]) for j in range(3)] for i in range(steps)]
     mean = [sum(s[j] for s in st) / steps for j in range(3)]
     return total_ms / steps, mean
+
+
+def decode_stage_rooflines(inp, stages):
+    """Achieved HBM GB/s of the decode stages against 8 TB/s: the indexer on its key
+    scan (+ q_I, w), the attention on the selected latent rows (+ q, out); the top-k
+    on the fp32 score rows it reads (overhead of the path, not algorithmic bytes)."""
+    wl = inp.wl
+    n = inp.q_pos.to("cpu").long() + 1
+    T = inp.num_q
+    idx_b, _ = algorithmic_bytes(inp)
+    rows = int(n.clamp(max=wl.topk).sum())
+    e = ELEM[wl.mla_dtype]
+    att_b = rows * wl.qk_dim * e + T * wl.heads * (wl.qk_dim + wl.v_dim) * e
+    sc_b = int(n.sum()) * 4
+    gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
+    return {"indexer": {"bytes": idx_b, "gbs": round(gbs(idx_b, stages[0]), 1),
+                        "frac": round(gbs(idx_b, stages[0]) / HBM_PEAK_GBS, 4)},
+            "attention_gather": {"bytes": att_b, "rows": rows, "gbs": round(gbs(att_b, stages[2]), 1),
+                                 "frac": round(gbs(att_b, stages[2]) / HBM_PEAK_GBS, 4)},
+            "topk_select": {"score_bytes_read": sc_b, "gbs": round(gbs(sc_b, stages[1]), 1),
+                            "frac": round(gbs(sc_b, stages[1]) / HBM_PEAK_GBS, 4)}}
+
+
+def env_info():
+    """Host and software the numbers were taken on (read before the GPU is touched)."""
+    import platform
+    import subprocess
+    info = {"cpu_count": os.cpu_count(), "cpu_model": None, "rocm": None, "hipcc": None,
+            "python": platform.python_version()}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        pass
+    try:
+        out = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True, timeout=60).stdout
+        info["hipcc"] = next((l.strip() for l in out.splitlines() if "HIP version" in l), None)
+    except Exception:
+        pass
+    return info
 
 
 def fused_prefill_stages(B, torch, pin, settle_ms, reps=2):
@@ -357,8 +439,81 @@ def cpu_baseline(inp, seconds):
     el = time.perf_counter() - t0
     passes = done / inp.num_q
     return {"value": done / el, "unit": "tokens/s", "cores": threads or os.cpu_count(), "kind": "oracle",
+            "host_cpu_count": os.cpu_count(),
             "sample": f"{done} decode queries ({passes:.1f} passes over the {inp.num_q} queries of the timed "
-                      f"batch; full indexer over each context, top-k, attention), float64 NumPy, {el:.1f} s wall"}
+                      f"batch; full indexer over each context, top-k, attention), float64 NumPy with "
+                      f"{threads or os.cpu_count()} BLAS threads on a host of {os.cpu_count()} CPUs, {el:.1f} s wall"}
+
+
+def prefill_line(B, torch, generate, wl, settle_ms, rotate, dense=False, warmup_objective=False, steps=3):
+    """One prefill workload: the fused step (input sets rotated), each op alone over
+    every query row, the stages as the fused call runs them, and their matrix-core
+    fractions (indexer against its own dtype's peak, attention against bf16)."""
+    log(f"prefill: {wl.name}")
+    pins = make_sets(generate, wl, rotate)
+    pin = pins[0]
+    pms, _ = time_forward(B, torch, pins, steps, 1, settle_ms)
+    pf_idx, pf_mla = algorithmic_flops(pin)
+    idx_peak = MFMA_PEAK_TFLOPS[wl.index_dtype]
+    mla_peak = MFMA_PEAK_TFLOPS[wl.mla_dtype]
+    # each stage alone over every query row, one call each (the forward processes
+    # the rows in query chunks; its stage events cover the first chunk only)
+    pb = B.problem_from_inputs(pin)
+    sc = torch.empty((pin.num_q, pin.max_ctx), dtype=torch.float32, device="cuda")
+    idx = torch.empty((pin.num_q, pin.topk), dtype=torch.int32, device="cuda")
+    tws = torch.empty(B.workspace_size(B.OP_TOPK, pb), dtype=torch.uint8, device="cuda")
+    mws = torch.empty(max(1, B.workspace_size(B.OP_SPARSE_MLA, pb)), dtype=torch.uint8, device="cuda")
+    ops = [lambda: B.index_scores(pb, pin.q_idx, pin.q_scale, pin.w, pin.k_cache, pin.k_scale, scores=sc),
+           lambda: B.topk(pb, sc, idx=idx, ws=tws),
+           lambda: B.sparse_mla(pb, pin.sm_scale, pin.q, pin.kv_cache, idx, ws=mws)]
+    stage_ms = []
+    for op in ops:
+        settle(torch, op, settle_ms / 2)
+        e0, e1 = make_events(torch, 2)
+        e0.record()
+        for _ in range(3):
+            op()
+        e1.record()
+        torch.cuda.synchronize()
+        stage_ms.append(e0.elapsed_time(e1) / 3)
+    fused = fused_prefill_stages(B, torch, pin, settle_ms / 2)
+    planted = None
+    if pin.planted is not None:
+        # share of planted keys among the selected positions of the rows that
+        # select (n > k), against their share among those rows' candidates
+        mark = torch.zeros(pin.max_ctx, dtype=torch.bool, device="cuda")
+        mark[pin.planted] = True
+        rows_sel = (pin.q_pos.long() + 1) > pin.topk
+        sel = idx[rows_sel]
+        cum = torch.cumsum(mark.long(), 0)
+        planted = {"share_in_topk": round(mark[sel.long()].float().mean().item(), 4),
+                   "share_in_candidates": round((cum[pin.q_pos.long()[rows_sel]].float() /
+                                                 (pin.q_pos.long()[rows_sel] + 1).float()).mean().item(), 4)}
+    tf = lambda f, ms, peak: round(f / (ms * 1e-3) / 1e12 / peak, 4)
+    line = {
+        "workload": wl.name, "index_dtype": wl.index_dtype, "tokens_per_s": round(pin.num_q / (pms * 1e-3), 1),
+        "ms_per_step": round(pms, 3), "input_sets_rotated": len(pins),
+        "stage_ops_ms_all_rows": {"index_scores": round(stage_ms[0], 3), "topk": round(stage_ms[1], 3),
+                                  "sparse_mla": round(stage_ms[2], 3)},
+        "fused_stages_ms": {"indexer": round(fused[0], 3), "topk": round(fused[1], 3), "attention": round(fused[2], 3)},
+        "indexer_peak_tflops": idx_peak,
+        "indexer_mfma_frac_fused": tf(pf_idx, fused[0], idx_peak),
+        "attention_mfma_frac_fused": tf(pf_mla, fused[2], mla_peak),
+        "indexer_mfma_frac": tf(pf_idx, stage_ms[0], idx_peak),
+        "attention_mfma_frac": tf(pf_mla, stage_ms[2], mla_peak),
+        "step_mfma_time_frac": round((pf_idx / (idx_peak * 1e12) + pf_mla / (mla_peak * 1e12)) / (pms * 1e-3), 4),
+        "planted_keys": planted}
+    log(f"prefill {wl.name}: {pms:.2f} ms/step, indexer {stage_ms[0]:.2f} ms alone, {fused[0]:.2f} ms fused")
+    del sc, idx, tws, mws, pins
+    torch.cuda.empty_cache()
+    extra = {}
+    if dense:
+        extra["dense"] = dense_line(B, torch, pin, pms, 2, 1, settle_ms)
+    if warmup_objective:
+        log("indexer warm-up objective on the prefill inputs")
+        extra["warmup_objective"] = warmup_objective_line(B, torch, pin, 2, settle_ms)
+        log(f"warm-up objective: {extra['warmup_objective']['ms_per_step']:.2f} ms")
+    return line, extra
 
 
 def main():
@@ -370,13 +525,18 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--settle-ms", type=float, default=400.0,
                     help="untimed run-in before each timed region, so the shader clock has settled")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input sets each timed region cycles through (0: enough that no step finds its inputs "
+                         "left in the 256 MB MALL by an earlier step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurement")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurements")
+    ap.add_argument("--no-prefill-64k", action="store_true", help="skip the 64K prefill with the e4m3fn indexer")
     ap.add_argument("--no-fp8-decode", action="store_true", help="skip the secondary fp8-indexer decode measurement")
     ap.add_argument("--fp8-workload", default="decode_128k_paged_fp8")
     ap.add_argument("--no-exact-decode", action="store_true",
                     help="skip the secondary decode line with every context exactly 128K tokens")
     ap.add_argument("--exact-workload", default="decode_128k_exact_paged_bf16")
+    ap.add_argument("--no-8k-decode", action="store_true", help="skip the 16 x 8K contiguous decode line")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense-MLA comparison (attention over every candidate) on the same inputs")
     ap.add_argument("--no-warmup-objective", action="store_true",
@@ -391,9 +551,12 @@ def main():
               "(the path is data-parallel across sequences; sharding is described, not built)", file=sys.stderr)
         sys.exit(2)
 
+    env = env_info()
     import torch
     from sparse_long_context_relu_amd import binding as B
     from workloads import WORKLOADS, BENCH_DEFAULT, generate
+    env["torch"] = torch.__version__
+    env["hip_runtime"] = getattr(torch.version, "hip", None)
 
     if args.copy_mib:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE calibrate the traffic counters
@@ -404,13 +567,17 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy: {args.copy_mib} MiB read + {args.copy_mib} MiB written")
         del src, dst
+    env["gpu"] = torch.cuda.get_device_name(0)
+    n_sets = lambda wl_inp: args.rotate if args.rotate > 0 else rotation_sets(algorithmic_bytes(wl_inp)[1])
     name = args.workload or BENCH_DEFAULT
     wl = WORKLOADS[name]
     log(f"generating {name} on cuda:0")
     inp = generate(wl, "cuda")
+    sets = [inp] + make_sets(generate, wl, n_sets(inp))[1:]
     torch.cuda.synchronize()
-    log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
-    ms, stages = time_forward(B, torch, inp, args.steps, args.warmup, args.settle_ms)
+    log(f"timing {args.steps} steps after {args.warmup} warm-up steps, cycling {len(sets)} input sets")
+    ms, stages = time_forward(B, torch, sets, args.steps, args.warmup, args.settle_ms)
+    del sets
     tokens = inp.num_q
     value = tokens / (ms * 1e-3)
     idx_bytes, step_bytes = algorithmic_bytes(inp)
@@ -447,9 +614,13 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roof,
         "stages_ms": {"indexer": round(stages[0], 4), "topk": round(stages[1], 4), "attention": round(stages[2], 4)},
+        "input_sets_rotated": n_sets(inp),
         "step_algorithmic_bytes": step_bytes,
         "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "env": env,
     }
+    if wl.mode == "decode":
+        result["stage_rooflines"] = decode_stage_rooflines(inp, stages)
 
     if wl.mode == "decode" and wl.index_dtype == "bf16" and not args.no_extras:
         log("fp8 indexing quality against bf16 on the same inputs")
@@ -462,43 +633,52 @@ def main():
         log(f"dense: {dense[name]['dense_mla_ms']:.3f} ms ({dense[name]['dense_over_dsa']:.2f}x the DSA step)")
 
     def decode_line(name, fp8_prep):
-        """Another decode workload through the same step (for e4m3fn indexing: the new
-        tokens' index queries and keys arrive in bf16 and are quantised with
-        dsa_quantize_fp8 and appended with dsa_append_index_keys inside the step)."""
+        """Another decode workload through the same step, cycling its input sets (for
+        e4m3fn indexing: the new tokens' index queries and keys arrive in bf16 and are
+        quantised with dsa_quantize_fp8 and appended with dsa_append_index_keys inside
+        the step)."""
         log(f"secondary: {name}")
         din = generate(WORKLOADS[name], "cuda")
+        dsets = [din] + make_sets(generate, WORKLOADS[name], n_sets(din))[1:]
         T, HI, DI = din.num_q, din.wl.index_heads, din.wl.index_dim
-        prep, extra = None, 0
+        preps, extra = None, 0
         if fp8_prep:
             g = torch.Generator(device="cuda").manual_seed(1234)
             q_new = torch.randn((T, HI * DI), device="cuda", generator=g).to(torch.bfloat16)
             k_new = torch.randn((T, DI), device="cuda", generator=g).to(torch.bfloat16)
-            dpb = B.problem_from_inputs(din)
-            q8 = din.q_idx.view(T, HI * DI)
 
-            def prep():
-                B.quantize_fp8(q_new, scale_repeat=HI, dst=q8, scale=din.q_scale)
-                B.append_index_keys(dpb, k_new, din.k_cache, din.k_scale)
+            def prep_for(x):
+                dpb = B.problem_from_inputs(x)
+                q8 = x.q_idx.view(T, HI * DI)
 
+                def prep():
+                    B.quantize_fp8(q_new, scale_repeat=HI, dst=q8, scale=x.q_scale)
+                    B.append_index_keys(dpb, k_new, x.k_cache, x.k_scale)
+                return prep
+
+            preps = [prep_for(x) for x in dsets]
             extra = T * (HI * DI * 3 + HI * 4) + T * (DI * 3 + 4)      # bf16 in, e4m3 + scales out
-        dms, dst = time_forward(B, torch, din, args.steps, args.warmup, args.settle_ms, prep=prep)
+        dms, dst = time_forward(B, torch, dsets, args.steps, args.warmup, args.settle_ms, preps=preps)
         d_idx, d_step = algorithmic_bytes(din)
         line = {"workload": name, "step": "quantise q_I + append k_I + dsa_forward" if fp8_prep else "dsa_forward",
-                "context_total": int((din.q_pos.long() + 1).sum()),
+                "batch": T, "context_total": int((din.q_pos.long() + 1).sum()),
                 "tokens_per_s": round(T / (dms * 1e-3), 1), "ms_per_step": round(dms, 4),
+                "input_sets_rotated": len(dsets),
                 "stages_ms": {"indexer": round(dst[0], 4), "topk": round(dst[1], 4), "attention": round(dst[2], 4)},
                 "indexer_bytes_per_launch": d_idx,
                 "indexer_hbm_frac": round(d_idx / (dst[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "stage_rooflines": decode_stage_rooflines(din, dst),
                 "step_algorithmic_bytes": d_step + extra,
                 "step_hbm_frac": round((d_step + extra) / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         log(f"{name}: {dms:.3f} ms/step, indexer {dst[0]:.4f} ms")
+        del dsets
         if not args.no_dense and not fp8_prep:
             dense[name] = dense_line(B, torch, din, dms, max(3, args.steps // 4), 1, args.settle_ms)
         del din
         torch.cuda.empty_cache()
         return line
 
-    if wl.mode == "decode" and not (args.no_exact_decode and args.no_fp8_decode):
+    if wl.mode == "decode":
         inp = None
         torch.cuda.empty_cache()
         if not args.no_exact_decode:
@@ -506,72 +686,26 @@ def main():
             result["exact_128k_decode"] = decode_line(args.exact_workload, False)
         if not args.no_fp8_decode:
             result["fp8_decode"] = decode_line(args.fp8_workload, True)
+        if not args.no_8k_decode:
+            # 16 sequences of 8K tokens, contiguous caches (small enough for the MALL: rotated)
+            result["decode_8k"] = decode_line("decode_8k_bf16", False)
 
     if not args.no_prefill:
-        pname = "prefill_16k_bf16"
-        log(f"secondary: {pname}")
         inp = None
         torch.cuda.empty_cache()
-        pin = generate(WORKLOADS[pname], "cuda")
-        pms, pst = time_forward(B, torch, pin, 3, 1, args.settle_ms)
-        pf_idx, pf_mla = algorithmic_flops(pin)
-        # each stage alone over every query row, one call each (the forward
-        # processes the rows in chunks; its stage events cover the first chunk)
-        pb = B.problem_from_inputs(pin)
-        sc = torch.empty((pin.num_q, pin.max_ctx), dtype=torch.float32, device="cuda")
-        idx = torch.empty((pin.num_q, pin.topk), dtype=torch.int32, device="cuda")
-        tws = torch.empty(B.workspace_size(B.OP_TOPK, pb), dtype=torch.uint8, device="cuda")
-        mws = torch.empty(max(1, B.workspace_size(B.OP_SPARSE_MLA, pb)), dtype=torch.uint8, device="cuda")
-        ops = [lambda: B.index_scores(pb, pin.q_idx, pin.q_scale, pin.w, pin.k_cache, pin.k_scale, scores=sc),
-               lambda: B.topk(pb, sc, idx=idx, ws=tws),
-               lambda: B.sparse_mla(pb, pin.sm_scale, pin.q, pin.kv_cache, idx, ws=mws)]
-        stage_ms = []
-        for op in ops:
-            settle(torch, op, args.settle_ms / 2)
-            e0, e1 = make_events(torch, 2)
-            e0.record()
-            for _ in range(3):
-                op()
-            e1.record()
-            torch.cuda.synchronize()
-            stage_ms.append(e0.elapsed_time(e1) / 3)
-        ims = stage_ms[0]
-        fused = fused_prefill_stages(B, torch, pin, args.settle_ms / 2)
-        planted = None
-        if pin.planted is not None:
-            # share of planted keys among the selected positions of the rows
-            # that select (n > k), against their share among those rows' candidates
-            mark = torch.zeros(pin.max_ctx, dtype=torch.bool, device="cuda")
-            mark[pin.planted] = True
-            rows_sel = (pin.q_pos.long() + 1) > pin.topk
-            sel = idx[rows_sel]
-            cum = torch.cumsum(mark.long(), 0)
-            planted = {"share_in_topk": round(mark[sel.long()].float().mean().item(), 4),
-                       "share_in_candidates": round((cum[pin.q_pos.long()[rows_sel]].float() /
-                                                     (pin.q_pos.long()[rows_sel] + 1).float()).mean().item(), 4)}
-        result["prefill"] = {
-            "workload": pname, "tokens_per_s": round(pin.num_q / (pms * 1e-3), 1), "ms_per_step": round(pms, 3),
-            "stage_ops_ms_all_rows": {"index_scores": round(stage_ms[0], 3), "topk": round(stage_ms[1], 3),
-                                      "sparse_mla": round(stage_ms[2], 3)},
-            "fused_stages_ms": {"indexer": round(fused[0], 3), "topk": round(fused[1], 3), "attention": round(fused[2], 3)},
-            "indexer_mfma_frac_fused": round(pf_idx / (fused[0] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
-            "attention_mfma_frac_fused": round(pf_mla / (fused[2] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
-            "indexer_mfma_frac": round(pf_idx / (ims * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
-            "attention_mfma_frac": round(pf_mla / (stage_ms[2] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
-            "step_mfma_frac": round((pf_idx + pf_mla) / (pms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
-            "planted_keys": planted}
-        log(f"prefill {pms:.2f} ms/step, indexer {ims:.2f} ms")
-        del sc, idx, tws, mws
+        pwl = WORKLOADS["prefill_16k_bf16"]
+        result["prefill"], extra = prefill_line(B, torch, generate, pwl, args.settle_ms, max(2, args.rotate),
+                                                dense=not args.no_dense,
+                                                warmup_objective=not args.no_warmup_objective)
+        if "dense" in extra:
+            dense[pwl.name] = extra["dense"]
+        if "warmup_objective" in extra:
+            result["warmup_objective"] = extra["warmup_objective"]
         torch.cuda.empty_cache()
-        if not args.no_dense:
-            dense[pname] = dense_line(B, torch, pin, pms, 2, 1, args.settle_ms)
-        if not args.no_warmup_objective:
-            log("indexer warm-up objective on the prefill inputs")
-            result["warmup_objective"] = warmup_objective_line(B, torch, pin, 2, args.settle_ms)
-            log(f"warm-up objective: {result['warmup_objective']['ms_per_step']:.2f} ms")
-        del pin
-        torch.cuda.empty_cache()
-        inp = None
+        if not args.no_prefill_64k:
+            result["prefill_64k_fp8"], _ = prefill_line(B, torch, generate, WORKLOADS["prefill_64k_fp8"],
+                                                        args.settle_ms, max(2, args.rotate))
+            torch.cuda.empty_cache()
     if dense:
         # the comparison the pages draw: DSA against dense MLA over the same contexts
         result["dense_comparison"] = dense
