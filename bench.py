@@ -208,7 +208,6 @@ def decode_stage_rooflines(inp, stages):
 def env_info():
     """Host and software the numbers were taken on (read before the GPU is touched)."""
     import platform
-    import subprocess
     info = {"cpu_count": os.cpu_count(), "cpu_model": None, "rocm": None, "hipcc": None,
             "python": platform.python_version()}
     try:
@@ -225,9 +224,11 @@ def env_info():
     except OSError:
         pass
     try:
-        out = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True, timeout=60).stdout
-        info["hipcc"] = next((l.strip() for l in out.splitlines() if "HIP version" in l), None)
-    except Exception:
+        # recorded by the library's build (no child process here: under a profiler the
+        # GPU is initialised before this program starts)
+        with open(KERNEL_ISA_FILE) as f:
+            info["hipcc"] = json.load(f).get("hipcc_version")
+    except (OSError, ValueError):
         pass
     return info
 

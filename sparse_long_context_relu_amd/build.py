@@ -88,8 +88,11 @@ def kernel_isa_text(asm: str, kernel: str) -> str:
 
 
 def write_kernel_hashes(cc: str) -> dict:
-    """SHA-256 of the gfx950 assembly of each fingerprinted kernel, to kernel_isa.json."""
+    """SHA-256 of the gfx950 assembly of each fingerprinted kernel, to kernel_isa.json,
+    with the compiler version line the library was built with."""
     out = {}
+    ver = subprocess.run([cc, "--version"], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True).stdout
+    out["hipcc_version"] = next((l.strip() for l in ver.splitlines() if "HIP version" in l), None)
     for name, (src, kernel) in HASHED_KERNELS.items():
         asm_path = os.path.join(BUILD_DIR, src + ".s")
         subprocess.run([cc, *CXXFLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm_path],
