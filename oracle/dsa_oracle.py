@@ -43,6 +43,10 @@ Every step is the plain definition:
 8. the indexer's warm-up objective [ZS 3.3 Stage 1; LD Objective Functions]: the KL divergence
    between the head-aggregated, L1-normalised dense attention distribution
    and softmax(I), and its gradient into q_I, w and k_I.
+9. Stage 2, sparse training [ZS 3.3 Stage 2]: the gradient of eq. U's
+   attention over the selected rows (dq, and the latent-row gradients summed
+   into the cache rows), and the indexer's KL loss restricted to the selected
+   subset S_t with its gradient.
 
 Readings where the pages are silent are stated at each function.
 """
@@ -518,3 +522,140 @@ def indexer_kl_loss(inp: OracleInputs, rows=None) -> dict:
             blocks = np.asarray(inp.block_table[b], dtype=np.int64)[pos // inp.block_size]
             np.add.at(dk, (blocks, pos % inp.block_size), dk_t)
     return {"rows": rows, "loss": loss, "grad_scores": grads, "dq": dq, "dw": dw, "dk": dk}
+
+
+# --------------------------------------------------------------------------
+# 9. Stage 2, sparse training [ZS 3.3 Stage 2: the main attention switches to
+#    top-k, every parameter trains, and the indexer keeps learning from a loss
+#    taken on the selected subset S_t; NH DSA section: 2048 key-value pairs
+#    per query in this stage]
+# --------------------------------------------------------------------------
+
+def sparse_mla_backward(q_t: np.ndarray, rows: np.ndarray, v_dim: int, sm_scale: float, dout: np.ndarray) -> tuple:
+    """Gradient of eq. U's attention for one query over its selected rows.
+
+    Forward (sparse_mla): z = sm_scale q c^T [H, m], p = softmax_rows(z),
+    out = p c[:, :Dv].  Given dL/dout [H, Dv], the chain rule gives
+      dp  = dout c[:, :Dv]^T                       [H, m]
+      dz  = p * (dp - sum_s p_s dp_s)              [H, m]   (softmax backward)
+      dq  = sm_scale dz c                          [H, D]
+      dc  = sm_scale dz^T q  (+ p^T dout in the first Dv columns)   [m, D]
+    The key and the value of a selected token are the same latent row (MQA
+    mode), so its row gradient adds both parts.  An empty selection gives
+    zeros.  Returns (dq [H, D], drows [m, D])."""
+    H, D = q_t.shape
+    m = rows.shape[0]
+    if m == 0:
+        return np.zeros((H, D)), np.zeros((0, D))
+    z = sm_scale * (q_t @ rows.T)
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    dp = dout @ rows[:, :v_dim].T
+    dz = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    dq = sm_scale * (dz @ rows)
+    drows = sm_scale * (dz.T @ q_t)
+    drows[:, :v_dim] += p.T @ dout
+    return dq, drows
+
+
+def _add_rows(acc: np.ndarray, inp: OracleInputs, b: int, positions: np.ndarray, values: np.ndarray) -> None:
+    """acc[slot(b, s)] += values for each logical position s (cache layout; a
+    position selected twice adds twice)."""
+    positions = np.asarray(positions, dtype=np.int64)
+    if inp.block_table is None:
+        np.add.at(acc, (np.full(positions.shape[0], b), positions), values)
+    else:
+        blocks = np.asarray(inp.block_table[b], dtype=np.int64)[positions // inp.block_size]
+        if np.any(blocks < 0) or np.any(blocks >= acc.shape[0]):
+            raise ValueError("block table entry out of range for a selected position")
+        np.add.at(acc, (blocks, positions % inp.block_size), values)
+
+
+def sparse_attention_backward(inp: OracleInputs, idx: np.ndarray, dout: np.ndarray, rows=None) -> dict:
+    """The main attention's gradient in Stage 2, for query rows ``rows``.
+
+    Query t attends over its selected positions idx[t] (entries < 0 ignored);
+    dout [R, H, Dv] is dL/dout of those rows.  Returns ``dq`` [R, H, D] and
+    ``dkv``, shaped like the latent cache, holding for every cache row the sum
+    over all queries that selected its token of that query's row gradient (0
+    for rows no query selected).  The selection itself has no gradient."""
+    rows = list(range(inp.num_q)) if rows is None else [int(r) for r in rows]
+    H, D = inp.q.shape[1], inp.q.shape[2]
+    dq = np.zeros((len(rows), H, D))
+    dkv = np.zeros(inp.kv_cache.shape[:-1] + (D,))
+    for i, t in enumerate(rows):
+        sel = np.asarray(idx[i], dtype=np.int64)
+        sel = sel[sel >= 0]
+        if np.any(sel >= candidate_count(inp, t)):
+            raise ValueError("selected position outside the causal candidates")
+        b = sequence_of(inp, t)
+        q_t = _finite(decode(inp.q[t], inp.mla_dtype), "MLA query")
+        crow = _finite(decode(gather_rows(inp.kv_cache, inp, b, sel), inp.mla_dtype), "latent row")
+        dq[i], dr = sparse_mla_backward(q_t, crow, inp.v_dim, inp.sm_scale, np.asarray(dout[i], dtype=np.float64))
+        _add_rows(dkv, inp, b, sel, dr)
+    return {"rows": rows, "dq": dq, "dkv": dkv}
+
+
+def sparse_attention_distribution(inp: OracleInputs, t: int, selected) -> np.ndarray:
+    """p_t over the selected positions (order of ``selected``, entries < 0 ignored):
+    the Stage-2 main attention's softmax weights over S_t, summed over the heads
+    and L1-normalised (each head's weights sum to 1 over S_t, so this is their
+    mean).  Reading of the pages' "loss on the selected subset": the target of
+    the warm-up objective, taken from the attention that now runs over S_t."""
+    sel = np.asarray(selected, dtype=np.int64)
+    sel = sel[sel >= 0]
+    if sel.shape[0] == 0:
+        return np.zeros(0)
+    b = sequence_of(inp, t)
+    q_t = _finite(decode(inp.q[t], inp.mla_dtype), "MLA query")
+    crow = _finite(decode(gather_rows(inp.kv_cache, inp, b, sel), inp.mla_dtype), "latent row")
+    z = inp.sm_scale * (q_t @ crow.T)
+    a = np.exp(z - z.max(axis=1, keepdims=True))
+    a /= a.sum(axis=1, keepdims=True)
+    agg = a.sum(axis=0)
+    return agg / agg.sum()
+
+
+def sparse_indexer_kl_loss(inp: OracleInputs, rows=None, selections=None) -> dict:
+    """Stage 2's indexer objective over query rows ``rows``: per query
+    L_t = KL(p_t,S || softmax(I_t,S)) with S = S_t the query's selection (the
+    top-k of its current scores, or ``selections[i]`` when given), p from
+    sparse_attention_distribution and the softmax taken over S_t only.  Its
+    gradient with respect to I(t, s) is softmax(I_S)_s - p_s for s in S_t and 0
+    for every other candidate, back-propagated through eq. I.  Returns
+    ``loss`` [R], ``idx`` [R, k] (the selections, -1 padded), ``grad_scores``
+    (list of dense [n_t] gradients), ``dq`` [R, H_I, d_I], ``dw`` [R, H_I] and
+    ``dk`` (key cache layout)."""
+    rows = list(range(inp.num_q)) if rows is None else [int(r) for r in rows]
+    H_I, d_I = inp.q_idx.shape[1], inp.q_idx.shape[2]
+    k = inp.topk
+    loss = np.zeros(len(rows))
+    idx = np.full((len(rows), k), -1, dtype=np.int64)
+    dq = np.zeros((len(rows), H_I, d_I))
+    dw = np.zeros((len(rows), H_I))
+    dk = np.zeros(inp.k_cache.shape[:-1] + (d_I,))
+    grads = []
+    for i, t in enumerate(rows):
+        q_t, w_t, keys = query_index_operands(inp, t)
+        I = index_scores(q_t, w_t, keys)
+        if selections is None:
+            sel = topk(I, k)
+        else:
+            sel = np.asarray(selections[i], dtype=np.int64)
+            sel = sel[sel >= 0]
+        idx[i, : sel.shape[0]] = sel
+        p = sparse_attention_distribution(inp, t, sel)
+        loss[i], g_sel = kl_rows(I[sel], p)
+        g = np.zeros(I.shape[0])
+        g[sel] = g_sel
+        grads.append(g)
+        dq[i], dw[i], dk_t = index_scores_backward(q_t, w_t, keys, g)
+        b = sequence_of(inp, t)
+        n = candidate_count(inp, t)
+        pos = np.arange(n)
+        if inp.block_table is None:
+            dk[b, pos] += dk_t
+        else:
+            blocks = np.asarray(inp.block_table[b], dtype=np.int64)[pos // inp.block_size]
+            np.add.at(dk, (blocks, pos % inp.block_size), dk_t)
+    return {"rows": rows, "loss": loss, "idx": idx, "grad_scores": grads, "dq": dq, "dw": dw, "dk": dk}

@@ -731,4 +731,240 @@ def pin_append_index_keys(o):
     assert np.all(c4[0, [1, 2, 4, 5]] == 0) and s4[0, 3] == sc[1]
 
 
+
+
+# ---------------------------------------------------------------- Stage 2: sparse training
+
+def _mla_torch(q, rows, Dv, scale):
+    """eq. U's attention written in torch ops (float64): K is the whole row, V its
+    first Dv entries, both taken from the one leaf tensor `rows`."""
+    p = torch.softmax(scale * (q @ rows.T), dim=-1)
+    return p @ rows[:, :Dv]
+
+
+def pin_sparse_mla_backward_autograd(o):
+    """dq and the row gradients equal torch autograd of eq. U's attention (float64),
+    key and value parts of a row summed because they are one leaf."""
+    rng = np.random.default_rng(31)
+    for H, D, Dv, m in ((1, 4, 3, 1), (2, 6, 4, 3), (3, 12, 8, 17), (4, 10, 10, 9)):
+        q = rng.normal(size=(H, D))
+        rows = rng.normal(size=(m, D))
+        dout = rng.normal(size=(H, Dv))
+        qt, rt = torch.tensor(q, requires_grad=True), torch.tensor(rows, requires_grad=True)
+        (_mla_torch(qt, rt, Dv, 0.41) * torch.tensor(dout)).sum().backward()
+        dq, dr = o.sparse_mla_backward(q, rows, Dv, 0.41, dout)
+        _close(dq, qt.grad.numpy(), 1e-12, f"dq m={m}")
+        _close(dr, rt.grad.numpy(), 1e-12, f"drows m={m}")
+    # one selected row: the softmax is constant, so dq = 0 and the row gets dout
+    q, rows, dout = rng.normal(size=(3, 6)), rng.normal(size=(1, 6)), rng.normal(size=(3, 4))
+    dq, dr = o.sparse_mla_backward(q, rows, 4, 0.3, dout)
+    assert np.all(np.abs(dq) < 1e-15)
+    _close(dr[0, :4], dout.sum(axis=0), 1e-12, "single row value gradient")
+    assert np.all(np.abs(dr[0, 4:]) < 1e-15)
+    dq, dr = o.sparse_mla_backward(q, rows[:0], 4, 0.3, dout)       # empty selection
+    assert dq.shape == (3, 6) and np.all(dq == 0) and dr.shape == (0, 6)
+
+
+def pin_sparse_mla_backward_finite_differences(o):
+    """Central differences (float64, h = 1e-6) of sum(dout * out) in q and in the
+    selected rows match the analytic gradients."""
+    rng = np.random.default_rng(32)
+    H, D, Dv, m = 3, 7, 5, 6
+    q, rows, dout = rng.normal(size=(H, D)), rng.normal(size=(m, D)), rng.normal(size=(H, Dv))
+    f = lambda qq, rr: float(np.sum(dout * o.sparse_mla(qq, rr, Dv, 0.5)[0]))
+    dq, dr = o.sparse_mla_backward(q, rows, Dv, 0.5, dout)
+    h = 1e-6
+    for _ in range(8):
+        i, j = int(rng.integers(0, H)), int(rng.integers(0, D))
+        qp, qm = q.copy(), q.copy()
+        qp[i, j] += h
+        qm[i, j] -= h
+        _close((f(qp, rows) - f(qm, rows)) / (2 * h), dq[i, j], 1e-7, f"dq[{i},{j}]")
+        i, j = int(rng.integers(0, m)), int(rng.integers(0, D))
+        rp, rm = rows.copy(), rows.copy()
+        rp[i, j] += h
+        rm[i, j] -= h
+        _close((f(q, rp) - f(q, rm)) / (2 * h), dr[i, j], 1e-7, f"drows[{i},{j}]")
+
+
+def pin_sparse_backward_equals_masked_dense(o):
+    """The sparse backward equals torch SDPA's backward over every candidate with a
+    mask equal to the chosen set (float64): the same dq, the chosen rows' gradients,
+    and zero gradient on every row outside the set."""
+    rng = np.random.default_rng(33)
+    for _ in range(6):
+        H, D, Dv, n = 3, 12, 8, int(rng.integers(2, 30))
+        q, rows, dout = rng.normal(size=(H, D)), rng.normal(size=(n, D)), rng.normal(size=(H, Dv))
+        sel = np.sort(rng.choice(n, size=int(rng.integers(1, n + 1)), replace=False))
+        mask = np.zeros(n, bool)
+        mask[sel] = True
+        qt = torch.tensor(q, requires_grad=True)
+        rt = torch.tensor(rows, requires_grad=True)
+        kt = rt.reshape(1, 1, n, D).expand(1, H, n, D)
+        vt = rt[:, :Dv].reshape(1, 1, n, Dv).expand(1, H, n, Dv)
+        out = torch.nn.functional.scaled_dot_product_attention(qt.reshape(1, H, 1, D), kt, vt,
+                                                               attn_mask=torch.tensor(mask).reshape(1, 1, 1, n),
+                                                               scale=0.29)
+        (out.reshape(H, Dv) * torch.tensor(dout)).sum().backward()
+        dq, dr = o.sparse_mla_backward(q, rows[sel], Dv, 0.29, dout)
+        _close(dq, qt.grad.numpy(), 1e-12, "masked dense dq")
+        _close(dr, rt.grad.numpy()[sel], 1e-12, "masked dense drows")
+        assert np.all(np.abs(rt.grad.numpy()[~mask]) < 1e-15)
+
+
+def pin_sparse_attention_backward_dense_causal(o):
+    """With every candidate selected (k >= n) the Stage-2 attention gradient of a whole
+    prefill equals torch's causal SDPA backward (float64): dq per query, and the
+    cache-row gradients summed over all the queries that read each row."""
+    wl = small_workload(mode="prefill", length=21, k=32, H=3, D=10, Dv=6)
+    oi = to_oracle(generate(wl, "cpu"))
+    T = oi.num_q
+    idx = np.full((T, 32), -1)
+    for t in range(T):
+        idx[t, : t + 1] = np.arange(t + 1)
+    dout = np.random.default_rng(34).normal(size=(T, 3, 6))
+    res = o.sparse_attention_backward(oi, idx, dout)
+    qt = torch.tensor(oi.q.astype(np.float64), requires_grad=True)           # [T, H, D]
+    ct = torch.tensor(oi.kv_cache[0].astype(np.float64), requires_grad=True)  # [T, D]
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qt.permute(1, 0, 2).unsqueeze(0), ct.reshape(1, 1, T, 10).expand(1, 3, T, 10),
+        ct[:, :6].reshape(1, 1, T, 6).expand(1, 3, T, 6), is_causal=True, scale=oi.sm_scale)
+    (out[0].permute(1, 0, 2) * torch.tensor(dout)).sum().backward()
+    _close(res["dq"], qt.grad.numpy(), 1e-12, "causal dq")
+    _close(res["dkv"][0, :T], ct.grad.numpy(), 1e-12, "causal dkv")
+
+
+def pin_sparse_attention_backward_paged(o):
+    """Paged caches (permuted 4-token blocks, NaN poison elsewhere) give the same dq,
+    and each row gradient lands in the slot the block table names; slots of rows no
+    query selected hold 0."""
+    rng = np.random.default_rng(35)
+    wl = small_workload(mode="decode", num_seqs=3, length=23, k=6)
+    oi = to_oracle(generate(wl, "cpu", lengths=[23, 9, 16]))
+    res = o.forward(oi)
+    dout = rng.normal(size=(3, oi.q.shape[1], oi.v_dim))
+    a = o.sparse_attention_backward(oi, res["idx"], dout)
+    bs = 4
+    B, L = oi.kv_cache.shape[:2]
+    nb = (L + bs - 1) // bs
+    table = rng.permutation(B * nb).reshape(B, nb)
+    vc = np.full((B * nb, bs) + oi.kv_cache.shape[2:], np.nan, oi.kv_cache.dtype)
+    for b in range(B):
+        for s in range(L):
+            vc[table[b, s // bs], s % bs] = oi.kv_cache[b, s]
+    oi.block_table, oi.block_size, oi.kv_cache = table, bs, vc
+    b_ = o.sparse_attention_backward(oi, res["idx"], dout)
+    _close(b_["dq"], a["dq"], 1e-15, "paged dq")
+    for b in range(B):
+        for s in range(L):
+            _close(b_["dkv"][table[b, s // bs], s % bs], a["dkv"][b, s], 1e-15, f"dkv seq {b} pos {s}")
+    sel0 = set(res["idx"][0][res["idx"][0] >= 0].tolist())
+    for s in range(23):
+        if s not in sel0:
+            assert np.all(a["dkv"][0, s] == 0), f"unselected row {s}"
+
+
+def pin_sparse_distribution_torch(o):
+    """The Stage-2 target is the head mean of torch's softmax over the selected rows;
+    with every candidate selected it is the Stage-1 target."""
+    wl = small_workload(mode="decode", num_seqs=2, length=30, k=5, H=3, D=12, Dv=8)
+    oi = to_oracle(generate(wl, "cpu", lengths=[30, 17]))
+    rng = np.random.default_rng(36)
+    for t in range(2):
+        n = int(oi.q_pos[t]) + 1
+        sel = np.sort(rng.choice(n, size=7, replace=False))
+        q = torch.from_numpy(oi.q[t].astype(np.float64))
+        kv = torch.from_numpy(oi.kv_cache[t, sel].astype(np.float64))
+        want = torch.softmax(oi.sm_scale * (q @ kv.T), dim=-1).mean(dim=0).numpy()
+        _close(o.sparse_attention_distribution(oi, t, sel), want, 1e-12, f"query {t}")
+        _close(o.sparse_attention_distribution(oi, t, np.arange(n)), o.attention_distribution(oi, t), 1e-12,
+               f"query {t} full set")
+
+
+def _stage2_workload():
+    wl = small_workload(mode="prefill", length=16, k=5, H_I=3, d_I=8, H=2, D=12, Dv=8, w_high=1.0, w_low=-0.5)
+    return to_oracle(generate(wl, "cpu"))
+
+
+def pin_sparse_indexer_kl_autograd(o):
+    """Stage 2's indexer objective against torch in float64: the selection from
+    torch's stable descending sort, the target from torch's softmax over the selected
+    latent rows, the loss from kl_div over the selection, gradients by autograd (mixed-
+    sign weights)."""
+    oi = _stage2_workload()
+    res = o.sparse_indexer_kl_loss(oi)
+    T, k = oi.num_q, oi.topk
+    q = torch.tensor(oi.q_idx.astype(np.float64), requires_grad=True)
+    w = torch.tensor(oi.w.astype(np.float64), requires_grad=True)
+    kk = torch.tensor(oi.k_cache[0].astype(np.float64), requires_grad=True)
+    qm = torch.tensor(oi.q.astype(np.float64))
+    kv = torch.tensor(oi.kv_cache[0].astype(np.float64))
+    total = 0.0
+    for t in range(T):
+        n = t + 1
+        I = (w[t][:, None] * torch.relu(q[t] @ kk[:n].T)).sum(dim=0)
+        sel = torch.sort(-I.detach(), stable=True).indices[: min(k, n)]
+        assert sorted(sel.tolist()) == sorted(res["idx"][t][res["idx"][t] >= 0].tolist()), f"selection {t}"
+        p = torch.softmax(oi.sm_scale * (qm[t] @ kv[sel].T), dim=-1).mean(dim=0)
+        lt = torch.nn.functional.kl_div(torch.log_softmax(I[sel], dim=0), p, reduction="sum")
+        _close(res["loss"][t], lt.item(), 1e-12, f"loss[{t}]")
+        total = total + lt
+    total.backward()
+    _close(res["dq"], q.grad.numpy(), 1e-11, "dq")
+    _close(res["dw"], w.grad.numpy(), 1e-11, "dw")
+    _close(res["dk"][0, :T], kk.grad.numpy(), 1e-11, "dk")
+    for t in range(T):                                   # no gradient outside the selection
+        g = res["grad_scores"][t]
+        off = np.ones(g.shape[0], bool)
+        off[res["idx"][t][res["idx"][t] >= 0]] = False
+        assert np.all(g[off] == 0), f"gradient outside S_{t}"
+
+
+def pin_sparse_indexer_kl_full_selection(o):
+    """k >= n: the selection is every candidate, and Stage 2's indexer objective is
+    the Stage-1 warm-up objective (loss and every gradient)."""
+    oi = _stage2_workload()
+    oi.topk = 64
+    a = o.sparse_indexer_kl_loss(oi)
+    b = o.indexer_kl_loss(oi)
+    for key in ("loss", "dq", "dw", "dk"):
+        _close(a[key], b[key], 1e-12, key)
+
+
+def pin_sparse_indexer_kl_finite_differences(o):
+    """With the selections held fixed, central differences (2^-10, exact in float32)
+    of the summed loss in w and in q_I (away from the ReLU kink) match the gradients."""
+    oi = _stage2_workload()
+    res = o.sparse_indexer_kl_loss(oi)
+    sels = res["idx"]
+    h = 2.0 ** -10
+
+    def total(field, idx, delta):
+        arr = getattr(oi, field)
+        old = arr[idx]
+        arr[idx] = np.float32(old + delta)
+        try:
+            return float(o.sparse_indexer_kl_loss(oi, selections=sels)["loss"].sum())
+        finally:
+            arr[idx] = old
+
+    fd = lambda field, idx: (total(field, idx, h) - total(field, idx, -h)) / (2 * h)
+    rng = np.random.default_rng(37)
+    for _ in range(6):
+        t, j = int(rng.integers(6, 16)), int(rng.integers(0, 3))
+        _close(fd("w", (t, j)), res["dw"][t, j], 1e-5, f"dw[{t},{j}]")
+    q = oi.q_idx.astype(np.float64)
+    k = oi.k_cache[0].astype(np.float64)
+    checked = 0
+    for t in range(6, 16):
+        for j in range(3):
+            if np.min(np.abs(q[t, j] @ k[: t + 1].T)) < 0.05:
+                continue
+            d = int(rng.integers(0, 8))
+            _close(fd("q_idx", (t, j, d)), res["dq"][t, j, d], 1e-5, f"dq[{t},{j},{d}]")
+            checked += 1
+            break
+    assert checked >= 4
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

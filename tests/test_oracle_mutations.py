@@ -210,6 +210,81 @@ def _bwd_dw_unmasked(q, w, keys, grad):
     return dq, (grad[None, :] * (q @ keys.T)).sum(axis=1), dk
 
 
+def _sbwd(drop_delta=False, no_value=False, no_scale=False, no_rope=False):
+    def f(q, rows, v_dim, sm, dout):
+        H, D = q.shape
+        if rows.shape[0] == 0:
+            return np.zeros((H, D)), np.zeros((0, D))
+        z = sm * (q @ rows.T)
+        p = np.exp(z - z.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        dp = dout @ rows[:, :v_dim].T
+        dz = p * dp if drop_delta else p * (dp - (p * dp).sum(axis=1, keepdims=True))
+        dq = (1.0 if no_scale else sm) * (dz @ rows)
+        dr = sm * (dz.T @ q)
+        if no_rope:
+            dr[:, v_dim:] = 0.0
+        if not no_value:
+            dr[:, :v_dim] += p.T @ dout
+        return dq, dr
+    return f
+
+
+def _add_rows_overwrite(acc, inp, b, positions, values):
+    positions = np.asarray(positions, dtype=np.int64)
+    if inp.block_table is None:
+        acc[b, positions] = values
+    else:
+        blocks = np.asarray(inp.block_table[b], dtype=np.int64)[positions // inp.block_size]
+        acc[blocks, positions % inp.block_size] = values
+
+
+def _add_rows_ignore_table(acc, inp, b, positions, values):
+    positions = np.asarray(positions, dtype=np.int64)
+    if inp.block_table is None:
+        np.add.at(acc, (np.full(positions.shape[0], b), positions), values)
+    else:
+        nb = inp.block_table.shape[1]
+        np.add.at(acc, (b * nb + positions // inp.block_size, positions % inp.block_size), values)
+
+
+def _sdist_dense_restricted(inp, t, selected):
+    # the dense (all-candidate) target restricted to S and renormalised: not the
+    # sparse attention's own distribution (heads are weighted differently)
+    sel = np.asarray(selected, dtype=np.int64)
+    sel = sel[sel >= 0]
+    if sel.shape[0] == 0:
+        return np.zeros(0)
+    p = od.attention_distribution(inp, t)[sel]
+    return p / p.sum()
+
+
+def _skl(variant):
+    def f(inp, rows=None, selections=None):
+        res = od.__dict__["_orig_skl"](inp, rows, selections)
+        if variant == "softmax_all":
+            # softmax over every candidate, KL terms over S only
+            for i, t in enumerate(res["rows"]):
+                q_t, w_t, keys = od.query_index_operands(inp, t)
+                I = od.index_scores(q_t, w_t, keys)
+                sel = res["idx"][i][res["idx"][i] >= 0]
+                p = od.sparse_attention_distribution(inp, t, sel)
+                lq = I - (I.max() + np.log(np.exp(I - I.max()).sum()))
+                res["loss"][i] = float(np.sum(p * (np.log(np.maximum(p, 1e-300)) - lq[sel])))
+        elif variant == "grad_leaks":
+            for i, t in enumerate(res["rows"]):
+                q_t, w_t, keys = od.query_index_operands(inp, t)
+                I = od.index_scores(q_t, w_t, keys)
+                g = res["grad_scores"][i]
+                off = np.ones(g.shape[0], bool)
+                off[res["idx"][i][res["idx"][i] >= 0]] = False
+                e = np.exp(I - I.max())
+                g[off] = (e / e.sum())[off]
+                res["dq"][i], res["dw"][i], _ = od.index_scores_backward(q_t, w_t, keys, g)
+        return res
+    return f
+
+
 MUTATIONS = {
     "indexer_no_relu": ("index_scores", _no_relu),
     "indexer_relu_after_weight": ("index_scores", _relu_after_weight),
@@ -243,6 +318,15 @@ MUTATIONS = {
     "bwd_relu_value_as_mask": ("index_scores_backward", _bwd_relu_value),
     "bwd_dk_without_weight": ("index_scores_backward", _bwd_dk_no_weight),
     "bwd_dw_without_relu": ("index_scores_backward", _bwd_dw_unmasked),
+    "sparse_bwd_no_softmax_delta": ("sparse_mla_backward", _sbwd(drop_delta=True)),
+    "sparse_bwd_no_value_gradient": ("sparse_mla_backward", _sbwd(no_value=True)),
+    "sparse_bwd_dq_without_scale": ("sparse_mla_backward", _sbwd(no_scale=True)),
+    "sparse_bwd_key_gradient_without_rope": ("sparse_mla_backward", _sbwd(no_rope=True)),
+    "sparse_dkv_overwrites_instead_of_adding": ("_add_rows", _add_rows_overwrite),
+    "sparse_dkv_ignores_block_table": ("_add_rows", _add_rows_ignore_table),
+    "sparse_target_from_dense_attention": ("sparse_attention_distribution", _sdist_dense_restricted),
+    "sparse_kl_softmax_over_all_candidates": ("sparse_indexer_kl_loss", _skl("softmax_all")),
+    "sparse_kl_gradient_outside_selection": ("sparse_indexer_kl_loss", _skl("grad_leaks")),
 }
 
 
@@ -256,6 +340,7 @@ def test_mutation_is_caught(name, monkeypatch):
     monkeypatch.setattr(od, "_orig_dist", od.attention_distribution, raising=False)
     monkeypatch.setattr(od, "_orig_kl", od.kl_rows, raising=False)
     monkeypatch.setattr(od, "_orig_bwd", od.index_scores_backward, raising=False)
+    monkeypatch.setattr(od, "_orig_skl", od.sparse_indexer_kl_loss, raising=False)
     monkeypatch.setattr(od, attr, repl)
     caught = []
     for pin in pins.ALL_PINS:
