@@ -106,7 +106,8 @@ typedef enum dsa_op {
   DSA_OP_DENSE_MLA = 4,
   DSA_OP_ATTENTION_PROBS = 5,
   DSA_OP_INDEXER_BACKWARD = 6,
-  DSA_OP_INDEXER_KL_LOSS = 7
+  DSA_OP_INDEXER_KL_LOSS = 7,
+  DSA_OP_SPARSE_MLA_BACKWARD = 8
 } dsa_op;
 
 /* Where each query sits and which cache rows it may read (host struct). */
@@ -330,6 +331,43 @@ int dsa_indexer_backward(const dsa_seqs *seqs, const dsa_dims *dims, const void 
  * Workspace: dsa_workspace_size(DSA_OP_INDEXER_KL_LOSS, ...). */
 int dsa_indexer_kl_loss(const dsa_seqs *seqs, const dsa_dims *dims, const dsa_kl_args *args, void *ws,
                         size_t ws_bytes, hipStream_t stream);
+
+/* Stage 2 of training, the main attention's gradient [ZS 3.3, Stage 2: the
+ * main attention switches to top-k sparse and every parameter trains]: the
+ * backward of dsa_sparse_mla over each query's selection.  Given the forward's
+ * out [T, H, Dv] and lse [T, H] (natural log) and dout = dL/dout [T, H, Dv],
+ * with P = exp(sm_scale q . c(s) - lse) over the selected rows c(s):
+ *   dS[h, s] = P (dout[h] . c(s)[0:Dv] - sum_d dout[h,d] out[h,d])
+ *   dq[t, h, :] = sm_scale sum_s dS[h, s] c(s)                       [T, H, D] fp32
+ *   the cache row of token s gets sm_scale sum_h dS[h, s] q[t, h, :] plus
+ *   sum_h P[h, s] dout[t, h, :] (its first Dv entries), summed over every
+ *   query that selected s                           dkv: latent cache layout, fp32
+ * The rows of positions 0..max_ctx-1 of sequence 0 are written (0 where no
+ * query selected the token); other rows are left as they are.  The selection
+ * has no gradient.  probs, if not NULL, receives the Stage-2 target of the
+ * indexer, the attention weights over the selection averaged over the heads
+ * ([T, k] fp32, 0 at absent entries).  Entries of topk_idx outside
+ * 0..q_pos[t] are absent; a query must not select a position twice.
+ * bf16 operands (P and sm_scale dS rounded to bf16 as MFMA operands), fp32
+ * accumulation; the token sums run in ascending query order, so the result is
+ * deterministic.  Supported: prefill (training runs over whole sequences),
+ * bf16 H = 128, D = 576, Dv = 512, k a multiple of 16.
+ * Workspace: dsa_workspace_size(DSA_OP_SPARSE_MLA_BACKWARD, ...). */
+int dsa_sparse_mla_backward(const dsa_seqs *seqs, const dsa_dims *dims, float sm_scale, const void *q,
+                            const void *kv_cache, const int32_t *topk_idx, const void *out, const float *lse,
+                            const void *dout, float *dq, float *dkv, float *probs, void *ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* Stage 2 of training, the indexer's loss on the selected subset [ZS 3.3,
+ * Stage 2: the indexer keeps learning from a loss on S_t].  Per query,
+ *   loss[t] = KL(p_t || softmax over S_t of I(t, .))
+ * with p_t = probs[t, :] (e.g. from dsa_sparse_mla_backward) over the entries
+ * of topk_idx[t, :] that lie in 0..q_pos[t].  scores [T, ld] holds I on entry
+ * and dL/dI on return: softmax_S(I) - p at the selected positions, 0 at every
+ * other position < ld (feed it to dsa_indexer_backward).  fp32;
+ * deterministic.  No workspace. */
+int dsa_sparse_indexer_kl(const dsa_seqs *seqs, float *scores, int64_t ld, const int32_t *topk_idx, int32_t k,
+                          const float *probs, float *loss, hipStream_t stream);
 
 /* Upstream of step 1: per-row fp8 quantisation for an indexer that "runs in
  * FP8" [ZS 3.1; BT (1)].  The pages fix neither scale nor rounding; the

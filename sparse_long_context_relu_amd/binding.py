@@ -20,13 +20,13 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "dsa.h")
 F32, BF16, FP8_E4M3FN = 0, 1, 2
 PREFILL, DECODE = 0, 1
 (OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_MLA, OP_FORWARD, OP_DENSE_MLA, OP_ATTENTION_PROBS,
- OP_INDEXER_BACKWARD, OP_INDEXER_KL_LOSS) = 0, 1, 2, 3, 4, 5, 6, 7
+ OP_INDEXER_BACKWARD, OP_INDEXER_KL_LOSS, OP_SPARSE_MLA_BACKWARD) = 0, 1, 2, 3, 4, 5, 6, 7, 8
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH_LIMIT = 0, -1, -2, -3, -4, -5
 
 EXPORTS = ("dsa_workspace_size", "dsa_index_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward",
            "dsa_forward_noalloc",
            "dsa_dense_mla", "dsa_attention_probs", "dsa_indexer_kl", "dsa_indexer_backward", "dsa_indexer_kl_loss", "dsa_forward_chunk_rows",
-           "dsa_quantize_fp8", "dsa_append_index_keys",
+           "dsa_quantize_fp8", "dsa_append_index_keys", "dsa_sparse_mla_backward", "dsa_sparse_indexer_kl",
            "dsa_status_string")
 
 
@@ -100,6 +100,10 @@ def _load() -> ctypes.CDLL:
     lib.dsa_quantize_fp8.restype = ctypes.c_int
     lib.dsa_append_index_keys.argtypes = [sp, I32, I32, P, P, P, P]
     lib.dsa_append_index_keys.restype = ctypes.c_int
+    lib.dsa_sparse_mla_backward.argtypes = [sp, dp, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.dsa_sparse_mla_backward.restype = ctypes.c_int
+    lib.dsa_sparse_indexer_kl.argtypes = [sp, P, I64, P, I32, P, P, P]
+    lib.dsa_sparse_indexer_kl.restype = ctypes.c_int
     lib.dsa_status_string.argtypes = [ctypes.c_int]
     lib.dsa_status_string.restype = ctypes.c_char_p
     return lib
@@ -399,3 +403,34 @@ def append_index_keys(pb: Problem, k_new: torch.Tensor, k_cache: torch.Tensor, k
     st = LIB.dsa_append_index_keys(ctypes.byref(pb.seqs), k_new.shape[-1], dtype_code(k_new), _ptr(k_new),
                                    _ptr(k_cache), _ptr(k_scale), _stream(stream))
     _check(st, "dsa_append_index_keys")
+
+
+def sparse_mla_backward(pb: Problem, sm_scale: float, q, kv_cache, topk_idx, out, lse, dout, dq=None, dkv=None,
+                        probs=None, want_probs: bool = True, ws=None, stream=None):
+    """dsa_sparse_mla_backward: returns (dq [T, H, D] fp32, dkv (latent cache layout, fp32), probs [T, k] or None).
+    dkv defaults to zeros (rows outside the prefill's positions are not written)."""
+    dev = q.device
+    T, H, D = pb.num_q, pb.dims.heads, pb.dims.qk_dim
+    if dq is None:
+        dq = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+    if dkv is None:
+        dkv = torch.zeros(tuple(kv_cache.shape[:-1]) + (D,), dtype=torch.float32, device=dev)
+    if probs is None and want_probs:
+        probs = torch.empty((T, pb.dims.topk), dtype=torch.float32, device=dev)
+    ws = _workspace(OP_SPARSE_MLA_BACKWARD, pb, ws, dev)
+    st = LIB.dsa_sparse_mla_backward(ctypes.byref(pb.seqs), ctypes.byref(pb.dims), float(sm_scale), _ptr(q),
+                                     _ptr(kv_cache), _ptr(topk_idx), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                                     _ptr(dkv), _ptr(probs), _ptr(ws), _nbytes(ws), _stream(stream))
+    _check(st, "dsa_sparse_mla_backward")
+    return dq, dkv, probs
+
+
+def sparse_indexer_kl(pb: Problem, scores: torch.Tensor, topk_idx: torch.Tensor, probs: torch.Tensor, loss=None,
+                      stream=None):
+    """dsa_sparse_indexer_kl: per-query KL on the selection; dL/dI is written over `scores` (in place)."""
+    if loss is None:
+        loss = torch.empty(pb.num_q, dtype=torch.float32, device=scores.device)
+    st = LIB.dsa_sparse_indexer_kl(ctypes.byref(pb.seqs), _ptr(scores), scores.stride(0), _ptr(topk_idx),
+                                   topk_idx.shape[1], _ptr(probs), _ptr(loss), _stream(stream))
+    _check(st, "dsa_sparse_indexer_kl")
+    return loss

@@ -304,6 +304,35 @@ int scratch_on_current_device(void **out) {
   return DSA_OK;
 }
 
+// Stage-2 attention backward: per chunk of up to kSBwdChunk query rows, the
+// bf16 weights and score gradients, the fp32 row gradients and the key map.
+constexpr int kSBwdChunk = 256;
+
+struct SBwdLayout {
+  int chunk, jstride;
+  long long off_dst, off_pd, off_contrib, off_jpos, total;
+};
+
+SBwdLayout sbwd_layout(const dsa_seqs *s, const dsa_dims *d) {
+  SBwdLayout L;
+  const int T = s->num_q;
+  L.chunk = T < kSBwdChunk ? T : kSBwdChunk;
+  L.jstride = (L.chunk + 7) / 8 * 8;
+  const long long c = L.chunk, k = d->topk, ntk = (k + 31) / 32;
+  L.off_dst = align256(c * d->heads * 4);
+  L.off_pd = L.off_dst + align256(c * ntk * d->heads * 32 * 2);
+  L.off_contrib = L.off_pd + align256(c * k * 2 * d->heads * 2);
+  L.off_jpos = L.off_contrib + align256(c * k * d->qk_dim * 4);
+  L.total = L.off_jpos + align256((long long)s->max_ctx * L.jstride * 2);
+  return L;
+}
+
+int check_sbwd(const dsa_seqs *s, const dsa_dims *d) {
+  if (int e = check_mla_dims(d)) return e;
+  if (d->mla_dtype != DSA_BF16 || s->mode != DSA_PREFILL || d->topk % 16 != 0) return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
+}
+
 int check_ws(size_t need, const void *ws, size_t ws_bytes) {
   if (need == 0) return DSA_OK;
   if (ws == nullptr || ws_bytes < need) return DSA_ERR_WORKSPACE;
@@ -414,6 +443,9 @@ DSA_EXPORT size_t dsa_workspace_size(int op, const dsa_seqs *seqs, const dsa_dim
     case DSA_OP_INDEXER_KL_LOSS:
       if (check_bwd_dims(dims) != DSA_OK || check_probs_dims(seqs, dims) != DSA_OK) return 0;
       return (size_t)kl_loss_layout(seqs, dims).total;
+    case DSA_OP_SPARSE_MLA_BACKWARD:
+      if (check_sbwd(seqs, dims) != DSA_OK) return 0;
+      return (size_t)sbwd_layout(seqs, dims).total;
     default:
       return 0;
   }
@@ -697,6 +729,69 @@ DSA_EXPORT int dsa_indexer_kl_loss(const dsa_seqs *seqs, const dsa_dims *dims, c
   }
   if (!mark(4)) return DSA_ERR_HIP;
   return DSA_OK;
+}
+
+DSA_EXPORT int dsa_sparse_mla_backward(const dsa_seqs *seqs, const dsa_dims *dims, float sm_scale, const void *q,
+                                       const void *kv_cache, const int32_t *topk_idx, const void *out,
+                                       const float *lse, const void *dout, float *dq, float *dkv, float *probs,
+                                       void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (int e = check_seqs(seqs)) return e;
+  if (int e = check_sbwd(seqs, dims)) return e;
+  if (seqs->num_q == 0) return DSA_OK;
+  if (q == nullptr || kv_cache == nullptr || topk_idx == nullptr || out == nullptr || lse == nullptr ||
+      dout == nullptr || dq == nullptr || dkv == nullptr)
+    return DSA_ERR_INVALID_ARG;
+  if (!(sm_scale == sm_scale)) return DSA_ERR_INVALID_ARG;
+  const SBwdLayout L = sbwd_layout(seqs, dims);
+  if (int e = check_ws((size_t)L.total, ws, ws_bytes)) return e;
+  uint8_t *base = reinterpret_cast<uint8_t *>(ws);
+  MlaBwdArgs a;
+  a.sv = view(seqs);
+  a.k = dims->topk;
+  a.sm_scale = sm_scale;
+  a.q = q;
+  a.kv = kv_cache;
+  a.idx = topk_idx;
+  a.out = out;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dkv = dkv;
+  a.probs = probs;
+  a.delta = reinterpret_cast<float *>(base);
+  a.ds_t = reinterpret_cast<uint16_t *>(base + L.off_dst);
+  a.pd = reinterpret_cast<uint16_t *>(base + L.off_pd);
+  a.contrib = reinterpret_cast<float *>(base + L.off_contrib);
+  a.jpos = reinterpret_cast<uint16_t *>(base + L.off_jpos);
+  a.jstride = L.jstride;
+  a.nkeys = seqs->max_ctx;
+  const int T = seqs->num_q;
+  for (int c0 = 0; c0 < T; c0 += L.chunk) {
+    a.q_begin = c0;
+    a.rows = c0 + L.chunk < T ? L.chunk : T - c0;
+    a.first = c0 == 0 ? 1 : 0;
+    if (launch_sparse_mla_bwd(a, stream) != hipSuccess) return DSA_ERR_HIP;
+  }
+  return DSA_OK;
+}
+
+DSA_EXPORT int dsa_sparse_indexer_kl(const dsa_seqs *seqs, float *scores, int64_t ld, const int32_t *topk_idx,
+                                     int32_t k, const float *probs, float *loss, hipStream_t stream) {
+  if (int e = check_seqs(seqs)) return e;
+  if (int e = check_k(k)) return e;
+  if (seqs->num_q == 0) return DSA_OK;
+  if (scores == nullptr || topk_idx == nullptr || probs == nullptr || loss == nullptr || ld < seqs->max_ctx)
+    return DSA_ERR_INVALID_ARG;
+  SparseKlArgs a;
+  a.sv = view(seqs);
+  a.rows = seqs->num_q;
+  a.k = k;
+  a.scores = scores;
+  a.ld = ld;
+  a.idx = topk_idx;
+  a.probs = probs;
+  a.loss = loss;
+  return hip_status(launch_sparse_kl(a, stream));
 }
 
 DSA_EXPORT int dsa_quantize_fp8(int64_t rows, int32_t len, int32_t src_dtype, const void *src, void *dst,

@@ -135,6 +135,44 @@ struct BwdArgs {
   float *part;              // split partials
 };
 
+// Stage-2 gradient of the sparse attention (bf16, H = 128, D = 576, Dv = 512),
+// one chunk of query rows [q_begin, q_begin + rows) of a prefill per call of
+// the launcher.  Buffers marked ws are the caller's workspace.
+struct MlaBwdArgs {
+  SeqView sv;
+  int k;                    // selection length (a multiple of 16)
+  float sm_scale;
+  const void *q;            // [T, H, D]
+  const void *kv;           // latent cache
+  const int32_t *idx;       // [T, k] selected positions (entries < 0 or > q_pos: absent)
+  const void *out;          // [T, H, Dv] forward output
+  const float *lse;         // [T, H] forward log-sum-exp (natural log)
+  const void *dout;         // [T, H, Dv] dL/dout
+  float *dq;                // [T, H, D]
+  float *dkv;               // latent cache layout, fp32 rows of D
+  float *probs;             // [T, k] head-mean weights over the selection, or null
+  int q_begin, rows;
+  float *delta;             // ws [rows, H]: sum_d dout * out
+  uint16_t *ds_t;           // ws [rows, k / 32, H, 32] bf16: sm_scale dS per tile, rows in k-slot order
+  uint16_t *pd;             // ws [rows, k, 2, H] bf16: P and sm_scale dS per row, heads in k-slot order
+  float *contrib;           // ws [rows, k, D]: each selected row's gradient from its query
+  uint16_t *jpos;           // ws [nkeys, jstride]: slot j of query row r that selected key s, or 0xFFFF
+  int jstride;              // rows rounded up to 8
+  int nkeys;                // keys reduced (positions 0..nkeys-1 of sequence 0)
+  int first;                // 1: dkv rows are written; 0: added to
+};
+
+// Stage-2 indexer KL over each query's selection.
+struct SparseKlArgs {
+  SeqView sv;
+  int rows, k;
+  float *scores;            // [rows, ld]: I in, dL/dI out (0 outside the selection)
+  long long ld;
+  const int32_t *idx;       // [rows, k]
+  const float *probs;       // [rows, k] target over the selection
+  float *loss;              // [rows]
+};
+
 struct TopkLayout {
   int slices, slice_len, sel_seg;
   long long row_words;
@@ -158,6 +196,8 @@ hipError_t launch_indexer_bwd_q(const BwdArgs &a, hipStream_t s);   // dq, dw (+
 hipError_t launch_indexer_bwd_k(const BwdArgs &a, hipStream_t s);   // dk (+ split merge)
 constexpr int kBwdKeysPerBlock = 128;                                // keys per dk workgroup
 int bwd_q_splits(int rows, int span);                                // dq key splits per query
+hipError_t launch_sparse_mla_bwd(const MlaBwdArgs &a, hipStream_t s);   // one query chunk
+hipError_t launch_sparse_kl(const SparseKlArgs &a, hipStream_t s);
 hipError_t launch_fp8_quantize(const QuantArgs &a, hipStream_t s);
 hipError_t launch_fp8_append(const AppendArgs &a, hipStream_t s);
 

@@ -1,0 +1,522 @@
+// Stage 2 of DSA training: the gradient of the sparse attention over each
+// query's selected rows, and the indexer's KL loss restricted to the selection
+// ("DeepSeek V3.2: How Far Can Open Models Go If You Actually Try?", section
+// 3.3, Stage 2: the main attention switches to top-k, every parameter trains,
+// and the indexer keeps learning from a loss on the selected subset S_t).
+//
+// For query t with selected rows c_j (j < k), logits z = sm_scale q c^T,
+// weights P = exp(z - lse) (the forward's log-sum-exp) and output O:
+//   Delta_h = sum_d dO[h,d] O[h,d]
+//   dP = dO V^T,   dS = P (dP - Delta)                (per head, per row)
+//   dq = sm_scale dS C                                 [H, D]
+//   dc_j = sm_scale dS[:, j]^T Q + P[:, j]^T dO        [D] (key and value are one row)
+// and the cache row of a token receives the sum of dc_j over every query that
+// selected it.  Kernels, per chunk of up to 256 query rows:
+//   bwd_delta     Delta from the forward output and dO
+//   bwd_scores    gathers each query's rows into LDS (the forward's tiles); every
+//                 tile operand read feeds the logit and the dP MFMA; writes
+//                 P and sm_scale dS in bf16 (per tile for dq, per row for the row
+//                 gradients) and the head-mean weights (the Stage-2 target)
+//   bwd_dq        gathers the rows again: dq^T += C^T dS^T (LDS transpose reads)
+//   bwd_contrib   the row gradients as a GEMM per query, [P | dS] rows against
+//                 dO and Q slices staged in LDS: one fp32 row per (query, j)
+//   bwd_jpos_*    which slot j of which query row selected each key
+//   bwd_dkv       per key, its rows' gradients summed in ascending query order,
+//                 chunk after chunk: no atomics, so the result is deterministic.
+#include "mla_tile.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kKv = kDv / 32;                 // 16 k-steps of dP over the value dims
+constexpr int kDbAll = kD / 16;               // 36 dim blocks of the row and dq products
+constexpr uint16_t kNoSlot = 0xFFFF;
+
+// k-slot position of head h inside its group of 32 heads: the row-gradient
+// product reads heads 4g..4g+3 and 16+4g..16+4g+3 of a group in lane group g,
+// and they sit together so one 16-byte load fetches them.
+__device__ __forceinline__ int head_slot(int h) {
+  const int hh = h & 31;
+  const int p = hh < 16 ? ((hh >> 2) << 3) + (hh & 3) : (((hh - 16) >> 2) << 3) + 4 + (hh & 3);
+  return (h & ~31) + p;
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) { return f32_to_bf16(x); }
+
+// Slots of query t's k selected positions (prefill: sequence 0) into LDS, -1
+// for absent entries and past the list; returns after a barrier with the
+// largest present slot in *fallback (-1 when none).
+__device__ void fill_slots(const MlaBwdArgs &a, int t, int n, int ntiles, int *slots, int *fallback) {
+  if (threadIdx.x == 0) *fallback = -1;
+  __syncthreads();
+  const int32_t *irow = a.idx + (long long)t * a.k;
+  const int nfill = ntiles * kR + 3 * kR;
+  for (int j = threadIdx.x; j < nfill; j += kThreads) {
+    int sl = -1;
+    const int p = j < a.k ? irow[j] : -1;
+    if (p >= 0 && p < n) {
+      if (a.sv.block_table == nullptr) {
+        sl = p;
+      } else {
+        const int blk = a.sv.block_table[p >> 6];
+        if (blk >= 0 && blk < a.sv.num_blocks) sl = blk * 64 + (p & 63);
+      }
+    }
+    slots[j] = sl;
+    if (sl >= 0) atomicMax(fallback, sl);
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- Delta
+
+__global__ __launch_bounds__(256) void bwd_delta_kernel(MlaBwdArgs a) {
+  const long long i = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= (long long)a.rows * kH) return;
+  const int r = (int)(i / kH), h = (int)(i % kH);
+  const long long base = ((long long)(a.q_begin + r) * kH + h) * kDv + lane_id() * 8;
+  const uint4 o = ld16(reinterpret_cast<const uint16_t *>(a.out) + base);
+  const uint4 d = ld16(reinterpret_cast<const uint16_t *>(a.dout) + base);
+  const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, dw[4] = {d.x, d.y, d.z, d.w};
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    s = fmaf(__uint_as_float(ow[u] << 16), __uint_as_float(dw[u] << 16), s);
+    s = fmaf(__uint_as_float(ow[u] & 0xFFFF0000u), __uint_as_float(dw[u] & 0xFFFF0000u), s);
+  }
+  s = wave_sum(s);
+  if (lane_id() == 0) a.delta[i] = s;
+}
+
+// ---------------------------------------------------------------- P and dS
+
+__global__ __launch_bounds__(kThreads) void bwd_scores_kernel(MlaBwdArgs a) {
+  __shared__ uint4 tiles[kBufs][kTileBufChunks];
+  __shared__ int slots[kMaxSplitRows + 4 * kR];
+  __shared__ int fallback;
+  __shared__ float psums[2][kWaves * kR];
+
+  const int r = blockIdx.x;
+  const int t = a.q_begin + r;
+  const int n = a.sv.candidates(t);
+  const int ntiles = (a.k + kR - 1) / kR;
+  const int lane = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, g = lane >> 4;
+  const int h = wv * 16 + col;
+
+  // Q^T (dims 32 ks + 8 g + [0, 8), 18 k-steps) and dO^T (16 k-steps) of head h
+  bf16x8 qb[kKs], ob[kKv];
+  {
+    const uint8_t *qrow = reinterpret_cast<const uint8_t *>(a.q) + ((long long)t * kH + h) * (kD * 2);
+    const uint8_t *orow = reinterpret_cast<const uint8_t *>(a.dout) + ((long long)t * kH + h) * (kDv * 2);
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) qb[ks] = as_bf16x8(ld16(qrow + ks * 64 + g * 16));
+#pragma unroll
+    for (int ks = 0; ks < kKv; ++ks) ob[ks] = as_bf16x8(ld16(orow + ks * 64 + g * 16));
+  }
+  const float lse2 = a.lse[(long long)t * kH + h] * kLog2e;
+  const float dlt = a.delta[(long long)r * kH + h];
+  const float scale2 = a.sm_scale * kLog2e;
+  fill_slots(a, t, n, ntiles, slots, &fallback);
+  const int fb = fallback;
+
+  const uint32_t qk_off = col * kRowStride + (g ^ swz(col)) * 16;
+  const uint32_t tile_lds = lds_addr(&tiles[0][0]);
+  constexpr uint32_t kTileBytes = kTileBufChunks * 16;
+  const uint8_t *kv = reinterpret_cast<const uint8_t *>(a.kv);
+  // head sums of tile tt's weights (wave 0, after the barrier that follows the tile)
+  auto write_probs = [&](int tt) {
+    if (a.probs != nullptr && lane < kR) {
+      const int j = tt * kR + lane;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) v += psums[tt & 1][w * kR + lane];
+      if (j < a.k) a.probs[(long long)t * a.k + j] = v * (1.f / kH);
+    }
+  };
+
+  // the bf16 outputs of tile tt (held in registers, stored at the start of the
+  // next iteration: stores count in the vector-memory counter, and stored after
+  // the next tile's loads they would make its in-order wait drain them too)
+  const int hs = head_slot(h);
+  auto store_tile = [&](int tt, const float (&pw)[8], const float (&sd)[8]) {
+    uint4 pk;
+    pk.x = pack_bf16x2(sd[0], sd[1]);
+    pk.y = pack_bf16x2(sd[2], sd[3]);
+    pk.z = pack_bf16x2(sd[4], sd[5]);
+    pk.w = pack_bf16x2(sd[6], sd[7]);
+    // sm_scale dS^T of the tile for the dq product: head h, rows in k-slot order
+    st16(a.ds_t + (((long long)r * ntiles + tt) * kH + h) * kR + g * 8, pk);
+    // P and sm_scale dS per row for the row-gradient product
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = tt * kR + 16 * rb + 4 * g + v;
+        if (j < a.k) {
+          uint16_t *row = a.pd + ((long long)r * a.k + j) * (2 * kH);
+          row[hs] = bf16_bits(pw[rb * 4 + v]);
+          row[kH + hs] = bf16_bits(sd[rb * 4 + v]);
+        }
+      }
+  };
+
+  if (fb >= 0) {
+    issue_tile(tile_lds, kv, slots, 0, fb, wv, lane);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);         // query, dO operands and tile 0
+    if (ntiles > 1) issue_tile(tile_lds + kTileBytes, kv, slots, kR, fb, wv, lane);
+    int cur = 0;
+    float pw[8], sd[8];
+    for (int tt = 0; tt < ntiles; ++tt) {
+      if (tt + 1 >= ntiles)
+        __builtin_amdgcn_s_waitcnt(kWaitVm0 & ~0x0F00);
+      else
+        __builtin_amdgcn_s_waitcnt(wait_vm(kWaveLoads) & ~0x0F00);
+      lds_barrier();
+      if (tt > 0) store_tile(tt - 1, pw, sd);
+      if (tt + 2 < ntiles) issue_tile(tile_lds + (cur == 0 ? 2 : cur - 1) * kTileBytes, kv, slots, (tt + 2) * kR, fb,
+                                      wv, lane);
+      if (tt > 0 && wv == 0) write_probs(tt - 1);
+      const uint32_t tile = tile_lds + cur * kTileBytes;
+      const int row_slot = slots[tt * kR + (lane & (kR - 1))];
+      f32x4 st[2] = {zero_vec<f32x4>(), zero_vec<f32x4>()};
+      f32x4 dp[2] = {zero_vec<f32x4>(), zero_vec<f32x4>()};
+#pragma unroll
+      for (int ks = 0; ks < kKs; ++ks) {
+        u32x4 fr[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) fr[rb] = *(lds_u32x4 *)(uintptr_t)(tile + qk_off + rb * 16 * kRowStride + ks * 64);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          st[rb] = mfma16_bf16(__builtin_bit_cast(bf16x8, fr[rb]), qb[ks], st[rb]);
+          if (ks < kKv) dp[rb] = mfma16_bf16(__builtin_bit_cast(bf16x8, fr[rb]), ob[ks], dp[rb]);
+        }
+      }
+      // rows 16 rb + 4 g + v of the tile; head h
+      const uint32_t rowmask = (uint32_t)__ballot(lane < kR && row_slot >= 0);
+      const uint32_t mine = rowmask >> (4 * g);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const bool on = (mine >> (16 * rb + v)) & 1u;
+          const float p = on ? __builtin_amdgcn_exp2f(st[rb][v] * scale2 - lse2) : 0.f;
+          pw[rb * 4 + v] = p;
+          sd[rb * 4 + v] = a.sm_scale * (p * (dp[rb][v] - dlt));
+        }
+      // the weights summed over this wave's 16 heads, per row
+      if (a.probs != nullptr) {
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = sum16(pw[i]);
+        float mine_e = e[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) mine_e = col == i ? e[i] : mine_e;
+        if (col < 8) psums[tt & 1][wv * kR + 16 * (col >> 2) + 4 * g + (col & 3)] = mine_e;
+      }
+      cur = cur == 2 ? 0 : cur + 1;
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    lds_barrier();
+    store_tile(ntiles - 1, pw, sd);
+    if (wv == 0) write_probs(ntiles - 1);
+  } else {
+    // no selected row: P = dS = 0
+    for (int i = threadIdx.x; i < ntiles * kH * kR / 8; i += kThreads)
+      st16(a.ds_t + (long long)r * ntiles * kH * kR + i * 8, make_uint4(0, 0, 0, 0));
+    for (int i = threadIdx.x; i < a.k * 2 * kH / 8; i += kThreads)
+      st16(a.pd + (long long)r * a.k * 2 * kH + i * 8, make_uint4(0, 0, 0, 0));
+    if (a.probs != nullptr)
+      for (int j = threadIdx.x; j < a.k; j += kThreads) a.probs[(long long)t * a.k + j] = 0.f;
+  }
+}
+
+// ---------------------------------------------------------------- dq
+
+__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(MlaBwdArgs a) {
+  __shared__ uint4 tiles[kBufs][kTileBufChunks];
+  __shared__ uint4 dst[kBufs][kH * kR * 2 / 16];   // sm_scale dS^T of each buffered tile (8 KB)
+  __shared__ int slots[kMaxSplitRows + 4 * kR];
+  __shared__ int fallback;
+
+  const int r = blockIdx.x;
+  const int t = a.q_begin + r;
+  const int n = a.sv.candidates(t);
+  const int ntiles = (a.k + kR - 1) / kR;
+  const int lane = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, g = lane >> 4;
+  const int h = wv * 16 + col;
+  fill_slots(a, t, n, ntiles, slots, &fallback);
+  const int fb = fallback;
+
+  f32x4 acc[kDbAll];
+#pragma unroll
+  for (int db = 0; db < kDbAll; ++db) acc[db] = zero_vec<f32x4>();
+  if (fb >= 0) {
+    const int vc = col & 3;
+    const uint32_t pv_row = (4 * g + (col >> 2)) * kRowStride + (vc & 1) * 8;
+    const uint32_t pv_even = pv_row + (((vc >> 1)) ^ g) * 16;
+    const uint32_t pv_odd = pv_row + ((2 + (vc >> 1)) ^ g) * 16;
+    const uint32_t tile_lds = lds_addr(&tiles[0][0]);
+    const uint32_t ds_lds = lds_addr(&dst[0][0]);
+    constexpr uint32_t kTileBytes = kTileBufChunks * 16;
+    constexpr uint32_t kDsBytes = kH * kR * 2;
+    const uint8_t *kv = reinterpret_cast<const uint8_t *>(a.kv);
+    // wave wv's 1 KB of a tile's dS^T (heads 16 wv.., 32 rows each): lane l's 16 bytes
+    const uint16_t *ds_src = a.ds_t + ((long long)r * ntiles * kH + wv * 16) * kR + lane * 8;
+    auto issue = [&](int bi, int tt) {
+      issue_tile(tile_lds + bi * kTileBytes, kv, slots, tt * kR, fb, wv, lane);
+      lds_dma16(ds_src + (long long)tt * kH * kR, ds_lds + bi * kDsBytes + wv * 1024);
+    };
+    constexpr int kLoads = kWaveLoads + 1;
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    if (ntiles > 1) issue(1, 1);
+    int cur = 0;
+    for (int tt = 0; tt < ntiles; ++tt) {
+      if (tt + 1 >= ntiles)
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      else
+        __builtin_amdgcn_s_waitcnt(wait_vm(kLoads));
+      lds_barrier();
+      if (tt + 2 < ntiles) issue(cur == 0 ? 2 : cur - 1, tt + 2);
+      const uint32_t tile = tile_lds + cur * kTileBytes;
+      const bf16x8 pb = __builtin_bit_cast(
+          bf16x8, *(lds_u32x4 *)(uintptr_t)(ds_lds + cur * kDsBytes + (wv * 16 + col) * (kR * 2) + g * 16));
+#pragma unroll
+      for (int db = 0; db < kDbAll; ++db) {
+        const uint32_t v0 = tile + ((db & 1) ? pv_odd : pv_even) + (db >> 1) * 64;
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)v0);
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)(v0 + 16 * kRowStride));
+        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[db] = mfma16_bf16(av, pb, acc[db]);
+      }
+      cur = cur == 2 ? 0 : cur + 1;
+    }
+  }
+  float *drow = a.dq + ((long long)t * kH + h) * kD;
+#pragma unroll
+  for (int db = 0; db < kDbAll; ++db)
+    *reinterpret_cast<float4 *>(drow + db * 16 + 4 * g) = make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+}
+
+// ---------------------------------------------------------------- row gradients
+
+// One workgroup per (query row r, block of 128 selected slots); wave w owns slots
+// 16 w.. of the block.  C^T[dims, slots] = dO^T[dims, heads] P^T[heads, slots]
+// + Q^T[dims, heads] (sm_scale dS)^T[heads, slots], over four groups of 32
+// heads whose dO and Q rows are staged in LDS in the tile layout.
+constexpr int kContribRows = 128;
+
+__global__ __launch_bounds__(kThreads) void bwd_contrib_kernel(MlaBwdArgs a) {
+  __shared__ uint4 qs[kTileChunks];
+  __shared__ uint4 os[kTileChunks];
+  const int r = blockIdx.y;
+  const int t = a.q_begin + r;
+  const int lane = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, g = lane >> 4;
+  const int jb = blockIdx.x * kContribRows + wv * 16;
+  const bool active = jb < a.k;                 // k is a multiple of 16
+
+  const int vc = col & 3;
+  const uint32_t pv_row = (4 * g + (col >> 2)) * kRowStride + (vc & 1) * 8;
+  const uint32_t pv_even = pv_row + (((vc >> 1)) ^ g) * 16;
+  const uint32_t pv_odd = pv_row + ((2 + (vc >> 1)) ^ g) * 16;
+  const uint32_t q_lds = lds_addr(&qs[0]), o_lds = lds_addr(&os[0]);
+  const uint8_t *qsrc = reinterpret_cast<const uint8_t *>(a.q) + (long long)t * kH * (kD * 2);
+  const uint8_t *osrc = reinterpret_cast<const uint8_t *>(a.dout) + (long long)t * kH * (kDv * 2);
+  const uint16_t *prow = a.pd + ((long long)r * a.k + (active ? jb + col : 0)) * (2 * kH);
+
+  f32x4 acc[kDbAll];
+#pragma unroll
+  for (int db = 0; db < kDbAll; ++db) acc[db] = zero_vec<f32x4>();
+  for (int hg = 0; hg < kH / 32; ++hg) {
+    __syncthreads();                            // the previous group's operands are read
+    // stage heads 32 hg.. : row hr of the group, data chunk c at position c ^ swz(hr)
+    for (int i = threadIdx.x; i < 32 * kDataChunks; i += kThreads) {
+      const int hr = i / kDataChunks, c = i - hr * kDataChunks;
+      qs[hr * kRowChunks + (c ^ swz(hr))] = ld16(qsrc + (long long)(32 * hg + hr) * (kD * 2) + c * 16);
+    }
+    for (int i = threadIdx.x; i < 32 * (kDv / 8); i += kThreads) {
+      const int hr = i / (kDv / 8), c = i - hr * (kDv / 8);
+      os[hr * kRowChunks + (c ^ swz(hr))] = ld16(osrc + (long long)(32 * hg + hr) * (kDv * 2) + c * 16);
+    }
+    __syncthreads();
+    if (!active) continue;
+    const bf16x8 pp = as_bf16x8(ld16(prow + 32 * hg + 8 * g));
+    const bf16x8 ps = as_bf16x8(ld16(prow + kH + 32 * hg + 8 * g));
+#pragma unroll
+    for (int db = 0; db < kDbAll; ++db) {
+      const uint32_t off = ((db & 1) ? pv_odd : pv_even) + (db >> 1) * 64;
+      {
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)(q_lds + off));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)(q_lds + off + 16 * kRowStride));
+        acc[db] = mfma16_bf16(__builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)), ps,
+                              acc[db]);
+      }
+      if (db < kDv / 16) {
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)(o_lds + off));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)(o_lds + off + 16 * kRowStride));
+        acc[db] = mfma16_bf16(__builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)), pp,
+                              acc[db]);
+      }
+    }
+  }
+  if (!active) return;
+  float *crow = a.contrib + ((long long)r * a.k + jb + col) * kD;
+#pragma unroll
+  for (int db = 0; db < kDbAll; ++db)
+    *reinterpret_cast<float4 *>(crow + db * 16 + 4 * g) = make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+}
+
+// ---------------------------------------------------------------- the reduction into the cache rows
+
+__global__ __launch_bounds__(256) void bwd_jpos_fill_kernel(MlaBwdArgs a) {
+  const long long words = (long long)a.nkeys * a.jstride / 8;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < words; i += (long long)gridDim.x * 256)
+    st16(a.jpos + i * 8, make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu));
+}
+
+__global__ __launch_bounds__(256) void bwd_jpos_scatter_kernel(MlaBwdArgs a) {
+  const int r = blockIdx.y;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= a.k) return;
+  const int t = a.q_begin + r;
+  const int n = a.sv.candidates(t);
+  const int s = a.idx[(long long)t * a.k + j];
+  if (s >= 0 && s < n && s < a.nkeys) a.jpos[(long long)s * a.jstride + r] = (uint16_t)j;
+}
+
+// One wave per key position s of sequence 0: the gradients of the rows that
+// selected it, in ascending query order, into its cache row.
+__global__ __launch_bounds__(256) void bwd_dkv_kernel(MlaBwdArgs a) {
+  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (s >= a.nkeys) return;
+  const int lane = lane_id();
+  long long slot = s;
+  if (a.sv.block_table != nullptr) {
+    const int blk = a.sv.block_table[s >> 6];
+    slot = (blk >= 0 && blk < a.sv.num_blocks) ? (long long)blk * 64 + (s & 63) : -1;
+  }
+  if (slot < 0) return;
+  float acc[kD / 64];
+#pragma unroll
+  for (int u = 0; u < kD / 64; ++u) acc[u] = 0.f;
+  const uint16_t *jrow = a.jpos + (long long)s * a.jstride;
+  for (int t0 = 0; t0 < a.rows; t0 += 64) {
+    const int jv = t0 + lane < a.rows ? (int)jrow[t0 + lane] : (int)kNoSlot;
+    unsigned long long m = __ballot(jv != kNoSlot);
+    while (m) {
+      const int b = __ffsll((long long)m) - 1;
+      m &= m - 1;
+      const int j = __builtin_amdgcn_readlane(jv, b);
+      const float *c = a.contrib + ((long long)(t0 + b) * a.k + j) * kD + lane;
+#pragma unroll
+      for (int u = 0; u < kD / 64; ++u) acc[u] += c[64 * u];
+    }
+  }
+  float *drow = a.dkv + slot * kD + lane;
+#pragma unroll
+  for (int u = 0; u < kD / 64; ++u) drow[64 * u] = a.first ? acc[u] : drow[64 * u] + acc[u];
+}
+
+// ---------------------------------------------------------------- Stage-2 indexer KL
+
+constexpr int kKlThreads = 256;
+constexpr int kKlMaxWords = 262144 / 32;
+
+__device__ float block_max(float v, float *red) {
+  v = wave_max(v);
+  if (lane_id() == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float m = red[0];
+#pragma unroll
+  for (int w = 1; w < kKlThreads / 64; ++w) m = fmaxf(m, red[w]);
+  __syncthreads();
+  return m;
+}
+
+__device__ float block_sum(float v, float *red) {
+  v = wave_sum(v);
+  if (lane_id() == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < kKlThreads / 64; ++w) s += red[w];
+  __syncthreads();
+  return s;
+}
+
+// One workgroup per query: softmax of the scores over the selected positions,
+// the KL term against the target, and dL/dI written over the whole score row
+// (softmax - p on the selection, 0 elsewhere).
+__global__ __launch_bounds__(kKlThreads) void sparse_kl_kernel(SparseKlArgs a) {
+  __shared__ uint32_t bits[kKlMaxWords];
+  __shared__ float ival[kTopkMaxK];
+  __shared__ float red[kKlThreads / 64];
+  const int r = blockIdx.x;
+  const int n = a.sv.candidates(r);
+  float *srow = a.scores + (long long)r * a.ld;
+  const int32_t *irow = a.idx + (long long)r * a.k;
+  const float *prow = a.probs + (long long)r * a.k;
+  const int words = (n + 31) >> 5;
+  for (int i = threadIdx.x; i < words; i += kKlThreads) bits[i] = 0u;
+  __syncthreads();
+  float mx = neg_inf();
+  for (int j = threadIdx.x; j < a.k; j += kKlThreads) {
+    const int s = irow[j];
+    float v = neg_inf();
+    if (s >= 0 && s < n) {
+      v = srow[s];
+      atomicOr(&bits[s >> 5], 1u << (s & 31));
+      mx = fmaxf(mx, v);
+    }
+    ival[j] = v;
+  }
+  mx = block_max(mx, red);
+  float se = 0.f;
+  for (int j = threadIdx.x; j < a.k; j += kKlThreads)
+    if (ival[j] != neg_inf()) se += __expf(ival[j] - mx);
+  se = block_sum(se, red);
+  const float lse = mx + __logf(se);
+  float kl = 0.f;
+  for (int j = threadIdx.x; j < a.k; j += kKlThreads) {
+    const float p = prow[j];
+    if (ival[j] != neg_inf() && p > 0.f) kl += p * (__logf(p) - (ival[j] - lse));
+  }
+  kl = block_sum(kl, red);
+  // 0 at every position outside the selection, then the gradient on it
+  for (long long s = threadIdx.x; s < a.ld; s += kKlThreads)
+    if (s >= n || !((bits[s >> 5] >> (s & 31)) & 1u)) srow[s] = 0.f;
+  for (int j = threadIdx.x; j < a.k; j += kKlThreads)
+    if (ival[j] != neg_inf()) srow[irow[j]] = __expf(ival[j] - lse) - prow[j];
+  if (threadIdx.x == 0) a.loss[r] = mx == neg_inf() ? 0.f : kl;
+}
+
+}  // namespace
+
+hipError_t launch_sparse_mla_bwd(const MlaBwdArgs &a, hipStream_t st) {
+  if (a.rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)(((long long)a.rows * kH + 3) / 4)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(bwd_scores_kernel, dim3(a.rows), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3(a.rows), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL(bwd_contrib_kernel, dim3((a.k + kContribRows - 1) / kContribRows, a.rows), dim3(kThreads), 0, st,
+                     a);
+  const long long words = (long long)a.nkeys * a.jstride / 8;
+  hipLaunchKernelGGL(bwd_jpos_fill_kernel, dim3((unsigned)((words + 255) / 256 < 4096 ? (words + 255) / 256 : 4096)),
+                     dim3(256), 0, st, a);
+  hipLaunchKernelGGL(bwd_jpos_scatter_kernel, dim3((a.k + 255) / 256, a.rows), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(bwd_dkv_kernel, dim3((a.nkeys + 3) / 4), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_kl(const SparseKlArgs &a, hipStream_t st) {
+  if (a.rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sparse_kl_kernel, dim3(a.rows), dim3(kKlThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -327,3 +327,39 @@ def test_forward_noalloc_rejects_problems_over_its_scratch():
     fits = B.make_problem(mode="decode", q_pos=torch.full((32,), 131071, dtype=torch.int32), max_ctx=131072,
                           num_seqs=32, max_seq_len=131072)
     assert B.workspace_size(B.OP_FORWARD, fits) <= (128 << 20)   # the 128K decode batch fits
+
+
+def test_stage2_validation_and_workspace():
+    """Host checks of the Stage-2 entry points and the backward's chunked workspace (no launch)."""
+    L = B.LIB
+    qp = torch.arange(16384, dtype=torch.int32)
+    pf = B.make_problem(mode="prefill", q_pos=qp, max_ctx=16384, num_seqs=1, max_seq_len=16384)
+    sp, dp = ctypes.byref(pf.seqs), ctypes.byref(pf.dims)
+    a256 = lambda x: (x + 255) // 256 * 256
+    # chunks of 256 query rows: Delta, per-tile dS, per-row P | dS, fp32 row gradients, the key map
+    want = (a256(256 * 128 * 4) + a256(256 * 64 * 128 * 32 * 2) + a256(256 * 2048 * 2 * 128 * 2)
+            + a256(256 * 2048 * 576 * 4) + a256(16384 * 256 * 2))
+    need = B.workspace_size(B.OP_SPARSE_MLA_BACKWARD, pf)
+    assert need == want
+    call = lambda pb, **kw: L.dsa_sparse_mla_backward(
+        ctypes.byref(pb.seqs), ctypes.byref(pb.dims), 0.04, *[kw.get(k, FAKE) for k in
+                                                              ("q", "kv", "idx", "out", "lse", "dout", "dq", "dkv")],
+        None, kw.get("ws", FAKE), kw.get("nb", 1 << 40), None)
+    assert call(pf, dkv=None) == B.ERR_INVALID_ARG and call(pf, lse=None) == B.ERR_INVALID_ARG
+    assert call(pf, ws=None, nb=0) == B.ERR_WORKSPACE and call(pf, nb=need - 1) == B.ERR_WORKSPACE
+    dec = _problem()
+    assert call(dec) == B.ERR_UNSUPPORTED                         # training runs over whole sequences
+    odd = B.make_problem(mode="prefill", q_pos=qp[:100], max_ctx=100, num_seqs=1, max_seq_len=100, topk=40)
+    assert call(odd) == B.ERR_UNSUPPORTED                         # k not a multiple of 16
+    f32 = B.make_problem(mode="prefill", q_pos=qp[:100], max_ctx=100, num_seqs=1, max_seq_len=100,
+                         mla_dtype=B.F32, heads=8, qk_dim=80, v_dim=64, topk=32)
+    assert call(f32) == B.ERR_UNSUPPORTED
+    few = B.make_problem(mode="prefill", q_pos=qp[:44], max_ctx=300, num_seqs=1, max_seq_len=300, topk=64)
+    assert B.workspace_size(B.OP_SPARSE_MLA_BACKWARD, few) == (
+        a256(44 * 128 * 4) + a256(44 * 2 * 128 * 32 * 2) + a256(44 * 64 * 2 * 128 * 2) + a256(44 * 64 * 576 * 4)
+        + a256(300 * 48 * 2))
+    kl = lambda pb, sc=FAKE, ld=16384, idx=FAKE, k=2048, pr=FAKE, loss=FAKE: L.dsa_sparse_indexer_kl(
+        ctypes.byref(pb.seqs), sc, ld, idx, k, pr, loss, None)
+    assert kl(pf, sc=None) == B.ERR_INVALID_ARG and kl(pf, pr=None) == B.ERR_INVALID_ARG
+    assert kl(pf, ld=100) == B.ERR_INVALID_ARG and kl(pf, k=0) == B.ERR_INVALID_ARG
+    assert kl(pf, k=4096) == B.ERR_UNSUPPORTED
