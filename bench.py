@@ -410,6 +410,82 @@ def warmup_objective_line(B, torch, inp, steps, settle_ms):
             "step_mfma_frac": frac(f_probs + f_scores + f_bwd, ms)}
 
 
+def stage2_line(B, torch, inp, steps, settle_ms):
+    """Stage 2 of training on the prefill inputs: the sparse forward (selection,
+    output, lse), the indexer scores, the attention backward (dq, the cache rows'
+    gradients, the indexer's target over the selection), the KL on the selection
+    and the indexer backward.  Step time, stage times and matrix-core fractions."""
+    wl = inp.wl
+    pb = B.problem_from_inputs(inp)
+    T, H, D, Dv, k = inp.num_q, wl.heads, wl.qk_dim, wl.v_dim, inp.topk
+    fws = torch.empty(B.workspace_size(B.OP_FORWARD, pb), dtype=torch.uint8, device="cuda")
+    bws = torch.empty(B.workspace_size(B.OP_SPARSE_MLA_BACKWARD, pb), dtype=torch.uint8, device="cuda")
+    iws = torch.empty(max(1, B.workspace_size(B.OP_INDEXER_BACKWARD, pb)), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, H, Dv), dtype=inp.q.dtype, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    scores = torch.empty((T, (inp.max_ctx + 63) // 64 * 64), dtype=torch.float32, device="cuda")
+    dq = torch.empty((T, H, D), dtype=torch.float32, device="cuda")
+    dkv = torch.zeros(tuple(inp.kv_cache.shape[:-1]) + (D,), dtype=torch.float32, device="cuda")
+    probs = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    loss = torch.empty(T, dtype=torch.float32, device="cuda")
+    dqi = torch.empty((T, wl.index_heads, wl.index_dim), dtype=torch.float32, device="cuda")
+    dwi = torch.empty((T, wl.index_heads), dtype=torch.float32, device="cuda")
+    dki = torch.zeros(tuple(inp.k_cache.shape), dtype=torch.float32, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(77)
+    dout = (torch.randn((T, H, Dv), device="cuda", generator=g) * 0.05).to(torch.bfloat16)
+
+    def call(ev=None):
+        mark = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        mark(0)
+        B.forward(pb, inp.q_idx, inp.q_scale, inp.w, inp.k_cache, inp.k_scale, inp.q, inp.kv_cache, inp.sm_scale,
+                  out=out, lse=lse, topk_idx=idx, ws=fws)
+        mark(1)
+        B.index_scores(pb, inp.q_idx, inp.q_scale, inp.w, inp.k_cache, inp.k_scale, scores=scores,
+                       ld=scores.shape[1])
+        mark(2)
+        B.sparse_mla_backward(pb, inp.sm_scale, inp.q, inp.kv_cache, idx, out, lse, dout, dq=dq, dkv=dkv,
+                              probs=probs, ws=bws)
+        mark(3)
+        B.sparse_indexer_kl(pb, scores, idx, probs, loss=loss)
+        mark(4)
+        B.indexer_backward(pb, inp.q_idx, inp.w, inp.k_cache, scores, dq=dqi, dw=dwi, dk=dki, ws=iws)
+        mark(5)
+
+    ms = time_op(torch, call, steps, 1, settle_ms)
+    evs = [make_events(torch, 6) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        call(evs[i])
+    torch.cuda.synchronize()
+    st = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps for j in range(5)]
+    n = inp.q_pos.to("cpu").long() + 1
+    pairs = int(n.sum())
+    sel = int(n.clamp(max=k).sum())
+    f_idx = pairs * wl.index_heads * 2 * wl.index_dim
+    f_fwd = f_idx + sel * H * 2 * (D + Dv)
+    # per selected (query, row): the logits again, dP, dq, and the row's key and value gradients
+    f_bwd = sel * H * 2 * (D + Dv + D + Dv + D)
+    f_ibwd = 4 * f_idx
+    peak = MFMA_PEAK_TFLOPS["bf16"]
+    frac = lambda f, t: round(f / (t * 1e-3) / 1e12 / peak, 4)
+    contrib_bytes = 2 * sel * D * 4
+    del fws, bws, iws, out, lse, idx, scores, dq, dkv, probs, loss, dqi, dwi, dki, dout
+    torch.cuda.empty_cache()
+    return {"workload": wl.name,
+            "step": "dsa_forward + dsa_index_scores + dsa_sparse_mla_backward + dsa_sparse_indexer_kl + "
+                    "dsa_indexer_backward",
+            "ms_per_step": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "stages_ms": {"forward": round(st[0], 3), "index_scores": round(st[1], 3),
+                          "attention_backward": round(st[2], 3), "sparse_kl": round(st[3], 3),
+                          "indexer_backward": round(st[4], 3)},
+            "mfma_frac": {"forward": frac(f_fwd, st[0]), "attention_backward": frac(f_bwd, st[2]),
+                          "indexer_backward": frac(f_ibwd, st[4])},
+            "attention_backward_row_gradient_bytes": contrib_bytes,
+            "note": "the attention backward's cache-row gradients make one fp32 round trip through HBM "
+                    "(written per selected row, summed per token in query order)"}
+
+
 def cpu_baseline(inp, seconds):
     """The float64 oracle, as it stands, on the queries of the timed batch, for a bounded time."""
     import numpy as np
@@ -446,7 +522,8 @@ def cpu_baseline(inp, seconds):
                       f"{threads or os.cpu_count()} BLAS threads on a host of {os.cpu_count()} CPUs, {el:.1f} s wall"}
 
 
-def prefill_line(B, torch, generate, wl, settle_ms, rotate, dense=False, warmup_objective=False, steps=3):
+def prefill_line(B, torch, generate, wl, settle_ms, rotate, dense=False, warmup_objective=False, steps=3,
+                 stage2=False):
     """One prefill workload: the fused step (input sets rotated), each op alone over
     every query row, the stages as the fused call runs them, and their matrix-core
     fractions (indexer against its own dtype's peak, attention against bf16)."""
@@ -514,6 +591,10 @@ def prefill_line(B, torch, generate, wl, settle_ms, rotate, dense=False, warmup_
         log("indexer warm-up objective on the prefill inputs")
         extra["warmup_objective"] = warmup_objective_line(B, torch, pin, 2, settle_ms)
         log(f"warm-up objective: {extra['warmup_objective']['ms_per_step']:.2f} ms")
+    if stage2:
+        log("stage-2 sparse training step on the prefill inputs")
+        extra["sparse_training"] = stage2_line(B, torch, pin, 2, settle_ms)
+        log(f"stage-2 step: {extra['sparse_training']['ms_per_step']:.2f} ms")
     return line, extra
 
 
@@ -542,6 +623,8 @@ def main():
                     help="skip the dense-MLA comparison (attention over every candidate) on the same inputs")
     ap.add_argument("--no-warmup-objective", action="store_true",
                     help="skip the indexer warm-up objective (loss and backward) on the prefill inputs")
+    ap.add_argument("--no-stage2", action="store_true",
+                    help="skip the Stage-2 sparse training step (forward, attention and indexer backward)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the measured ceilings and the fp8 indexing-quality report")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -697,11 +780,14 @@ def main():
         pwl = WORKLOADS["prefill_16k_bf16"]
         result["prefill"], extra = prefill_line(B, torch, generate, pwl, args.settle_ms, max(2, args.rotate),
                                                 dense=not args.no_dense,
-                                                warmup_objective=not args.no_warmup_objective)
+                                                warmup_objective=not args.no_warmup_objective,
+                                                stage2=not args.no_stage2)
         if "dense" in extra:
             dense[pwl.name] = extra["dense"]
         if "warmup_objective" in extra:
             result["warmup_objective"] = extra["warmup_objective"]
+        if "sparse_training" in extra:
+            result["sparse_training"] = extra["sparse_training"]
         torch.cuda.empty_cache()
         if not args.no_prefill_64k:
             result["prefill_64k_fp8"], _ = prefill_line(B, torch, generate, WORKLOADS["prefill_64k_fp8"],
