@@ -14,7 +14,9 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libdsa.so")
+# DSA_LIBRARY_PATH selects another build of the same library (e.g. one whose
+# host code is compiled with sanitizers); by default the in-tree build.
+LIB_PATH = os.environ.get("DSA_LIBRARY_PATH") or os.path.join(_PKG, "libdsa.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "dsa.h")
 
 F32, BF16, FP8_E4M3FN = 0, 1, 2

@@ -44,16 +44,27 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the DSA library needs ROCm's hipcc to build")
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every source for gfx950 and link libdsa.so next to this file."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+# Host-side sanitizers for a checking build of the C ABI (the device code is
+# compiled as usual): each flag applies to the host compilation only.
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def build(verbose: bool = False, jobs: int = 4, out_path: str = None, build_dir: str = None,
+          sanitize_host: bool = False) -> str:
+    """Compile every source for gfx950 and link libdsa.so next to this file (or
+    at `out_path`; with `sanitize_host`, the host code under ASan and UBSan)."""
+    build_dir = build_dir or BUILD_DIR
+    out_path = out_path or LIB_PATH
+    os.makedirs(build_dir, exist_ok=True)
     cc = hipcc()
     procs = []
     objs = []
+    extra = SANITIZE_HOST if sanitize_host else []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [cc, *CXXFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *CXXFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -61,16 +72,19 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             _wait(procs.pop(0), verbose)
     for p in procs:
         _wait(p, verbose)
-    tmp = LIB_PATH + ".tmp"
+    tmp = out_path + ".tmp"
     link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    if sanitize_host:
+        link += ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libsan"]
     if verbose:
         print(" ".join(link), flush=True)
     res = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}")
-    os.replace(tmp, LIB_PATH)
-    write_kernel_hashes(cc)
-    return LIB_PATH
+    os.replace(tmp, out_path)
+    if out_path == LIB_PATH:
+        write_kernel_hashes(cc)
+    return out_path
 
 
 def kernel_isa_text(asm: str, kernel: str) -> str:
