@@ -35,6 +35,10 @@ CXXFLAGS = [
     "-Wno-unused-command-line-argument",
     "-I", INCLUDE, "-I", CSRC,
 ]
+# Per-source flags.  The prefill indexer interleaves each group's MFMAs with the
+# reduction of the previous group; machine sinking would move those MFMAs past
+# the next branch, right in front of the instructions that read their results.
+SOURCE_FLAGS = {"indexer.hip": ["-mllvm", "-disable-machine-sink"]}
 
 
 def hipcc() -> str:
@@ -64,7 +68,7 @@ def build(verbose: bool = False, jobs: int = 4, out_path: str = None, build_dir:
     for src in SOURCES:
         obj = os.path.join(build_dir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [cc, *CXXFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *CXXFLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -109,7 +113,7 @@ def write_kernel_hashes(cc: str) -> dict:
     out["hipcc_version"] = next((l.strip() for l in ver.splitlines() if "HIP version" in l), None)
     for name, (src, kernel) in HASHED_KERNELS.items():
         asm_path = os.path.join(BUILD_DIR, src + ".s")
-        subprocess.run([cc, *CXXFLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm_path],
+        subprocess.run([cc, *CXXFLAGS, *SOURCE_FLAGS.get(src, []), "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm_path],
                        check=True, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
         with open(asm_path) as f:
             text = kernel_isa_text(f.read(), kernel)

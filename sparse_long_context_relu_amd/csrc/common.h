@@ -52,6 +52,44 @@ __host__ __device__ constexpr int wait_vm(int n) { return 0x0F70 | n; }   // vmc
 constexpr int kWaitLgkm0 = 0xC07F;    // LDS / scalar counts <= 0, vector memory left in flight
 constexpr int kWaitNone = 0xCF7F;     // every count at its maximum: no wait
 
+// Buffer resources (raw, stride 0): the fourth descriptor word of the gfx9
+// family (32-bit data format; the format does not affect untyped accesses),
+// and an offset past any range used here, whose accesses the hardware's
+// range check drops (stores) or returns as zero (loads).
+constexpr int kBufferDword3 = 0x00020000;
+constexpr uint32_t kBufferDrop = 0x80000000u;
+
+// Raw buffer descriptor (stride 0) over `bytes` bytes from `base`; the values
+// are wave-uniform and end up in scalar registers.
+typedef int i32x4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4s buffer_desc(const void *base, int bytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  i32x4s d;
+  d[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
+  d[1] = __builtin_amdgcn_readfirstlane((int)((unsigned)(a >> 32) & 0xffffu));
+  d[2] = __builtin_amdgcn_readfirstlane(bytes);
+  d[3] = kBufferDword3;
+  return d;
+}
+
+// Buffer loads straight into LDS: lane i's 16 (or 4) bytes at voffset land at
+// LDS address m0 + 16 i (4 i); lanes outside the descriptor's range write
+// zeros.  Written as asm so that the compiler does not wait for them before
+// every later LDS access (it cannot tell which LDS bytes they write): the
+// caller waits on the vector-memory count itself, as for lds_dma16.
+__device__ __forceinline__ void buffer_lds16(i32x4s d, uint32_t m0, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(d)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void buffer_lds4(i32x4s d, uint32_t m0, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(d)
+               : "memory", "m0");
+}
+
 // Workgroup barrier without a memory fence: the fence of __syncthreads would
 // also wait for the tile loads still streaming into the other buffers.  LDS
 // reads are complete once their values are used, and the direct-to-LDS writes

@@ -15,6 +15,8 @@
 // e4m3fn: scores = k_scale(s) * sum_j (w_j q_scale_j) ReLU(q8_j . k8_s),
 // exact because ReLU(a x) = a ReLU(x) for a > 0.
 //   (the decode tiling is in indexer_decode.hip)
+#include <type_traits>
+
 #include "indexer_common.h"
 
 namespace dsa {
@@ -37,21 +39,29 @@ __device__ __forceinline__ long long block_slot(const SeqView &sv, int s) {
   return (blk < 0 || blk >= sv.num_blocks) ? -1 : (long long)blk * 64;
 }
 
-template <int DT>
-__global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
+// kHist: also count the row's scores into the top-k's first-digit histogram
+// (the fused forward's hist_mode 2); kPaged: the cache is a block pool read
+// through the block table (else one contiguous array).  Both are compile-time
+// switches so that the group loop holds no branch and, for a contiguous cache,
+// no block bookkeeping.
+template <int DT, bool kHist, bool kPaged>
+__global__ __launch_bounds__(kPrefillQ * 64) void indexer_prefill_kernel(IndexerArgs a) {
   typedef IdxTraits<DT> Tr;
   constexpr int kChunks = Tr::kRowBytes / 16;           // 16-byte chunks per key row (16 or 8)
   // keys per LDS tile: 64 for bf16, 128 for e4m3fn (the same 16 KB)
   constexpr int kPrefillKeys = DT == DSA_BF16 ? 64 : 128;
   constexpr int kBlocks = kPrefillKeys / 64;            // 64-token blocks per tile
   constexpr int kTileChunks = kPrefillKeys * kChunks;   // 1024 chunks per tile
-  constexpr int kLoads = kTileChunks / 512;             // direct loads per wave per tile (2)
+  constexpr int kLoads = kTileChunks / (kPrefillQ * 64);   // tile loads per wave per tile (2)
+  constexpr int kScaleKeys = kPrefillKeys / kPrefillQ;   // e4m3fn key scales each wave loads (16)
   constexpr bool kScaled = DT == DSA_FP8_E4M3FN;
   constexpr int kWaveLoads = kLoads + (kScaled ? 1 : 0);   // + the key scales (fp8)
   constexpr int kBufs = 3;                              // tiles tt+1, tt+2 stream in while tt is used
   constexpr uint32_t kTileBytes = kTileChunks * 16;
   __shared__ uint4 tile[kBufs][kTileChunks];
-  __shared__ float kscale[kBufs][kScaled ? kPrefillKeys : 1];
+  // fp8 key scales: wave wv's load fills [wv][0, 64) of a buffer, its first
+  // kScaleKeys entries being keys kScaleKeys wv + [0, kScaleKeys) of the tile
+  __shared__ float kscale[kBufs][kScaled ? kPrefillQ * 64 : 1];
 
   const int grp = gridDim.x - 1 - blockIdx.x;           // longest rows first
   const int lane = lane_id();
@@ -77,22 +87,58 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
   load_query<DT>(a, t, col, g, qa, wt);
 
   // first radix digit of the top-k: each wave owns its query row's bins
-  __shared__ uint32_t wh[kPrefillQ][kTopkBins];
-  const bool hist = a.hist_mode == 2;
-  if (hist)
+  __shared__ uint32_t wh[kPrefillQ][kHist ? kTopkBins : 1];
+  if (kHist)
     for (int i = lane; i < kTopkBins; i += 64) wh[wv][i] = 0u;
 
   const uint8_t *kbase = reinterpret_cast<const uint8_t *>(a.k_cache);
+  // Tile gather: buffer loads straight into LDS.  Load j of wave wv fills tile
+  // positions (kPrefillQ j + wv) 64 + [0, 64), i.e. the kChunks 16-byte chunks
+  // of 64 / kChunks consecutive keys from key kf_j = (kPrefillQ j + wv) 64 / kChunks
+  // of the tile, which lie in one 64-token block.  Position p holds data chunk
+  // (p % kChunks) ^ swz(key) of key p / kChunks, so that the lanes of one MFMA
+  // operand read touch distinct banks: swz = key mod 16 for bf16 (16 chunks a
+  // row), (key / 2) mod 8 for e4m3fn (8 chunks a row; key mod 8 there leaves
+  // about half the read cycles bank-conflicted, measured).  Each load's buffer
+  // resource starts at the cache row of its first key and spans only the keys
+  // below nmax of a block that is present; the hardware's range check returns
+  // zeros (finite in both formats) for the rest, so the per-lane offsets are
+  // constants and the loads need no per-tile vector work.
+  constexpr int kLoadKeys = 64 / kChunks;                // keys per load instruction (8 or 4)
+  // e4m3fn: the next group's key operands are read from LDS while the current
+  // group is multiplied (two operand sets, 16 registers each); bf16 reads them
+  // at the start of the group (its sets are twice the size)
+  constexpr bool kPrefetchKb = DT != DSA_BF16;
+  auto swz = [](int key) { return DT == DSA_BF16 ? (key & 15) : ((key >> 1) & 7); };
+  uint32_t lane_off[kLoads];
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const int p = (j * kPrefillQ + wv) * 64 + lane;
+    const int key = p / kChunks, ch = (p % kChunks) ^ swz(key);
+    lane_off[j] = (uint32_t)((lane / kChunks) * Tr::kRowBytes + ch * 16);
+  }
+  const uint32_t scale_off = lane < kScaleKeys ? (uint32_t)lane * 4u : kBufferDrop;
   const uint32_t tile_lds = lds_addr(&tile[0][0]);
   const uint32_t scale_lds = lds_addr(&kscale[0][0]);
-  // Direct-to-LDS gather of the tile at key `base` (< nmax) into buffer `bi`.
-  // Position p of a tile holds data chunk (p % kChunks) ^ (key & (kChunks - 1))
-  // of key p / kChunks, so the 16 lanes of one MFMA operand read touch distinct
-  // bank groups; wave wv's j-th load fills positions (8 j + wv) 64 + [0, 64).
-  // Keys at or past nmax load the last valid key, absent blocks slot 0: every
-  // byte the MFMAs read is a finite cache entry, and neither is written out.
-  // Returns the block presence bits of the tile.
+  // Issues the tile at key `base` (< nmax) into buffer `bi`; returns its block
+  // presence bits.
+  // contiguous cache: one descriptor over the candidate rows of every query of
+  // the workgroup (key s in row s), and the key offset goes into voffset
+  const i32x4s dk_all = buffer_desc(kbase, kPaged ? 0 : nmax * Tr::kRowBytes);
+  const i32x4s ds_all = buffer_desc(a.k_scale, kPaged || !kScaled ? 0 : nmax * 4);
   auto issue = [&](int base, int bi) -> uint32_t {
+    if constexpr (!kPaged) {
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) {
+        const int kf = (j * kPrefillQ + wv) * kLoadKeys;
+        buffer_lds16(dk_all, tile_lds + bi * kTileBytes + (j * kPrefillQ + wv) * 1024,
+                     lane_off[j] + (uint32_t)((base + kf) * Tr::kRowBytes));
+      }
+      if constexpr (kScaled)
+        buffer_lds4(ds_all, scale_lds + (bi * kPrefillQ + wv) * 256,
+                    scale_off + (uint32_t)((base + wv * kScaleKeys) * 4));
+      return (1u << kBlocks) - 1;
+    }
     long long sl0[kBlocks];
     uint32_t ok = 0;
 #pragma unroll
@@ -100,53 +146,59 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
       sl0[j] = base + 64 * j < nmax ? block_slot(a.sv, base + 64 * j) : -1;
       ok |= (sl0[j] >= 0 ? 1u : 0u) << j;
     }
-    const int last = nmax - 1 - base;                    // last valid key of the tile
+    // Resource from the cache row of tile key kf on: the keys below nmax of a
+    // present block are in range (a range past the load's own keys changes
+    // nothing), none otherwise.  Uniform scalar work: no clamp that would
+    // select a vector instruction, and 32-bit slots.
+    auto desc = [&](const void *arr, int row, int kf) {
+      const int b0 = (int)(kBlocks == 1 ? sl0[0] : sl0[kf >> 6]);
+      const int left = nmax - base - kf;
+      const int bytes = b0 < 0 ? 0 : (left > 0 ? left : 0) * row;
+      const int slot = b0 < 0 ? 0 : b0 + (kf & 63);
+      return buffer_desc(reinterpret_cast<const uint8_t *>(arr) + (long long)slot * row, bytes);
+    };
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
-      const int p = (j * kPrefillQ + wv) * 64 + lane;
-      const int key = p / kChunks, ch = (p % kChunks) ^ (key & (kChunks - 1));
-      const int kk = key <= last ? key : last;
-      const long long b0 = sl0[kk >> 6];
-      const long long sl = b0 >= 0 ? b0 + (kk & 63) : 0;
-      lds_dma16(kbase + sl * Tr::kRowBytes + ch * 16, tile_lds + bi * kTileBytes + (j * kPrefillQ + wv) * 1024);
+      const int kf = (j * kPrefillQ + wv) * kLoadKeys;
+      buffer_lds16(desc(kbase, Tr::kRowBytes, kf), tile_lds + bi * kTileBytes + (j * kPrefillQ + wv) * 1024,
+                   lane_off[j]);
     }
     if constexpr (kScaled) {
-      // the 128 key scales, one per lane: wave wv's lanes 0..15 fetch keys 16 wv + lane
-      if (lane < 16) {
-        const int key = wv * 16 + lane;
-        const int kk = key <= last ? key : last;
-        const long long b0 = sl0[kk >> 6];
-        const long long sl = b0 >= 0 ? b0 + (kk & 63) : 0;
-        lds_dma4(a.k_scale + sl, scale_lds + bi * (kPrefillKeys * 4) + wv * 64);
-      }
+      // keys kScaleKeys wv + [0, kScaleKeys); the other lanes are dropped by the
+      // range check (and leave zeros in LDS that no one reads)
+      buffer_lds4(desc(a.k_scale, 4, wv * kScaleKeys), scale_lds + (bi * kPrefillQ + wv) * 256, scale_off);
     }
     return ok;
   };
 
-  // MFMAs of 32-key group nb of the tile in buffer bi (rows nb*32 + col) into
-  // (c0a, c1a), interleaved in program order with the ReLU-weighted head sum of
-  // the previous group's accumulators (p0a, p1a): each k-step's two MFMAs are
-  // followed by a slice of the reduction, and scheduling barriers keep that
-  // order, so the VALU work runs while the matrix core is busy.
-  auto mma_reduce = [&](int bi, int nb, f32x16 &c0a, f32x16 &c1a, const f32x16 &p0a,
-                        const f32x16 &p1a) -> float {
+  // Key operands of 32-key group nb of the tile in buffer bi (rows nb*32 + col).
+  typedef typename Tr::Op KOp[Tr::kSteps];
+  auto read_kb = [&](int bi, int nb, KOp &kb) {
     const int key = nb * 32 + col;
-    typename Tr::Op kb[Tr::kSteps];
     const uint4 *trow = &tile[bi][key * kChunks];
 #pragma unroll
     for (int ks = 0; ks < Tr::kSteps; ++ks) {
       if constexpr (DT == DSA_BF16) {
         const int ch = g * 8 + ks;
-        kb[ks] = __builtin_bit_cast(typename Tr::Op, trow[ch ^ (key & 15)]);
+        kb[ks] = __builtin_bit_cast(typename Tr::Op, trow[ch ^ swz(key)]);
       } else {
         const int ch = g * 4 + ks * 2;
-        const uint4 lo = trow[ch ^ (key & 7)], hi = trow[(ch + 1) ^ (key & 7)];
+        const uint4 lo = trow[ch ^ swz(key)], hi = trow[(ch + 1) ^ swz(key)];
         typename Tr::Op o;
         o[0] = lo.x; o[1] = lo.y; o[2] = lo.z; o[3] = lo.w;
         o[4] = hi.x; o[5] = hi.y; o[6] = hi.z; o[7] = hi.w;
         kb[ks] = o;
       }
     }
+  };
+  // MFMAs of one group's key operands kb into (c0a, c1a), interleaved in program
+  // order with the ReLU-weighted head sum of the previous group's accumulators
+  // (p0a, p1a): each k-step's two MFMAs are followed by a slice of the
+  // reduction, and scheduling barriers keep that order (MFMAs first), so the
+  // VALU work runs while the matrix core is busy and never waits on a result
+  // that has just been started.
+  auto mma_reduce = [&](const KOp &kb, f32x16 &c0a, f32x16 &c1a, const f32x16 &p0a,
+                        const f32x16 &p1a) -> float {
     c0a = zero_vec<f32x16>();
     c1a = zero_vec<f32x16>();
     constexpr int kPerStep = 16 / Tr::kSteps;     // reduction elements (per block) per k-step
@@ -155,6 +207,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
     for (int ks = 0; ks < Tr::kSteps; ++ks) {
       c0a = Tr::mma(qa[0][ks], kb[ks], c0a);
       c1a = Tr::mma(qa[1][ks], kb[ks], c1a);
+      if constexpr (kPrefetchKb) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int e = 0; e < kPerStep; ++e) {
         const int v = ks * kPerStep + e;
@@ -168,23 +221,43 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
     }
     return sum_xor32(r0 + r1);
   };
-  auto emit = [&](int s, float sc, bool gone, float kscl) {
-    if (g == 0 && s < n && row_ok) {
-      float v = neg_inf();
-      if (!gone) {
-        v = sc;
-        if (kScaled) v *= kscl;
-      }
-      srow[s] = v;
-      if (hist) atomicAdd(&wh[wv][score_key(v) >> 21], 1u);
+  // Scores leave through a buffer store whose range is this row's first n
+  // entries (none for a row past the last); the lanes of the upper half, and
+  // keys at or past n, fall outside it and the hardware drops them.  The store
+  // therefore needs no branch: a branch here would let the compiler move the
+  // next group's MFMAs below it, behind the reduction they are meant to overlap.
+  const __amdgpu_buffer_rsrc_t srsrc =
+      __builtin_amdgcn_make_buffer_rsrc(srow, (short)0, row_ok ? n * 4 : 0, kBufferDword3);
+  const uint32_t lane_off_s = g == 0 ? (uint32_t)col * 4u : kBufferDrop;
+  // group of 32 keys starting at `s0` (wave-uniform); `live` false drops it.
+  // The stored score is never -0 (the head sums start from +0, and the e4m3fn
+  // key scale is applied as an fma with a +0 addend), so its histogram bin,
+  // score_key(v) >> 21, is (u >> 21) ^ (sign ? 0x7ff : 0x400) for its bits u.
+  auto emit = [&](int s0, float sc, bool gone, float kscl, bool live) {
+    float v = kScaled ? fmaf(sc, kscl, 0.f) : sc;
+    if (kPaged) v = gone ? neg_inf() : v;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srsrc,
+                                          live ? lane_off_s + (uint32_t)s0 * 4u : kBufferDrop, 0, 0);
+    if constexpr (kHist) {
+      const uint32_t u = __float_as_uint(v);
+      const uint32_t bin = (u >> 21) ^ (((uint32_t)((int)u >> 31) & 0x3ffu) | 0x400u);
+      // every lane's bin is in range; only the stored lanes count
+      const bool cnt = live && g == 0 && col < n - s0 && row_ok;
+      atomicAdd(&wh[wv][bin], cnt ? 1u : 0u);
     }
   };
 
   // Software pipeline over the 32-key groups of all tiles: while group i+1 is
-  // multiplied, group i is reduced and written.  Tile tt+2 is issued right after
-  // the barrier that opens tile tt, into the buffer of tile tt-1, which every
-  // wave has finished reading by then.  Block presence bits travel with the
-  // tile (3 buffers x kBlocks bits); fp8 key scales are read into registers one
+  // multiplied, group i is reduced and written.  Tile tt + kBufs - 1 goes into
+  // the buffer of tile tt-1, which every wave has finished reading once the
+  // barrier that opens tile tt is passed.  Each wave issues its share of that
+  // tile after group K = wv mod kGroups rather than right after the barrier:
+  // a vector-memory instruction holds its wave until the address unit takes
+  // it, and eight waves queueing their loads at the same moment leave the
+  // matrix cores idle meanwhile.  Past the last tile the loads repeat the last
+  // tile (into a buffer no one reads), so every iteration issues the same
+  // instructions and needs no branch.  Block presence bits travel with the
+  // tile (kBufs x kBlocks bits); fp8 key scales are read into registers one
   // group ahead of their use.
   constexpr int kGroups = kPrefillKeys / 32;             // 32-key groups per tile (even)
   const int ntiles = (nmax + kPrefillKeys - 1) / kPrefillKeys;
@@ -193,37 +266,67 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
   // drain the query / weight loads (with tile 0) here, so that no wait for
   // them lands inside the loop, where it would also wait for the prefetches
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  if (kBufs > 2 && ntiles > 1) okbits |= issue(kPrefillKeys, 1) << kBlocks;
+#pragma unroll
+  for (int j = 1; j < kBufs - 1; ++j)
+    if (j < ntiles) okbits |= issue(j * kPrefillKeys, j) << (j * kBlocks);
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = zero_vec<f32x16>();
   float scl[2] = {1.f, 1.f};
   bool gone_prev = false;
   int bi = 0;
-  for (int tt = 0; tt < ntiles; ++tt) {
-    // this wave's loads of tile tt have landed once at most the loads of tile
-    // tt+1 are outstanding; the barrier then covers every wave's
-    if (kBufs > 2 && tt + 1 < ntiles)
-      __builtin_amdgcn_s_waitcnt(wait_vm(kWaveLoads));
-    else
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    lds_barrier();
-    if (tt + kBufs - 1 < ntiles) {
+  auto tile_loop = [&](auto kc) {
+    constexpr int K = decltype(kc)::value;               // group after which this wave issues
+    // vector-memory operations issued after this wave's loads of a tile: the
+    // stores of groups K+1.. of that iteration, then kBufs-2 whole iterations
+    constexpr int kAfter = (kGroups - 1 - K) + (kBufs - 2) * (kWaveLoads + kGroups);
+    static_assert(kAfter < 64, "vmcnt field");
+    for (int tt = 0; tt < ntiles; ++tt) {
+      // tiles 1 .. kBufs-2 came from before the loop: wait for everything then
+      if (tt >= kBufs - 1)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (kAfter & 15) | ((kAfter >> 4) << 14));
+      else if (tt > 0)
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      lds_barrier();
       const int nb2 = bi == 0 ? kBufs - 1 : bi - 1;      // (tt + kBufs - 1) % kBufs
-      okbits = (okbits & ~(((1u << kBlocks) - 1) << (nb2 * kBlocks))) |
-               (issue((tt + kBufs - 1) * kPrefillKeys, nb2) << (nb2 * kBlocks));
-    }
-    const uint32_t okt = okbits >> (bi * kBlocks);
-    const int base = tt * kPrefillKeys;
+      const bool fresh = tt + kBufs - 1 < ntiles;
+      const int tn = fresh ? tt + kBufs - 1 : ntiles - 1;
+      const uint32_t okt = okbits >> (bi * kBlocks);
+      const int base = tt * kPrefillKeys;
+      KOp kbs[kPrefetchKb ? 2 : 1];
+      if constexpr (kPrefetchKb) read_kb(bi, 0, kbs[0]);
 #pragma unroll
-    for (int nb = 0; nb < kGroups; ++nb) {
-      const int cur = nb & 1, prv = cur ^ 1;
-      const float sc = mma_reduce(bi, nb, acc[cur][0], acc[cur][1], acc[prv][0], acc[prv][1]);
-      if (kScaled) scl[cur] = kscale[bi][nb * 32 + col];
-      if (tt > 0 || nb > 0) emit(base + nb * 32 - 32 + col, sc, gone_prev, scl[prv]);
-      gone_prev = ((okt >> (nb >> 1)) & 1u) == 0;
+      for (int nb = 0; nb < kGroups; ++nb) {
+        const int cur = nb & 1, prv = cur ^ 1;
+        if constexpr (kPrefetchKb) {
+          if (nb + 1 < kGroups) read_kb(bi, nb + 1, kbs[(nb + 1) & 1]);
+        } else {
+          read_kb(bi, nb, kbs[0]);
+        }
+        const float sc = mma_reduce(kbs[kPrefetchKb ? (nb & 1) : 0], acc[cur][0], acc[cur][1], acc[prv][0], acc[prv][1]);
+        if (kScaled) {
+          const int k = nb * 32 + col;
+          scl[cur] = kscale[bi][(k / kScaleKeys) * 64 + k % kScaleKeys];
+        }
+        emit(base + nb * 32 - 32, sc, gone_prev, scl[prv], tt > 0 || nb > 0);
+        gone_prev = ((okt >> (nb >> 1)) & 1u) == 0;
+        if (nb == K) {
+          const uint32_t ok = issue(tn * kPrefillKeys, nb2);
+          okbits = fresh ? (okbits & ~(((1u << kBlocks) - 1) << (nb2 * kBlocks))) | (ok << (nb2 * kBlocks))
+                         : okbits;
+        }
+      }
+      bi = bi == kBufs - 1 ? 0 : bi + 1;
     }
-    bi = bi == kBufs - 1 ? 0 : bi + 1;
+    // the repeated loads of the last iterations land before the workgroup ends
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  };
+  static_assert(kGroups == 2 || kGroups == 4, "issue groups");
+  switch (wv & (kGroups - 1)) {
+    case 0: tile_loop(std::integral_constant<int, 0>{}); break;
+    case 1: tile_loop(std::integral_constant<int, 1>{}); break;
+    case 2: tile_loop(std::integral_constant<int, (kGroups > 2 ? 2 : 0)>{}); break;
+    default: tile_loop(std::integral_constant<int, (kGroups > 3 ? 3 : 0)>{}); break;
   }
   if (ntiles > 0) {
     // the last group (in acc[1], kGroups being even) is reduced alone
@@ -233,12 +336,12 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerArgs a) {
       p0 = fmaf(wt[0][v], __int_as_float(max(__float_as_int(acc[1][0][v]), 0)), p0);
       p1 = fmaf(wt[1][v], __int_as_float(max(__float_as_int(acc[1][1][v]), 0)), p1);
     }
-    emit(ntiles * kPrefillKeys - 32 + col, sum_xor32(p0 + p1), gone_prev, scl[1]);
+    emit(ntiles * kPrefillKeys - 32, sum_xor32(p0 + p1), gone_prev, scl[1], true);
   }
   if (a.fill_masked && row_ok) {
     for (long long s = n + lane; s < a.ld; s += 64) srow[s] = neg_inf();
   }
-  if (hist && row_ok) {
+  if (kHist && row_ok) {
     uint32_t *hrow = a.hist + (long long)r * a.hist_stride;
     for (int i = lane; i < kTopkBins; i += 64) hrow[i] = wh[wv][i];
   }
@@ -293,10 +396,17 @@ hipError_t launch_index_scores(const IndexerArgs &a, hipStream_t st) {
   if (decode) return launch_index_decode(a, st);
   {
     dim3 grid((unsigned)((a.rows + kPrefillQ - 1) / kPrefillQ));
-    if (a.dtype == DSA_BF16)
-      hipLaunchKernelGGL(indexer_prefill_kernel<DSA_BF16>, grid, dim3(512), 0, st, a);
-    else
-      hipLaunchKernelGGL(indexer_prefill_kernel<DSA_FP8_E4M3FN>, grid, dim3(512), 0, st, a);
+    const bool hist = a.hist_mode == 2, paged = a.sv.block_table != nullptr;
+    const dim3 block(kPrefillQ * 64);
+#define DSA_PREFILL_LAUNCH(D, H, P) hipLaunchKernelGGL((indexer_prefill_kernel<D, H, P>), grid, block, 0, st, a)
+    if (a.dtype == DSA_BF16) {
+      if (hist) { if (paged) DSA_PREFILL_LAUNCH(DSA_BF16, true, true); else DSA_PREFILL_LAUNCH(DSA_BF16, true, false); }
+      else { if (paged) DSA_PREFILL_LAUNCH(DSA_BF16, false, true); else DSA_PREFILL_LAUNCH(DSA_BF16, false, false); }
+    } else {
+      if (hist) { if (paged) DSA_PREFILL_LAUNCH(DSA_FP8_E4M3FN, true, true); else DSA_PREFILL_LAUNCH(DSA_FP8_E4M3FN, true, false); }
+      else { if (paged) DSA_PREFILL_LAUNCH(DSA_FP8_E4M3FN, false, true); else DSA_PREFILL_LAUNCH(DSA_FP8_E4M3FN, false, false); }
+    }
+#undef DSA_PREFILL_LAUNCH
   }
   return hipGetLastError();
 }
