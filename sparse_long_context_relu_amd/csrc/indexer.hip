@@ -219,7 +219,14 @@ __global__ __launch_bounds__(kPrefillQ * 64) void indexer_prefill_kernel(Indexer
       asm volatile("" : "+v"(r0), "+v"(r1));
       __builtin_amdgcn_sched_barrier(0);
     }
-    return sum_xor32(r0 + r1);
+    return r0 + r1;   // this half-wave's heads; the other half's come in pair_total
+  };
+  // Scores of two consecutive groups: lanes 0..31 get the head sum of key
+  // col of the even group (its two half-waves' partials added across the
+  // halves), lanes 32..63 that of the odd group, with one lane swap.
+  auto pair_total = [](float even_part, float odd_part) {
+    const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(even_part), __float_as_uint(odd_part), false, false);
+    return __uint_as_float(x[0]) + __uint_as_float(x[1]);
   };
   // Scores leave through a buffer store whose range is this row's first n
   // entries (none for a row past the last); the lanes of the upper half, and
@@ -228,28 +235,29 @@ __global__ __launch_bounds__(kPrefillQ * 64) void indexer_prefill_kernel(Indexer
   // next group's MFMAs below it, behind the reduction they are meant to overlap.
   const __amdgpu_buffer_rsrc_t srsrc =
       __builtin_amdgcn_make_buffer_rsrc(srow, (short)0, row_ok ? n * 4 : 0, kBufferDword3);
-  const uint32_t lane_off_s = g == 0 ? (uint32_t)col * 4u : kBufferDrop;
-  // group of 32 keys starting at `s0` (wave-uniform); `live` false drops it.
-  // The stored score is never -0 (the head sums start from +0, and the e4m3fn
-  // key scale is applied as an fma with a +0 addend), so its histogram bin,
-  // score_key(v) >> 21, is (u >> 21) ^ (sign ? 0x7ff : 0x400) for its bits u.
-  auto emit = [&](int s0, float sc, bool gone, float kscl, bool live) {
-    float v = kScaled ? fmaf(sc, kscl, 0.f) : sc;
+  // 64 keys from `s0` (wave-uniform), lane l holding key s0 + l; `live` false
+  // drops them.  The stored score is never -0 (the head sums start from +0,
+  // and the e4m3fn key scale is applied as an fma with a +0 addend), so its
+  // histogram bin, score_key(v) >> 21, is (u >> 21) ^ (sign ? 0x7ff : 0x400)
+  // for its bits u.
+  auto emit = [&](int s0, float v, bool gone, float kscl, bool live) {
+    if (kScaled) v = fmaf(v, kscl, 0.f);
     if (kPaged) v = gone ? neg_inf() : v;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srsrc,
-                                          live ? lane_off_s + (uint32_t)s0 * 4u : kBufferDrop, 0, 0);
+                                          live ? (uint32_t)(s0 + lane) * 4u : kBufferDrop, 0, 0);
     if constexpr (kHist) {
       const uint32_t u = __float_as_uint(v);
       const uint32_t bin = (u >> 21) ^ (((uint32_t)((int)u >> 31) & 0x3ffu) | 0x400u);
       // every lane's bin is in range; only the stored lanes count
-      const bool cnt = live && g == 0 && col < n - s0 && row_ok;
+      const bool cnt = live && lane < n - s0 && row_ok;
       atomicAdd(&wh[wv][bin], cnt ? 1u : 0u);
     }
   };
 
   // Software pipeline over the 32-key groups of all tiles: while group i+1 is
-  // multiplied, group i is reduced and written.  Tile tt + kBufs - 1 goes into
-  // the buffer of tile tt-1, which every wave has finished reading once the
+  // multiplied, group i is reduced, and every second step the last two
+  // groups' scores are written together.  Tile tt + kBufs - 1 goes into the
+  // buffer of tile tt-1, which every wave has finished reading once the
   // barrier that opens tile tt is passed.  Each wave issues its share of that
   // tile after group K = wv mod kGroups rather than right after the barrier:
   // a vector-memory instruction holds its wave until the address unit takes
@@ -257,8 +265,9 @@ __global__ __launch_bounds__(kPrefillQ * 64) void indexer_prefill_kernel(Indexer
   // matrix cores idle meanwhile.  Past the last tile the loads repeat the last
   // tile (into a buffer no one reads), so every iteration issues the same
   // instructions and needs no branch.  Block presence bits travel with the
-  // tile (kBufs x kBlocks bits); fp8 key scales are read into registers one
-  // group ahead of their use.
+  // tile (kBufs x kBlocks bits); a pair of groups is one 64-token block, and
+  // its fp8 key scales are read while its second group is multiplied (the
+  // tile's buffer may be refilled once the next tile has begun).
   constexpr int kGroups = kPrefillKeys / 32;             // 32-key groups per tile (even)
   const int ntiles = (nmax + kPrefillKeys - 1) / kPrefillKeys;
   uint32_t okbits = 0;
@@ -272,15 +281,18 @@ __global__ __launch_bounds__(kPrefillQ * 64) void indexer_prefill_kernel(Indexer
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = zero_vec<f32x16>();
-  float scl[2] = {1.f, 1.f};
-  bool gone_prev = false;
+  float part_even = 0.f;       // partial head sum of the pending even group
+  float scl_pair = 1.f;        // key scale of this lane's key in the pending pair
+  bool gone_pair = false;      // the pending pair's 64-token block is absent
   int bi = 0;
   auto tile_loop = [&](auto kc) {
     constexpr int K = decltype(kc)::value;               // group after which this wave issues
     // vector-memory operations issued after this wave's loads of a tile: the
-    // stores of groups K+1.. of that iteration, then kBufs-2 whole iterations
-    constexpr int kAfter = (kGroups - 1 - K) + (kBufs - 2) * (kWaveLoads + kGroups);
-    static_assert(kAfter < 64, "vmcnt field");
+    // pair stores of steps K+1.. of that iteration (even steps store), then
+    // kBufs-2 whole iterations
+    constexpr int kStoresAfter = (kGroups - 1) / 2 - K / 2;   // even steps in (K, kGroups)
+    constexpr int kAfter = kStoresAfter + (kBufs - 2) * (kWaveLoads + kGroups / 2);
+    static_assert(kStoresAfter >= 0 && kAfter < 64, "vmcnt field");
     for (int tt = 0; tt < ntiles; ++tt) {
       // tiles 1 .. kBufs-2 came from before the loop: wait for everything then
       if (tt >= kBufs - 1)
@@ -303,13 +315,21 @@ __global__ __launch_bounds__(kPrefillQ * 64) void indexer_prefill_kernel(Indexer
         } else {
           read_kb(bi, nb, kbs[0]);
         }
-        const float sc = mma_reduce(kbs[kPrefetchKb ? (nb & 1) : 0], acc[cur][0], acc[cur][1], acc[prv][0], acc[prv][1]);
-        if (kScaled) {
-          const int k = nb * 32 + col;
-          scl[cur] = kscale[bi][(k / kScaleKeys) * 64 + k % kScaleKeys];
+        // multiplies group nb, reduces group nb-1 (the previous tile's last for nb = 0)
+        const float part = mma_reduce(kbs[kPrefetchKb ? (nb & 1) : 0], acc[cur][0], acc[cur][1], acc[prv][0], acc[prv][1]);
+        if (nb & 1) {
+          // group nb-1 is even: hold it; read the scales and the presence of
+          // the pair (nb-1, nb) while this tile is current
+          part_even = part;
+          if (kScaled) {
+            const int k = (nb - 1) * 32 + lane;
+            scl_pair = kscale[bi][(k / kScaleKeys) * 64 + k % kScaleKeys];
+          }
+          gone_pair = ((okt >> (nb >> 1)) & 1u) == 0;
+        } else {
+          // group nb-1 is odd: write the pair (nb-2, nb-1)
+          emit(base + nb * 32 - 64, pair_total(part_even, part), gone_pair, scl_pair, tt > 0 || nb > 0);
         }
-        emit(base + nb * 32 - 32, sc, gone_prev, scl[prv], tt > 0 || nb > 0);
-        gone_prev = ((okt >> (nb >> 1)) & 1u) == 0;
         if (nb == K) {
           const uint32_t ok = issue(tn * kPrefillKeys, nb2);
           okbits = fresh ? (okbits & ~(((1u << kBlocks) - 1) << (nb2 * kBlocks))) | (ok << (nb2 * kBlocks))
@@ -329,14 +349,15 @@ __global__ __launch_bounds__(kPrefillQ * 64) void indexer_prefill_kernel(Indexer
     default: tile_loop(std::integral_constant<int, (kGroups > 3 ? 3 : 0)>{}); break;
   }
   if (ntiles > 0) {
-    // the last group (in acc[1], kGroups being even) is reduced alone
+    // the last group (in acc[1], kGroups being even) is reduced alone and
+    // written with the pending even group
     float p0 = 0.f, p1 = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       p0 = fmaf(wt[0][v], __int_as_float(max(__float_as_int(acc[1][0][v]), 0)), p0);
       p1 = fmaf(wt[1][v], __int_as_float(max(__float_as_int(acc[1][1][v]), 0)), p1);
     }
-    emit(ntiles * kPrefillKeys - 32, sum_xor32(p0 + p1), gone_prev, scl[1], true);
+    emit(ntiles * kPrefillKeys - 64, pair_total(part_even, p0 + p1), gone_pair, scl_pair, true);
   }
   if (a.fill_masked && row_ok) {
     for (long long s = n + lane; s < a.ld; s += 64) srow[s] = neg_inf();
