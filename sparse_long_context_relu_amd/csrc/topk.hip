@@ -305,12 +305,25 @@ __global__ __launch_bounds__(kNT) void topk_collect_kernel(TopkArgs a) {
       }
     __syncthreads();   // wcnt is rewritten by the next round; h is complete after the last
   }
+  // The row's second histogram gets this slice's nonzero bins.  Buffer atomics
+  // with a constant lane offset and the bin block in the scalar offset: no
+  // address register is rewritten between them, so they issue back to back
+  // (a rewritten address register makes the compiler wait for the previous
+  // atomic to complete).
+  static_assert(kTopkBins % kNT == 0, "bins per thread");
+  const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(w.hist2, (short)0, kTopkBins * 4, kBufferDword3);
+  uint32_t hv[kTopkBins / kNT];
+#pragma unroll
+  for (int j = 0; j < kTopkBins / kNT; ++j) hv[j] = h[threadIdx.x + j * kNT];
+#pragma unroll
+  for (int j = 0; j < kTopkBins / kNT; ++j)
+    if (hv[j]) __builtin_amdgcn_raw_ptr_buffer_atomic_add_i32((int)hv[j], hr, (int)threadIdx.x * 4, j * kNT * 4, 0);
+  // last: a store's address registers rewritten after it would make the
+  // compiler wait for the store
   if (threadIdx.x == 0) {
     w.counts[b] = ns_run;
     w.counts[kTopkMaxSlices + b] = nc_run;
   }
-  for (int i = threadIdx.x; i < kTopkBins; i += kNT)
-    if (h[i]) atomicAdd(&w.hist2[i], h[i]);
 }
 
 // Sliced select, one workgroup per row: the second digit from the collected
@@ -340,6 +353,31 @@ __global__ __launch_bounds__(kRowNT) void topk_select_sliced_kernel(TopkArgs a) 
   __shared__ uint32_t nties;
 
   RowWs w = row_ws(a, r);
+  const int sb = threadIdx.x % a.slices;         // this thread's slice
+  const int tps = kRowNT / a.slices;             // threads per slice
+  const int t0 = threadIdx.x / a.slices;
+  const bool active = t0 < tps;
+  const uint32_t *ssel = w.sel + (long long)sb * a.sel_seg;
+  const uint32_t *scand = w.cand + 2ll * sb * a.slice_len;
+  // This thread's first list entries are loaded before the slice counts and
+  // the second digit are known (the loads depend on neither; entries past a
+  // slice's count are read but not used), so the list reads overlap the
+  // histogram read instead of following it.
+  constexpr int kSelPT = 4, kCandPT = 16;
+  uint32_t s_pre[kSelPT];
+  uint2 c_pre[kCandPT];
+  // (indices clamped into the slice's regions, so the loads need no branch and
+  // go out back to back; the use below masks them by the counts)
+#pragma unroll
+  for (int u = 0; u < kSelPT; ++u) {
+    const int i = t0 + u * tps;
+    s_pre[u] = ssel[i < a.sel_seg ? i : a.sel_seg - 1];
+  }
+#pragma unroll
+  for (int u = 0; u < kCandPT; ++u) {
+    const int i = t0 + u * tps;
+    c_pre[u] = *reinterpret_cast<const uint2 *>(scand + 2 * (i < a.slice_len ? i : a.slice_len - 1));
+  }
   for (int i = threadIdx.x; i < kTopkBins; i += kRowNT) h[i] = w.hist2[i];
   for (int i = threadIdx.x; i < W; i += kRowNT) {
     selmap[i] = 0u;
@@ -360,45 +398,42 @@ __global__ __launch_bounds__(kRowNT) void topk_select_sliced_kernel(TopkArgs a) 
   const uint32_t d2 = (uint32_t)res[2];
   const int need3 = need - res[3];
 
-  const int sb = threadIdx.x % a.slices;         // this thread's slice
-  const int tps = kRowNT / a.slices;             // threads per slice
-  const int t0 = threadIdx.x / a.slices;
-  const bool active = t0 < tps;
-  const uint32_t *ssel = w.sel + (long long)sb * a.sel_seg;
-  const uint32_t *scand = w.cand + 2ll * sb * a.slice_len;
   const int nsel = active ? (int)min(cnt_s[sb], (uint32_t)a.sel_seg) : 0;
   const int ncand = active ? (int)cnt_c[sb] : 0;
   // selected outright
-  for (int i0 = t0; i0 < nsel; i0 += 4 * tps) {
-    uint32_t s[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) s[u] = i0 + u * tps < nsel ? ssel[i0 + u * tps] : 0xffffffffu;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (s[u] < (uint32_t)n) atomicOr(&selmap[s[u] >> 5], 1u << (s[u] & 31));
+  for (int u = 0; u < kSelPT; ++u)
+    if (t0 + u * tps < nsel && s_pre[u] < (uint32_t)n) atomicOr(&selmap[s_pre[u] >> 5], 1u << (s_pre[u] & 31));
+  for (int i = t0 + kSelPT * tps; i < nsel; i += tps) {
+    const uint32_t sv = ssel[i];
+    if (sv < (uint32_t)n) atomicOr(&selmap[sv >> 5], 1u << (sv & 31));
   }
   // candidates: above the second digit -> selected; equal -> the tie list
-  for (int i0 = t0; i0 < ncand; i0 += 4 * tps) {
+  auto candidate = [&](uint2 e) {
+    const uint32_t lo = e.x & 0x1fffffu, sv = e.y;
+    if (sv >= (uint32_t)n) return;
+    const uint32_t dig = lo >> 10;
+    if (dig > d2) {
+      atomicOr(&selmap[sv >> 5], 1u << (sv & 31));
+    } else if (dig == d2) {
+      const uint32_t p = atomicAdd(&nties, 1u);
+      if (p < (uint32_t)kTieCap) {
+        ties[2 * p] = lo;
+        ties[2 * p + 1] = sv;
+      }
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < kCandPT; ++u)
+    if (t0 + u * tps < ncand) candidate(c_pre[u]);
+  for (int i0 = t0 + kCandPT * tps; i0 < ncand; i0 += 4 * tps) {
     uint2 e[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       e[u] = i0 + u * tps < ncand ? *reinterpret_cast<const uint2 *>(scand + 2 * (i0 + u * tps))
                                   : make_uint2(0u, 0xffffffffu);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t lo = e[u].x & 0x1fffffu, s = e[u].y;
-      if (s >= (uint32_t)n) continue;
-      const uint32_t dig = lo >> 10;
-      if (dig > d2) {
-        atomicOr(&selmap[s >> 5], 1u << (s & 31));
-      } else if (dig == d2) {
-        const uint32_t p = atomicAdd(&nties, 1u);
-        if (p < (uint32_t)kTieCap) {
-          ties[2 * p] = lo;
-          ties[2 * p + 1] = s;
-        }
-      }
-    }
+    for (int u = 0; u < 4; ++u) candidate(e[u]);
   }
   __syncthreads();
   const int nt = (int)nties;
