@@ -143,18 +143,28 @@ __device__ void compact_selection(uint32_t *selmap, const uint32_t *eqmap, int W
 // Load one round of row[s], s in [base, base + NT*16) clipped to [.., s1),
 // into x: thread t holds elements base + (i*NT + t)*4 + c.  Sixteen scores per
 // thread are in flight together (16-byte loads when the row is aligned).
+// Buffer loads over [row, row + s1): elements past s1 read as zero (their
+// keys are masked by the caller), so no load needs a branch; a branch per
+// element group made the compiler wait for each group's loads in turn.
 template <int NT>
 __device__ __forceinline__ void load_round(const float *row, int base, int s1, bool vec, float (&x)[4][4]) {
+  const __amdgpu_buffer_rsrc_t d =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(row), (short)0, s1 * 4, kBufferDword3);
+  if (vec) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = base + (i * NT + (int)threadIdx.x) * 4;
-    if (vec && e + 3 < s1) {
-      const float4 v = *reinterpret_cast<const float4 *>(row + e);
-      x[i][0] = v.x; x[i][1] = v.y; x[i][2] = v.z; x[i][3] = v.w;
-    } else {
+    for (int i = 0; i < 4; ++i) {
+      const int e = base + (i * NT + (int)threadIdx.x) * 4;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(d, e * 4, 0, 0);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) x[i][c] = e + c < s1 ? row[e + c] : 0.f;
+      for (int c = 0; c < 4; ++c) x[i][c] = __uint_as_float(v[c]);
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        x[i][c] = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(d, (base + (i * NT + (int)threadIdx.x) * 4 + c) * 4, 0, 0));
   }
 }
 
@@ -228,7 +238,14 @@ __global__ __launch_bounds__(kNT) void topk_collect_kernel(TopkArgs a) {
   const bool vec = ((uintptr_t)(row + s0) & 15) == 0;
   float x[4][4];
   load_round<kNT>(row, s0, s1, vec, x);
-  for (int i = threadIdx.x; i < kTopkBins; i += kNT) h[i] = w.hist1[i];
+  {
+    // all of this thread's bins in flight at once
+    uint32_t hv[kTopkBins / kNT];
+#pragma unroll
+    for (int j = 0; j < kTopkBins / kNT; ++j) hv[j] = w.hist1[threadIdx.x + j * kNT];
+#pragma unroll
+    for (int j = 0; j < kTopkBins / kNT; ++j) h[threadIdx.x + j * kNT] = hv[j];
+  }
   __syncthreads();
   find_digit<kNT>(h, kTopkBins, a.k, res, tmp);
   const uint32_t d1 = (uint32_t)res[0];
@@ -378,7 +395,13 @@ __global__ __launch_bounds__(kRowNT) void topk_select_sliced_kernel(TopkArgs a) 
     const int i = t0 + u * tps;
     c_pre[u] = *reinterpret_cast<const uint2 *>(scand + 2 * (i < a.slice_len ? i : a.slice_len - 1));
   }
-  for (int i = threadIdx.x; i < kTopkBins; i += kRowNT) h[i] = w.hist2[i];
+  {
+    uint32_t hv[kTopkBins / kRowNT];
+#pragma unroll
+    for (int j = 0; j < kTopkBins / kRowNT; ++j) hv[j] = w.hist2[threadIdx.x + j * kRowNT];
+#pragma unroll
+    for (int j = 0; j < kTopkBins / kRowNT; ++j) h[threadIdx.x + j * kRowNT] = hv[j];
+  }
   for (int i = threadIdx.x; i < W; i += kRowNT) {
     selmap[i] = 0u;
     eqmap[i] = 0u;
@@ -507,7 +530,13 @@ __global__ __launch_bounds__(kRowNT) void topk_select_rows_kernel(TopkArgs a) {
   __shared__ uint32_t lcount;
 
   RowWs w = row_ws(a, r);
-  for (int i = threadIdx.x; i < kTopkBins; i += kRowNT) h[i] = w.hist1[i];
+  {
+    uint32_t hv[kTopkBins / kRowNT];
+#pragma unroll
+    for (int j = 0; j < kTopkBins / kRowNT; ++j) hv[j] = w.hist1[threadIdx.x + j * kRowNT];
+#pragma unroll
+    for (int j = 0; j < kTopkBins / kRowNT; ++j) h[threadIdx.x + j * kRowNT] = hv[j];
+  }
   for (int i = threadIdx.x; i < W; i += kRowNT) {
     selmap[i] = 0u;
     eqmap[i] = 0u;
