@@ -26,7 +26,8 @@
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
  *     null stream).  The library never synchronises, never allocates device
  *     memory and keeps no state between calls; callers own every buffer,
- *     including the workspace sized by dsa_workspace_size().  The one
+ *     including the workspace sized by dsa_workspace_size() (its base
+ *     256-byte aligned, as every hipMalloc and torch allocation is).  The one
  *     exception is dsa_forward_noalloc, whose scratch is a static device
  *     array of the library (see there).
  *   - Arguments are checked on the host before any launch; a failed check
@@ -88,7 +89,7 @@ typedef enum dsa_status {
   DSA_OK = 0,
   DSA_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent shape */
   DSA_ERR_UNSUPPORTED = -2, /* valid but outside the supported shapes/types */
-  DSA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  DSA_ERR_WORKSPACE = -3,   /* workspace missing, smaller than required, or not 256-byte aligned */
   DSA_ERR_HIP = -4,         /* a kernel launch failed */
   DSA_ERR_SCRATCH_LIMIT = -5 /* dsa_forward_noalloc: the problem needs more than its static scratch */
 } dsa_status;

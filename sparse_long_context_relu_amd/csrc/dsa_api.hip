@@ -335,7 +335,9 @@ int check_sbwd(const dsa_seqs *s, const dsa_dims *d) {
 
 int check_ws(size_t need, const void *ws, size_t ws_bytes) {
   if (need == 0) return DSA_OK;
-  if (ws == nullptr || ws_bytes < need) return DSA_ERR_WORKSPACE;
+  // the kernels address workspace regions with 16-byte accesses; every region
+  // offset is a multiple of 256 bytes, so the base must be too
+  if (ws == nullptr || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return DSA_ERR_WORKSPACE;
   return DSA_OK;
 }
 

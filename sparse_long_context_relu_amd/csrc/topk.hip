@@ -195,8 +195,10 @@ __device__ __forceinline__ void slice_range(const TopkArgs &a, int n, int b, int
 }
 
 __global__ __launch_bounds__(kNT) void topk_zero_kernel(TopkArgs a) {
-  uint32_t *base = a.ws + (long long)blockIdx.x * a.row_words;
-  for (int i = threadIdx.x; i < kTopkHdrWords; i += kNT) base[i] = 0u;
+  // rows start 16-byte aligned (row_words and the workspace base are multiples of 4 words)
+  static_assert(kTopkHdrWords % 4 == 0, "16-byte stores");
+  uint4 *base = reinterpret_cast<uint4 *>(a.ws + (long long)blockIdx.x * a.row_words);
+  for (int i = threadIdx.x; i < kTopkHdrWords / 4; i += kNT) base[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // hist1 for scores handed in from outside (the fused path builds it in the indexer).

@@ -126,6 +126,7 @@ def test_topk_validation():
     assert call(4096, FAKE, need) == B.ERR_UNSUPPORTED
     assert call(2048, None, 0) == B.ERR_WORKSPACE
     assert call(2048, FAKE, need - 1) == B.ERR_WORKSPACE
+    assert call(2048, FAKE + 16, need) == B.ERR_WORKSPACE     # base not 256-byte aligned
     assert call(2048, FAKE, need, sc=None) == B.ERR_INVALID_ARG
     assert call(2048, FAKE, need, idx=None) == B.ERR_INVALID_ARG
 
@@ -238,6 +239,7 @@ def test_forward_validation_and_workspace():
                                             ws, nb, None)
     assert call(None, 0) == B.ERR_WORKSPACE
     assert call(FAKE, need - 1) == B.ERR_WORKSPACE
+    assert call(FAKE + 4, need) == B.ERR_WORKSPACE            # base not 256-byte aligned
     args.out = None
     assert call(FAKE, need) == B.ERR_INVALID_ARG
     args.out = FAKE
