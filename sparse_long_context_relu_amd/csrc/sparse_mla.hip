@@ -146,9 +146,14 @@ __device__ __forceinline__ void consume_tile(uint32_t tile, const int *slots, in
   // transpose read at row 4g+e (resp. 16+4g+e), dims d0+4c..d0+4c+3, and receives
   // V[row_e][d0 + (lane%16)] for e = 0..3.  The swizzle permutes chunks within
   // aligned groups of four, so even and odd value blocks have their own lane offsets.
+  // The per-lane bases are formed once per tile (pinned as vector values) so
+  // that each block's part of the address lands in the reads' offset field
+  // instead of costing an add per read.
+  uint32_t pvb[2] = {tile + pv_even, tile + pv_odd};
+  asm volatile("" : "+v"(pvb[0]), "+v"(pvb[1]));
 #pragma unroll
   for (int db = 0; db < kDb; ++db) {
-    const uint32_t v0 = tile + ((db & 1) ? pv_odd : pv_even) + (db >> 1) * 64;
+    const uint32_t v0 = pvb[db & 1] + (db >> 1) * 64;
     const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)v0);
     const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)(v0 + 16 * kRowStride));
     const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
