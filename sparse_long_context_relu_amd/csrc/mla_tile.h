@@ -89,35 +89,60 @@ struct TileLoads {
   const uint8_t *src[kWaveLoads];   // this lane's source of each of the wave's loads
 };
 
+// Per-lane coordinates of a wave's tile loads, the same for every tile: load
+// j's tile row (5 bits) and its data chunk (7 bits, swizzled; 0 for a pad
+// chunk), 12 bits a load: loads 0, 1 and the low byte of load 4 in the first
+// word, loads 2, 3 and the high nibble of load 4 in the second.  Positions past
+// the tile (rows 32..) only fill LDS that no one reads, so their row is kept
+// modulo 32: they load some valid row.  Formed once per kernel; a tile then
+// unpacks them with a few bit-field extracts instead of re-deriving row and
+// chunk (two registers, where per-load values would not fit beside the MFMA
+// operands).
+static_assert(kWaveLoads == 5, "coordinate packing");
+struct TileCoords {
+  uint32_t w[2];
+};
+__device__ __forceinline__ TileCoords tile_coords(int wv, int lane) {
+  uint32_t f[kWaveLoads];
+#pragma unroll
+  for (int j = 0; j < kWaveLoads; ++j) {
+    const int p = (j * kWaves + wv) * 64 + lane;
+    const int row = p / kRowChunks, ch = p - row * kRowChunks;
+    const int dc = ch < kDataChunks ? ch ^ swz(row) : 0;
+    f[j] = (uint32_t)((row & 31) | (dc << 5));
+  }
+  TileCoords c;
+  c.w[0] = f[0] | (f[1] << 12) | ((f[4] & 0xffu) << 24);
+  c.w[1] = f[2] | (f[3] << 12) | ((f[4] >> 8) << 24);
+  return c;
+}
+__device__ __forceinline__ uint32_t tile_coord(const TileCoords &c, int j) {
+  if (j < 2) return (c.w[0] >> (12 * j)) & 0xfffu;
+  if (j < 4) return (c.w[1] >> (12 * (j - 2))) & 0xfffu;
+  return (c.w[0] >> 24) | ((c.w[1] >> 24) << 8);
+}
+
 // Sources of this wave's loads of the tile of split rows [j0, j0+32): slot reads
 // first (independent LDS reads, one wait), then the addresses.  Rows past the
 // tile (the pad) read the slot list's -1 tail and load the fallback row.
-__device__ __forceinline__ TileLoads tile_loads(const uint8_t *kv, const int *slots, int j0, int fallback, int wv,
-                                                int lane) {
-  // Recompute the per-lane coordinates on every call rather than keep them live
-  // across the tile loop (the registers are needed by the MFMA operands).
-  asm volatile("" : "+v"(lane));
-  int p = wv * 64 + lane;
-  int row = p / kRowChunks;
-  int ch = p - row * kRowChunks;
+__device__ __forceinline__ TileLoads tile_loads(const uint8_t *kv, const int *slots, int j0, int fallback,
+                                                const TileCoords &c0) {
+  // unpacked per call (pinned so that the compiler does not hoist the
+  // unpacked values out of the tile loop and keep them live across it)
+  TileCoords c = c0;
+  asm volatile("" : "+v"(c.w[0]), "+v"(c.w[1]));
   int sl[kWaveLoads], dc[kWaveLoads];
 #pragma unroll
   for (int j = 0; j < kWaveLoads; ++j) {
-    sl[j] = slots[j0 + row];
-    dc[j] = ch < kDataChunks ? ch ^ swz(row) : 0;
-    p += kWaves * 64;
-    row += (kWaves * 64) / kRowChunks;
-    ch += (kWaves * 64) % kRowChunks;
-    if (ch >= kRowChunks) {
-      ch -= kRowChunks;
-      row += 1;
-    }
+    const uint32_t f = tile_coord(c, j);
+    sl[j] = slots[j0 + (int)(f & 31u)];
+    dc[j] = (int)(f >> 5);
   }
   TileLoads t;
 #pragma unroll
   for (int j = 0; j < kWaveLoads; ++j) {
     const int s = sl[j] < 0 ? fallback : sl[j];
-    t.src[j] = kv + (long long)s * (kD * 2) + dc[j] * 16;
+    t.src[j] = kv + (unsigned long long)(unsigned)s * (kD * 2) + dc[j] * 16;
   }
   return t;
 }
@@ -128,8 +153,8 @@ __device__ __forceinline__ void tile_load(const TileLoads &t, int j, uint32_t ti
 }
 
 __device__ __forceinline__ void issue_tile(uint32_t tile, const uint8_t *kv, const int *slots, int j0,
-                                           int fallback, int wv, int lane) {
-  const TileLoads t = tile_loads(kv, slots, j0, fallback, wv, lane);
+                                           int fallback, int wv, const TileCoords &c) {
+  const TileLoads t = tile_loads(kv, slots, j0, fallback, c);
 #pragma unroll
   for (int j = 0; j < kWaveLoads; ++j) tile_load(t, j, tile, wv);
 }

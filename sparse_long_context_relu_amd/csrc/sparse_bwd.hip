@@ -163,9 +163,10 @@ __global__ __launch_bounds__(kThreads) void bwd_scores_kernel(MlaBwdArgs a) {
   };
 
   if (fb >= 0) {
-    issue_tile(tile_lds, kv, slots, 0, fb, wv, lane);
+    const TileCoords tc = tile_coords(wv, lane);
+    issue_tile(tile_lds, kv, slots, 0, fb, wv, tc);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);         // query, dO operands and tile 0
-    if (ntiles > 1) issue_tile(tile_lds + kTileBytes, kv, slots, kR, fb, wv, lane);
+    if (ntiles > 1) issue_tile(tile_lds + kTileBytes, kv, slots, kR, fb, wv, tc);
     int cur = 0;
     float pw[8], sd[8];
     for (int tt = 0; tt < ntiles; ++tt) {
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void bwd_scores_kernel(MlaBwdArgs a) {
       lds_barrier();
       if (tt > 0) store_tile(tt - 1, pw, sd);
       if (tt + 2 < ntiles) issue_tile(tile_lds + (cur == 0 ? 2 : cur - 1) * kTileBytes, kv, slots, (tt + 2) * kR, fb,
-                                      wv, lane);
+                                      wv, tc);
       if (tt > 0 && wv == 0) write_probs(tt - 1);
       const uint32_t tile = tile_lds + cur * kTileBytes;
       const int row_slot = slots[tt * kR + (lane & (kR - 1))];
@@ -266,8 +267,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(MlaBwdArgs a) {
     const uint8_t *kv = reinterpret_cast<const uint8_t *>(a.kv);
     // wave wv's 1 KB of a tile's dS^T (heads 16 wv.., 32 rows each): lane l's 16 bytes
     const uint16_t *ds_src = a.ds_t + ((long long)r * ntiles * kH + wv * 16) * kR + lane * 8;
+    const TileCoords tc = tile_coords(wv, lane);
     auto issue = [&](int bi, int tt) {
-      issue_tile(tile_lds + bi * kTileBytes, kv, slots, tt * kR, fb, wv, lane);
+      issue_tile(tile_lds + bi * kTileBytes, kv, slots, tt * kR, fb, wv, tc);
       lds_dma16(ds_src + (long long)tt * kH * kR, ds_lds + bi * kDsBytes + wv * 1024);
     };
     constexpr int kLoads = kWaveLoads + 1;

@@ -326,11 +326,12 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
     // tile tt's gather: every wave (attention), or half (tt even: waves 0-3, odd: 4-7)
     constexpr bool kHalf = kMode != kModeAttn;
     const int half = wv / kHalfWaves, hw = wv % kHalfWaves;
+    const TileCoords tc = tile_coords(wv, lane);
     auto issue = [&](uint32_t buf, int tt) {
       if constexpr (kHalf) {
         if ((tt & 1) == half) issue_tile_half(buf, kv, slots, tt * kR, fb, hw, lane);
       } else {
-        issue_tile(buf, kv, slots, tt * kR, fb, wv, lane);
+        issue_tile(buf, kv, slots, tt * kR, fb, wv, tc);
       }
     };
     issue(tile_lds, 0);
