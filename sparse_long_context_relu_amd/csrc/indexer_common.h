@@ -68,9 +68,9 @@ __device__ __forceinline__ void load_query(const IndexerArgs &a, int t, int col,
     }
 }
 
-// ReLU-weighted head sum of the two 32-head accumulator blocks for the key in
-// column l%32; the result is valid in every lane.
-__device__ __forceinline__ float head_reduce(const f32x16 &c0, const f32x16 &c1, const float (&wt)[2][16]) {
+// ReLU-weighted sum, for the key in column l%32, of the heads whose
+// accumulator rows this half-wave holds (the other half-wave holds the rest).
+__device__ __forceinline__ float head_partial(const f32x16 &c0, const f32x16 &c1, const float (&wt)[2][16]) {
   // ReLU as an integer max on the float's bits: non-negative floats are
   // non-negative integers, negative floats (and -0.0) negative ones.
   float p0 = 0.f, p1 = 0.f;
@@ -79,14 +79,22 @@ __device__ __forceinline__ float head_reduce(const f32x16 &c0, const f32x16 &c1,
     p0 = fmaf(wt[0][v], __int_as_float(max(__float_as_int(c0[v]), 0)), p0);
     p1 = fmaf(wt[1][v], __int_as_float(max(__float_as_int(c1[v]), 0)), p1);
   }
-  float p = p0 + p1;
+  return p0 + p1;
+}
+
+// The full head sum of the two 32-head accumulator blocks for the key in
+// column l%32; the result is valid in every lane.
+__device__ __forceinline__ float head_reduce(const f32x16 &c0, const f32x16 &c1, const float (&wt)[2][16]) {
+  const float p = head_partial(c0, c1, wt);
   return p + shfl_xor(p, 32);
 }
 
-template <int DT>
-__device__ __forceinline__ float key_scale(const IndexerArgs &a, long long slot) {
-  if (DT == DSA_FP8_E4M3FN) return a.k_scale[slot];
-  return 1.f;
+// Full head sums of two 32-key groups from their half-wave partials: lanes
+// 0..31 get key l of group 0, lanes 32..63 key l-32 of group 1 (one lane swap
+// exchanges the halves the other lanes need).
+__device__ __forceinline__ float pair_head_total(float part0, float part1) {
+  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(part0), __float_as_uint(part1), false, false);
+  return __uint_as_float(x[0]) + __uint_as_float(x[1]);
 }
 
 }  // namespace

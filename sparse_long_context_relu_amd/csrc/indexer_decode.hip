@@ -8,8 +8,9 @@
 // the head weights and the head sum are applied to the accumulators in
 // registers, so only one fp32 score per (query, key) leaves the kernel.
 //   * decode tiling: one query per workgroup row of the grid, the candidate
-//     keys split into chunks across workgroups; each wave streams 32-key
-//     tiles straight from HBM into MFMA operand registers.
+//     keys split into chunks across workgroups; each wave streams 8 KB key
+//     tiles (32 bf16 or 64 e4m3fn keys) from HBM through registers and LDS
+//     into MFMA operands.
 //   (this file; the prefill tiling and the fp32 path are in indexer.hip)
 #include "indexer_common.h"
 
@@ -20,12 +21,13 @@ constexpr int kDecodeChunk = 2048;  // keys per decode workgroup
 
 // ------------------------------------------------------------------ decode tiling
 //
-// Each wave owns 32-key tiles (kRowBytes * 32 contiguous bytes: a tile never
-// straddles a 64-token block).  It loads a tile with fully coalesced 16-byte
-// loads -- one instruction covers whole rows -- into registers one tile ahead,
-// stores it into a wave-private LDS buffer with the 16-byte chunks of row r
-// XOR-swizzled by r, and reads the MFMA operands (lane: key l%32, chunks of
-// k-group l/32) back from there without bank conflicts.
+// Each wave owns 8 KB tiles: 32 bf16 keys or 64 e4m3fn keys, contiguous
+// bytes that never straddle a 64-token block, so both types keep the same
+// bytes in flight.  A wave loads a tile with fully coalesced 16-byte loads --
+// one instruction covers whole rows -- into registers two tiles ahead, stores
+// it into a wave-private LDS buffer with the 16-byte chunks of row r
+// XOR-swizzled by r, and reads the MFMA operands (lane: key l%32 of a 32-key
+// group, chunks of k-group l/32) back from there without bank conflicts.
 
 constexpr int kDecodeWaves = 4;
 
@@ -34,8 +36,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     IndexerArgs a) {
   typedef IdxTraits<DT> Tr;
   constexpr int kChunks = Tr::kRowBytes / 16;       // 16-byte chunks per key row (16 bf16, 8 fp8)
-  constexpr int kPer = 32 * kChunks / 64;           // chunks each lane loads per tile (8 or 4)
-  __shared__ uint4 wtile[kDecodeWaves][32 * kChunks];
+  constexpr int kTileKeys = 8192 / Tr::kRowBytes;   // keys per 8 KB tile (32 bf16, 64 fp8)
+  constexpr int kGroups = kTileKeys / 32;           // 32-key MFMA groups per tile
+  constexpr int kPer = kTileKeys * kChunks / 64;    // chunks each lane loads per tile (8)
+  __shared__ uint4 wtile[kDecodeWaves][kTileKeys * kChunks];
   __shared__ uint32_t lh[kTopkBins];
 
   const int r = blockIdx.y;
@@ -52,8 +56,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int c1 = c0 + kDecodeChunk < n ? c0 + kDecodeChunk : n;
 
   const int lane = lane_id();
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar loop control
   const int g = lane >> 5, col = lane & 31;
+  const int ek = kGroups == 2 ? lane : col;         // key of the tile whose score this lane stores
   // Start-up, ordered so that the first tiles are in flight after one
   // block-table latency: the query operands and weights are loaded first (the
   // oldest loads), then the block-table entries of the chunk for the LDS copy
@@ -104,8 +109,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Every lane always loads (absent rows read the chunk's first row instead) and
   // `put` zeroes what is absent: no branches, and no register initialised
   // before a load that might be skipped.
-  auto fetch = [&](int base, long long sl0, uint4 (&st)[kPer]) {
+  // For e4m3fn the scale of key ek is loaded with the tile, ahead of its rows,
+  // so the wait for the rows covers it too.
+  auto fetch = [&](int base, long long sl0, uint4 (&st)[kPer], float &scl) {
     const long long first = sl0 >= 0 ? sl0 : 0;
+    if constexpr (DT != DSA_BF16) scl = a.k_scale[first + (base + ek < c1 ? ek : 0)];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int p = i * 64 + lane;
@@ -114,25 +122,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       st[i] = ld16(kbase + (first + rr) * Tr::kRowBytes + ch * 16);
     }
   };
-  auto put = [&](const uint4 (&st)[kPer], int base, long long sl0) {
+  // Absent rows are zeroed with an opaque all-ones / zero mask: as a select the
+  // compiler lowers this to branches with the load waits inside them, and the
+  // merged wait state at the loop head then drains the other stage as well.
+  auto put = [&](uint4 (&st)[kPer], int base, long long sl0, float &scl) {
+    if constexpr (DT != DSA_BF16) asm volatile("" : "+v"(scl));
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int p = i * 64 + lane;
       const int row = p / kChunks, ch = p % kChunks;
-      const bool ok = sl0 >= 0 && base + row < c1;
-      tile[row * kChunks + (ch ^ (row & (kChunks - 1)))] = ok ? st[i] : make_uint4(0, 0, 0, 0);
+      uint32_t m = sl0 >= 0 && base + row < c1 ? ~0u : 0u;
+      asm volatile("" : "+v"(m));
+      const uint4 v = st[i];
+      tile[row * kChunks + (ch ^ (row & (kChunks - 1)))] = make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
     }
   };
   // Two tiles in flight per wave: stage A holds tile i+1 (loaded one tile ago),
   // stage B receives tile i+2 while tile i is multiplied from LDS.  The loop is
   // unrolled by two so the stages keep fixed registers.
-  constexpr int kStep = kDecodeWaves * 32;
+  constexpr int kStep = kDecodeWaves * kTileKeys;
   uint4 sa[kPer], sb[kPer];
-  int base = c0 + wv * 32;
+  float ka = 1.f, kb = 1.f;                        // key scales of stages A and B (e4m3fn)
+  int base = c0 + wv * kTileKeys;
   long long sl0, sla, slb = -1;
   first_slots(base, base + kStep, sl0, sla);
-  fetch(base, sl0, sb);                            // tile 0, through stage B
-  fetch(base + kStep, sla, sa);                    // tile 1
+  fetch(base, sl0, sb, kb);                        // tile 0, through stage B
+  fetch(base + kStep, sla, sa, ka);                // tile 1
   // first radix digit of the top-k, counted per workgroup and added to the row's bins
   const bool hist = a.hist_mode == 1;
   if (hist)
@@ -152,12 +167,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // The query, weight and table loads and tile 0 have landed once at most the
   // loads of tile 1 are outstanding; draining them here keeps every wait for
   // them out of the loop (where it would also wait for the prefetch).
-  __builtin_amdgcn_s_waitcnt(wait_vm(kPer));
-  put(sb, base, sl0);
-  // Scores of the tile resident in LDS (valid in every lane for key col).
-  auto consume = [&]() {
+  __builtin_amdgcn_s_waitcnt(wait_vm(kPer + (DT != DSA_BF16)));
+  put(sb, base, sl0, kb);
+  float kt = kb;                                   // key scale of the tile in LDS
+  // Half-wave head partials of 32-key group h of the tile resident in LDS.
+  auto group = [&](int h) {
     typename Tr::Op kb[Tr::kSteps];
-    const uint4 *trow = tile + col * kChunks;
+    const uint4 *trow = tile + (h * 32 + col) * kChunks;
 #pragma unroll
     for (int ks = 0; ks < Tr::kSteps; ++ks) {
       if constexpr (DT == DSA_BF16) {
@@ -177,12 +193,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       c0a = Tr::mma(qa[0][ks], kb[ks], c0a);
       c1a = Tr::mma(qa[1][ks], kb[ks], c1a);
     }
-    return head_reduce(c0a, c1a, wt);
+    return head_partial(c0a, c1a, wt);
   };
-  auto emit = [&](int tb, long long tsl, float sc) {
-    const int s = tb + col;
-    if (g == 0 && s < c1) {
-      const float v = tsl >= 0 ? sc * key_scale<DT>(a, tsl + col) : neg_inf();
+  // Score of key ek of the tile resident in LDS.
+  auto consume = [&]() {
+    if constexpr (kGroups == 1) {
+      const float p = group(0);
+      return p + shfl_xor(p, 32);
+    } else {
+      return pair_head_total(group(0), group(1));
+    }
+  };
+  auto emit = [&](int tb, long long tsl, float sc, float ksc) {
+    const int s = tb + ek;
+    if ((kGroups == 2 || g == 0) && s < c1) {
+      const float v = tsl >= 0 ? (DT == DSA_BF16 ? sc : sc * ksc) : neg_inf();
       srow[s] = v;
       if (hist) atomicAdd(&lh[score_key(v) >> 21], 1u);
     }
@@ -193,18 +218,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // The fetch is unconditional (past c1 it reads slot 0 and is discarded), so
     // the compiler's wait counts stay exact on every path.
     slb = b2 < c1 ? tile_slot(b2) : -1;
-    fetch(b2, slb, sb);
+    fetch(b2, slb, sb, kb);
     float sc = consume();
-    put(sa, b1, sla);                              // the LDS reads above completed before the MFMAs
-    emit(base, sl0, sc);
-    if (b1 >= c1) break;
-    // LDS: tile b1; stage B: tile b2 (slb); tile b3 -> stage A
+    put(sa, b1, sla, ka);                          // the LDS reads above completed before the MFMAs
+    emit(base, sl0, sc, kt);
+    kt = ka;
+    // LDS: tile b1; stage B: tile b2 (slb); tile b3 -> stage A.  No exit in
+    // between: past c1 tile b1 is all zeros and its scores are not stored (an
+    // exit here would reach the loop head with stage B's loads outstanding on
+    // that path, and the wait there would drain stage A every iteration).
     const long long s1 = sla;
     sla = b3 < c1 ? tile_slot(b3) : -1;
-    fetch(b3, sla, sa);
+    fetch(b3, sla, sa, ka);
     sc = consume();
-    put(sb, b2, slb);                              // past c1 this stores zeros that are never read
-    emit(b1, s1, sc);
+    put(sb, b2, slb, kb);                          // past c1 this stores zeros that are never read
+    emit(b1, s1, sc, kt);
+    kt = kb;
     sl0 = slb;
   }
   if (hist) {
