@@ -229,9 +229,15 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   lds_barrier();
   // Slots of this split's rows (-1: absent, and past the last row), so the
-  // gather depends on LDS only.  All of a thread's positions are loaded first,
-  // then all of their block-table entries: two dependent latencies in all.
+  // gather depends on LDS only.  All of a thread's positions are loaded first.
+  // With a block table, the sequence's entries up to its last candidate are
+  // loaded at the same time (they do not depend on the positions) into the
+  // tile buffers, idle until the first gather, and looked up there: one global
+  // round trip in all.  A table too long for that room is read per position
+  // after the positions have landed: two dependent round trips.
   constexpr int kFill = (kMaxSplitRows + 4 * kR + kThreads - 1) / kThreads;
+  // block-table entries the tile buffers hold (less one pass of the copy below)
+  constexpr int kTableCap = kBufs * kTileBufChunks * 4 - 4 * kThreads;
   const int nfill = ntiles * kR + 3 * kR;
   int pos[kFill];
 #pragma unroll
@@ -239,11 +245,40 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
     const int j = threadIdx.x + u * kThreads;
     pos[u] = j < rows ? (a.dense ? i0 + j : irow[i0 + j]) : -1;
   }
+  const int nblk = (n + 63) >> 6;
   int sl[kFill];
   if (a.sv.block_table == nullptr) {
 #pragma unroll
     for (int u = 0; u < kFill; ++u)
       sl[u] = (pos[u] >= 0 && pos[u] < n) ? (int)((long long)b * a.sv.max_seq_len + pos[u]) : -1;
+  } else if (nblk <= kTableCap) {
+    const int32_t *bt = a.sv.block_table + (long long)b * a.sv.max_blocks;
+    int32_t *tbl = reinterpret_cast<int32_t *>(&tiles[0][0]);
+    // Every lane loads (entries past the last needed one read that one) and
+    // stores; entries past nblk are never looked up.  No branches.
+    // The first pass (contexts up to 128K) is straight-line code, so that its
+    // loads are not held back by a wait at a loop head.
+    const int last = nblk > 0 ? nblk - 1 : 0;
+    auto copy_pass = [&](int e0) {
+      int te[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + (int)threadIdx.x + u * kThreads;
+        te[u] = bt[e < last ? e : last];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) tbl[e0 + threadIdx.x + u * kThreads] = te[u];
+    };
+    copy_pass(0);
+    for (int e0 = 4 * kThreads; e0 < nblk; e0 += 4 * kThreads) copy_pass(e0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    lds_barrier();
+#pragma unroll
+    for (int u = 0; u < kFill; ++u) {
+      const bool ok = pos[u] >= 0 && pos[u] < n;
+      const int blk = tbl[ok ? (pos[u] >> 6) : 0];
+      sl[u] = (ok && blk >= 0 && blk < a.sv.num_blocks) ? blk * 64 + (pos[u] & 63) : -1;
+    }
   } else {
     // every lane loads (an invalid position reads the sequence's first entry),
     // so the loads are issued back to back
@@ -462,6 +497,14 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
   const float2 *ml = reinterpret_cast<const float2 *>(reinterpret_cast<const uint16_t *>(a.part) +
                                                       (long long)a.rows * ns * kH * kDv) +
                      (long long)r * ns * kH + h;
+  // The first eight splits' partials are loaded together with the (max, sum)
+  // pairs, ahead of them, so that one memory latency covers both; split
+  // indices past the last are clamped to it, and those loads are not used.
+  uint4 v[8];
+  const int slast = nm > 0 ? nm - 1 : 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    v[u] = *reinterpret_cast<const uint4 *>(po + (long long)(u < slast ? u : slast) * kH * kDv);
   float ms0 = neg_inf(), ls0 = 0.f, ms1 = neg_inf(), ls1 = 0.f;
   if (lane < nm) {
     const float2 v = ml[(long long)lane * kH];
@@ -479,12 +522,9 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
   const float L = wave_sum(w0 + w1);
   const float inv = L > 0.f ? 1.f / L : 0.f;
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < nm; s0 += 8) {
+  // splits s0..s0+7 (those below nm) added in split order
+  auto accumulate = [&](int s0) {
     const float w = s0 < 64 ? w0 : w1;
-    uint4 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (s0 + u < nm) v[u] = *reinterpret_cast<const uint4 *>(po + (long long)(s0 + u) * kH * kDv);
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       if (s0 + u < nm) {
@@ -497,6 +537,15 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
           o[2 * i + 1] = fmaf(wu, __builtin_bit_cast(float, x[i] & 0xFFFF0000u), o[2 * i + 1]);
         }
       }
+  };
+  accumulate(0);
+  for (int s0 = 8; s0 < nm; s0 += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int su = s0 + u < nm ? s0 + u : nm - 1;
+      v[u] = *reinterpret_cast<const uint4 *>(po + (long long)su * kH * kDv);
+    }
+    accumulate(s0);
   }
   uint16_t *orow = reinterpret_cast<uint16_t *>(a.out) + ((long long)t * kH + h) * kDv + lane * 8;
   uint4 pk;
