@@ -127,9 +127,14 @@ def rotation_sets(step_bytes):
     return int(min(8, max(2, 1 + math.ceil(2 * MALL_BYTES / max(step_bytes, 1)))))
 
 
-def make_sets(generate, wl, n):
-    """n seeded input sets of workload wl (set 0 is the canonical seed)."""
-    return [generate(wl, "cuda", seed=wl.seed + 7919 * j) for j in range(n)]
+def make_sets(generate, wl, n, first=None):
+    """n seeded input sets of workload wl: set 0 is the canonical seed (`first`,
+    when already generated); the others draw new values and a new block order
+    for the same decode context lengths, so every timed step has one shape and
+    the same algorithmic bytes."""
+    s0 = first if first is not None else generate(wl, "cuda")
+    lens = (s0.q_pos.to("cpu").long() + 1).tolist() if wl.mode == "decode" else None
+    return [s0] + [generate(wl, "cuda", seed=wl.seed + 7919 * j, lengths=lens) for j in range(1, n)]
 
 
 def time_forward(B, torch, inps, steps, warmup, settle_ms=0, preps=None):
@@ -273,24 +278,35 @@ def fused_prefill_stages(B, torch, pin, settle_ms, reps=2):
     return fused
 
 
-def measured_ceilings(torch):
-    """Ceilings measured with library kernels next to the vendor peaks: a streaming
-    read (a reduction over 4 GiB) and a large bf16 GEMM (8192^3)."""
+def measured_ceilings(B, torch):
+    """Ceilings measured next to the vendor peaks: streaming reads (a reduction over
+    4 GiB, and the library's read-only kernel with the decode indexer's tiling over
+    the same 4 GiB, contiguous and as scattered 16 KB blocks), a device copy and a
+    large bf16 GEMM (8192^3)."""
     x = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
     a = torch.randn((8192, 8192), device="cuda").to(torch.bfloat16)
     b = torch.randn((8192, 8192), device="cuda").to(torch.bfloat16)
     y = torch.empty_like(x)
+    sink = torch.empty(x.numel() * 4 // 131072, dtype=torch.int32, device="cuda")
     read_ms = time_op(torch, lambda: x.sum(), 10, 3, 100)
+    shape_ms = time_op(torch, lambda: B.read_ceiling(x, False, sink), 10, 3, 100)
+    paged_ms = time_op(torch, lambda: B.read_ceiling(x, True, sink), 10, 3, 100)
     copy_ms = time_op(torch, lambda: y.copy_(x), 10, 3, 100)
     gemm_ms = time_op(torch, lambda: torch.matmul(a, b), 10, 3, 200)
     gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
-    res = {"hbm_copy_gbs": round(gbs(2 * x.numel() * 4, copy_ms), 1),
-           "hbm_copy_frac_of_spec": round(gbs(2 * x.numel() * 4, copy_ms) / HBM_PEAK_GBS, 4),
-           "hbm_reduce_read_gbs": round(gbs(x.numel() * 4, read_ms), 1),
+    nb = x.numel() * 4
+    res = {"hbm_copy_gbs": round(gbs(2 * nb, copy_ms), 1),
+           "hbm_copy_frac_of_spec": round(gbs(2 * nb, copy_ms) / HBM_PEAK_GBS, 4),
+           "hbm_reduce_read_gbs": round(gbs(nb, read_ms), 1),
+           "indexer_shape_read_gbs": round(gbs(nb, shape_ms), 1),
+           "indexer_shape_paged_read_gbs": round(gbs(nb, paged_ms), 1),
+           "indexer_shape_paged_read_frac_of_spec": round(gbs(nb, paged_ms) / HBM_PEAK_GBS, 4),
            "bf16_gemm_tflops": round(2 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
            "bf16_gemm_frac_of_spec": round(2 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
-           "how": "device copy of 4 GiB (read + write bytes); torch sum over the same 4 GiB; torch.matmul of two "
-                  "8192x8192 bf16 matrices"}
+           "how": "device copy of 4 GiB (read + write bytes); torch sum over the same 4 GiB; dsa_read_ceiling over "
+                  "the same 4 GiB (the decode indexer's tiling with no arithmetic: 8 KB tiles, two in flight per "
+                  "wave; paged = 16 KB blocks in a scattered order); torch.matmul of two 8192x8192 bf16 matrices"}
+    del sink
     del x, y, a, b
     torch.cuda.empty_cache()
     return res
@@ -657,7 +673,7 @@ def main():
     wl = WORKLOADS[name]
     log(f"generating {name} on cuda:0")
     inp = generate(wl, "cuda")
-    sets = [inp] + make_sets(generate, wl, n_sets(inp))[1:]
+    sets = make_sets(generate, wl, n_sets(inp), first=inp)
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps after {args.warmup} warm-up steps, cycling {len(sets)} input sets")
     ms, stages = time_forward(B, torch, sets, args.steps, args.warmup, args.settle_ms)
@@ -723,7 +739,7 @@ def main():
         the step)."""
         log(f"secondary: {name}")
         din = generate(WORKLOADS[name], "cuda")
-        dsets = [din] + make_sets(generate, WORKLOADS[name], n_sets(din))[1:]
+        dsets = make_sets(generate, WORKLOADS[name], n_sets(din), first=din)
         T, HI, DI = din.num_q, din.wl.index_heads, din.wl.index_dim
         preps, extra = None, 0
         if fp8_prep:
@@ -800,7 +816,11 @@ def main():
         inp = None
         torch.cuda.empty_cache()
         log("measured ceilings")
-        result["measured_ceilings"] = measured_ceilings(torch)
+        result["measured_ceilings"] = mc = measured_ceilings(B, torch)
+        if result["roofline"].get("bound") == "hbm" and wl.paged:
+            # the dominant kernel against the read rate its own access shape reaches with no arithmetic
+            result["roofline"]["frac_of_measured_shape_read"] = round(
+                result["roofline"]["achieved"] / mc["indexer_shape_paged_read_gbs"], 4)
     if not args.no_cpu_baseline:
         if inp is None:
             inp = generate(wl, "cuda")

@@ -29,7 +29,7 @@ EXPORTS = ("dsa_workspace_size", "dsa_index_scores", "dsa_topk", "dsa_sparse_mla
            "dsa_forward_noalloc",
            "dsa_dense_mla", "dsa_attention_probs", "dsa_indexer_kl", "dsa_indexer_backward", "dsa_indexer_kl_loss", "dsa_forward_chunk_rows",
            "dsa_quantize_fp8", "dsa_append_index_keys", "dsa_sparse_mla_backward", "dsa_sparse_indexer_kl",
-           "dsa_status_string")
+           "dsa_read_ceiling", "dsa_status_string")
 
 
 class DsaSeqs(ctypes.Structure):
@@ -106,6 +106,8 @@ def _load() -> ctypes.CDLL:
     lib.dsa_sparse_mla_backward.restype = ctypes.c_int
     lib.dsa_sparse_indexer_kl.argtypes = [sp, P, I64, P, I32, P, P, P]
     lib.dsa_sparse_indexer_kl.restype = ctypes.c_int
+    lib.dsa_read_ceiling.argtypes = [P, I64, I32, P, P]
+    lib.dsa_read_ceiling.restype = ctypes.c_int
     lib.dsa_status_string.argtypes = [ctypes.c_int]
     lib.dsa_status_string.restype = ctypes.c_char_p
     return lib
@@ -397,6 +399,18 @@ def quantize_fp8(src: torch.Tensor, scale_repeat: int = 1, dst=None, scale=None,
                               _stream(stream))
     _check(st, "dsa_quantize_fp8")
     return dst, scale
+
+
+def read_ceiling(src: torch.Tensor, paged: bool, sink=None, stream=None) -> torch.Tensor:
+    """Stream src's bytes with the decode indexer's read shape (a measurement aid);
+    returns the per-wave XOR words [nbytes / 131072] (uint32 as int32)."""
+    assert src.is_contiguous()
+    nbytes = src.numel() * src.element_size()
+    if sink is None:
+        sink = torch.empty(max(nbytes // 131072, 1), dtype=torch.int32, device=src.device)
+    st = LIB.dsa_read_ceiling(_ptr(src), nbytes, int(paged), _ptr(sink), _stream(stream))
+    _check(st, "dsa_read_ceiling")
+    return sink
 
 
 def append_index_keys(pb: Problem, k_new: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tensor, stream=None):

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libdsa.so")
 SOURCES = ["dsa_api.hip", "indexer.hip", "indexer_decode.hip", "topk.hip", "sparse_mla.hip", "quantize.hip",
-           "loss.hip", "sparse_bwd.hip"]
+           "loss.hip", "sparse_bwd.hip", "ceiling.hip"]
 HEADERS = ["common.h", "kernels.h", "indexer_common.h", "mla_tile.h"]
 
 # Kernels whose machine code is fingerprinted at build time: a record measured

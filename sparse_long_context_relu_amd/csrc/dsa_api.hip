@@ -2,6 +2,7 @@
 // and kernel orchestration on the caller's stream.  See include/dsa.h for the
 // contract of every entry point.
 #include <mutex>
+#include <stdint.h>
 
 #include "kernels.h"
 
@@ -831,6 +832,15 @@ DSA_EXPORT int dsa_append_index_keys(const dsa_seqs *seqs, int32_t index_dim, in
   a.cache = reinterpret_cast<uint8_t *>(k_cache);
   a.scale = k_scale;
   return hip_status(launch_fp8_append(a, stream));
+}
+
+DSA_EXPORT int dsa_read_ceiling(const void *src, int64_t bytes, int32_t paged, uint32_t *sink, hipStream_t stream) {
+  if (src == nullptr || sink == nullptr || bytes <= 0 || (reinterpret_cast<uintptr_t>(src) & 15) != 0)
+    return DSA_ERR_INVALID_ARG;
+  if (bytes % kReadCeilingChunk != 0 || bytes / kReadCeilingChunk > INT32_MAX) return DSA_ERR_UNSUPPORTED;
+  const int64_t nblk = bytes / 16384;
+  if (paged && (nblk & (nblk - 1)) != 0) return DSA_ERR_UNSUPPORTED;
+  return hip_status(launch_read_ceiling(src, bytes, paged != 0, sink, stream));
 }
 
 DSA_EXPORT const char *dsa_status_string(int status) {

@@ -276,6 +276,19 @@ def test_quantize_and_append_validation():
     assert L.dsa_append_index_keys(None, 128, B.BF16, fake, fake, fake, None) == B.ERR_INVALID_ARG
 
 
+def test_read_ceiling_validation():
+    """Host-side checks of the read-rate measurement entry point (no launch)."""
+    L, P = B.LIB, ctypes.c_void_p
+    fake = P(0x1000)
+    chunk = 512 * 1024
+    assert L.dsa_read_ceiling(None, chunk, 0, fake, None) == B.ERR_INVALID_ARG
+    assert L.dsa_read_ceiling(fake, chunk, 0, None, None) == B.ERR_INVALID_ARG
+    assert L.dsa_read_ceiling(P(0x1008), chunk, 0, fake, None) == B.ERR_INVALID_ARG   # src not 16-byte aligned
+    assert L.dsa_read_ceiling(fake, 0, 0, fake, None) == B.ERR_INVALID_ARG
+    assert L.dsa_read_ceiling(fake, chunk + 16, 0, fake, None) == B.ERR_UNSUPPORTED
+    assert L.dsa_read_ceiling(fake, 3 * chunk, 1, fake, None) == B.ERR_UNSUPPORTED    # 96 blocks: not a power of two
+
+
 def test_status_strings():
     for s in (B.OK, B.ERR_INVALID_ARG, B.ERR_UNSUPPORTED, B.ERR_WORKSPACE, B.ERR_HIP):
         assert B.status_string(s).startswith("DSA_")
