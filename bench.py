@@ -291,6 +291,8 @@ def measured_ceilings(B, torch):
     read_ms = time_op(torch, lambda: x.sum(), 10, 3, 100)
     shape_ms = time_op(torch, lambda: B.read_ceiling(x, False, sink), 10, 3, 100)
     paged_ms = time_op(torch, lambda: B.read_ceiling(x, True, sink), 10, 3, 100)
+    cached_ms = time_op(torch, lambda: B.read_ceiling(x, False, sink, cached=True), 10, 3, 100)
+    cached_paged_ms = time_op(torch, lambda: B.read_ceiling(x, True, sink, cached=True), 10, 3, 100)
     copy_ms = time_op(torch, lambda: y.copy_(x), 10, 3, 100)
     gemm_ms = time_op(torch, lambda: torch.matmul(a, b), 10, 3, 200)
     gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
@@ -301,11 +303,14 @@ def measured_ceilings(B, torch):
            "indexer_shape_read_gbs": round(gbs(nb, shape_ms), 1),
            "indexer_shape_paged_read_gbs": round(gbs(nb, paged_ms), 1),
            "indexer_shape_paged_read_frac_of_spec": round(gbs(nb, paged_ms) / HBM_PEAK_GBS, 4),
+           "indexer_shape_cached_loads_read_gbs": round(gbs(nb, cached_ms), 1),
+           "indexer_shape_cached_loads_paged_read_gbs": round(gbs(nb, cached_paged_ms), 1),
            "bf16_gemm_tflops": round(2 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
            "bf16_gemm_frac_of_spec": round(2 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
            "how": "device copy of 4 GiB (read + write bytes); torch sum over the same 4 GiB; dsa_read_ceiling over "
                   "the same 4 GiB (the decode indexer's tiling with no arithmetic: 8 KB tiles, two in flight per "
-                  "wave; paged = 16 KB blocks in a scattered order); torch.matmul of two 8192x8192 bf16 matrices"}
+                  "wave, streaming loads as the indexer issues them, or default-policy loads (cached_loads); "
+                  "paged = 16 KB blocks in a scattered order); torch.matmul of two 8192x8192 bf16 matrices"}
     del sink
     del x, y, a, b
     torch.cuda.empty_cache()

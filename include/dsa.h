@@ -403,16 +403,19 @@ int dsa_append_index_keys(const dsa_seqs *seqs, int32_t index_dim, int32_t src_d
  * at `src` with the decode indexer's read shape and no arithmetic, so that its
  * duration gives the HBM read rate that shape can reach.  One 256-thread
  * workgroup per 512 KB (524288 B) chunk; its four waves read the chunk's 8 KB
- * tiles w, w+4, ... with two tiles in flight and 16-byte loads.  With `paged`
- * nonzero, the buffer is read as 16 KB (64-key) blocks scattered over it:
- * block b comes from physical block (b * 0x9E3779B1) mod (bytes / 16384),
- * which must then be a power of two.  Each wave writes the XOR of every
- * 32-bit word it read to sink[chunk * 4 + wave] (bytes / 131072 entries,
- * owned by the caller), so the reads are observable.  src must be 16-byte
- * aligned; bytes a positive multiple of 524288.  Errors: DSA_ERR_INVALID_ARG
- * (null pointers, misaligned src, bytes <= 0), DSA_ERR_UNSUPPORTED (other
+ * tiles w, w+4, ... with two tiles in flight and 16-byte streaming
+ * (nontemporal) loads, as the indexer does.  `flags`: DSA_READ_PAGED reads the
+ * buffer as 16 KB (64-key) blocks scattered over it: block b comes from
+ * physical block (b * 0x9E3779B1) mod (bytes / 16384), which must then be a
+ * power of two; DSA_READ_CACHED uses loads with the default cache policy
+ * instead of streaming ones.  Each wave writes the XOR of every 32-bit word it
+ * read to sink[chunk * 4 + wave] (bytes / 131072 entries, owned by the
+ * caller), so the reads are observable.  src must be 16-byte aligned; bytes a
+ * positive multiple of 524288.  Errors: DSA_ERR_INVALID_ARG (null pointers,
+ * misaligned src, bytes <= 0, unknown flags), DSA_ERR_UNSUPPORTED (other
  * sizes).  No workspace. */
-int dsa_read_ceiling(const void *src, int64_t bytes, int32_t paged, uint32_t *sink, hipStream_t stream);
+enum { DSA_READ_PAGED = 1, DSA_READ_CACHED = 2 };
+int dsa_read_ceiling(const void *src, int64_t bytes, int32_t flags, uint32_t *sink, hipStream_t stream);
 
 /* Static string naming a dsa_status value. */
 const char *dsa_status_string(int status);

@@ -401,14 +401,16 @@ def quantize_fp8(src: torch.Tensor, scale_repeat: int = 1, dst=None, scale=None,
     return dst, scale
 
 
-def read_ceiling(src: torch.Tensor, paged: bool, sink=None, stream=None) -> torch.Tensor:
-    """Stream src's bytes with the decode indexer's read shape (a measurement aid);
-    returns the per-wave XOR words [nbytes / 131072] (uint32 as int32)."""
+def read_ceiling(src: torch.Tensor, paged: bool, sink=None, stream=None, cached: bool = False) -> torch.Tensor:
+    """Stream src's bytes with the decode indexer's read shape (a measurement aid;
+    `cached`: default-policy loads instead of streaming ones); returns the
+    per-wave XOR words [nbytes / 131072] (uint32 as int32)."""
     assert src.is_contiguous()
     nbytes = src.numel() * src.element_size()
     if sink is None:
         sink = torch.empty(max(nbytes // 131072, 1), dtype=torch.int32, device=src.device)
-    st = LIB.dsa_read_ceiling(_ptr(src), nbytes, int(paged), _ptr(sink), _stream(stream))
+    st = LIB.dsa_read_ceiling(_ptr(src), nbytes, (1 if paged else 0) | (2 if cached else 0), _ptr(sink),
+                              _stream(stream))
     _check(st, "dsa_read_ceiling")
     return sink
 

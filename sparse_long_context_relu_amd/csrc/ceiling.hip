@@ -8,8 +8,10 @@
 // 16 KB blocks (64 keys) are scattered over the buffer as a paged key cache
 // is: block b of the buffer's sequence of blocks is read from physical block
 // (b * 0x9E3779B1) mod nblk, a bijection since nblk is a power of two and the
-// multiplier odd.  Every word read is folded into an XOR that the wave
-// writes out, so no load is dead.
+// multiplier odd.  The loads are streaming (nontemporal) loads as in the
+// indexer; with `cached` they use the default cache policy instead, which
+// shows what the streaming policy gains.  Every word read is folded into an
+// XOR that the wave writes out, so no load is dead.
 #include "kernels.h"
 
 namespace dsa {
@@ -20,7 +22,7 @@ constexpr int kTilesPerChunk = kReadCeilingChunk / kTileBytes;   // 64
 constexpr int kWaveTiles = kTilesPerChunk / 4;                   // 16 per wave
 constexpr int kLoads = kTileBytes / (64 * 16);                   // 8 per lane and tile
 
-template <bool kPaged>
+template <bool kPaged, bool kStream>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void read_ceiling_kernel(
     const uint8_t *src, long long nblk, uint32_t *sink) {
   const int lane = lane_id();
@@ -30,7 +32,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const long long phys = kPaged ? ((((g >> 1) * 0x9E3779B1LL) & (nblk - 1)) << 1) | (g & 1) : g;
     const uint8_t *p = src + phys * kTileBytes + lane * 16;
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) st[i] = ld16(p + i * 1024);
+    for (int i = 0; i < kLoads; ++i) st[i] = kStream ? ld16_stream(p + i * 1024) : ld16(p + i * 1024);
   };
   uint32_t acc = 0;
   auto fold = [&](const uint4 (&st)[kLoads]) {
@@ -55,14 +57,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 }  // namespace
 
-hipError_t launch_read_ceiling(const void *src, long long bytes, bool paged, uint32_t *sink, hipStream_t st) {
+hipError_t launch_read_ceiling(const void *src, long long bytes, bool paged, bool cached, uint32_t *sink,
+                               hipStream_t st) {
   const long long chunks = bytes / kReadCeilingChunk;
   const long long nblk = bytes / (2 * kTileBytes);
   const uint8_t *s = reinterpret_cast<const uint8_t *>(src);
-  if (paged)
-    hipLaunchKernelGGL(read_ceiling_kernel<true>, dim3((unsigned)chunks), dim3(256), 0, st, s, nblk, sink);
+  const dim3 grid((unsigned)chunks);
+  if (paged && cached)
+    hipLaunchKernelGGL((read_ceiling_kernel<true, false>), grid, dim3(256), 0, st, s, nblk, sink);
+  else if (paged)
+    hipLaunchKernelGGL((read_ceiling_kernel<true, true>), grid, dim3(256), 0, st, s, nblk, sink);
+  else if (cached)
+    hipLaunchKernelGGL((read_ceiling_kernel<false, false>), grid, dim3(256), 0, st, s, nblk, sink);
   else
-    hipLaunchKernelGGL(read_ceiling_kernel<false>, dim3((unsigned)chunks), dim3(256), 0, st, s, nblk, sink);
+    hipLaunchKernelGGL((read_ceiling_kernel<false, true>), grid, dim3(256), 0, st, s, nblk, sink);
   return hipGetLastError();
 }
 

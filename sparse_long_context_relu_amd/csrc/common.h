@@ -225,6 +225,15 @@ __device__ __forceinline__ V zero_vec() {
 
 // 16-byte global load / store helpers.
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// 16-byte streaming load (the nontemporal cache policy: data read once).  On
+// this part a stream of such loads reaches a higher HBM read rate than the same
+// loads with the default policy (about 7.0 against 6.2 TB/s for 8 KB tiles).
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const void *p) {
+  const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v *>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 __device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }

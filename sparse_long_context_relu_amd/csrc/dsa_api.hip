@@ -834,13 +834,15 @@ DSA_EXPORT int dsa_append_index_keys(const dsa_seqs *seqs, int32_t index_dim, in
   return hip_status(launch_fp8_append(a, stream));
 }
 
-DSA_EXPORT int dsa_read_ceiling(const void *src, int64_t bytes, int32_t paged, uint32_t *sink, hipStream_t stream) {
-  if (src == nullptr || sink == nullptr || bytes <= 0 || (reinterpret_cast<uintptr_t>(src) & 15) != 0)
+DSA_EXPORT int dsa_read_ceiling(const void *src, int64_t bytes, int32_t flags, uint32_t *sink, hipStream_t stream) {
+  if (src == nullptr || sink == nullptr || bytes <= 0 || (reinterpret_cast<uintptr_t>(src) & 15) != 0 ||
+      (flags & ~(DSA_READ_PAGED | DSA_READ_CACHED)) != 0)
     return DSA_ERR_INVALID_ARG;
   if (bytes % kReadCeilingChunk != 0 || bytes / kReadCeilingChunk > INT32_MAX) return DSA_ERR_UNSUPPORTED;
   const int64_t nblk = bytes / 16384;
+  const bool paged = (flags & DSA_READ_PAGED) != 0;
   if (paged && (nblk & (nblk - 1)) != 0) return DSA_ERR_UNSUPPORTED;
-  return hip_status(launch_read_ceiling(src, bytes, paged != 0, sink, stream));
+  return hip_status(launch_read_ceiling(src, bytes, paged, (flags & DSA_READ_CACHED) != 0, sink, stream));
 }
 
 DSA_EXPORT const char *dsa_status_string(int status) {

@@ -102,7 +102,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     sA = (bA < c1 && kA >= 0 && kA < a.sv.num_blocks) ? (long long)kA * 64 + (bA & 63) : -1;
     sB = (bB < c1 && kB >= 0 && kB < a.sv.num_blocks) ? (long long)kB * 64 + (bB & 63) : -1;
   };
-  // Coalesced fetch of the tile at key `base`: lane l takes chunk (i*64 + l) of
+  // Coalesced fetch of the tile at key `base` (streaming loads: each key is
+  // read once per query): lane l takes chunk (i*64 + l) of
   // the tile for i < kPer, i.e. row (i*64 + l) / kChunks.  A tile lies inside
   // one 64-token block, so one wave-uniform lookup gives the slot of its first
   // row and the others follow.  Rows past c1 or in an absent block load zeros.
@@ -113,13 +114,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // so the wait for the rows covers it too.
   auto fetch = [&](int base, long long sl0, uint4 (&st)[kPer], float &scl) {
     const long long first = sl0 >= 0 ? sl0 : 0;
-    if constexpr (DT != DSA_BF16) scl = a.k_scale[first + (base + ek < c1 ? ek : 0)];
+    if constexpr (DT != DSA_BF16) scl = __builtin_nontemporal_load(&a.k_scale[first + (base + ek < c1 ? ek : 0)]);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int p = i * 64 + lane;
       const int row = p / kChunks, ch = p % kChunks;
       const int rr = base + row < c1 ? row : 0;
-      st[i] = ld16(kbase + (first + rr) * Tr::kRowBytes + ch * 16);
+      st[i] = ld16_stream(kbase + (first + rr) * Tr::kRowBytes + ch * 16);
     }
   };
   // Absent rows are zeroed with an opaque all-ones / zero mask: as a select the

@@ -204,6 +204,7 @@ hipError_t launch_fp8_append(const AppendArgs &a, hipStream_t s);
 // Read-rate measurement with the decode indexer's access shape (ceiling.hip):
 // one workgroup per kReadCeilingChunk bytes, one XOR word per wave into sink.
 constexpr long long kReadCeilingChunk = 512 * 1024;
-hipError_t launch_read_ceiling(const void *src, long long bytes, bool paged, uint32_t *sink, hipStream_t s);
+hipError_t launch_read_ceiling(const void *src, long long bytes, bool paged, bool cached, uint32_t *sink,
+                               hipStream_t s);
 
 }  // namespace dsa

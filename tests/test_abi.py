@@ -287,6 +287,9 @@ def test_read_ceiling_validation():
     assert L.dsa_read_ceiling(fake, 0, 0, fake, None) == B.ERR_INVALID_ARG
     assert L.dsa_read_ceiling(fake, chunk + 16, 0, fake, None) == B.ERR_UNSUPPORTED
     assert L.dsa_read_ceiling(fake, 3 * chunk, 1, fake, None) == B.ERR_UNSUPPORTED    # 96 blocks: not a power of two
+    assert L.dsa_read_ceiling(fake, 3 * chunk, 3, fake, None) == B.ERR_UNSUPPORTED    # paged + cached: same check
+    assert L.dsa_read_ceiling(fake, chunk, 4, fake, None) == B.ERR_INVALID_ARG        # unknown flag bit
+    assert L.dsa_read_ceiling(fake, chunk, -1, fake, None) == B.ERR_INVALID_ARG
 
 
 def test_status_strings():

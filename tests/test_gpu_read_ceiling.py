@@ -1,6 +1,7 @@
 """The read-rate measurement entry point (dsa_read_ceiling) reads what it says:
 every wave's XOR word equals the XOR of the 8 KB tiles that the indexer's tiling
-assigns to it, through the scattered-block mapping when paged."""
+assigns to it, through the scattered-block mapping when paged, with streaming
+and with default-policy loads."""
 import numpy as np
 import pytest
 import torch
@@ -30,12 +31,13 @@ def expected_words(words: np.ndarray, nbytes: int, paged: bool) -> np.ndarray:
     return np.array(out, dtype=np.uint32)
 
 
+@pytest.mark.parametrize("cached", [False, True])
 @pytest.mark.parametrize("paged", [False, True])
-def test_read_ceiling_reads_every_word(paged):
+def test_read_ceiling_reads_every_word(paged, cached):
     nbytes = 4 << 20
     gen = torch.Generator().manual_seed(11)
     host = torch.randint(-(2 ** 31), 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, generator=gen)
-    sink = B.read_ceiling(host.cuda(), paged)
+    sink = B.read_ceiling(host.cuda(), paged, cached=cached)
     torch.cuda.synchronize()
     got = sink.cpu().numpy().view(np.uint32)
     assert np.array_equal(got, expected_words(host.numpy().view(np.uint32), nbytes, paged))
