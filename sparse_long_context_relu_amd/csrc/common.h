@@ -38,6 +38,15 @@ __device__ __forceinline__ void lds_dma16(const void *gsrc, uint32_t m0) {
                : "memory", "m0");
 }
 
+// The same load with the streaming (nontemporal) cache policy, for rows that
+// are read once.
+__device__ __forceinline__ void lds_dma16_stream(const void *gsrc, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+               :
+               : "s"(m0), "v"(gsrc)
+               : "memory", "m0");
+}
+
 // The 4-byte form: lane l's 4 bytes land at LDS address m0 + 4 l.
 __device__ __forceinline__ void lds_dma4(const void *gsrc, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"

@@ -147,16 +147,22 @@ __device__ __forceinline__ TileLoads tile_loads(const uint8_t *kv, const int *sl
   return t;
 }
 
-// The wave's j-th load of a tile into the buffer at LDS address `tile`.
+// The wave's j-th load of a tile into the buffer at LDS address `tile`
+// (kStream: streaming loads, for rows that no other workgroup reads again).
+template <bool kStream = false>
 __device__ __forceinline__ void tile_load(const TileLoads &t, int j, uint32_t tile, int wv) {
-  lds_dma16(t.src[j], tile + (j * kWaves + wv) * 1024);
+  if constexpr (kStream)
+    lds_dma16_stream(t.src[j], tile + (j * kWaves + wv) * 1024);
+  else
+    lds_dma16(t.src[j], tile + (j * kWaves + wv) * 1024);
 }
 
+template <bool kStream = false>
 __device__ __forceinline__ void issue_tile(uint32_t tile, const uint8_t *kv, const int *slots, int j0,
                                            int fallback, int wv, const TileCoords &c) {
   const TileLoads t = tile_loads(kv, slots, j0, fallback, c);
 #pragma unroll
-  for (int j = 0; j < kWaveLoads; ++j) tile_load(t, j, tile, wv);
+  for (int j = 0; j < kWaveLoads; ++j) tile_load<kStream>(t, j, tile, wv);
 }
 
 // The same gather issued by half of the waves (h = wave index within the half,

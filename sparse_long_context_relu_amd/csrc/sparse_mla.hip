@@ -172,8 +172,9 @@ __device__ __forceinline__ void consume_tile(uint32_t tile, const int *slots, in
 
 // One workgroup per (group of kQ query rows, split of their lists); kQ > 1
 // only for the lse and probs passes of a prefill (dense lists of sequence 0,
-// one tile serving every query of the group).
-template <int kMode, int kQ>
+// one tile serving every query of the group).  kStream: the rows are gathered
+// with streaming loads (decode: no other query of the launch reads them).
+template <int kMode, int kQ, bool kStream = false>
 __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
   __shared__ uint4 tiles[kBufs][kTileBufChunks];
   __shared__ int slots[kMaxSplitRows + 4 * kR];
@@ -366,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void mla_bf16_kernel(MlaArgs a) {
       if constexpr (kHalf) {
         if ((tt & 1) == half) issue_tile_half(buf, kv, slots, tt * kR, fb, hw, lane);
       } else {
-        issue_tile(buf, kv, slots, tt * kR, fb, wv, tc);
+        issue_tile<kStream>(buf, kv, slots, tt * kR, fb, wv, tc);
       }
     };
     issue(tile_lds, 0);
@@ -704,7 +705,10 @@ hipError_t launch_sparse_mla(const MlaArgs &a, hipStream_t st) {
     else
       hipLaunchKernelGGL((mla_bf16_kernel<kModeProbs, 1>), grid, dim3(kThreads), 0, st, a);
   } else {
-    hipLaunchKernelGGL((mla_bf16_kernel<kModeAttn, 1>), grid, dim3(kThreads), 0, st, a);
+    if (a.sv.mode == DSA_DECODE)
+      hipLaunchKernelGGL((mla_bf16_kernel<kModeAttn, 1, true>), grid, dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((mla_bf16_kernel<kModeAttn, 1>), grid, dim3(kThreads), 0, st, a);
     if (a.n_split > 1) hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(kH / 4) * (unsigned)a.rows), dim3(256), 0, st, a);
   }
   return hipGetLastError();
