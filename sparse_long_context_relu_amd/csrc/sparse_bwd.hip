@@ -368,10 +368,11 @@ __global__ __launch_bounds__(kThreads) void bwd_contrib_kernel(MlaBwdArgs a) {
     }
   }
   if (!active) return;
+  // streaming stores: the rows are read back once, by the key-major reduction
   float *crow = a.contrib + ((long long)r * a.k + jb + col) * kD;
 #pragma unroll
   for (int db = 0; db < kDbAll; ++db)
-    *reinterpret_cast<float4 *>(crow + db * 16 + 4 * g) = make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+    __builtin_nontemporal_store(acc[db], reinterpret_cast<f32x4 *>(crow + db * 16 + 4 * g));
 }
 
 // ---------------------------------------------------------------- the reduction into the cache rows
@@ -408,16 +409,31 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(MlaBwdArgs a) {
 #pragma unroll
   for (int u = 0; u < kD / 64; ++u) acc[u] = 0.f;
   const uint16_t *jrow = a.jpos + (long long)s * a.jstride;
+  // Two rows' loads in flight at a time (streaming loads: each row is read
+  // once); they are still added in ascending query order.
   for (int t0 = 0; t0 < a.rows; t0 += 64) {
     const int jv = t0 + lane < a.rows ? (int)jrow[t0 + lane] : (int)kNoSlot;
     unsigned long long m = __ballot(jv != kNoSlot);
     while (m) {
-      const int b = __ffsll((long long)m) - 1;
+      const int b0 = __ffsll((long long)m) - 1;
       m &= m - 1;
-      const int j = __builtin_amdgcn_readlane(jv, b);
-      const float *c = a.contrib + ((long long)(t0 + b) * a.k + j) * kD + lane;
+      const bool two = m != 0;
+      const int b1 = two ? __ffsll((long long)m) - 1 : b0;
+      if (two) m &= m - 1;
+      const int j0 = __builtin_amdgcn_readlane(jv, b0), j1 = __builtin_amdgcn_readlane(jv, b1);
+      const float *c0 = a.contrib + ((long long)(t0 + b0) * a.k + j0) * kD + lane;
+      const float *c1 = a.contrib + ((long long)(t0 + b1) * a.k + j1) * kD + lane;
+      float x0[kD / 64], x1[kD / 64];
 #pragma unroll
-      for (int u = 0; u < kD / 64; ++u) acc[u] += c[64 * u];
+      for (int u = 0; u < kD / 64; ++u) {
+        x0[u] = __builtin_nontemporal_load(c0 + 64 * u);
+        x1[u] = __builtin_nontemporal_load(c1 + 64 * u);
+      }
+#pragma unroll
+      for (int u = 0; u < kD / 64; ++u) {
+        acc[u] += x0[u];
+        if (two) acc[u] += x1[u];
+      }
     }
   }
   float *drow = a.dkv + slot * kD + lane;

@@ -29,7 +29,7 @@ namespace {
 
 constexpr int kNT = 256;
 constexpr int kRowNT = 512;
-constexpr int kLdsCap = 8192;    // candidates held in LDS by the one-workgroup-per-row path
+constexpr int kLdsCap = 2048;    // candidates held in LDS by the one-workgroup-per-row path (4 workgroups per CU at 64K)
 constexpr int kTieCap = 4096;    // second-digit ties held in LDS by the sliced select
 
 struct RowWs {
@@ -508,9 +508,14 @@ __global__ __launch_bounds__(kRowNT) void topk_select_sliced_kernel(TopkArgs a) 
   compact_selection<kRowNT>(selmap, eqmap, W, quota, m, a.k, out, tmp);
 }
 
-// One workgroup per row (many rows): collect the row itself (selected keys
-// straight into the bitmap, candidates into LDS), then the exact threshold
-// among the candidates and the compaction.
+// One workgroup per row (many rows): one pass over the row selects the keys
+// above the top digit straight into the bitmap, counts the second-digit
+// histogram of the candidates (keys in the top digit) and keeps the candidates
+// in LDS while they fit.  The second digit then comes from that histogram.  The
+// third-digit histogram runs over the candidates in LDS or, when they did not
+// fit, over a second pass of the row that also keeps the ties of the second
+// digit in LDS (a third pass only when those do not fit either); then the
+// exact threshold and the compaction.
 __global__ __launch_bounds__(kRowNT) void topk_select_rows_kernel(TopkArgs a) {
   extern __shared__ uint32_t smem[];
   const int r = blockIdx.x;
@@ -526,7 +531,7 @@ __global__ __launch_bounds__(kRowNT) void topk_select_rows_kernel(TopkArgs a) {
   uint32_t *selmap = smem;
   uint32_t *eqmap = smem + Wmax;
   uint32_t *h = smem + 2 * Wmax;                 // kTopkBins words
-  uint32_t *lcand = h + kTopkBins;               // 2 * kLdsCap words: the candidates
+  uint32_t *lcand = h + kTopkBins;               // 2 * kLdsCap words: (low 21 key bits, position)
   __shared__ int res[6];
   __shared__ int tmp[kRowNT / 64];
   __shared__ uint32_t lcount;
@@ -550,62 +555,83 @@ __global__ __launch_bounds__(kRowNT) void topk_select_rows_kernel(TopkArgs a) {
   find_digit<kRowNT>(h, kTopkBins, m, res, tmp);
   const uint32_t d1 = (uint32_t)res[0];
   const int need = m - res[1];                   // still to take among the candidates (>= 1)
+  for (int i = threadIdx.x; i < kTopkBins; i += kRowNT) h[i] = 0u;
+  __syncthreads();
 
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  scan_row<kRowNT>(row, 0, n, [&](int s, uint32_t key, bool valid) {
-    const uint32_t dig = key >> 21;
-    if (valid && dig > d1) atomicOr(&selmap[s >> 5], 1u << (s & 31));
-    const bool is_cand = valid && dig == d1;
-    const unsigned long long mc = __ballot(is_cand);
+  // Appends (low key bits, position) of the lanes with `take` to the LDS list.
+  auto append = [&](bool take, uint32_t lo, int s) {
+    const unsigned long long mc = __ballot(take);
     if (mc == 0ull) return;
     uint32_t bc = 0u;
     if (lane == 0) bc = atomicAdd(&lcount, (uint32_t)__popcll(mc));
     bc = __shfl(bc, 0, kWave);
-    if (is_cand) {
+    if (take) {
       const uint32_t pos = bc + __popcll(mc & below);
       if (pos < (uint32_t)kLdsCap) {
-        lcand[2 * pos] = key & 0x1fffffu;
+        lcand[2 * pos] = lo;
         lcand[2 * pos + 1] = (uint32_t)s;
       }
     }
+  };
+  // ---- pass 1: selected keys, second-digit histogram and list of the candidates
+  scan_row<kRowNT>(row, 0, n, [&](int s, uint32_t key, bool valid) {
+    const uint32_t dig = key >> 21;
+    if (valid && dig > d1) atomicOr(&selmap[s >> 5], 1u << (s & 31));
+    const bool is_cand = valid && dig == d1;
+    if (is_cand) atomicAdd(&h[(key >> 10) & (kTopkBins - 1)], 1u);
+    append(is_cand, key & 0x1fffffu, s);
   });
   __syncthreads();
-  const int ncand = (int)lcount <= kLdsCap ? (int)lcount : -1;
-  // Visit every candidate (low 21 key bits, position): from the LDS list, or by
-  // rescanning the row when the list overflowed.
-  auto for_each_cand = [&](auto &&f) {
-    if (ncand >= 0) {
-      for (int i = threadIdx.x; i < ncand; i += kRowNT) f(lcand[2 * i], lcand[2 * i + 1]);
-    } else {
-      for (int s = threadIdx.x; s < n; s += kRowNT) {
-        const uint32_t key = score_key(row[s]);
-        if ((key >> 21) == d1) f(key & 0x1fffffu, (uint32_t)s);
-      }
-    }
-  };
-
+  const bool fit = lcount <= (uint32_t)kLdsCap;   // every candidate is in the list
   // ---- second digit key[20:10]
-  for (int i = threadIdx.x; i < kTopkBins; i += kRowNT) h[i] = 0u;
-  __syncthreads();
-  for_each_cand([&](uint32_t lo, uint32_t) { atomicAdd(&h[lo >> 10], 1u); });
-  __syncthreads();
   find_digit<kRowNT>(h, kTopkBins, need, res + 2, tmp);
   const uint32_t d2 = (uint32_t)res[2];
   const int need3 = need - res[3];
-  // ---- third digit key[9:0]
+  // ---- third-digit histogram key[9:0] over the ties of the second digit;
+  // candidates above the second digit are selected
   for (int i = threadIdx.x; i < 1024; i += kRowNT) h[i] = 0u;
+  if (!fit && threadIdx.x == 0) lcount = 0u;      // the list now collects the ties
   __syncthreads();
-  for_each_cand([&](uint32_t lo, uint32_t) {
-    if ((lo >> 10) == d2) atomicAdd(&h[lo & 1023u], 1u);
-  });
+  if (fit) {
+    const int nc = (int)lcount;
+    for (int i = threadIdx.x; i < nc; i += kRowNT) {
+      const uint32_t lo = lcand[2 * i], sv = lcand[2 * i + 1];
+      const uint32_t dig = lo >> 10;
+      if (dig > d2) atomicOr(&selmap[sv >> 5], 1u << (sv & 31));
+      else if (dig == d2) atomicAdd(&h[lo & 1023u], 1u);
+    }
+  } else {
+    scan_row<kRowNT>(row, 0, n, [&](int s, uint32_t key, bool valid) {
+      const bool cand = valid && (key >> 21) == d1;
+      const uint32_t lo = key & 0x1fffffu, dig = lo >> 10;
+      if (cand && dig > d2) atomicOr(&selmap[s >> 5], 1u << (s & 31));
+      const bool tie = cand && dig == d2;
+      if (tie) atomicAdd(&h[lo & 1023u], 1u);
+      append(tie, lo, s);
+    });
+  }
   __syncthreads();
+  // ties of the second digit: the candidate list filtered by it, the tie list,
+  // or a pass over the row when the tie list overflowed too
+  const int nlist = (int)lcount;
+  const bool tie_fit = fit || nlist <= kLdsCap;
   find_digit<kRowNT>(h, 1024, need3, res + 4, tmp);
   const uint32_t T = (d2 << 10) | (uint32_t)res[4];
   const int quota = need3 - res[5];
-  for_each_cand([&](uint32_t lo, uint32_t s) {
-    if (lo > T) atomicOr(&selmap[s >> 5], 1u << (s & 31));
-    else if (lo == T) atomicOr(&eqmap[s >> 5], 1u << (s & 31));
-  });
+  auto mark = [&](uint32_t lo, uint32_t sv) {
+    if ((lo >> 10) != d2) return;
+    if (lo > T) atomicOr(&selmap[sv >> 5], 1u << (sv & 31));
+    else if (lo == T) atomicOr(&eqmap[sv >> 5], 1u << (sv & 31));
+  };
+  if (tie_fit) {
+    for (int i = threadIdx.x; i < nlist; i += kRowNT) mark(lcand[2 * i], lcand[2 * i + 1]);
+  } else {
+    for (int s = threadIdx.x; s < n; s += kRowNT) {
+      const uint32_t key = score_key(row[s]);
+      if ((key >> 21) == d1) mark(key & 0x1fffffu, (uint32_t)s);
+    }
+  }
   __syncthreads();
   compact_selection<kRowNT>(selmap, eqmap, W, quota, m, a.k, out, tmp);
 }

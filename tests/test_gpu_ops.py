@@ -108,6 +108,14 @@ TOPK_CASES = [
     ("small_k", 5, 3000, 1, "normal", "decode"),
     ("k7", 5, 3000, 7, "ties", "decode"),
     ("prefill_rows", 300, 4200, 2048, "normal", "prefill"),
+    # one workgroup per row (256 rows or more): candidate lists past the LDS
+    # capacity (long rows), and rows whose threshold digit holds every key
+    ("prefill_rows_overflow", 260, 40000, 2048, "normal", "prefill"),
+    ("prefill_rows_all_equal", 256, 9000, 2048, "all_equal", "prefill"),
+    ("prefill_rows_plateau", 256, 12000, 2048, "plateau", "prefill"),
+    ("prefill_rows_narrow", 256, 20000, 2048, "narrow", "prefill"),
+    ("prefill_rows_ties", 256, 7000, 2048, "ties", "prefill"),
+    ("prefill_rows_signed_zero", 256, 5000, 300, "signed_zero", "prefill"),
     ("long_row", 2, 131072, 2048, "normal", "decode"),
 ]
 
