@@ -17,7 +17,11 @@
 namespace dsa {
 namespace {
 
-constexpr int kDecodeChunk = 2048;  // keys per decode workgroup
+// Keys per decode workgroup: 2048, halved (down to 256) while the grid would
+// have fewer than 1024 workgroups, so that short contexts still fill the chip.
+constexpr int kDecodeChunk = 2048;
+constexpr int kDecodeMinChunk = 256;
+constexpr int kDecodeMinGrid = 1024;
 
 // ------------------------------------------------------------------ decode tiling
 //
@@ -46,14 +50,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int t = a.q_begin + r;
   const int n = a.sv.candidates(t);
   const int b = a.sv.seq_of(t);
-  const int c0 = blockIdx.x * kDecodeChunk;
+  const int chunk = a.chunk;
+  const int c0 = blockIdx.x * chunk;
   float *srow = a.scores + (long long)r * a.ld;
-  const long long cend = c0 + kDecodeChunk < a.ld ? c0 + kDecodeChunk : a.ld;
+  const long long cend = c0 + chunk < a.ld ? c0 + chunk : a.ld;
   if (a.fill_masked) {
     for (long long s = (c0 > n ? c0 : n) + threadIdx.x; s < cend; s += blockDim.x) srow[s] = neg_inf();
   }
   if (c0 >= n) return;
-  const int c1 = c0 + kDecodeChunk < n ? c0 + kDecodeChunk : n;
+  const int c1 = c0 + chunk < n ? c0 + chunk : n;
 
   const int lane = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar loop control
@@ -74,7 +79,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // issued, so that no wait is placed before them.
   __shared__ long long blk0[kDecodeChunk / 64];
   const int my_s = c0 + (int)threadIdx.x * 64;
-  const bool my_fill = threadIdx.x < kDecodeChunk / 64 && my_s < c1;
+  const bool my_fill = threadIdx.x < chunk / 64 && my_s < c1;
   int my_raw = 0;
   if (my_fill && a.sv.block_table != nullptr)
     my_raw = a.sv.block_table[(long long)b * a.sv.max_blocks + (my_s >> 6)];
@@ -249,11 +254,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 hipError_t launch_index_decode(const IndexerArgs &a, hipStream_t st) {
   const long long span = a.fill_masked ? a.ld : a.sv.max_ctx;
-  dim3 grid((unsigned)((span + kDecodeChunk - 1) / kDecodeChunk), (unsigned)a.rows);
+  IndexerArgs b = a;
+  b.chunk = kDecodeChunk;
+  while (b.chunk > kDecodeMinChunk && (long long)a.rows * ((span + b.chunk - 1) / b.chunk) < kDecodeMinGrid)
+    b.chunk >>= 1;
+  dim3 grid((unsigned)((span + b.chunk - 1) / b.chunk), (unsigned)a.rows);
   if (a.dtype == DSA_BF16)
-    hipLaunchKernelGGL(indexer_decode_kernel<DSA_BF16>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(indexer_decode_kernel<DSA_BF16>, grid, dim3(256), 0, st, b);
   else
-    hipLaunchKernelGGL(indexer_decode_kernel<DSA_FP8_E4M3FN>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(indexer_decode_kernel<DSA_FP8_E4M3FN>, grid, dim3(256), 0, st, b);
   return hipGetLastError();
 }
 

@@ -30,6 +30,7 @@ struct IndexerArgs {
   uint32_t *hist;
   long long hist_stride;
   int hist_mode;
+  int chunk;        // decode tiling: candidate keys per workgroup (set by its launcher)
 };
 
 struct TopkArgs {
