@@ -490,7 +490,7 @@ def stage2_line(B, torch, inp, steps, settle_ms):
     f_ibwd = 4 * f_idx
     peak = MFMA_PEAK_TFLOPS["bf16"]
     frac = lambda f, t: round(f / (t * 1e-3) / 1e12 / peak, 4)
-    contrib_bytes = 2 * sel * D * 4
+    contrib_bytes = 2 * sel * D * 2
     del fws, bws, iws, out, lse, idx, scores, dq, dkv, probs, loss, dqi, dwi, dki, dout
     torch.cuda.empty_cache()
     return {"workload": wl.name,
@@ -503,8 +503,8 @@ def stage2_line(B, torch, inp, steps, settle_ms):
             "mfma_frac": {"forward": frac(f_fwd, st[0]), "attention_backward": frac(f_bwd, st[2]),
                           "indexer_backward": frac(f_ibwd, st[4])},
             "attention_backward_row_gradient_bytes": contrib_bytes,
-            "note": "the attention backward's cache-row gradients make one fp32 round trip through HBM "
-                    "(written per selected row, summed per token in query order)"}
+            "note": "the attention backward's cache-row gradients make one bf16 round trip through HBM "
+                    "(written per selected row, summed in fp32 per token in query order)"}
 
 
 def cpu_baseline(inp, seconds):

@@ -306,7 +306,7 @@ int scratch_on_current_device(void **out) {
 }
 
 // Stage-2 attention backward: per chunk of up to kSBwdChunk query rows, the
-// bf16 weights and score gradients, the fp32 row gradients and the key map.
+// bf16 weights and score gradients, the bf16 row gradients and the key map.
 constexpr int kSBwdChunk = 256;
 
 struct SBwdLayout {
@@ -323,7 +323,7 @@ SBwdLayout sbwd_layout(const dsa_seqs *s, const dsa_dims *d) {
   L.off_dst = align256(c * d->heads * 4);
   L.off_pd = L.off_dst + align256(c * ntk * d->heads * 32 * 2);
   L.off_contrib = L.off_pd + align256(c * k * 2 * d->heads * 2);
-  L.off_jpos = L.off_contrib + align256(c * k * d->qk_dim * 4);
+  L.off_jpos = L.off_contrib + align256(c * k * d->qk_dim * 2);
   L.total = L.off_jpos + align256((long long)s->max_ctx * L.jstride * 2);
   return L;
 }
@@ -764,7 +764,7 @@ DSA_EXPORT int dsa_sparse_mla_backward(const dsa_seqs *seqs, const dsa_dims *dim
   a.delta = reinterpret_cast<float *>(base);
   a.ds_t = reinterpret_cast<uint16_t *>(base + L.off_dst);
   a.pd = reinterpret_cast<uint16_t *>(base + L.off_pd);
-  a.contrib = reinterpret_cast<float *>(base + L.off_contrib);
+  a.contrib = reinterpret_cast<uint16_t *>(base + L.off_contrib);
   a.jpos = reinterpret_cast<uint16_t *>(base + L.off_jpos);
   a.jstride = L.jstride;
   a.nkeys = seqs->max_ctx;

@@ -156,7 +156,7 @@ struct MlaBwdArgs {
   float *delta;             // ws [rows, H]: sum_d dout * out
   uint16_t *ds_t;           // ws [rows, k / 32, H, 32] bf16: sm_scale dS per tile, rows in k-slot order
   uint16_t *pd;             // ws [rows, k, 2, H] bf16: P and sm_scale dS per row, heads in k-slot order
-  float *contrib;           // ws [rows, k, D]: each selected row's gradient from its query
+  uint16_t *contrib;        // ws [rows, k, D] bf16: each selected row's gradient from its query
   uint16_t *jpos;           // ws [nkeys, jstride]: slot j of query row r that selected key s, or 0xFFFF
   int jstride;              // rows rounded up to 8
   int nkeys;                // keys reduced (positions 0..nkeys-1 of sequence 0)

@@ -19,9 +19,9 @@
 //                 gradients) and the head-mean weights (the Stage-2 target)
 //   bwd_dq        gathers the rows again: dq^T += C^T dS^T (LDS transpose reads)
 //   bwd_contrib   the row gradients as a GEMM per query, [P | dS] rows against
-//                 dO and Q slices staged in LDS: one fp32 row per (query, j)
+//                 dO and Q slices staged in LDS: one bf16 row per (query, j)
 //   bwd_jpos_*    which slot j of which query row selected each key
-//   bwd_dkv       per key, its rows' gradients summed in ascending query order,
+//   bwd_dkv       per key, its rows' gradients summed in fp32 in ascending query order,
 //                 chunk after chunk: no atomics, so the result is deterministic.
 #include "mla_tile.h"
 
@@ -368,11 +368,15 @@ __global__ __launch_bounds__(kThreads) void bwd_contrib_kernel(MlaBwdArgs a) {
     }
   }
   if (!active) return;
-  // streaming stores: the rows are read back once, by the key-major reduction
-  float *crow = a.contrib + ((long long)r * a.k + jb + col) * kD;
+  // bf16 rows (their sum per key stays fp32), with streaming stores: the rows
+  // are read back once, by the key-major reduction
+  uint16_t *crow = a.contrib + ((long long)r * a.k + jb + col) * kD;
+  typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
 #pragma unroll
-  for (int db = 0; db < kDbAll; ++db)
-    __builtin_nontemporal_store(acc[db], reinterpret_cast<f32x4 *>(crow + db * 16 + 4 * g));
+  for (int db = 0; db < kDbAll; ++db) {
+    const u32x2v pk = {pack_bf16x2(acc[db][0], acc[db][1]), pack_bf16x2(acc[db][2], acc[db][3])};
+    __builtin_nontemporal_store(pk, reinterpret_cast<u32x2v *>(crow + db * 16 + 4 * g));
+  }
 }
 
 // ---------------------------------------------------------------- the reduction into the cache rows
@@ -421,9 +425,9 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(MlaBwdArgs a) {
       const int b1 = two ? __ffsll((long long)m) - 1 : b0;
       if (two) m &= m - 1;
       const int j0 = __builtin_amdgcn_readlane(jv, b0), j1 = __builtin_amdgcn_readlane(jv, b1);
-      const float *c0 = a.contrib + ((long long)(t0 + b0) * a.k + j0) * kD + lane;
-      const float *c1 = a.contrib + ((long long)(t0 + b1) * a.k + j1) * kD + lane;
-      float x0[kD / 64], x1[kD / 64];
+      const uint16_t *c0 = a.contrib + ((long long)(t0 + b0) * a.k + j0) * kD + lane;
+      const uint16_t *c1 = a.contrib + ((long long)(t0 + b1) * a.k + j1) * kD + lane;
+      uint16_t x0[kD / 64], x1[kD / 64];
 #pragma unroll
       for (int u = 0; u < kD / 64; ++u) {
         x0[u] = __builtin_nontemporal_load(c0 + 64 * u);
@@ -431,8 +435,8 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(MlaBwdArgs a) {
       }
 #pragma unroll
       for (int u = 0; u < kD / 64; ++u) {
-        acc[u] += x0[u];
-        if (two) acc[u] += x1[u];
+        acc[u] += bf16_to_f32(x0[u]);
+        if (two) acc[u] += bf16_to_f32(x1[u]);
       }
     }
   }
