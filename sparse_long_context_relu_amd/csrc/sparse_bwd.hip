@@ -368,14 +368,16 @@ __global__ __launch_bounds__(kThreads) void bwd_contrib_kernel(MlaBwdArgs a) {
     }
   }
   if (!active) return;
-  // bf16 rows (their sum per key stays fp32), with streaming stores: the rows
-  // are read back once, by the key-major reduction
+  // bf16 rows (their sum per key stays fp32).  Default-policy stores: a
+  // store instruction writes 32 contiguous bytes per row, and the L2 merges
+  // the pieces of a row before they go out.
   uint16_t *crow = a.contrib + ((long long)r * a.k + jb + col) * kD;
-  typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
 #pragma unroll
   for (int db = 0; db < kDbAll; ++db) {
-    const u32x2v pk = {pack_bf16x2(acc[db][0], acc[db][1]), pack_bf16x2(acc[db][2], acc[db][3])};
-    __builtin_nontemporal_store(pk, reinterpret_cast<u32x2v *>(crow + db * 16 + 4 * g));
+    uint2 pk;
+    pk.x = pack_bf16x2(acc[db][0], acc[db][1]);
+    pk.y = pack_bf16x2(acc[db][2], acc[db][3]);
+    *reinterpret_cast<uint2 *>(crow + db * 16 + 4 * g) = pk;
   }
 }
 
