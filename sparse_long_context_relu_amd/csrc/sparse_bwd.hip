@@ -312,9 +312,16 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(MlaBwdArgs a) {
 // heads whose dO and Q rows are staged in LDS in the tile layout.
 constexpr int kContribRows = 128;
 
+// The Q and dO rows of a head group (32 heads) go into LDS by direct-to-LDS
+// loads in the tile layout (position p: row p/74, slot p%74, holding data
+// chunk slot ^ swz(row); pad slots load the row's first chunk, never read):
+// 37 loads of 64 lanes per array, five for waves 0..4 and four for 5..7.
+// Two buffers: group hg+1 streams in while group hg is multiplied.
+constexpr int kStageLoads = (kTileChunks + 63) / 64;   // 37
+
 __global__ __launch_bounds__(kThreads) void bwd_contrib_kernel(MlaBwdArgs a) {
-  __shared__ uint4 qs[kTileChunks];
-  __shared__ uint4 os[kTileChunks];
+  __shared__ uint4 qs[2][kTileChunks];
+  __shared__ uint4 os[2][kTileChunks];
   const int r = blockIdx.y;
   const int t = a.q_begin + r;
   const int lane = lane_id();
@@ -327,42 +334,61 @@ __global__ __launch_bounds__(kThreads) void bwd_contrib_kernel(MlaBwdArgs a) {
   const uint32_t pv_row = (4 * g + (col >> 2)) * kRowStride + (vc & 1) * 8;
   const uint32_t pv_even = pv_row + (((vc >> 1)) ^ g) * 16;
   const uint32_t pv_odd = pv_row + ((2 + (vc >> 1)) ^ g) * 16;
-  const uint32_t q_lds = lds_addr(&qs[0]), o_lds = lds_addr(&os[0]);
   const uint8_t *qsrc = reinterpret_cast<const uint8_t *>(a.q) + (long long)t * kH * (kD * 2);
   const uint8_t *osrc = reinterpret_cast<const uint8_t *>(a.dout) + (long long)t * kH * (kDv * 2);
   const uint16_t *prow = a.pd + ((long long)r * a.k + (active ? jb + col : 0)) * (2 * kH);
+  const int nloads = wv < kStageLoads - 4 * kWaves ? 5 : 4;    // wave-uniform
+  auto stage = [&](int hg, int bi) {
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      if (j < nloads) {
+        const int p = (j * kWaves + wv) * 64 + lane;
+        const int row = p / kRowChunks, ch = p - row * kRowChunks;
+        const int cq = ch < kDataChunks ? ch ^ swz(row) : 0;
+        const int co = ch < kDv / 8 ? ch ^ swz(row) : 0;
+        const uint32_t dst = (j * kWaves + wv) * 1024;
+        const uint32_t mq = __builtin_amdgcn_readfirstlane(lds_addr(&qs[bi][0]) + dst);
+        const uint32_t mo = __builtin_amdgcn_readfirstlane(lds_addr(&os[bi][0]) + dst);
+        lds_dma16(qsrc + (long long)(32 * hg + row) * (kD * 2) + cq * 16, mq);
+        lds_dma16(osrc + (long long)(32 * hg + row) * (kDv * 2) + co * 16, mo);
+      }
+    }
+  };
 
   f32x4 acc[kDbAll];
 #pragma unroll
   for (int db = 0; db < kDbAll; ++db) acc[db] = zero_vec<f32x4>();
+  // P and dS operands of the group being multiplied, loaded one group ahead
+  // (before that group's gather, whose loads they would otherwise wait for)
+  bf16x8 pp = as_bf16x8(ld16(prow + 8 * g)), ps = as_bf16x8(ld16(prow + kH + 8 * g));
+  stage(0, 0);
   for (int hg = 0; hg < kH / 32; ++hg) {
-    __syncthreads();                            // the previous group's operands are read
-    // stage heads 32 hg.. : row hr of the group, data chunk c at position c ^ swz(hr)
-    for (int i = threadIdx.x; i < 32 * kDataChunks; i += kThreads) {
-      const int hr = i / kDataChunks, c = i - hr * kDataChunks;
-      qs[hr * kRowChunks + (c ^ swz(hr))] = ld16(qsrc + (long long)(32 * hg + hr) * (kD * 2) + c * 16);
+    const int bi = hg & 1;
+    // group hg (and its P, dS operands) landed for this wave; the barrier covers
+    // every wave's and orders the reads of group hg-1 before its buffer refills
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    lds_barrier();
+    const bf16x8 ppc = pp, psc = ps;
+    if (hg + 1 < kH / 32) {
+      pp = as_bf16x8(ld16(prow + 32 * (hg + 1) + 8 * g));
+      ps = as_bf16x8(ld16(prow + kH + 32 * (hg + 1) + 8 * g));
+      stage(hg + 1, bi ^ 1);
     }
-    for (int i = threadIdx.x; i < 32 * (kDv / 8); i += kThreads) {
-      const int hr = i / (kDv / 8), c = i - hr * (kDv / 8);
-      os[hr * kRowChunks + (c ^ swz(hr))] = ld16(osrc + (long long)(32 * hg + hr) * (kDv * 2) + c * 16);
-    }
-    __syncthreads();
     if (!active) continue;
-    const bf16x8 pp = as_bf16x8(ld16(prow + 32 * hg + 8 * g));
-    const bf16x8 ps = as_bf16x8(ld16(prow + kH + 32 * hg + 8 * g));
+    const uint32_t q_lds = lds_addr(&qs[bi][0]), o_lds = lds_addr(&os[bi][0]);
 #pragma unroll
     for (int db = 0; db < kDbAll; ++db) {
       const uint32_t off = ((db & 1) ? pv_odd : pv_even) + (db >> 1) * 64;
       {
         const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)(q_lds + off));
         const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)(q_lds + off + 16 * kRowStride));
-        acc[db] = mfma16_bf16(__builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)), ps,
+        acc[db] = mfma16_bf16(__builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)), psc,
                               acc[db]);
       }
       if (db < kDv / 16) {
         const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)(o_lds + off));
         const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)(o_lds + off + 16 * kRowStride));
-        acc[db] = mfma16_bf16(__builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)), pp,
+        acc[db] = mfma16_bf16(__builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)), ppc,
                               acc[db]);
       }
     }
