@@ -350,8 +350,9 @@ int dsa_indexer_kl_loss(const dsa_seqs *seqs, const dsa_dims *dims, const dsa_kl
  * ([T, k] fp32, 0 at absent entries).  Entries of topk_idx outside
  * 0..q_pos[t] are absent; a query must not select a position twice.
  * bf16 operands (P and sm_scale dS rounded to bf16 as MFMA operands), fp32
- * accumulation; the token sums run in ascending query order, so the result is
- * deterministic.  Supported: prefill (training runs over whole sequences),
+ * accumulation; each query's contribution to a cache row is rounded to bf16
+ * once before the token sums, which run in fp32 in ascending query order, so
+ * the result is deterministic.  Supported: prefill (training runs over whole sequences),
  * bf16 H = 128, D = 576, Dv = 512, k a multiple of 16.
  * Workspace: dsa_workspace_size(DSA_OP_SPARSE_MLA_BACKWARD, ...). */
 int dsa_sparse_mla_backward(const dsa_seqs *seqs, const dsa_dims *dims, float sm_scale, const void *q,

@@ -354,9 +354,9 @@ def test_stage2_validation_and_workspace():
     pf = B.make_problem(mode="prefill", q_pos=qp, max_ctx=16384, num_seqs=1, max_seq_len=16384)
     sp, dp = ctypes.byref(pf.seqs), ctypes.byref(pf.dims)
     a256 = lambda x: (x + 255) // 256 * 256
-    # chunks of 256 query rows: Delta, per-tile dS, per-row P | dS, fp32 row gradients, the key map
+    # chunks of 256 query rows: Delta, per-tile dS, per-row P | dS, bf16 row gradients, the key map
     want = (a256(256 * 128 * 4) + a256(256 * 64 * 128 * 32 * 2) + a256(256 * 2048 * 2 * 128 * 2)
-            + a256(256 * 2048 * 576 * 4) + a256(16384 * 256 * 2))
+            + a256(256 * 2048 * 576 * 2) + a256(16384 * 256 * 2))
     need = B.workspace_size(B.OP_SPARSE_MLA_BACKWARD, pf)
     assert need == want
     call = lambda pb, **kw: L.dsa_sparse_mla_backward(
@@ -374,7 +374,7 @@ def test_stage2_validation_and_workspace():
     assert call(f32) == B.ERR_UNSUPPORTED
     few = B.make_problem(mode="prefill", q_pos=qp[:44], max_ctx=300, num_seqs=1, max_seq_len=300, topk=64)
     assert B.workspace_size(B.OP_SPARSE_MLA_BACKWARD, few) == (
-        a256(44 * 128 * 4) + a256(44 * 2 * 128 * 32 * 2) + a256(44 * 64 * 2 * 128 * 2) + a256(44 * 64 * 576 * 4)
+        a256(44 * 128 * 4) + a256(44 * 2 * 128 * 32 * 2) + a256(44 * 64 * 2 * 128 * 2) + a256(44 * 64 * 576 * 2)
         + a256(300 * 48 * 2))
     kl = lambda pb, sc=FAKE, ld=16384, idx=FAKE, k=2048, pr=FAKE, loss=FAKE: L.dsa_sparse_indexer_kl(
         ctypes.byref(pb.seqs), sc, ld, idx, k, pr, loss, None)
