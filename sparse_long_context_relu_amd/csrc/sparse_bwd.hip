@@ -437,40 +437,77 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(MlaBwdArgs a) {
     slot = (blk >= 0 && blk < a.sv.num_blocks) ? (long long)blk * 64 + (s & 63) : -1;
   }
   if (slot < 0) return;
-  float acc[kD / 64];
+  // lane l sums dims 8 l .. 8 l + 7 and, for l < 8, dims 512 + 8 l .. + 7: one
+  // 16-byte load per row (two for lanes 0..7)
+  constexpr int kExt = (kD - 512) / 8;          // lanes with a second chunk (8)
+  const bool ext = lane < kExt;
+  float acc[16];
 #pragma unroll
-  for (int u = 0; u < kD / 64; ++u) acc[u] = 0.f;
+  for (int u = 0; u < 16; ++u) acc[u] = 0.f;
   const uint16_t *jrow = a.jpos + (long long)s * a.jstride;
-  // Two rows' loads in flight at a time (streaming loads: each row is read
-  // once); they are still added in ascending query order.
+  auto add8 = [&](const uint4 &v, int o) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[o + 2 * i] += __uint_as_float(w[i] << 16);
+      acc[o + 2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  };
+  // Up to four rows' loads in flight at a time (streaming loads: each row is
+  // read once); they are added in ascending query order.
+  constexpr int kAhead = 4;
   for (int t0 = 0; t0 < a.rows; t0 += 64) {
     const int jv = t0 + lane < a.rows ? (int)jrow[t0 + lane] : (int)kNoSlot;
     unsigned long long m = __ballot(jv != kNoSlot);
     while (m) {
-      const int b0 = __ffsll((long long)m) - 1;
-      m &= m - 1;
-      const bool two = m != 0;
-      const int b1 = two ? __ffsll((long long)m) - 1 : b0;
-      if (two) m &= m - 1;
-      const int j0 = __builtin_amdgcn_readlane(jv, b0), j1 = __builtin_amdgcn_readlane(jv, b1);
-      const uint16_t *c0 = a.contrib + ((long long)(t0 + b0) * a.k + j0) * kD + lane;
-      const uint16_t *c1 = a.contrib + ((long long)(t0 + b1) * a.k + j1) * kD + lane;
-      uint16_t x0[kD / 64], x1[kD / 64];
+      int bs[kAhead];
+      int cnt = 0;
 #pragma unroll
-      for (int u = 0; u < kD / 64; ++u) {
-        x0[u] = __builtin_nontemporal_load(c0 + 64 * u);
-        x1[u] = __builtin_nontemporal_load(c1 + 64 * u);
+      for (int u = 0; u < kAhead; ++u) {
+        if (m) {
+          bs[u] = __ffsll((long long)m) - 1;
+          m &= m - 1;
+          cnt = u + 1;
+        } else {
+          bs[u] = bs[0];
+        }
+      }
+      uint4 x[kAhead], y[kAhead];
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) {
+        const int j = __builtin_amdgcn_readlane(jv, bs[u]);
+        const uint16_t *c = a.contrib + ((long long)(t0 + bs[u]) * a.k + j) * kD + 8 * lane;
+        x[u] = ld16_stream(c);
+        y[u] = ext ? ld16_stream(c + 512) : make_uint4(0u, 0u, 0u, 0u);
       }
 #pragma unroll
-      for (int u = 0; u < kD / 64; ++u) {
-        acc[u] += bf16_to_f32(x0[u]);
-        if (two) acc[u] += bf16_to_f32(x1[u]);
-      }
+      for (int u = 0; u < kAhead; ++u)
+        if (u < cnt) {
+          add8(x[u], 0);
+          add8(y[u], 8);
+        }
     }
   }
-  float *drow = a.dkv + slot * kD + lane;
-#pragma unroll
-  for (int u = 0; u < kD / 64; ++u) drow[64 * u] = a.first ? acc[u] : drow[64 * u] + acc[u];
+  float *drow = a.dkv + slot * kD;
+  float4 *d0 = reinterpret_cast<float4 *>(drow + 8 * lane);
+  float4 *d1 = reinterpret_cast<float4 *>(drow + 512 + 8 * lane);
+  if (a.first) {
+    d0[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    d0[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    if (ext) {
+      d1[0] = make_float4(acc[8], acc[9], acc[10], acc[11]);
+      d1[1] = make_float4(acc[12], acc[13], acc[14], acc[15]);
+    }
+  } else {
+    const float4 o0 = d0[0], o1 = d0[1];
+    d0[0] = make_float4(o0.x + acc[0], o0.y + acc[1], o0.z + acc[2], o0.w + acc[3]);
+    d0[1] = make_float4(o1.x + acc[4], o1.y + acc[5], o1.z + acc[6], o1.w + acc[7]);
+    if (ext) {
+      const float4 p0 = d1[0], p1 = d1[1];
+      d1[0] = make_float4(p0.x + acc[8], p0.y + acc[9], p0.z + acc[10], p0.w + acc[11]);
+      d1[1] = make_float4(p1.x + acc[12], p1.y + acc[13], p1.z + acc[14], p1.w + acc[15]);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- Stage-2 indexer KL
