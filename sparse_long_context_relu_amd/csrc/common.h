@@ -237,7 +237,8 @@ __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<
 
 // 16-byte streaming load (the nontemporal cache policy: data read once).  On
 // this part a stream of such loads reaches a higher HBM read rate than the same
-// loads with the default policy (about 7.0 against 6.2 TB/s for 8 KB tiles).
+// loads with the default policy (about 6.8 against 6.0 TB/s for the decode
+// indexer's 8 KB tiles).
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld16_stream(const void *p) {
   const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v *>(p));

@@ -50,6 +50,12 @@ INDEXER_CASES = [
     ("decode_paged_fp8_mixed_w", dict(mode="decode", num_seqs=3, length=2600, k=64, paged=True, index_dtype="fp8",
                                       w_low=-1 / 8), [2600, 33, 1999]),
     ("prefill_fp8_mixed_w", dict(mode="prefill", length=310, k=64, index_dtype="fp8", w_low=-1 / 8), None),
+    # decode grids with fewer than 1024 workgroups of 2048 keys take smaller ones:
+    # 32 rows of up to 16K keys -> 512-key workgroups, 16 rows of 64K -> 1024
+    ("decode_paged_bf16_chunk512", dict(mode="decode", num_seqs=32, length=16384, k=64, paged=True),
+     [16384 - 509 * i for i in range(32)]),
+    ("decode_paged_fp8_chunk1024", dict(mode="decode", num_seqs=16, length=65536, k=64, paged=True,
+                                        index_dtype="fp8"), [65536 - 3001 * i for i in range(16)]),
     ("prefill_f32", dict(mode="prefill", length=200, k=16, H_I=4, d_I=32, H=8, D=80, Dv=64,
                          index_dtype="f32", mla_dtype="f32", qkv_std=1 / math.sqrt(80), w_high=1.0), None),
     ("decode_f32_paged", dict(mode="decode", num_seqs=3, length=700, k=16, H_I=4, d_I=32, H=8, D=80, Dv=64,
