@@ -326,6 +326,8 @@ def indexer_kl_loss(pb: Problem, q_idx, w, k_cache, q, kv_cache, sm_scale: float
     ev_arr = None
     if stage_events is not None:
         assert len(stage_events) == 5
+        if any(e.cuda_event == 0 for e in stage_events):
+            raise ValueError("stage_events: record each event once first (torch creates the HIP event then)")
         ev_arr = (ctypes.c_void_p * 5)(*[e.cuda_event for e in stage_events])
     args = DsaKlArgs(q_idx=_ptr(q_idx), w=_ptr(w), k_cache=_ptr(k_cache), q=_ptr(q), kv_cache=_ptr(kv_cache),
                      sm_scale=float(sm_scale), reserved=0, lse=_ptr(lse), loss=_ptr(loss), dq_idx=_ptr(dq) if backward else None,
@@ -352,6 +354,8 @@ def forward(pb: Problem, q_idx, q_scale, w, k_cache, k_scale, q, kv_cache, sm_sc
     ev_arr = None
     if stage_events is not None:
         assert len(stage_events) == 4
+        if any(e.cuda_event == 0 for e in stage_events):
+            raise ValueError("stage_events: record each event once first (torch creates the HIP event then)")
         ev_arr = (ctypes.c_void_p * 4)(*[e.cuda_event for e in stage_events])
     args = DsaForwardArgs(q_idx=_ptr(q_idx), q_scale=_ptr(q_scale), w=_ptr(w), k_cache=_ptr(k_cache),
                           k_scale=_ptr(k_scale), q=_ptr(q), kv_cache=_ptr(kv_cache),

@@ -87,6 +87,34 @@ def test_forward_matches_staged_ops():
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
+BATCH_CASES = [
+    ("decode_paged_bf16_33", dict(mode="decode", num_seqs=33, length=9000, k=2048, paged=True),
+     [9000 - 271 * i for i in range(31)] + [2048, 1]),
+    ("decode_paged_fp8_20", dict(mode="decode", num_seqs=20, length=7000, k=2048, paged=True, index_dtype="fp8"),
+     [7000 - 301 * i for i in range(19)] + [2049]),
+    ("decode_contig_bf16_16", dict(mode="decode", num_seqs=16, length=4500, k=2048),
+     [4500 - 150 * i for i in range(16)]),
+]
+
+
+@pytest.mark.parametrize("name,kw,lengths", BATCH_CASES, ids=[c[0] for c in BATCH_CASES])
+def test_forward_decode_batches(name, kw, lengths):
+    """Decode batches of 16 to 33 queries with ragged contexts (one of a single
+    token, one of exactly k): every row against the oracle, and the same bits
+    from the stage-timed call (events between the stages) and from a repeat."""
+    _say("forward batch", name)
+    inp = generate(big_dims(**kw), DEV, lengths=lengths)
+    out, lse, idx = run_forward(inp)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:             # torch creates the HIP event on first record
+        e.record()
+    out2, lse2, idx2 = B().forward_inputs(inp, stage_events=ev)
+    out3, lse3, idx3 = run_forward(inp)
+    for x, y in ((idx, idx2), (out, out2), (lse, lse2), (idx, idx3), (out, out3), (lse, lse3)):
+        assert torch.equal(x, y)
+    check_all_rows(inp, out, lse, idx, name)
+
+
 def _paged_copy(inp, rng):
     """The same logical caches re-laid into permuted 64-token blocks."""
     B_, L = inp.k_cache.shape[:2]
