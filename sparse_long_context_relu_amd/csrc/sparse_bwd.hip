@@ -318,16 +318,29 @@ constexpr int kContribRows = 128;
 // 37 loads of 64 lanes per array, five for waves 0..4 and four for 5..7.
 // Two buffers: group hg+1 streams in while group hg is multiplied.
 constexpr int kStageLoads = (kTileChunks + 63) / 64;   // 37
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 
 __global__ __launch_bounds__(kThreads) void bwd_contrib_kernel(MlaBwdArgs a) {
-  __shared__ uint4 qs[2][kTileChunks];
-  __shared__ uint4 os[2][kTileChunks];
-  const int r = blockIdx.y;
+  // Q of head group hg in sbuf[hg & 1], dO in sbuf[2 + (hg & 1)]; at the end
+  // the row gradients on their way out
+  __shared__ uint4 sbuf[4][kTileChunks];
+  // Workgroups are dealt to the 8 XCDs round-robin by linear id, each XCD with
+  // its own L2.  When the rows divide by 8, XCD x takes rows x, x+8, ..., every
+  // slot block of a row in turn, so a row's Q and dO come into one L2 once and
+  // serve all of its blocks (the grid's own order spreads a row's blocks over
+  // every XCD, each fetching the row).
+  int r = blockIdx.y, bx = blockIdx.x;
+  if ((a.rows & 7) == 0) {
+    const int v = blockIdx.x + gridDim.x * blockIdx.y, k = v >> 3;
+    r = (k / (int)gridDim.x) * 8 + (v & 7);
+    bx = k - (k / (int)gridDim.x) * (int)gridDim.x;
+  }
   const int t = a.q_begin + r;
   const int lane = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, g = lane >> 4;
-  const int jb = blockIdx.x * kContribRows + wv * 16;
+  const int jb = bx * kContribRows + wv * 16;
   const bool active = jb < a.k;                 // k is a multiple of 16
 
   const int vc = col & 3;
@@ -347,8 +360,8 @@ __global__ __launch_bounds__(kThreads) void bwd_contrib_kernel(MlaBwdArgs a) {
         const int cq = ch < kDataChunks ? ch ^ swz(row) : 0;
         const int co = ch < kDv / 8 ? ch ^ swz(row) : 0;
         const uint32_t dst = (j * kWaves + wv) * 1024;
-        const uint32_t mq = __builtin_amdgcn_readfirstlane(lds_addr(&qs[bi][0]) + dst);
-        const uint32_t mo = __builtin_amdgcn_readfirstlane(lds_addr(&os[bi][0]) + dst);
+        const uint32_t mq = __builtin_amdgcn_readfirstlane(lds_addr(&sbuf[bi][0]) + dst);
+        const uint32_t mo = __builtin_amdgcn_readfirstlane(lds_addr(&sbuf[2 + bi][0]) + dst);
         lds_dma16(qsrc + (long long)(32 * hg + row) * (kD * 2) + cq * 16, mq);
         lds_dma16(osrc + (long long)(32 * hg + row) * (kDv * 2) + co * 16, mo);
       }
@@ -375,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void bwd_contrib_kernel(MlaBwdArgs a) {
       stage(hg + 1, bi ^ 1);
     }
     if (!active) continue;
-    const uint32_t q_lds = lds_addr(&qs[bi][0]), o_lds = lds_addr(&os[bi][0]);
+    const uint32_t q_lds = lds_addr(&sbuf[bi][0]), o_lds = lds_addr(&sbuf[2 + bi][0]);
 #pragma unroll
     for (int db = 0; db < kDbAll; ++db) {
       const uint32_t off = ((db & 1) ? pv_odd : pv_even) + (db >> 1) * 64;
@@ -393,17 +406,29 @@ __global__ __launch_bounds__(kThreads) void bwd_contrib_kernel(MlaBwdArgs a) {
       }
     }
   }
+  // bf16 rows (their sum per key stays fp32), staged through LDS: a wave's 16
+  // rows are 18 KB in one piece of the row-gradient array, written with 16-byte
+  // stores, 1 KB per instruction (where the accumulator layout would give 32
+  // bytes of each of 16 rows per instruction).
+  constexpr int kOutStride = kD * 2 + 16;      // LDS bytes per staged row (one pad chunk)
+  static_assert(kWaves * 16 * kOutStride <= 4 * kTileChunks * 16, "the staged rows fit the operand buffers");
+  lds_barrier();                               // every wave is done with the last group's operands
   if (!active) return;
-  // bf16 rows (their sum per key stays fp32).  Default-policy stores: a
-  // store instruction writes 32 contiguous bytes per row, and the L2 merges
-  // the pieces of a row before they go out.
-  uint16_t *crow = a.contrib + ((long long)r * a.k + jb + col) * kD;
+  const uint32_t stg = lds_addr(&sbuf[0][0]) + wv * 16 * kOutStride;
 #pragma unroll
   for (int db = 0; db < kDbAll; ++db) {
-    uint2 pk;
-    pk.x = pack_bf16x2(acc[db][0], acc[db][1]);
-    pk.y = pack_bf16x2(acc[db][2], acc[db][3]);
-    *reinterpret_cast<uint2 *>(crow + db * 16 + 4 * g) = pk;
+    u32x2 pk;
+    pk[0] = pack_bf16x2(acc[db][0], acc[db][1]);
+    pk[1] = pack_bf16x2(acc[db][2], acc[db][3]);
+    *(lds_u32x2 *)(uintptr_t)(stg + col * kOutStride + (16 * db + 4 * g) * 2) = pk;
+  }
+  uint8_t *dst = reinterpret_cast<uint8_t *>(a.contrib + ((long long)r * a.k + jb) * kD);
+  constexpr int kRowPieces = kD * 2 / 16;      // 72 16-byte pieces per row
+#pragma unroll
+  for (int it = 0; it < 16 * kRowPieces / 64; ++it) {
+    const int c = it * 64 + lane, row = c / kRowPieces, w = c - row * kRowPieces;
+    const u32x4 v = *(lds_u32x4 *)(uintptr_t)(stg + row * kOutStride + w * 16);
+    st16(dst + c * 16, make_uint4(v[0], v[1], v[2], v[3]));
   }
 }
 
