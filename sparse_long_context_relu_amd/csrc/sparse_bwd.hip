@@ -315,15 +315,16 @@ constexpr int kContribRows = 128;
 // The Q and dO rows of a head group (32 heads) go into LDS by direct-to-LDS
 // loads in the tile layout (position p: row p/74, slot p%74, holding data
 // chunk slot ^ swz(row); pad slots load the row's first chunk, never read):
-// 37 loads of 64 lanes per array, five for waves 0..4 and four for 5..7.
-// Two buffers: group hg+1 streams in while group hg is multiplied.
+// 37 loads of 64 lanes per array, five for waves 0..4 and four for 5..7.  The
+// arrays come in as eight stages (Q, then dO, of each group) through four
+// buffers, three stages ahead of the one being multiplied.
 constexpr int kStageLoads = (kTileChunks + 63) / 64;   // 37
+constexpr int kStages = 2 * (kH / 32);
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 
 __global__ __launch_bounds__(kThreads) void bwd_contrib_kernel(MlaBwdArgs a) {
-  // Q of head group hg in sbuf[hg & 1], dO in sbuf[2 + (hg & 1)]; at the end
-  // the row gradients on their way out
+  // the staged Q and dO arrays; at the end the row gradients on their way out
   __shared__ uint4 sbuf[4][kTileChunks];
   // Workgroups are dealt to the 8 XCDs round-robin by linear id, each XCD with
   // its own L2.  When the rows divide by 8, XCD x takes rows x, x+8, ..., every
@@ -351,60 +352,88 @@ __global__ __launch_bounds__(kThreads) void bwd_contrib_kernel(MlaBwdArgs a) {
   const uint8_t *osrc = reinterpret_cast<const uint8_t *>(a.dout) + (long long)t * kH * (kDv * 2);
   const uint16_t *prow = a.pd + ((long long)r * a.k + (active ? jb + col : 0)) * (2 * kH);
   const int nloads = wv < kStageLoads - 4 * kWaves ? 5 : 4;    // wave-uniform
-  auto stage = [&](int hg, int bi) {
+  // Stage st: Q (even st) or dO (odd st) of head group st / 2, into buffer st % 4.
+  auto stage = [&](int st) {
+    const int hg = st >> 1;
+    const uint32_t base = lds_addr(&sbuf[st & 3][0]);
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
       if (j < nloads) {
         const int p = (j * kWaves + wv) * 64 + lane;
         const int row = p / kRowChunks, ch = p - row * kRowChunks;
-        const int cq = ch < kDataChunks ? ch ^ swz(row) : 0;
-        const int co = ch < kDv / 8 ? ch ^ swz(row) : 0;
-        const uint32_t dst = (j * kWaves + wv) * 1024;
-        const uint32_t mq = __builtin_amdgcn_readfirstlane(lds_addr(&sbuf[bi][0]) + dst);
-        const uint32_t mo = __builtin_amdgcn_readfirstlane(lds_addr(&sbuf[2 + bi][0]) + dst);
-        lds_dma16(qsrc + (long long)(32 * hg + row) * (kD * 2) + cq * 16, mq);
-        lds_dma16(osrc + (long long)(32 * hg + row) * (kDv * 2) + co * 16, mo);
+        const uint32_t m = __builtin_amdgcn_readfirstlane(base + (j * kWaves + wv) * 1024);
+        if ((st & 1) == 0)
+          lds_dma16(qsrc + (long long)(32 * hg + row) * (kD * 2) + (ch < kDataChunks ? ch ^ swz(row) : 0) * 16, m);
+        else
+          lds_dma16(osrc + (long long)(32 * hg + row) * (kDv * 2) + (ch < kDv / 8 ? ch ^ swz(row) : 0) * 16, m);
       }
+    }
+  };
+  // Wait until at most n of this wave's vector-memory operations are in flight.
+  auto wait_loads = [&](int n) {
+    switch (n) {
+      case 0: __builtin_amdgcn_s_waitcnt(wait_vm(0)); break;
+      case 4: __builtin_amdgcn_s_waitcnt(wait_vm(4)); break;
+      case 5: __builtin_amdgcn_s_waitcnt(wait_vm(5)); break;
+      case 8: __builtin_amdgcn_s_waitcnt(wait_vm(8)); break;
+      case 10: __builtin_amdgcn_s_waitcnt(wait_vm(10)); break;
+      default: __builtin_amdgcn_s_waitcnt(wait_vm(12)); break;   // 12: 5 + 5 + 2
     }
   };
 
   f32x4 acc[kDbAll];
 #pragma unroll
   for (int db = 0; db < kDbAll; ++db) acc[db] = zero_vec<f32x4>();
-  // P and dS operands of the group being multiplied, loaded one group ahead
-  // (before that group's gather, whose loads they would otherwise wait for)
+  // Issue order: P, dS of group 0, stages 0..2; then at the Q stage of group hg
+  // the P, dS operands of group hg+1 followed by stage 2hg+3, and at its dO
+  // stage stage 2hg+4.  Three stages are in flight ahead of the one multiplied.
+  // Before stage st is used, the operations issued after it (and, for a Q
+  // stage, after its group's operands) may still be in flight: two stages at a
+  // Q stage (one at the last), two stages and two operand loads at a dO stage
+  // (none at the last).
   bf16x8 pp = as_bf16x8(ld16(prow + 8 * g)), ps = as_bf16x8(ld16(prow + kH + 8 * g));
-  stage(0, 0);
+  stage(0);
+  stage(1);
+  stage(2);
+  // the products of one stage, transpose reads kAhead MFMAs ahead of their use
+  constexpr int kAhead = 3;
+  auto product = [&](uint32_t lds, const bf16x8 &op, auto nblk) {
+    constexpr int kN = decltype(nblk)::value;
+#pragma unroll
+    for (int db = 0; db < kN; ++db) {
+      const uint32_t off = ((db & 1) ? pv_odd : pv_even) + (db >> 1) * 64;
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)(lds + off));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)(lds + off + 16 * kRowStride));
+      acc[db] = mfma16_bf16(__builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)), op,
+                            acc[db]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 1);
+#pragma unroll
+    for (int i = 0; i < kN - kAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 1);
+  };
+#pragma unroll 1
   for (int hg = 0; hg < kH / 32; ++hg) {
-    const int bi = hg & 1;
-    // group hg (and its P, dS operands) landed for this wave; the barrier covers
-    // every wave's and orders the reads of group hg-1 before its buffer refills
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    const bool last = hg + 1 == kH / 32;
+    // the Q stage: it (and the operands) landed for this wave; the barrier covers
+    // every wave's and orders the reads of the stage before, whose buffer refills
+    wait_loads(last ? nloads : 2 * nloads);
     lds_barrier();
     const bf16x8 ppc = pp, psc = ps;
-    if (hg + 1 < kH / 32) {
+    if (!last) {
       pp = as_bf16x8(ld16(prow + 32 * (hg + 1) + 8 * g));
       ps = as_bf16x8(ld16(prow + kH + 32 * (hg + 1) + 8 * g));
-      stage(hg + 1, bi ^ 1);
+      stage(2 * hg + 3);
     }
-    if (!active) continue;
-    const uint32_t q_lds = lds_addr(&sbuf[bi][0]), o_lds = lds_addr(&sbuf[2 + bi][0]);
-#pragma unroll
-    for (int db = 0; db < kDbAll; ++db) {
-      const uint32_t off = ((db & 1) ? pv_odd : pv_even) + (db >> 1) * 64;
-      {
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)(q_lds + off));
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)(q_lds + off + 16 * kRowStride));
-        acc[db] = mfma16_bf16(__builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)), psc,
-                              acc[db]);
-      }
-      if (db < kDv / 16) {
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)(o_lds + off));
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)(o_lds + off + 16 * kRowStride));
-        acc[db] = mfma16_bf16(__builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)), ppc,
-                              acc[db]);
-      }
-    }
+    if (active) product(lds_addr(&sbuf[(2 * hg) & 3][0]), psc, std::integral_constant<int, kDbAll>());
+    // the dO stage
+    wait_loads(last ? 0 : 2 * nloads + 2);
+    lds_barrier();
+    if (2 * hg + 4 < kStages) stage(2 * hg + 4);
+    if (active) product(lds_addr(&sbuf[(2 * hg + 1) & 3][0]), ppc, std::integral_constant<int, kDv / 16>());
   }
   // bf16 rows (their sum per key stays fp32), staged through LDS: a wave's 16
   // rows are 18 KB in one piece of the row-gradient array, written with 16-byte
