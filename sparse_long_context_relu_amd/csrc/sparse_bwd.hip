@@ -295,6 +295,15 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(MlaBwdArgs a) {
         const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[db] = mfma16_bf16(av, pb, acc[db]);
       }
+      // the dS^T read and the transpose reads three MFMAs ahead of their use
+      constexpr int kAhead = 3;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead + 1, 1);
+#pragma unroll
+      for (int i = 0; i < kDbAll - kAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 1);
       cur = cur == 2 ? 0 : cur + 1;
     }
   }
