@@ -325,16 +325,23 @@ constexpr int kContribRows = 128;
 // loads in the tile layout (position p: row p/74, slot p%74, holding data
 // chunk slot ^ swz(row); pad slots load the row's first chunk, never read):
 // 37 loads of 64 lanes per array, five for waves 0..4 and four for 5..7.  The
-// arrays come in as eight stages (Q, then dO, of each group) through four
-// buffers, three stages ahead of the one being multiplied.
+// arrays come in as eight stages (Q, then dO, of each group) through three
+// buffers, two stages ahead of the one being multiplied.  Each stage also
+// brings the block's operand of its product into LDS (sm_scale dS of the
+// group's heads for a Q stage, P for a dO stage: 64 bytes per slot, one load
+// per wave), so that every load of the loop is one the explicit waits count.
 constexpr int kStageLoads = (kTileChunks + 63) / 64;   // 37
 constexpr int kStages = 2 * (kH / 32);
+constexpr int kStageBufs = 3;
+constexpr int kOpChunks = kContribRows * 64 / 16;      // 512: 128 slots x 32 heads x 2 bytes
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 
 __global__ __launch_bounds__(kThreads) void bwd_contrib_kernel(MlaBwdArgs a) {
-  // the staged Q and dO arrays; at the end the row gradients on their way out
-  __shared__ uint4 sbuf[4][kTileChunks];
+  // the staged Q and dO arrays and the operands of their products; at the end
+  // the row gradients on their way out
+  __shared__ uint4 sbuf[kStageBufs][kTileChunks];
+  __shared__ uint4 opbuf[kStageBufs][kOpChunks];
   // Workgroups are dealt to the 8 XCDs round-robin by linear id, each XCD with
   // its own L2.  When the rows divide by 8, XCD x takes rows x, x+8, ..., every
   // slot block of a row in turn, so a row's Q and dO come into one L2 once and
@@ -359,12 +366,17 @@ __global__ __launch_bounds__(kThreads) void bwd_contrib_kernel(MlaBwdArgs a) {
   const uint32_t pv_odd = pv_row + ((2 + (vc >> 1)) ^ g) * 16;
   const uint8_t *qsrc = reinterpret_cast<const uint8_t *>(a.q) + (long long)t * kH * (kD * 2);
   const uint8_t *osrc = reinterpret_cast<const uint8_t *>(a.dout) + (long long)t * kH * (kDv * 2);
-  const uint16_t *prow = a.pd + ((long long)r * a.k + (active ? jb + col : 0)) * (2 * kH);
+  // this wave's operand load: slot (wv * 64 + lane) / 4 of the block, 16-byte
+  // part lane % 4 of its 32 heads (slots past k read the last row, unused)
+  int oslot = bx * kContribRows + ((wv * 64 + lane) >> 2);
+  oslot = oslot < a.k ? oslot : a.k - 1;
+  const uint16_t *osl = a.pd + ((long long)r * a.k + oslot) * (2 * kH) + (lane & 3) * 8;
   const int nloads = wv < kStageLoads - 4 * kWaves ? 5 : 4;    // wave-uniform
-  // Stage st: Q (even st) or dO (odd st) of head group st / 2, into buffer st % 4.
+  // Stage st: Q (even st) or dO (odd st) of head group st / 2, and its
+  // product's operand, into buffer st % 3.
   auto stage = [&](int st) {
-    const int hg = st >> 1;
-    const uint32_t base = lds_addr(&sbuf[st & 3][0]);
+    const int hg = st >> 1, bi = st % kStageBufs;
+    const uint32_t base = lds_addr(&sbuf[bi][0]);
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
       if (j < nloads) {
@@ -377,33 +389,13 @@ __global__ __launch_bounds__(kThreads) void bwd_contrib_kernel(MlaBwdArgs a) {
           lds_dma16(osrc + (long long)(32 * hg + row) * (kDv * 2) + (ch < kDv / 8 ? ch ^ swz(row) : 0) * 16, m);
       }
     }
-  };
-  // Wait until at most n of this wave's vector-memory operations are in flight.
-  auto wait_loads = [&](int n) {
-    switch (n) {
-      case 0: __builtin_amdgcn_s_waitcnt(wait_vm(0)); break;
-      case 4: __builtin_amdgcn_s_waitcnt(wait_vm(4)); break;
-      case 5: __builtin_amdgcn_s_waitcnt(wait_vm(5)); break;
-      case 8: __builtin_amdgcn_s_waitcnt(wait_vm(8)); break;
-      case 10: __builtin_amdgcn_s_waitcnt(wait_vm(10)); break;
-      default: __builtin_amdgcn_s_waitcnt(wait_vm(12)); break;   // 12: 5 + 5 + 2
-    }
+    lds_dma16(osl + ((st & 1) == 0 ? kH : 0) + 32 * hg,
+              __builtin_amdgcn_readfirstlane(lds_addr(&opbuf[bi][0]) + wv * 1024));
   };
 
   f32x4 acc[kDbAll];
 #pragma unroll
   for (int db = 0; db < kDbAll; ++db) acc[db] = zero_vec<f32x4>();
-  // Issue order: P, dS of group 0, stages 0..2; then at the Q stage of group hg
-  // the P, dS operands of group hg+1 followed by stage 2hg+3, and at its dO
-  // stage stage 2hg+4.  Three stages are in flight ahead of the one multiplied.
-  // Before stage st is used, the operations issued after it (and, for a Q
-  // stage, after its group's operands) may still be in flight: two stages at a
-  // Q stage (one at the last), two stages and two operand loads at a dO stage
-  // (none at the last).
-  bf16x8 pp = as_bf16x8(ld16(prow + 8 * g)), ps = as_bf16x8(ld16(prow + kH + 8 * g));
-  stage(0);
-  stage(1);
-  stage(2);
   // the products of one stage, transpose reads kAhead MFMAs ahead of their use
   constexpr int kAhead = 3;
   auto product = [&](uint32_t lds, const bf16x8 &op, auto nblk) {
@@ -424,49 +416,70 @@ __global__ __launch_bounds__(kThreads) void bwd_contrib_kernel(MlaBwdArgs a) {
     }
     __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 1);
   };
+  // Stages 0 and 1, then at stage st stage st+2.  Before stage st is used, the
+  // stage issued after it (nloads + 1 loads) may still be in flight.
+  stage(0);
+  stage(1);
+  const uint32_t op_off = ((wv * 16 + col) * 4 + g) * 16;   // this lane's operand: slot jb + col, heads 8 g..
+  // stage st landed for this wave; the barrier covers every wave's and orders
+  // the reads of stage st-1 before its buffer refills
+  auto land = [&](int st) {
+    if (st + 1 < kStages) {
+      if (nloads == 5)
+        __builtin_amdgcn_s_waitcnt(wait_vm(6));
+      else
+        __builtin_amdgcn_s_waitcnt(wait_vm(5));
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    }
+    lds_barrier();
+    if (st + 2 < kStages) stage(st + 2);
+  };
+  auto operand = [&](int st) {
+    return __builtin_bit_cast(bf16x8, *(lds_u32x4 *)(uintptr_t)(lds_addr(&opbuf[st % kStageBufs][0]) + op_off));
+  };
 #pragma unroll 1
   for (int hg = 0; hg < kH / 32; ++hg) {
-    const bool last = hg + 1 == kH / 32;
-    // the Q stage: it (and the operands) landed for this wave; the barrier covers
-    // every wave's and orders the reads of the stage before, whose buffer refills
-    wait_loads(last ? nloads : 2 * nloads);
-    lds_barrier();
-    const bf16x8 ppc = pp, psc = ps;
-    if (!last) {
-      pp = as_bf16x8(ld16(prow + 32 * (hg + 1) + 8 * g));
-      ps = as_bf16x8(ld16(prow + kH + 32 * (hg + 1) + 8 * g));
-      stage(2 * hg + 3);
-    }
-    if (active) product(lds_addr(&sbuf[(2 * hg) & 3][0]), psc, std::integral_constant<int, kDbAll>());
-    // the dO stage
-    wait_loads(last ? 0 : 2 * nloads + 2);
-    lds_barrier();
-    if (2 * hg + 4 < kStages) stage(2 * hg + 4);
-    if (active) product(lds_addr(&sbuf[(2 * hg + 1) & 3][0]), ppc, std::integral_constant<int, kDv / 16>());
+    const int sq = 2 * hg, so = 2 * hg + 1;
+    land(sq);
+    if (active) product(lds_addr(&sbuf[sq % kStageBufs][0]), operand(sq), std::integral_constant<int, kDbAll>());
+    land(so);
+    if (active) product(lds_addr(&sbuf[so % kStageBufs][0]), operand(so), std::integral_constant<int, kDv / 16>());
   }
   // bf16 rows (their sum per key stays fp32), staged through LDS: a wave's 16
   // rows are 18 KB in one piece of the row-gradient array, written with 16-byte
   // stores, 1 KB per instruction (where the accumulator layout would give 32
-  // bytes of each of 16 rows per instruction).
+  // bytes of each of 16 rows per instruction); eight rows at a time.
   constexpr int kOutStride = kD * 2 + 16;      // LDS bytes per staged row (one pad chunk)
-  static_assert(kWaves * 16 * kOutStride <= 4 * kTileChunks * 16, "the staged rows fit the operand buffers");
-  lds_barrier();                               // every wave is done with the last group's operands
+  static_assert(kWaves * 8 * kOutStride <= kStageBufs * kTileChunks * 16, "the staged rows fit the operand buffers");
+  lds_barrier();                               // every wave is done with the last stage's operands
   if (!active) return;
-  const uint32_t stg = lds_addr(&sbuf[0][0]) + wv * 16 * kOutStride;
-#pragma unroll
-  for (int db = 0; db < kDbAll; ++db) {
-    u32x2 pk;
-    pk[0] = pack_bf16x2(acc[db][0], acc[db][1]);
-    pk[1] = pack_bf16x2(acc[db][2], acc[db][3]);
-    *(lds_u32x2 *)(uintptr_t)(stg + col * kOutStride + (16 * db + 4 * g) * 2) = pk;
-  }
+  const uint32_t stg = lds_addr(&sbuf[0][0]) + wv * 8 * kOutStride;
   uint8_t *dst = reinterpret_cast<uint8_t *>(a.contrib + ((long long)r * a.k + jb) * kD);
   constexpr int kRowPieces = kD * 2 / 16;      // 72 16-byte pieces per row
+  // The staged rows are written as 8-byte and read back as 16-byte vectors of
+  // another type: the empty asm statements with a memory clobber keep the
+  // compiler from reordering or merging those accesses (it would otherwise take
+  // the two types as never aliasing).
 #pragma unroll
-  for (int it = 0; it < 16 * kRowPieces / 64; ++it) {
-    const int c = it * 64 + lane, row = c / kRowPieces, w = c - row * kRowPieces;
-    const u32x4 v = *(lds_u32x4 *)(uintptr_t)(stg + row * kOutStride + w * 16);
-    st16(dst + c * 16, make_uint4(v[0], v[1], v[2], v[3]));
+  for (int half = 0; half < 2; ++half) {
+    asm volatile("" ::: "memory");
+    if ((col >> 3) == half) {
+#pragma unroll
+      for (int db = 0; db < kDbAll; ++db) {
+        u32x2 pk;
+        pk[0] = pack_bf16x2(acc[db][0], acc[db][1]);
+        pk[1] = pack_bf16x2(acc[db][2], acc[db][3]);
+        *(lds_u32x2 *)(uintptr_t)(stg + (col & 7) * kOutStride + (16 * db + 4 * g) * 2) = pk;
+      }
+    }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int it = 0; it < 8 * kRowPieces / 64; ++it) {
+      const int c = it * 64 + lane, row = c / kRowPieces, w = c - row * kRowPieces;
+      const u32x4 v = *(lds_u32x4 *)(uintptr_t)(stg + row * kOutStride + w * 16);
+      st16(dst + (half * 8 * kRowPieces + c) * 16, make_uint4(v[0], v[1], v[2], v[3]));
+    }
   }
 }
 
