@@ -88,12 +88,19 @@ __global__ __launch_bounds__(kKlThreads) void indexer_kl_rows_kernel(KlArgs a) {
 constexpr int kBwdHeads = 64;                      // H_I
 constexpr int kBwdDim = 128;                       // d_I
 constexpr int kBwdRowBytes = kBwdDim * 2;          // bf16 rows
-constexpr int kBwdStride = kBwdRowBytes + 16;      // LDS bytes per tile row (one pad chunk)
+// LDS tile rows: a 288-byte stride (two pad chunks) and the two halves of
+// each 32-byte pair of chunks swapped in rows 8..15 and 24..31 (chunk c of row
+// r at position c ^ bwd_swz(r)).  With that, the 16-byte reads of the first
+// product (16 rows, one chunk each) and the transpose reads of the second (4
+// rows x 32 bytes per 16 lanes) both hit distinct LDS banks; the plain 272-byte
+// stride left the transpose reads two-way conflicted.
+constexpr int kBwdStride = kBwdRowBytes + 32;
 constexpr int kBwdR = 32;                          // rows per tile
-constexpr int kBwdTileBytes = kBwdR * kBwdStride;  // 8704
+constexpr int kBwdTileBytes = kBwdR * kBwdStride;  // 9216
 constexpr int kBwdKs = kBwdDim / 32;               // k-steps of the first product
 constexpr int kBwdDb = kBwdDim / 16;               // 16-dim blocks of the second
 constexpr int kBwdQParts = kBwdHeads * kBwdDim + kBwdHeads;   // floats of one dq split partial (dq, dw)
+__device__ __forceinline__ int bwd_swz(int r) { return (r >> 3) & 1; }
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
@@ -108,7 +115,8 @@ __device__ __forceinline__ void tile_product(uint32_t tile, const bf16x8 (&op)[k
     st[rb] = zero_vec<f32x4>();
 #pragma unroll
     for (int ks = 0; ks < kBwdKs; ++ks) {
-      const u32x4 fr = *(lds_u32x4 *)(uintptr_t)(tile + (16 * rb + col) * kBwdStride + (4 * ks + g) * 16);
+      const u32x4 fr =
+          *(lds_u32x4 *)(uintptr_t)(tile + (16 * rb + col) * kBwdStride + (4 * ks + (g ^ bwd_swz(col))) * 16);
       st[rb] = mfma16_bf16(__builtin_bit_cast(bf16x8, fr), op[ks], st[rb]);
     }
   }
@@ -121,7 +129,7 @@ __device__ __forceinline__ void tile_product(uint32_t tile, const bf16x8 (&op)[k
 __device__ __forceinline__ void tile_accumulate(uint32_t tile, const bf16x8 &pb, f32x4 (&acc)[kBwdDb], int g,
                                                 int lane) {
   const int e = (lane & 15) >> 2, c = lane & 3;
-  const uint32_t lo = tile + (4 * g + e) * kBwdStride + 8 * c;
+  const uint32_t lo = tile + (4 * g + e) * kBwdStride + 16 * ((c >> 1) ^ bwd_swz(4 * g + e)) + 8 * (c & 1);
 #pragma unroll
   for (int db = 0; db < kBwdDb; ++db) {
     const v4s l4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)(lo + 32 * db));
@@ -198,7 +206,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     for (int u = 0; u < 2; ++u) {
       const int c = tid + 256 * u, row = c >> 4, ch = c & 15;
       const bool ok = sn >= 0 && tt * kBwdR + row < nk;
-      *reinterpret_cast<uint4 *>(&tiles[buf][row * kBwdStride + ch * 16]) = ok ? pf[u] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4 *>(&tiles[buf][row * kBwdStride + (ch ^ bwd_swz(row)) * 16]) =
+          ok ? pf[u] : make_uint4(0, 0, 0, 0);
     }
   };
 
@@ -324,7 +333,7 @@ __global__ __launch_bounds__(512) void indexer_bwd_k_kernel(BwdArgs a) {
     gkn = kp <= actpos[i >> 1] ? a.grad[(long long)q * a.ld + kp] : 0.f;
   };
   auto put = [&](int buf) {
-    *reinterpret_cast<uint4 *>(&tiles[buf][(tid >> 4) * kBwdStride + (tid & 15) * 16]) = pf;
+    *reinterpret_cast<uint4 *>(&tiles[buf][(tid >> 4) * kBwdStride + ((tid & 15) ^ bwd_swz(tid >> 4)) * 16]) = pf;
   };
 
   f32x4 acc[kBwdDb];
