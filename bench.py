@@ -470,7 +470,8 @@ def stage2_line(B, torch, inp, steps, settle_ms):
         mark(3)
         B.sparse_indexer_kl(pb, scores, idx, probs, loss=loss)
         mark(4)
-        B.indexer_backward(pb, inp.q_idx, inp.w, inp.k_cache, scores, dq=dqi, dw=dwi, dk=dki, ws=iws)
+        B.indexer_backward_selected(pb, inp.q_idx, inp.w, inp.k_cache, scores, idx, dq=dqi, dw=dwi, dk=dki,
+                                    ws=iws)
         mark(5)
 
     ms = time_op(torch, call, steps, 1, settle_ms)
@@ -487,7 +488,8 @@ def stage2_line(B, torch, inp, steps, settle_ms):
     f_fwd = f_idx + sel * H * 2 * (D + Dv)
     # per selected (query, row): the logits again, dP, dq, and the row's key and value gradients
     f_bwd = sel * H * 2 * (D + Dv + D + Dv + D)
-    f_ibwd = 4 * f_idx
+    # dq, dw over the selected pairs (two products each), dk over every causal pair (two products)
+    f_ibwd = 2 * f_idx + 2 * sel * wl.index_heads * 2 * wl.index_dim
     peak = MFMA_PEAK_TFLOPS["bf16"]
     frac = lambda f, t: round(f / (t * 1e-3) / 1e12 / peak, 4)
     contrib_bytes = 2 * sel * D * 2
@@ -495,7 +497,7 @@ def stage2_line(B, torch, inp, steps, settle_ms):
     torch.cuda.empty_cache()
     return {"workload": wl.name,
             "step": "dsa_forward + dsa_index_scores + dsa_sparse_mla_backward + dsa_sparse_indexer_kl + "
-                    "dsa_indexer_backward",
+                    "dsa_indexer_backward_selected",
             "ms_per_step": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
             "stages_ms": {"forward": round(st[0], 3), "index_scores": round(st[1], 3),
                           "attention_backward": round(st[2], 3), "sparse_kl": round(st[3], 3),

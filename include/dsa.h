@@ -321,6 +321,20 @@ int dsa_indexer_backward(const dsa_seqs *seqs, const dsa_dims *dims, const void 
                          const void *k_cache, const float *grad_scores, int64_t ld, float *dq_idx,
                          float *dw, float *dk, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* dsa_indexer_backward for a score gradient that is zero outside each query's
+ * selection [ZS 3.3 Stage 2: the indexer's loss is restricted to the selected
+ * set S_t, e.g. grad_scores from dsa_sparse_indexer_kl]: dq_idx and dw are
+ * summed over the entries s of topk_idx[t, 0..k) only (ascending positions as
+ * dsa_topk writes them; an entry outside [0, q_pos[t]] adds nothing), where
+ * dsa_indexer_backward visits every candidate; dk as dsa_indexer_backward.
+ * Equal to dsa_indexer_backward on such a gradient up to the fp32 order of the
+ * sums.  Same types, layouts and workspace (DSA_OP_INDEXER_BACKWARD); k as
+ * dsa_topk. */
+int dsa_indexer_backward_selected(const dsa_seqs *seqs, const dsa_dims *dims, const void *q_idx, const float *w,
+                                  const void *k_cache, const float *grad_scores, int64_t ld,
+                                  const int32_t *topk_idx, int32_t k, float *dq_idx, float *dw, float *dk, void *ws,
+                                  size_t ws_bytes, hipStream_t stream);
+
 /* The indexer's warm-up objective in one call [ZS 3.3 Stage 1; LD Objective
  * Functions]: dsa_attention_probs (target p, from args->lse when given),
  * dsa_index_scores (I),

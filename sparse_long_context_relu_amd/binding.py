@@ -27,7 +27,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH_LIMIT 
 
 EXPORTS = ("dsa_workspace_size", "dsa_index_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward",
            "dsa_forward_noalloc",
-           "dsa_dense_mla", "dsa_attention_probs", "dsa_indexer_kl", "dsa_indexer_backward", "dsa_indexer_kl_loss", "dsa_forward_chunk_rows",
+           "dsa_dense_mla", "dsa_attention_probs", "dsa_indexer_kl", "dsa_indexer_backward", "dsa_indexer_backward_selected", "dsa_indexer_kl_loss", "dsa_forward_chunk_rows",
            "dsa_quantize_fp8", "dsa_append_index_keys", "dsa_sparse_mla_backward", "dsa_sparse_indexer_kl",
            "dsa_read_ceiling", "dsa_status_string")
 
@@ -94,6 +94,8 @@ def _load() -> ctypes.CDLL:
     lib.dsa_indexer_kl.restype = ctypes.c_int
     lib.dsa_indexer_backward.argtypes = [sp, dp, P, P, P, P, I64, P, P, P, P, SZ, P]
     lib.dsa_indexer_backward.restype = ctypes.c_int
+    lib.dsa_indexer_backward_selected.argtypes = [sp, dp, P, P, P, P, I64, P, ctypes.c_int32, P, P, P, P, SZ, P]
+    lib.dsa_indexer_backward_selected.restype = ctypes.c_int
     lib.dsa_indexer_kl_loss.argtypes = [sp, dp, ctypes.POINTER(DsaKlArgs), P, SZ, P]
     lib.dsa_indexer_kl_loss.restype = ctypes.c_int
     lib.dsa_forward_chunk_rows.argtypes = [sp, dp]
@@ -308,6 +310,27 @@ def indexer_backward(pb: Problem, q_idx, w, k_cache, grad_scores, dq=None, dw=No
                                   _ptr(grad_scores), int(grad_scores.stride(0)), _ptr(dq), _ptr(dw), _ptr(dk),
                                   _ptr(ws), _nbytes(ws), _stream(stream))
     _check(st, "dsa_indexer_backward")
+    return dq, dw, dk
+
+
+def indexer_backward_selected(pb: Problem, q_idx, w, k_cache, grad_scores, topk_idx, dq=None, dw=None, dk=None,
+                              ws=None, stream=None):
+    """indexer_backward for a score gradient that is zero outside the selection
+    topk_idx [T, k]: dq, dw summed over the selected keys only; dk as indexer_backward."""
+    dev = q_idx.device
+    T, HI, DI = q_idx.shape
+    if dq is None:
+        dq = torch.empty((T, HI, DI), dtype=torch.float32, device=dev)
+    if dw is None:
+        dw = torch.empty((T, HI), dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.zeros(tuple(k_cache.shape), dtype=torch.float32, device=dev)
+    ws = _workspace(OP_INDEXER_BACKWARD, pb, ws, dev)
+    st = LIB.dsa_indexer_backward_selected(ctypes.byref(pb.seqs), ctypes.byref(pb.dims), _ptr(q_idx), _ptr(w),
+                                           _ptr(k_cache), _ptr(grad_scores), int(grad_scores.stride(0)),
+                                           _ptr(topk_idx), int(topk_idx.shape[1]), _ptr(dq), _ptr(dw), _ptr(dk),
+                                           _ptr(ws), _nbytes(ws), _stream(stream))
+    _check(st, "dsa_indexer_backward_selected")
     return dq, dw, dk
 
 

@@ -685,7 +685,47 @@ DSA_EXPORT int dsa_indexer_backward(const dsa_seqs *seqs, const dsa_dims *dims, 
   a.n_split = L.q_splits;
   a.q_per_split = L.q_per_split;
   a.part = reinterpret_cast<float *>(ws);
+  a.sel = nullptr;
+  a.sel_k = 0;
   if (launch_indexer_bwd_q(a, stream) != hipSuccess) return DSA_ERR_HIP;
+  a.n_split = L.k_qsplits;
+  a.part = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(ws) + L.off_k);
+  return hip_status(launch_indexer_bwd_k(a, stream));
+}
+
+DSA_EXPORT int dsa_indexer_backward_selected(const dsa_seqs *seqs, const dsa_dims *dims, const void *q_idx,
+                                             const float *w, const void *k_cache, const float *grad_scores,
+                                             int64_t ld, const int32_t *topk_idx, int32_t k, float *dq_idx,
+                                             float *dw, float *dk, void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (int e = check_seqs(seqs)) return e;
+  if (int e = check_bwd_dims(dims)) return e;
+  if (int e = check_k(k)) return e;
+  if (seqs->num_q == 0) return DSA_OK;
+  if (q_idx == nullptr || w == nullptr || k_cache == nullptr || grad_scores == nullptr || topk_idx == nullptr ||
+      ld < seqs->max_ctx)
+    return DSA_ERR_INVALID_ARG;
+  if (dq_idx == nullptr || dw == nullptr || dk == nullptr) return DSA_ERR_INVALID_ARG;
+  const BwdLayout L = bwd_layout(seqs);
+  if (int e = check_ws((size_t)L.total, ws, ws_bytes)) return e;
+  BwdArgs a;
+  a.sv = view(seqs);
+  a.q_begin = 0;
+  a.rows = seqs->num_q;
+  a.q_idx = q_idx;
+  a.w = w;
+  a.k_cache = k_cache;
+  a.grad = grad_scores;
+  a.ld = ld;
+  a.dq = dq_idx;
+  a.dw = dw;
+  a.dk = dk;
+  a.span = seqs->max_ctx;
+  a.sel = topk_idx;
+  a.sel_k = k;
+  a.n_split = 1;
+  a.q_per_split = L.q_per_split;
+  a.part = nullptr;
+  if (launch_indexer_bwd_q_sel(a, stream) != hipSuccess) return DSA_ERR_HIP;
   a.n_split = L.k_qsplits;
   a.part = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(ws) + L.off_k);
   return hip_status(launch_indexer_bwd_k(a, stream));

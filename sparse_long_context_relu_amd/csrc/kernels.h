@@ -134,6 +134,8 @@ struct BwdArgs {
   int n_split;              // dq: key splits per query; dk: query splits
   int q_per_split;          // dk: queries per split (prefill)
   float *part;              // split partials
+  const int32_t *sel;       // dq over a selection: [rows, sel_k] positions (ascending; -1 or out of range: none)
+  int sel_k;
 };
 
 // Stage-2 gradient of the sparse attention (bf16, H = 128, D = 576, Dv = 512),
@@ -195,6 +197,7 @@ hipError_t launch_sparse_mla(const MlaArgs &a, hipStream_t s);     // also the d
 hipError_t launch_indexer_kl(const KlArgs &a, hipStream_t s);
 hipError_t launch_indexer_bwd_q(const BwdArgs &a, hipStream_t s);   // dq, dw (+ split merge)
 hipError_t launch_indexer_bwd_k(const BwdArgs &a, hipStream_t s);   // dk (+ split merge)
+hipError_t launch_indexer_bwd_q_sel(const BwdArgs &a, hipStream_t s);   // dq, dw over the selected keys only
 constexpr int kBwdKeysPerBlock = 128;                                // keys per dk workgroup
 int bwd_q_splits(int rows, int span);                                // dq key splits per query
 hipError_t launch_sparse_mla_bwd(const MlaBwdArgs &a, hipStream_t s);   // one query chunk

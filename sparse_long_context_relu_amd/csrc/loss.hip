@@ -266,6 +266,115 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   if (g == 0) *dwo = dwa;
 }
 
+// dq, dw over the selected keys only (Stage 2: the score gradient is zero
+// outside each query's selection, so only those keys contribute): one query
+// per workgroup, tiles of 32 consecutive entries of its selection list;
+// otherwise the tile loop above.  The list's cache rows (through the block
+// table) and score gradients are gathered into LDS first, so a tile's loads
+// wait on no other global load.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void indexer_bwd_q_sel_kernel(
+    BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[2][kBwdTileBytes];
+  __shared__ uint32_t srow[kTopkMaxK];             // cache row of each entry (0xFFFFFFFF: absent)
+  __shared__ float sgrad[kTopkMaxK];               // its score gradient (0 when absent)
+  const int r = blockIdx.x;
+  const int t = a.q_begin + r;
+  const int n = a.sv.candidates(t);
+  const int b = a.sv.seq_of(t);
+  const int32_t *irow = a.sel + (long long)r * a.sel_k;
+  const int ntiles = (a.sel_k + kBwdR - 1) / kBwdR;
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6, g = lane >> 4, col = lane & 15;
+  const int h = wv * 16 + col;
+  const float *grow = a.grad + (long long)r * a.ld;
+  for (int j = tid; j < ntiles * kBwdR; j += 256) {
+    const int s = j < a.sel_k ? irow[j] : -1;
+    const long long sl = (s >= 0 && s < n) ? a.sv.slot(b, s) : -1;
+    srow[j] = sl >= 0 ? (uint32_t)sl : 0xFFFFFFFFu;
+    sgrad[j] = sl >= 0 ? grow[s] : 0.f;
+  }
+
+  bf16x8 qb[kBwdKs];
+  {
+    const uint8_t *qrow = reinterpret_cast<const uint8_t *>(a.q_idx) + ((long long)t * kBwdHeads + h) * kBwdRowBytes;
+#pragma unroll
+    for (int ks = 0; ks < kBwdKs; ++ks) qb[ks] = as_bf16x8(ld16(qrow + ks * 64 + g * 16));
+  }
+  const float wh = a.w[(long long)t * kBwdHeads + h];
+  const uint8_t *kbase = reinterpret_cast<const uint8_t *>(a.k_cache);
+  __syncthreads();
+
+  // Tile tt holds selection entries tt*32 .. + 31.  Thread tid loads chunks tid
+  // and tid + 256 (row c / 16, chunk c % 16), and the score gradients of the 8
+  // rows it holds in S^T; an absent entry gives a zero row and gradient.
+  uint4 pf[2];
+  float gn[8];
+  auto fetch = [&](int tt) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = tid + 256 * u, row = c >> 4, ch = c & 15;
+      const uint32_t sl = srow[tt * kBwdR + row];
+      pf[u] = sl != 0xFFFFFFFFu ? ld16(kbase + (unsigned long long)sl * kBwdRowBytes + ch * 16) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) gn[rb * 4 + v] = sgrad[tt * kBwdR + 16 * rb + 4 * g + v];
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = tid + 256 * u, row = c >> 4, ch = c & 15;
+      *reinterpret_cast<uint4 *>(&tiles[buf][row * kBwdStride + (ch ^ bwd_swz(row)) * 16]) = pf[u];
+    }
+  };
+
+  f32x4 acc[kBwdDb];
+#pragma unroll
+  for (int db = 0; db < kBwdDb; ++db) acc[db] = zero_vec<f32x4>();
+  float dwa = 0.f;
+  float gv[8];
+  if (ntiles > 0) {
+    fetch(0);
+    put(0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) gv[i] = gn[i];
+  }
+  __syncthreads();
+  for (int tt = 0; tt < ntiles; ++tt) {
+    const int cur = tt & 1;
+    float gc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) gc[i] = gv[i];
+    if (tt + 1 < ntiles) fetch(tt + 1);
+    const uint32_t tile = lds_addr(&tiles[cur][0]);
+    f32x4 st[2];
+    tile_product(tile, qb, st, g, col);
+    bf16x8 pb;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float x = st[rb][v], gx = gc[rb * 4 + v];
+        dwa = fmaf(gx, fmaxf(x, 0.f), dwa);
+        pb[rb * 4 + v] = (__bf16)(x > 0.f ? gx * wh : 0.f);
+      }
+    tile_accumulate(tile, pb, acc, g, lane);
+    if (tt + 1 < ntiles) {
+      put(cur ^ 1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) gv[i] = gn[i];
+    }
+    __syncthreads();
+  }
+  dwa += shfl_xor(dwa, 16);
+  dwa += shfl_xor(dwa, 32);
+  float *dqo = a.dq + ((long long)t * kBwdHeads + h) * kBwdDim;
+#pragma unroll
+  for (int db = 0; db < kBwdDb; ++db)
+    *reinterpret_cast<float4 *>(dqo + 16 * db + 4 * g) = make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+  if (g == 0) a.dw[(long long)t * kBwdHeads + h] = dwa;
+}
+
 // dq, dw of several key splits: summed in split order over the splits that
 // hold a key.
 __global__ __launch_bounds__(256) void indexer_bwd_q_merge_kernel(BwdArgs a) {
@@ -437,6 +546,12 @@ hipError_t launch_indexer_bwd_q(const BwdArgs &a, hipStream_t st) {
   if (a.n_split > 1)
     hipLaunchKernelGGL(indexer_bwd_q_merge_kernel, dim3((kBwdQParts + 255) / 256, (unsigned)a.rows), dim3(256), 0, st,
                        a);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_bwd_q_sel(const BwdArgs &a, hipStream_t st) {
+  if (a.rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(indexer_bwd_q_sel_kernel, dim3((unsigned)a.rows), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -207,6 +207,12 @@ def test_warmup_objective_validation_and_workspace():
     bw = lambda **kw: L.dsa_indexer_backward(sp, dp, *[kw.get(k, FAKE) for k in ("q", "w", "k", "g")], 4096,
                                              *[kw.get(k, FAKE) for k in ("dq", "dw", "dk")], FAKE, 1 << 40, None)
     assert bw(dk=None) == B.ERR_INVALID_ARG and bw(g=None) == B.ERR_INVALID_ARG
+    # the same over a selection: the list is required and k is checked like dsa_topk's
+    bs = lambda sel=FAKE, k=2048, **kw: L.dsa_indexer_backward_selected(
+        sp, dp, *[kw.get(n, FAKE) for n in ("q", "w", "k", "g")], 4096, sel, k,
+        *[kw.get(n, FAKE) for n in ("dq", "dw", "dk")], FAKE, 1 << 40, None)
+    assert bs(sel=None) == B.ERR_INVALID_ARG and bs(dq=None) == B.ERR_INVALID_ARG and bs(g=None) == B.ERR_INVALID_ARG
+    assert bs(k=0) != B.OK and bs(k=-16) != B.OK
     fp8 = B.make_problem(mode="prefill", q_pos=qp, max_ctx=4096, num_seqs=1, max_seq_len=4096,
                          index_dtype=B.FP8_E4M3FN)
     assert L.dsa_indexer_backward(ctypes.byref(fp8.seqs), ctypes.byref(fp8.dims), FAKE, FAKE, FAKE, FAKE, 4096, FAKE,

@@ -170,7 +170,12 @@ def test_sparse_indexer_kl():
     oi = to_oracle(inp)
     ref = oracle.sparse_indexer_kl_loss(oi, selections=[ig[t][ig[t] >= 0] for t in range(inp.num_q)])
     assert np.max(np.abs(L - ref["loss"]) / np.maximum(np.abs(ref["loss"]), 1e-3)) <= 1e-3
+    # the same gradients summed over the selected keys only
+    dqs, dws, dks = B().indexer_backward_selected(pb, inp.q_idx, inp.w, inp.k_cache, scores, idx)
+    torch.cuda.synchronize()
+    assert torch.equal(dks, dki)                  # dk: the same kernel on the same gradient
     dqg, dwg = dqi.cpu().numpy(), dwi.cpu().numpy()
+    dqsg, dwsg = dqs.cpu().numpy(), dws.cpu().numpy()
     Gd = G.astype(np.float64)
     for t in range(inp.num_q):
         q_t, w_t, keys = oracle.query_index_operands(oi, t)
@@ -178,8 +183,43 @@ def test_sparse_indexer_kl():
         dq_r, dw_r, _, dq_b, dw_b, _, _ = _bwd_with_bounds(q_t, w_t, keys, Gd[t, :n])
         _check_within(dqg[t], dq_r, dq_b, f"stage-2 indexer dq of query {t}")
         _check_within(dwg[t], dw_r, dw_b, f"stage-2 indexer dw of query {t}")
+        _check_within(dqsg[t], dq_r, dq_b, f"stage-2 indexer dq over the selection, query {t}")
+        _check_within(dwsg[t], dw_r, dw_b, f"stage-2 indexer dw over the selection, query {t}")
     assert _rel_rms(dqg, ref["dq"]) <= 2e-2 and _rel_rms(dwg, ref["dw"]) <= 1e-3
+    assert _rel_rms(dqsg, ref["dq"]) <= 2e-2 and _rel_rms(dwsg, ref["dw"]) <= 1e-3
     assert _rel_rms(dki.cpu().numpy(), ref["dk"]) <= 2e-2
+
+
+def test_indexer_backward_selected_decode_paged():
+    """dq, dw over the selection on a paged decode batch (rows shorter than k, a
+    one-token row, a row of exactly k) for a score gradient that is random on
+    the selected positions and zero elsewhere: element by element against the
+    oracle's gradient bound, dk equal to dsa_indexer_backward's."""
+    _say("indexer_backward_selected decode paged")
+    inp = generate(big_dims(mode="decode", num_seqs=5, length=3000, k=2048, paged=True, w_low=-1 / 8), DEV,
+                   lengths=[3000, 2100, 2048, 700, 1])
+    pb = B().problem_from_inputs(inp)
+    _, _, idx = B().forward_inputs(inp)
+    torch.cuda.synchronize()
+    ig = idx.cpu().numpy()
+    rng = np.random.default_rng(5)
+    G = np.zeros((inp.num_q, pb.seqs.max_ctx), np.float32)
+    for t in range(inp.num_q):
+        sel = ig[t][ig[t] >= 0]
+        G[t, sel] = rng.standard_normal(sel.shape[0]).astype(np.float32) * 1e-3
+    grad = torch.from_numpy(G).to(DEV)
+    dqi, dwi, dki = B().indexer_backward(pb, inp.q_idx, inp.w, inp.k_cache, grad)
+    dqs, dws, dks = B().indexer_backward_selected(pb, inp.q_idx, inp.w, inp.k_cache, grad, idx)
+    torch.cuda.synchronize()
+    assert torch.equal(dks, dki)
+    oi = to_oracle(inp)
+    dqsg, dwsg = dqs.cpu().numpy(), dws.cpu().numpy()
+    for t in range(inp.num_q):
+        q_t, w_t, keys = oracle.query_index_operands(oi, t)
+        n = keys.shape[0]
+        dq_r, dw_r, _, dq_b, dw_b, _, _ = _bwd_with_bounds(q_t, w_t, keys, G[t, :n].astype(np.float64))
+        _check_within(dqsg[t], dq_r, dq_b, f"dq over the selection, query {t}")
+        _check_within(dwsg[t], dw_r, dw_b, f"dw over the selection, query {t}")
 
 
 def test_stage2_full_size():
