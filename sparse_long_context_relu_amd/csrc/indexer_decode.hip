@@ -23,6 +23,28 @@ constexpr int kDecodeChunk = 2048;
 constexpr int kDecodeMinChunk = 256;
 constexpr int kDecodeMinGrid = 1024;
 
+// Length-balanced decode grid (at most kBalRows rows, no -inf fill).  With
+// ragged contexts the fixed grid leaves a partial last round of workgroups on
+// the chip (U[32K, 128K] contexts: ~1118 chunks of 2048 keys on 512 slots,
+// 2.18 rounds).  Instead the batch is cut into about G = slots * round(K /
+// (slots * 2048)) workgroups (at least `slots`), K the total candidate count:
+// row r gets g_r = max(1, floor(n_r G / K)) of them (at most G + 2 rows in all,
+// allowing one unit of fp64 rounding per row),
+// each a 64-aligned chunk of ceil(n_r / g_r) keys, so the grid runs in whole
+// rounds, and a batch of equal rows gets the fixed grid's chunks.  Every wave
+// computes this schedule from the rows' candidate counts itself.  A chunk
+// stays below kBlk0 * 64 keys: n_r / g_r < 2 K / G and K / G < 3072.
+constexpr int kBalRows = 256;
+constexpr int kBalTarget = 2048;
+constexpr int kBlk0 = 128;                    // 64-token block entries a chunk may span
+
+// keys < 2^40 and slots * kBalTarget < 2^31: the fp64 quotient floors exactly
+__host__ __device__ inline long long bal_grid(long long keys, int slots) {
+  const long long rounds = (long long)floor((double)(keys + (long long)slots * (kBalTarget / 2)) /
+                                            (double)((long long)slots * kBalTarget));
+  return (long long)slots * (rounds > 1 ? rounds : 1);
+}
+
 // ------------------------------------------------------------------ decode tiling
 //
 // Each wave owns 8 KB tiles: 32 bf16 keys or 64 e4m3fn keys, contiguous
@@ -46,12 +68,77 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ uint4 wtile[kDecodeWaves][kTileKeys * kChunks];
   __shared__ uint32_t lh[kTopkBins];
 
-  const int r = blockIdx.y;
+  int r, chunk, c0, n;
+  if (a.balanced) {
+    // Schedule of the length-balanced grid, computed by every wave on its own
+    // (no barrier, no LDS): lane l holds rows rpl*l .. rpl*l + rpl - 1, rpl =
+    // ceil(rows / 64) <= 4.  The divisions run in fp64 (a 64-bit integer
+    // division is a long instruction sequence here); every quotient they give
+    // is a well-separated integer quotient (below 2^31, divisors below 2^31),
+    // and the workgroup count of a row is fixed up in integers so that its
+    // chunks tile [0, n_r) exactly.
+    const int ln = lane_id();
+    const int rpl = (a.rows + 63) >> 6;
+    int nr[4];
+    long long k = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = rpl * ln + j;
+      nr[j] = j < rpl && row < a.rows ? a.sv.candidates(a.q_begin + row) : 0;
+      k += nr[j];
+    }
+    for (int m = 32; m >= 1; m >>= 1) k += __shfl_xor(k, m, 64);
+    if (k == 0) return;
+    const long long G = bal_grid(k, a.slots);
+    const double share = (double)G / (double)k;
+    int cj[4], mj[4], local = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      cj[j] = mj[j] = 0;
+      if (j < rpl && nr[j] > 0) {
+        const double gd = floor((double)nr[j] * share);
+        const int g = gd > 1.0 ? (int)gd : 1;
+        const int c = (int)ceil((double)nr[j] / (double)g);
+        cj[j] = (c + 63) & ~63;
+        int m = (int)ceil((double)nr[j] / (double)cj[j]);
+        if ((long long)m * cj[j] < nr[j]) ++m;
+        if (m > 1 && (long long)(m - 1) * cj[j] >= nr[j]) --m;
+        mj[j] = m;
+      }
+      local += mj[j];
+    }
+    int x = local;                               // inclusive prefix of the counts over the lanes
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      if (ln >= d) x += y;
+    }
+    int first = x - local, hit = -1, hc = 0, hc0 = 0, hn = 0;
+    const int id = (int)blockIdx.x;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (mj[j] > 0 && id >= first && id < first + mj[j]) {
+        hit = rpl * ln + j;
+        hc = cj[j];
+        hc0 = (id - first) * cj[j];
+        hn = nr[j];
+      }
+      first += mj[j];
+    }
+    const unsigned long long owner = __ballot(hit >= 0);
+    if (owner == 0) return;                      // past the last row's workgroups
+    const int src = __builtin_amdgcn_readfirstlane(__ffsll((long long)owner) - 1);
+    r = __builtin_amdgcn_readlane(hit, src);
+    chunk = __builtin_amdgcn_readlane(hc, src);
+    c0 = __builtin_amdgcn_readlane(hc0, src);
+    n = __builtin_amdgcn_readlane(hn, src);
+  } else {
+    r = blockIdx.y;
+    chunk = a.chunk;
+    c0 = blockIdx.x * chunk;
+    n = a.sv.candidates(a.q_begin + r);
+  }
   const int t = a.q_begin + r;
-  const int n = a.sv.candidates(t);
   const int b = a.sv.seq_of(t);
-  const int chunk = a.chunk;
-  const int c0 = blockIdx.x * chunk;
   float *srow = a.scores + (long long)r * a.ld;
   const long long cend = c0 + chunk < a.ld ? c0 + chunk : a.ld;
   if (a.fill_masked) {
@@ -77,7 +164,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // on the vector-memory counter (which also counts the score stores in flight).
   // Only the raw entry is loaded here; it is checked after the tile loads are
   // issued, so that no wait is placed before them.
-  __shared__ long long blk0[kDecodeChunk / 64];
+  __shared__ long long blk0[kBlk0];
   const int my_s = c0 + (int)threadIdx.x * 64;
   const bool my_fill = threadIdx.x < chunk / 64 && my_s < c1;
   int my_raw = 0;
@@ -158,7 +245,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bool hist = a.hist_mode == 1;
   if (hist)
     for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) lh[i] = 0u;
-  if (threadIdx.x < kDecodeChunk / 64) {
+  if (threadIdx.x < kBlk0) {
     long long v = -1;
     if (my_fill) {
       if (a.sv.block_table == nullptr)
@@ -256,9 +343,34 @@ hipError_t launch_index_decode(const IndexerArgs &a, hipStream_t st) {
   const long long span = a.fill_masked ? a.ld : a.sv.max_ctx;
   IndexerArgs b = a;
   b.chunk = kDecodeChunk;
-  while (b.chunk > kDecodeMinChunk && (long long)a.rows * ((span + b.chunk - 1) / b.chunk) < kDecodeMinGrid)
-    b.chunk >>= 1;
-  dim3 grid((unsigned)((span + b.chunk - 1) / b.chunk), (unsigned)a.rows);
+  b.balanced = 0;
+  b.slots = 0;
+  dim3 grid;
+  // Two workgroups per CU run at once (two waves per SIMD, four-wave groups).
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (cus[dev] == 0) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+      return hipErrorInvalidDevice;
+    cus[dev] = c;
+  }
+  // The schedule costs each workgroup one dependent load of the rows' counts
+  // before its first tile (about 2 us on a 16 x 8K batch, one round of 512
+  // workgroups); it is taken where the fixed grid would need two rounds or more.
+  const long long fixed_wgs = (long long)a.rows * ((span + kDecodeChunk - 1) / kDecodeChunk);
+  if (!a.fill_masked && a.rows <= kBalRows && fixed_wgs >= 4LL * cus[dev]) {
+    b.balanced = 1;
+    b.slots = 2 * cus[dev];
+    // the workgroups' own G never exceeds the first term (K <= rows * max_ctx, bal_grid is
+    // monotone), and the rows' counts sum to at most G + 2 rows
+    grid = dim3((unsigned)(bal_grid((long long)a.rows * span, b.slots) + 2 * a.rows), 1u);
+  } else {
+    while (b.chunk > kDecodeMinChunk && (long long)a.rows * ((span + b.chunk - 1) / b.chunk) < kDecodeMinGrid)
+      b.chunk >>= 1;
+    grid = dim3((unsigned)((span + b.chunk - 1) / b.chunk), (unsigned)a.rows);
+  }
   if (a.dtype == DSA_BF16)
     hipLaunchKernelGGL(indexer_decode_kernel<DSA_BF16>, grid, dim3(256), 0, st, b);
   else

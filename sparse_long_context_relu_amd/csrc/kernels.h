@@ -31,6 +31,11 @@ struct IndexerArgs {
   long long hist_stride;
   int hist_mode;
   int chunk;        // decode tiling: candidate keys per workgroup (set by its launcher)
+  // decode tiling, set by its launcher: 1 when each workgroup derives its row
+  // and key range from the candidate counts of all rows (a grid of G_max
+  // workgroups, `slots` of which run at once); 0 for the fixed row x chunk grid
+  int balanced;
+  int slots;
 };
 
 struct TopkArgs {

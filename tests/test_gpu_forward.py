@@ -181,3 +181,44 @@ def test_empty_and_single_candidate():
     assert torch.all(idx[2] == -1) and torch.all(out[2] == 0) and torch.all(torch.isneginf(lse[2]))
     assert int(idx[1, 0]) == 0 and torch.all(idx[1, 1:] == -1)
     assert torch.equal(out[1], inp.kv_cache[1, 0, :512].expand(128, 512))
+
+
+# 16 queries with up to 131072 candidates: the fixed decode grid would be 16 x 64
+# chunks (two rounds or more of the chip's 512 workgroup slots), so the fused
+# forward's indexer takes the length-balanced grid (a row's workgroups in
+# proportion to its candidates, 64-aligned chunks); the standalone index_scores
+# op, which also writes -inf past each row's candidates, keeps the fixed grid.
+BALANCED_LENGTHS = [131072, 1, 63, 64, 65, 2047, 2048, 2049, 70001, 100000, 4096, 129, 50000, 131071, 8191, 30000]
+
+
+@pytest.mark.parametrize("index_dtype", ["bf16", "fp8"])
+def test_forward_balanced_decode_grid(index_dtype):
+    """Ragged decode batch on the length-balanced indexer grid (a row with no
+    candidates, rows of 1, 63-65, 2047-2049 and up to 131072 candidates): the same
+    bits as the staged ops on the fixed grid (key tiles start on 32-key boundaries
+    in both, so each score is the same arithmetic), and every row against the
+    oracle."""
+    _say("forward balanced grid", index_dtype)
+    kw = dict(mode="decode", num_seqs=len(BALANCED_LENGTHS), length=max(BALANCED_LENGTHS), k=2048, paged=True,
+              index_dtype=index_dtype)
+    inp = generate(big_dims(**kw), DEV, lengths=BALANCED_LENGTHS)
+    inp.q_pos[1] = -1                                 # no candidates
+    out, lse, idx = run_forward(inp)
+    pb = B().problem_from_inputs(inp)
+    sc = B().index_scores(pb, inp.q_idx, inp.q_scale, inp.w, inp.k_cache, inp.k_scale)
+    idx2 = B().topk(pb, sc)
+    out2, lse2 = B().sparse_mla(pb, inp.sm_scale, inp.q, inp.kv_cache, idx2)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    assert torch.all(idx[1] == -1) and torch.all(torch.isneginf(lse[1]))
+    oi = to_oracle(inp)
+    ig, og, lg = idx.cpu().numpy(), out.float().cpu().numpy(), lse.cpu().numpy()
+    for t in range(inp.num_q):
+        if t == 1:
+            continue
+        scores = oracle.query_index_scores(oi, t)
+        check_topk_row_e2e(ig[t], scores, inp.topk, f"balanced {index_dtype} row {t}")
+        m = min(inp.topk, scores.shape[0])
+        o_ref, l_ref = oracle.query_attention(oi, t, ig[t, :m])
+        check_attention(og[t], lg[t], o_ref, l_ref, OUT_TOL[inp.wl.mla_dtype], f"balanced {index_dtype} row {t}")
